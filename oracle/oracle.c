@@ -1,0 +1,421 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for the fused QK / KV
+ * RMSNorm + RoPE (+ cache) operators.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do. It shares no code, header, table or helper with the HIP
+ * kernels.
+ *
+ * Sources (cited by page title and section; the pages are described in
+ * the design doc):
+ *   [qkv_cte]  "Kernel reference: qkv_cte -- Wan2.2 additions to the NKI Library
+ *              QKV CTE MXFP8 projection", Design section 1 (across-heads QK
+ *              RMSNorm, steps a-c) and section 2 (bundled rotate-half RoPE,
+ *              its `out = ...` expression and the lane pairing (i, i+d/2)).
+ *   [CP]       "Context Parallelism in vLLM Omni Neuron", the WanSelfAttention
+ *              forward listing (norm_q / norm_k before the rotary embedding)
+ *              and "Distributed Normalization".
+ *   [KVRNRC]   "KvRmsNormRopeCache" (CANN ops-transformer), section
+ *              "function description -> formulas" (1) RmsNorm, (2) interleaveRope,
+ *              (3) quantisation, (4) scatter, (5) raw outputs; the parameter
+ *              table; the constraint tables for cache_mode / index.
+ *
+ * Everything is evaluated in IEEE double on the exactly decoded inputs and
+ * rounded once at the end. Readings of points the pages leave open are listed
+ * in DESIGN.md ("Readings of the pages").
+ *
+ * Every function here is pinned by tests/test_oracle_pins.py against closed
+ * forms, hand cases, library special cases and an independent pure-Python
+ * brute force.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* storage type codes used by the oracle's own wrapper (oracle/__init__.py) */
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2, ORC_F16 = 3, ORC_INT8 = 4, ORC_E4M3FN = 5 };
+enum { ORC_NORM = 0, ORC_PA_BNSD = 1 };
+
+/* ------------------------------------------------------------------------ */
+/* Format definitions: decode (exact) and encode (round to nearest, ties to  */
+/* even, written from the format definitions with frexp/ldexp/nearbyint).   */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 = the upper 16 bits of an IEEE binary32 */
+static double dec_bf16(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits */
+static double dec_f16(uint16_t h) {
+    int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp(1024.0 + m, e - 25);
+    return s ? -v : v;
+}
+
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa; no inf; S.1111.111 is NaN */
+static double dec_e4m3fn(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp(8.0 + m, e - 10);
+    return s ? -v : v;
+}
+
+/*
+ * Round |x| to a binary format with `p` significant bits, minimum normal
+ * exponent `emin` (value 2^emin) and subnormals spaced 2^(emin-p+1):
+ * the quantum of the binade that holds |x| is 2^(E-p+1), E = floor(log2|x|),
+ * floored at the subnormal quantum. nearbyint rounds half to even in the
+ * default rounding mode.
+ */
+static double round_to_format(double a, int p, int emin) {
+    if (a == 0.0) return 0.0;
+    int e;
+    frexp(a, &e);              /* a = m * 2^e, m in [0.5, 1) -> E = e - 1 */
+    int E = e - 1;
+    if (E < emin) E = emin;
+    double q = ldexp(1.0, E - p + 1);
+    return nearbyint(a / q) * q;
+}
+
+static uint16_t enc_bf16(double x) {
+    if (isnan(x)) return 0x7FC0;
+    double a = fabs(x);
+    double r = round_to_format(a, 8, -126);
+    uint16_t s = signbit(x) ? 0x8000 : 0;
+    /* largest finite bf16 is (2 - 2^-7) * 2^127; a value rounding past it is inf */
+    if (r > ldexp(255.0, 120)) return s | 0x7F80;
+    float f = (float)r;        /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return s | (uint16_t)(u >> 16);
+}
+
+static uint16_t enc_f16(double x) {
+    if (isnan(x)) return 0x7E00;
+    double a = fabs(x);
+    double r = round_to_format(a, 11, -14);
+    uint16_t s = signbit(x) ? 0x8000 : 0;
+    if (r > 65504.0) return s | 0x7C00;
+    if (r < ldexp(1.0, -14)) return s | (uint16_t)(r / ldexp(1.0, -24));  /* subnormal field */
+    int e;
+    double m = frexp(r, &e);   /* r = m * 2^e, m in [0.5,1) */
+    int E = e - 1;
+    uint16_t mant = (uint16_t)((m * 2.0 - 1.0) * 1024.0);
+    return s | (uint16_t)((E + 15) << 10) | mant;
+}
+
+/* saturating E4M3FN encoder: |x| at or above the largest finite (448) -> 448 */
+static uint8_t enc_e4m3fn(double x) {
+    if (isnan(x)) return 0x7F;
+    uint8_t s = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a >= 448.0) return s | 0x7E;
+    double r = round_to_format(a, 4, -6);
+    if (r >= 448.0) return s | 0x7E;
+    if (r < ldexp(1.0, -6)) return s | (uint8_t)(r / ldexp(1.0, -9));   /* subnormal field */
+    int e;
+    double m = frexp(r, &e);
+    int E = e - 1;
+    uint8_t mant = (uint8_t)((m * 2.0 - 1.0) * 8.0);
+    return s | (uint8_t)((E + 7) << 3) | mant;
+}
+
+static double load(int dtype, const void *p, int64_t i) {
+    switch (dtype) {
+    case ORC_F64: return ((const double *)p)[i];
+    case ORC_F32: return (double)((const float *)p)[i];
+    case ORC_BF16: return dec_bf16(((const uint16_t *)p)[i]);
+    case ORC_F16: return dec_f16(((const uint16_t *)p)[i]);
+    case ORC_INT8: return (double)((const int8_t *)p)[i];
+    case ORC_E4M3FN: return dec_e4m3fn(((const uint8_t *)p)[i]);
+    }
+    return NAN;
+}
+
+/* Round once from the exact value to the storage type (RNE). */
+static void store(int dtype, void *p, int64_t i, double v) {
+    switch (dtype) {
+    case ORC_F64: ((double *)p)[i] = v; break;
+    case ORC_F32: ((float *)p)[i] = (float)v; break;     /* IEEE cast: RNE */
+    case ORC_BF16: ((uint16_t *)p)[i] = enc_bf16(v); break;
+    case ORC_F16: ((uint16_t *)p)[i] = enc_f16(v); break;
+    default: break;
+    }
+}
+
+/* exported codec entry points (pinned by the codebook tests) */
+void oracle_decode(int dtype, const void *src, double *dst, int64_t n) {
+    for (int64_t i = 0; i < n; i++) dst[i] = load(dtype, src, i);
+}
+
+void oracle_encode(int dtype, const double *src, void *dst, int64_t n) {
+    for (int64_t i = 0; i < n; i++) {
+        if (dtype == ORC_E4M3FN) ((uint8_t *)dst)[i] = enc_e4m3fn(src[i]);
+        else store(dtype, dst, i, src[i]);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* (a) across-heads RMSNorm + rotate-half RoPE                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One segment (all heads of Q, or all heads of K) of one token.
+ *
+ * [qkv_cte] section 1: one RMS over the whole segment of n_heads*d_head
+ * channels (step b: inv_rms = 1/sqrt(sum(x^2)/(n_heads*d_head*tp) + eps) with
+ * tp = 1, all heads resident), then the per-channel segment-wide gamma
+ * (step c). [CP] forward listing: the norm runs before the rotary embedding.
+ * [qkv_cte] section 2: rotate-half RoPE per head, lanes i and i+d/2 paired,
+ * out = y*cos + [-y_hi, y_lo]*sin with cos/sin indexed by the output lane
+ * and shared by every head of the token. Folding inv_rms into the cos/sin
+ * products is an evaluation order, not a different result, so the
+ * definition is written here as norm-then-rotate.
+ */
+static void across_heads_segment(int64_t nh, int64_t d, int dtype,
+                                 const void *x, int64_t x0,
+                                 const void *gamma, const void *cs, const void *sn,
+                                 int64_t r0, double eps, int apply_norm,
+                                 int apply_rope, double *y, double *out) {
+    int64_t C = nh * d, h2 = d / 2;
+    double inv_rms = 1.0;
+    if (apply_norm) {
+        double ss = 0.0;
+        for (int64_t c = 0; c < C; c++) {
+            double v = load(dtype, x, x0 + c);
+            ss += v * v;
+        }
+        inv_rms = 1.0 / sqrt(ss / (double)C + eps);
+    }
+    for (int64_t c = 0; c < C; c++) {
+        double v = load(dtype, x, x0 + c);
+        y[c] = apply_norm ? v * inv_rms * load(dtype, gamma, c) : v;
+    }
+    for (int64_t h = 0; h < nh; h++) {
+        const double *yh = y + h * d;
+        double *oh = out + h * d;
+        for (int64_t i = 0; i < d; i++) {
+            if (!apply_rope) {
+                oh[i] = yh[i];
+                continue;
+            }
+            double rot = (i < h2) ? -yh[i + h2] : yh[i - h2];    /* [-y_hi, y_lo] */
+            oh[i] = yh[i] * load(dtype, cs, r0 + i) + rot * load(dtype, sn, r0 + i);
+        }
+    }
+}
+
+/*
+ * q: [T, n_q*d], k: [T, n_k*d] (NULL when n_k == 0), contiguous rows;
+ * q_gamma [n_q*d], k_gamma [n_k*d]; cos/sin [T, d]. Writes q_out/k_out in
+ * `dtype` (rounded once) and, if given, the exact results q_val/k_val.
+ * Returns 0, or -1 on bad dimensions.
+ */
+int oracle_qk_norm_rope_across_heads(int64_t T, int64_t n_q, int64_t n_k, int64_t d,
+                                     int dtype, const void *q, const void *k,
+                                     const void *q_gamma, const void *k_gamma,
+                                     const void *cs, const void *sn, double eps,
+                                     int apply_norm, int apply_rope, void *q_out,
+                                     void *k_out, double *q_val, double *k_val,
+                                     int nthreads) {
+    if (T < 0 || n_q < 1 || n_k < 0 || d < 2 || (d & 1)) return -1;
+    int64_t cq = n_q * d, ck = n_k * d;
+    int64_t cmax = cq > ck ? cq : ck;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *y = (double *)malloc(sizeof(double) * cmax);
+        double *o = (double *)malloc(sizeof(double) * cmax);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; t++) {
+            for (int seg = 0; seg < 2; seg++) {
+                int64_t nh = seg == 0 ? n_q : n_k;
+                if (nh == 0) continue;
+                int64_t C = nh * d;
+                const void *x = seg == 0 ? q : k;
+                const void *g = seg == 0 ? q_gamma : k_gamma;
+                void *dst = seg == 0 ? q_out : k_out;
+                double *val = seg == 0 ? q_val : k_val;
+                across_heads_segment(nh, d, dtype, x, t * C, g, cs, sn, t * d, eps,
+                                     apply_norm, apply_rope, y, o);
+                for (int64_t c = 0; c < C; c++) {
+                    if (dst) store(dtype, dst, t * C + c, o[c]);
+                    if (val) val[t * C + c] = o[c];
+                }
+            }
+        }
+        free(y);
+        free(o);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* (b) KvRmsNormRopeCache                                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [KVRNRC] formula (3): x*scale if a scale is given, then +offset if an
+ * offset is given; with any quantisation the value is rounded (half to even,
+ * as torch.round does) and clamped to [-128, 127] for INT8. For FLOAT8E4M3FN
+ * the pages give no separate formula; the value is cast to E4M3FN with round
+ * to nearest even, saturating at +-448. The rounding decision is taken on the
+ * fp32 value of t, the precision the GPU kernel computes t in.
+ * Returns t (the exact pre-rounding value) and writes the code.
+ */
+static double quantise(int cdtype, void *cache, int64_t pos, double x,
+                       const double *scale, const double *offset, int64_t qi) {
+    double t = x;
+    if (scale) t = t * scale[qi];
+    if (offset) t = t + offset[qi];
+    if (cdtype == ORC_INT8) {
+        double r = nearbyint((double)(float)t);
+        if (r < -128.0) r = -128.0;
+        if (r > 127.0) r = 127.0;
+        ((int8_t *)cache)[pos] = (int8_t)r;
+    } else if (cdtype == ORC_E4M3FN) {
+        ((uint8_t *)cache)[pos] = enc_e4m3fn((double)(float)t);
+    } else {
+        store(cdtype, cache, pos, t);
+    }
+    return t;
+}
+
+/*
+ * Dimensions (the parameter table and the V1/V2 scenario table of [KVRNRC]):
+ *   kv [B, N, S, Dkv]; V1 (v == NULL): rms over kv[..., :rms_size], RoPE on the
+ *   raw kv[..., rms_size:] (rope_size = Dkv - rms_size wide).
+ *   V2 (v != NULL, [B, N, S, Dv]): rms over all of kv (rms_size = Dkv), RoPE on
+ *   the first rope_size normed values, which are overwritten.
+ *   gamma [rms_size]; cos/sin [B, N, rope_S, rope_size], rope_S == S (or 1:
+ *   the S-axis broadcast the constraint tables allow).
+ *   index: Norm [B, S] rows of batch b's cache slab, in [-1, Scache);
+ *          PA_BNSD [B*S] global slots in [-1, block_num*block_size).
+ *   Caches: Norm [B, N, Scache, D]; PA_BNSD [block_num, block_size, N, D]
+ *   (the shape the cache/index table gives for PA/PA_BNSD).
+ *   k width Dk_out = rope_size (V1) or Dkv (V2); ckv width Dc = rms_size (V1)
+ *   or Dv (V2).
+ *   k_scale/k_offset [N, Dk_out], v_scale/v_offset [N, Dc] fp64 or NULL (the
+ *   wrapper broadcasts [1], [D], [1, D] to [N, D]).
+ *   index == -1: the token writes no cache row (reading in the design doc).
+ * Outputs: caches updated in place; k_rope/c_kv (if out_kv) in in_dtype;
+ * optional exact values: k_x/c_x (the values fed to Quant) and k_t/c_t (the
+ * values right before rounding, = x*scale+offset, or x without quantisation).
+ * Returns 0, or -1 on bad dimensions.
+ */
+int oracle_kv_rmsnorm_rope_cache(
+    int64_t B, int64_t N, int64_t S, int64_t Dkv, int64_t rms_size, int64_t rope_size,
+    int64_t Dv, int in_dtype, const void *kv, const void *v, const void *gamma,
+    const void *cs, const void *sn, int64_t rope_S, const int64_t *index,
+    int cache_mode, int64_t cache_dim0, int64_t block_size, int k_dtype,
+    int ckv_dtype, void *k_cache, void *ckv_cache, const double *k_scale,
+    const double *k_offset, const double *v_scale, const double *v_offset,
+    double eps, int out_kv, void *k_rope, void *c_kv, double *k_x, double *c_x,
+    double *k_t, double *c_t, int nthreads) {
+    int v2 = v != NULL;
+    if (B < 1 || N < 1 || S < 1 || rope_size < 2 || (rope_size & 1)) return -1;
+    if (!v2 && rms_size + rope_size != Dkv) return -1;
+    if (v2 && (rms_size != Dkv || rope_size > Dkv || Dv < 1)) return -1;
+    if (rope_S != S && rope_S != 1) return -1;
+    int64_t Dk_out = v2 ? Dkv : rope_size;
+    int64_t Dc = v2 ? Dv : rms_size;
+    int64_t half = rope_size / 2;
+    if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *y = (double *)malloc(sizeof(double) * rms_size);
+        double *rope_out = (double *)malloc(sizeof(double) * Dk_out);
+        double *c_src = (double *)malloc(sizeof(double) * Dc);
+        double *z = (double *)malloc(sizeof(double) * rope_size);
+#pragma omp for schedule(static)
+        for (int64_t row = 0; row < B * N * S; row++) {
+            int64_t b = row / (N * S), n = (row / S) % N, s = row % S;
+            int64_t kv0 = row * Dkv;
+
+            /* (1) RmsNorm over the first rms_size values of the kv row */
+            double ss = 0.0;
+            for (int64_t i = 0; i < rms_size; i++) {
+                double xi = load(in_dtype, kv, kv0 + i);
+                ss += xi * xi;
+            }
+            double rms = sqrt(ss / (double)rms_size + eps);
+            for (int64_t i = 0; i < rms_size; i++)
+                y[i] = load(in_dtype, kv, kv0 + i) / rms * load(in_dtype, gamma, i);
+
+            /* (2) interleaveRope: the input is the raw tail (V1) or the first
+             * rope_size normed values (V2); x1 = even lanes, x2 = odd lanes,
+             * out = cat(x1, x2)*cos + cat(-x2, x1)*sin, cos/sin indexed by the
+             * output lane. */
+            for (int64_t i = 0; i < rope_size; i++)
+                z[i] = v2 ? y[i] : load(in_dtype, kv, kv0 + rms_size + i);
+            int64_t r0 = ((b * N + n) * rope_S + (rope_S == 1 ? 0 : s)) * rope_size;
+            for (int64_t j = 0; j < rope_size; j++) {
+                double p1 = j < half ? z[2 * j] : z[2 * (j - half) + 1];
+                double p2 = j < half ? -z[2 * j + 1] : z[2 * (j - half)];
+                rope_out[j] = p1 * load(in_dtype, cs, r0 + j) + p2 * load(in_dtype, sn, r0 + j);
+            }
+            /* V2: rope_out = concat(y_rope, RmsNorm(x)[rope_size:]) */
+            for (int64_t j = rope_size; j < Dk_out; j++) rope_out[j] = y[j];
+
+            /* what goes to the ckv cache: RmsNorm(x) (V1) or v_optional (V2) */
+            for (int64_t i = 0; i < Dc; i++)
+                c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : y[i];
+
+            /* (4) scatter slot for token (b, s): Norm's index is [B, S] and
+             * PA_BNSD's is [B*S], the same flat position b*S + s */
+            int64_t slot = index[b * S + s];
+            int64_t krow = -1, crow = -1;   /* first element of the cache row */
+            if (slot >= 0) {
+                if (cache_mode == ORC_NORM) {
+                    int64_t r = (b * N + n) * cache_dim0 + slot;      /* [B, N, Scache, D] */
+                    krow = r * Dk_out;
+                    crow = r * Dc;
+                } else {
+                    int64_t blk = slot / block_size, off = slot % block_size;
+                    int64_t r = (blk * block_size + off) * N + n;     /* [blocks, bs, N, D] */
+                    krow = r * Dk_out;
+                    crow = r * Dc;
+                }
+            }
+            int kq = k_scale != NULL, cq = v_scale != NULL;
+            for (int64_t j = 0; j < Dk_out; j++) {
+                double t = rope_out[j];
+                if (kq) t = t * k_scale[n * Dk_out + j] + (k_offset ? k_offset[n * Dk_out + j] : 0.0);
+                if (krow >= 0)
+                    quantise(k_dtype, k_cache, krow + j, rope_out[j], kq ? k_scale : NULL,
+                             kq ? k_offset : NULL, n * Dk_out + j);
+                if (k_x) k_x[row * Dk_out + j] = rope_out[j];
+                if (k_t) k_t[row * Dk_out + j] = t;
+                /* (5) raw outputs */
+                if (out_kv && k_rope) store(in_dtype, k_rope, row * Dk_out + j, rope_out[j]);
+            }
+            for (int64_t i = 0; i < Dc; i++) {
+                double t = c_src[i];
+                if (cq) t = t * v_scale[n * Dc + i] + (v_offset ? v_offset[n * Dc + i] : 0.0);
+                if (crow >= 0)
+                    quantise(ckv_dtype, ckv_cache, crow + i, c_src[i], cq ? v_scale : NULL,
+                             cq ? v_offset : NULL, n * Dc + i);
+                if (c_x) c_x[row * Dc + i] = c_src[i];
+                if (c_t) c_t[row * Dc + i] = t;
+                if (out_kv && c_kv) store(in_dtype, c_kv, row * Dc + i, c_src[i]);
+            }
+        }
+        free(y);
+        free(rope_out);
+        free(c_src);
+        free(z);
+    }
+    return 0;
+}

@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that the pins in test_oracle_pins.py catch every one of them."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "rms_divides_by_head_dim": ("ss / (double)C + eps", "ss / (double)d + eps"),
+    "eps_outside_sqrt": ("1.0 / sqrt(ss / (double)C + eps)", "1.0 / (sqrt(ss / (double)C) + eps)"),
+    "gamma_dropped": ("v * inv_rms * load(dtype, gamma, c)", "v * inv_rms"),
+    "rotate_half_sign": ("(i < h2) ? -yh[i + h2] : yh[i - h2]", "(i < h2) ? yh[i + h2] : -yh[i - h2]"),
+    "rotate_half_partner": ("(i < h2) ? -yh[i + h2] : yh[i - h2]", "(i < h2) ? -yh[h2 - 1 - i] : yh[d - 1 - i]"),
+    "cos_half_index": ("yh[i] * load(dtype, cs, r0 + i)", "yh[i] * load(dtype, cs, r0 + i % h2)"),
+    "interleave_not_deinterleaved": ("double p1 = j < half ? z[2 * j] : z[2 * (j - half) + 1];",
+                                     "double p1 = z[j];"),
+    "interleave_sign": ("double p2 = j < half ? -z[2 * j + 1] : z[2 * (j - half)];",
+                        "double p2 = j < half ? z[2 * j + 1] : -z[2 * (j - half)];"),
+    "v2_rope_on_raw_kv": ("z[i] = v2 ? y[i] :", "z[i] = v2 ? load(in_dtype, kv, kv0 + i) :"),
+    "v1_rms_over_whole_row": ("for (int64_t i = 0; i < rms_size; i++) {\n                double xi",
+                              "for (int64_t i = 0; i < Dkv; i++) {\n                double xi"),
+    "pa_head_major_layout": ("int64_t r = (blk * block_size + off) * N + n;",
+                             "int64_t r = (blk * N + n) * block_size + off;"),
+    "norm_ignores_batch": ("int64_t r = (b * N + n) * cache_dim0 + slot;", "int64_t r = n * cache_dim0 + slot;"),
+    "round_half_up": ("double r = nearbyint((double)(float)t);", "double r = floor((double)(float)t + 0.5);"),
+    "offset_before_scale": ("    if (scale) t = t * scale[qi];\n    if (offset) t = t + offset[qi];",
+                            "    if (offset) t = t + offset[qi];\n    if (scale) t = t * scale[qi];"),
+    "e4m3_no_saturation": ("if (a >= 448.0) return s | 0x7E;", "if (a >= 464.0) return s | 0x7F;"),
+    "bf16_truncates": ("return nearbyint(a / q) * q;", "return floor(a / q) * q;"),
+    "c_kv_from_raw_in_v1": ("c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : y[i];",
+                            "c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : load(in_dtype, kv, kv0 + i);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-ffp-contract=off", str(mutant), "-o", str(lib), "-lm"])
+    env = dict(os.environ, QKNR_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
