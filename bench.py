@@ -1,0 +1,282 @@
+"""Benchmark of the fused QK / KV RMSNorm + RoPE (+ cache) library on one MI355X.
+
+One step is one pass of the across-heads QK norm + rotate-half RoPE over the
+Wan2.2-A14B-shaped self-attention epilogue: S = 75600 tokens (21x45x80 latent
+grid), Q and K 40 heads x 128 bf16 in a BSD buffer [1, 75600, 10240], written
+out of place. Inputs are synthetic and already resident in HBM.
+
+Printed: ONE JSON line with the headline throughput (algorithmic HBM GB/s over
+the timed steps), tokens/s, the roofline of the kernel (bytes it must move /
+its average launch time, measured with HIP events on the launch stream, vs
+MI355X's 8 TB/s), the fp64 CPU oracle timed on a bounded sample of the same
+workload, and the KvRmsNormRopeCache workloads (MLA V1 prefill, V1 decode
+quantised, V2 split) timed the same way, cold (L2 and MALL flushed by a 1 GiB
+write before every launch) and hot.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv]
+       python bench.py --profile {across,kv_v1_prefill,kv_v1_decode,kv_v2,copy}
+       (a short fixed run of one kernel, for rocprofv3 counter collection)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of MI355X peak) + tokens/s for fused norm+RoPE(+cache)"
+KERNEL_SOURCES = {
+    "qk_across_heads": ["qk_rmsnorm_rope_amd/csrc/qk_across_heads.hip",
+                        "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+    "kv_rmsnorm_rope_cache": ["qk_rmsnorm_rope_amd/csrc/kv_rmsnorm_rope_cache.hip",
+                              "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+}
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(workload)
+    if not k or k.get("source_hash") != source_hash(kernel):
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-kv", action="store_true", help="skip the KvRmsNormRopeCache workloads")
+    ap.add_argument("--cold-iters", type=int, default=30)
+    ap.add_argument("--profile", default=None,
+                    choices=["across", "kv_v1_prefill", "kv_v1_decode", "kv_v2", "copy"])
+    return ap.parse_args()
+
+
+def across_setup(torch, W, Q):
+    cfg = W.WAN22_SELF_ATTN
+    d = W.make_across_heads(cfg, device="cuda")
+    qkv = d["qkv"]
+    out = torch.empty_like(qkv)
+    nq, nk, hd = cfg.n_q_heads, cfg.n_k_heads, cfg.head_dim
+    q = qkv[..., : nq * hd].unflatten(-1, (nq, hd))
+    k = qkv[..., nq * hd:].unflatten(-1, (nk, hd))
+    qo = out[..., : nq * hd].unflatten(-1, (nq, hd))
+    ko = out[..., nq * hd:].unflatten(-1, (nk, hd))
+
+    def step():
+        Q.qk_norm_rope_across_heads(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"], eps=cfg.eps,
+                                    q_out=qo, k_out=ko)
+    return cfg, d, step
+
+
+def kv_setup(torch, W, Q, cfg):
+    d = W.make_kv_cache(cfg, device="cuda", prefill=False)
+    mode = "Norm" if cfg.cache_mode == W.NORM else "PA_BNSD"
+
+    def step():
+        Q.kv_rmsnorm_rope_cache(d["kv"], d["gamma"], d["cos"], d["sin"], d["index"], d["k_cache"],
+                                d["ckv_cache"], k_rope_scale=d["k_scale"], k_rope_offset=d["k_offset"],
+                                c_kv_scale=d["v_scale"], c_kv_offset=d["v_offset"], v=d["v"],
+                                epsilon=cfg.eps, cache_mode=mode, is_output_kv=cfg.is_output_kv,
+                                k_rope=d["k_rope"], c_kv=d["c_kv"])
+    return d, step
+
+
+def time_hot(torch, step, iters):
+    """Back-to-back launches bracketed by one event pair on the launch stream."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(iters):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e3   # us per launch
+
+
+def time_cold(torch, step, iters, flush):
+    """Each launch timed alone after a 1 GiB write evicts L2 and the MALL."""
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(iters):
+        flush.add_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        step()
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    times.sort()
+    return times[len(times) // 2]
+
+
+def cpu_baseline(torch, W, d, cfg):
+    """The fp64 oracle on the first `n` tokens of the same workload."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = max(1, min(threads, len(os.sched_getaffinity(0))))
+    hd, nq, nk = cfg.head_dim, cfg.n_q_heads, cfg.n_k_heads
+    qkv = d["qkv"]
+
+    def sample(n):
+        flat = qkv.reshape(-1, qkv.shape[-1])[:n]
+        bits = flat.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        cs = d["cos"].reshape(-1, hd)[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        sn = d["sin"].reshape(-1, hd)[:n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        g = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return (np.ascontiguousarray(bits[:, : nq * hd]), np.ascontiguousarray(bits[:, nq * hd:]),
+                g(d["q_gamma"]), g(d["k_gamma"]), cs, sn)
+
+    def run(n):
+        args = sample(n)
+        t0 = time.perf_counter()
+        oracle.qk_norm_rope_across_heads(*args, cfg.eps, nq, nk, hd, oracle.BF16, nthreads=threads,
+                                         values=False)
+        return time.perf_counter() - t0
+
+    probe = 2048
+    t_probe = run(probe)
+    n = int(min(cfg.seq, max(probe, probe * 10.0 / max(t_probe, 1e-6))))   # about 10 s of oracle time
+    t = run(n)
+    per_token = W.algorithmic_bytes_across_heads(cfg) / cfg.seq
+    return {"value": round(n * per_token / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "tokens_per_s": round(n / t, 1), "seconds": round(t, 3),
+            "sample": f"first {n} of {cfg.seq} tokens of the same workload, fp64 C oracle, "
+                      f"OpenMP over tokens, {threads} threads, bf16 outputs encoded"}
+
+
+def kv_measure(torch, W, Q, flush, cold_iters):
+    out = {}
+    for cfg in (W.MLA_V1_PREFILL, W.MLA_V1_DECODE_QUANT, W.MLA_V2_SPLIT):
+        d, step = kv_setup(torch, W, Q, cfg)
+        for _ in range(5):
+            step()
+        hot = time_hot(torch, step, 200)
+        cold = time_cold(torch, step, cold_iters, flush)
+        nbytes = W.algorithmic_bytes_kv_cache(cfg)
+        tokens = cfg.batch * cfg.seq
+        rec = {"algorithmic_bytes": nbytes, "tokens": tokens, "rows": cfg.batch * cfg.heads * cfg.seq,
+               "us_cold_median": round(cold, 3), "us_hot_mean": round(hot, 3),
+               "gbs_cold": round(nbytes / cold / 1e3, 1), "gbs_hot": round(nbytes / hot / 1e3, 1),
+               "frac_cold": round(nbytes / cold / 1e3 / PEAK_HBM_GBS, 4),
+               "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4),
+               "tokens_per_s_cold": round(tokens / cold * 1e6, 1),
+               "traffic": measured_traffic("kv_rmsnorm_rope_cache", cfg.name)}
+        out[cfg.name] = rec
+        del d
+        torch.cuda.empty_cache()
+    return out
+
+
+def profile_run(torch, W, Q, which):
+    """A short fixed run of one kernel for counter collection under rocprofv3."""
+    if which == "copy":
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
+    if which == "across":
+        cfg, d, step = across_setup(torch, W, Q)
+    else:
+        cfg = {"kv_v1_prefill": W.MLA_V1_PREFILL, "kv_v1_decode": W.MLA_V1_DECODE_QUANT,
+               "kv_v2": W.MLA_V2_SPLIT}[which]
+        d, step = kv_setup(torch, W, Q, cfg)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": which, "launches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described, not built)"}))
+        sys.exit(2)
+    import torch
+    import qk_rmsnorm_rope_amd as Q
+    import workloads as W
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.profile:
+        profile_run(torch, W, Q, args.profile)
+        return
+
+    cfg, d, step = across_setup(torch, W, Q)
+    nbytes = W.algorithmic_bytes_across_heads(cfg)
+    tokens = cfg.batch * cfg.seq
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(args.steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_us = e0.elapsed_time(e1) / args.steps * 1e3
+    achieved = nbytes / launch_us / 1e3          # GB/s per launch
+    value = nbytes * args.steps / wall / 1e9
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    cold_us = time_cold(torch, step, args.cold_iters, flush)
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "wan22_self_attn: across-heads QK RMSNorm + rotate-half RoPE, S=75600 "
+                               "(21x45x80), Q and K 40 heads x 128, BSD [1,75600,10240] bf16, out of place",
+                   "global_batch": 1, "seq_len": cfg.seq, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(tokens * args.steps / wall, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("qk_across_heads", cfg.name),
+                     "kernel": "qk_across_heads_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(launch_us, 3), "cold_launch_us_median": round(cold_us, 3),
+                     "frac_cold": round(nbytes / cold_us / 1e3 / PEAK_HBM_GBS, 4)},
+    }
+    if not args.no_kv:
+        result["kv_rmsnorm_rope_cache"] = kv_measure(torch, W, Q, flush, args.cold_iters)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(torch, W, d, cfg)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

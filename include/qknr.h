@@ -1,0 +1,255 @@
+/*
+ * qknr.h -- C ABI of the fused QK / KV RMSNorm + RoPE (+ KV-cache scatter)
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * Two operators, each one kernel launch on the caller's HIP stream:
+ *
+ *   qknr_qk_norm_rope_across_heads  -- per-token RMSNorm over the whole Q
+ *       segment (and, separately, the whole K segment) of n_heads*d_head
+ *       channels, segment-wide gamma, then rotate-half RoPE per head with the
+ *       inverse RMS folded into the rotation; V is never read or written.
+ *       Defined by "Kernel reference: qkv_cte -- Wan2.2 additions to the NKI
+ *       Library QKV CTE MXFP8 projection", Design section 1 (across-heads QK
+ *       RMSNorm, steps a-c, here with every head on one GPU) and section 2
+ *       (bundled rotate-half RoPE), and by the WanSelfAttention forward of
+ *       "Context Parallelism in vLLM Omni Neuron" (norm before rotary).
+ *
+ *   qknr_kv_rmsnorm_rope_cache  -- the MLA operator of the CANN page
+ *       "KvRmsNormRopeCache": RmsNorm (formula 1), interleaveRope (formula 2),
+ *       static quantisation (formula 3), index scatter into k_cache/ckv_cache
+ *       (formula 4) and optional raw outputs k_rope/c_kv (formula 5), with the
+ *       parameter table and the constraint tables of that page.
+ *
+ * Conventions for every call:
+ *   - Status: 0 OK; 1 INVALID_ARGUMENT (a constraint of the pages or of this
+ *     ABI is violated; nothing is launched); 2 UNSUPPORTED (legal on the pages
+ *     but not built here, e.g. FRACTAL_NZ cache layouts, HiFloat8); 3
+ *     DEVICE_ERROR (the HIP runtime reported an error at launch).
+ *     qknr_last_error() returns a message for the last non-zero status on the
+ *     calling thread. Nothing throws or aborts across the ABI.
+ *   - Ownership: every tensor pointer is device memory owned by the caller.
+ *     The library never allocates, frees or keeps a pointer after returning,
+ *     and uses no workspace.
+ *   - Asynchrony: work is enqueued on `stream` (NULL = the null stream) and
+ *     the call returns without synchronising.
+ *   - Layouts are given as element strides (not bytes); the innermost
+ *     (channel) dimension is always contiguous.
+ *   - Data values are not checked on the device: inf/nan inputs are outside
+ *     the operators' domain, and out-of-range or duplicate cache indices are
+ *     undefined behaviour (the KvRmsNormRopeCache constraint tables), except
+ *     that index -1 means "no cache write" for that token.
+ *   - Determinism: no atomics; every output element has exactly one writer
+ *     and every reduction runs in a fixed order, so results are bit-identical
+ *     from run to run.
+ */
+#ifndef QKNR_H
+#define QKNR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKNR_ABI_VERSION 1
+
+/* status codes */
+#define QKNR_OK 0
+#define QKNR_INVALID_ARGUMENT 1
+#define QKNR_UNSUPPORTED 2
+#define QKNR_DEVICE_ERROR 3
+
+/* element types */
+#define QKNR_F32 0
+#define QKNR_BF16 1
+#define QKNR_F16 2
+#define QKNR_INT8 3
+#define QKNR_FP8_E4M3FN 4
+
+/* cache modes (KvRmsNormRopeCache, cache_mode attribute) */
+#define QKNR_CACHE_NORM 0      /* "Norm": [Bkv, N, Scache, D], index [Bkv, Skv] */
+#define QKNR_CACHE_PA_BNSD 1   /* "PA" / "PA_BNSD": [block_num, block_size, N, D], index [Bkv*Skv] */
+
+/* shapes of a quantisation parameter (constraint table for k_rope_scale etc.) */
+#define QKNR_QSHAPE_SCALAR 0       /* [1]                 */
+#define QKNR_QSHAPE_CHANNEL 1      /* [D] or [1, D]       */
+#define QKNR_QSHAPE_HEAD_CHANNEL 2 /* [N, D], row-major   */
+
+/*
+ * (a) Across-heads QK RMSNorm + rotate-half RoPE.
+ *
+ * Token (b, s) of Q has channel c = h*d_head + i at
+ *   q_in[b*in_batch_stride + s*in_token_stride + h*in_head_stride + i]
+ * and K likewise from k_in (the same strides). With a BSD [B, S, I] projection
+ * output (Q at channel 0, K at n_q_heads*d_head, V after), pass
+ * q_in = base, k_in = base + n_q_heads*d_head, token stride I, head stride
+ * d_head; an NBSd [n_heads, B, S, d_head] layout is head stride B*S*d_head,
+ * batch stride S*d_head, token stride d_head. Outputs use the out_* strides
+ * and may alias the inputs exactly (in place); V is never touched.
+ *
+ * Per token and segment (Q: n = n_q_heads; K: n = n_k_heads):
+ *   r   = 1 / sqrt( sum_c x_c^2 / (n*d_head) + eps )                 (apply_norm)
+ *   y_c = x_c * gamma_c                                              (apply_norm)
+ *   out[h, i]        = r*(y[h,i]*cos[i]        - y[h,i+d/2]*sin[i])          i < d/2
+ *   out[h, i+d/2]    = r*(y[h,i+d/2]*cos[i+d/2] + y[h,i]*sin[i+d/2])        (apply_rope)
+ * with cos/sin[b, s, :] read at
+ *   cos[b*rope_batch_stride + s*rope_token_stride + i] (batch stride 0 = shared table).
+ * Without apply_norm, r = 1 and gamma is not read; without apply_rope the
+ * output is r*y. Arithmetic is fp32; results are rounded once (RNE) to `dtype`.
+ *
+ * Arguments:
+ *   dtype            QKNR_F32, QKNR_BF16 or QKNR_F16: Q/K in and out, gammas, cos, sin.
+ *   batch, seq       B, S >= 0 (zero tokens is a no-op).
+ *   n_q_heads >= 1, n_k_heads >= 0 (0: a Q-only projection; K pointers ignored).
+ *   head_dim         even, 2..1024.
+ *   q_gamma [n_q_heads*head_dim], k_gamma [n_k_heads*head_dim] (segment-wide gammas).
+ *   eps              added to the mean of squares inside the square root.
+ */
+typedef struct qknr_qk_args {
+    int32_t dtype;
+    int32_t n_q_heads;
+    int32_t n_k_heads;
+    int32_t head_dim;
+    int64_t batch;
+    int64_t seq;
+    const void *q_in;
+    const void *k_in;
+    void *q_out;
+    void *k_out;
+    int64_t in_batch_stride;
+    int64_t in_token_stride;
+    int64_t in_head_stride;
+    int64_t out_batch_stride;
+    int64_t out_token_stride;
+    int64_t out_head_stride;
+    const void *q_gamma;
+    const void *k_gamma;
+    const void *cos;
+    const void *sin;
+    int64_t rope_batch_stride;
+    int64_t rope_token_stride;
+    float eps;
+    int32_t apply_norm;
+    int32_t apply_rope;
+    int32_t reserved;
+} qknr_qk_args;
+
+int32_t qknr_qk_norm_rope_across_heads(const qknr_qk_args *args, hipStream_t stream);
+
+/* Host-only validation of (a)'s arguments: the same checks the launch call
+ * makes, without touching a device. Returns a status code. */
+int32_t qknr_qk_validate(const qknr_qk_args *args);
+
+/*
+ * (b) KvRmsNormRopeCache.
+ *
+ * Rows are (b, n, s) with b < batch (Bkv), n < heads (N), s < seq (Skv).
+ *   V1 (v_optional == NULL): kv rows are [rms_size | rope_size] (Dv | Dk);
+ *       y = RmsNorm(kv[:rms_size]) * gamma; rope_out = interleaveRope(kv[rms_size:]);
+ *       k_cache <- Quant(rope_out), ckv_cache <- Quant(y). heads must be 1.
+ *   V2 (v_optional != NULL): kv rows are rms_size = kv_dim wide;
+ *       y = RmsNorm(kv) * gamma; rope_out = [interleaveRope(y[:rope_size]) | y[rope_size:]];
+ *       k_cache <- Quant(rope_out), ckv_cache <- Quant(v_optional row).
+ *       heads in {1, 2, 4, 8}.
+ *   RmsNorm: x / sqrt(mean(x^2) + eps) * gamma.
+ *   interleaveRope(z): out[j] = z[2j]*cos[j] - z[2j+1]*sin[j],
+ *       out[j+R/2] = z[2j+1]*cos[j+R/2] + z[2j]*sin[j+R/2], j < R/2 (the even
+ *       lanes' results first, then the odd lanes'; cos/sin indexed by output lane).
+ *   Quant (per cache): t = x*scale (+offset); INT8: round half to even, clamp to
+ *       [-128, 127]; FP8_E4M3FN: round to nearest even, saturate at +-448;
+ *       cache dtype == dtype: round the value to dtype (no scale/offset allowed).
+ *       Rounding decisions are taken on the fp32 value of t.
+ *   Scatter: NORM: row index[b*Skv + s] (index is [Bkv, Skv]) inside batch b:
+ *       k_cache[b*kc_stride0 + n*kc_stride2 + row*kc_stride1];
+ *       PA_BNSD: slot = index[b*Skv + s] (index is [Bkv*Skv]):
+ *       k_cache[(slot/block_size)*kc_stride0 + (slot%block_size)*kc_stride1 + n*kc_stride2];
+ *       likewise ckv_cache with the ckv strides. index -1: no cache write.
+ *   Raw outputs (is_output_kv): k_rope[b,n,s,:] = rope_out and
+ *       c_kv[b,n,s,:] = y (V1) or v_optional row (V2), in `dtype`, unquantised.
+ *
+ * Widths: k rows are k_dim = rope_size (V1) or kv_dim (V2) wide; ckv rows are
+ * c_dim = rms_size (V1) or v_dim (V2) wide.
+ *
+ * Arguments:
+ *   dtype            QKNR_BF16 or QKNR_F16: kv, gamma, cos, sin, v_optional, k_rope, c_kv.
+ *   batch, heads, seq    Bkv, N, Skv >= 1 (empty tensors are not allowed).
+ *   kv_dim, rms_size, rope_size, v_dim   see above; rope_size even.
+ *   kv_strides[3], v_strides[3], rope_strides[3], k_rope_strides[3],
+ *   c_kv_strides[3]: element strides of the (b, n, s) axes; the channel axis is
+ *       contiguous. rope_strides[2] == 0 is the S-axis broadcast (Srope = 1).
+ *   index            int64 device array (see Scatter).
+ *   cache_mode       QKNR_CACHE_NORM or QKNR_CACHE_PA_BNSD.
+ *   cache_rows       NORM: Scache (>= Skv). PA_BNSD: block_num.
+ *   block_size       PA_BNSD: > 1 and block_size*sizeof(cache element) a multiple of 32.
+ *   k_cache_dtype, ckv_cache_dtype   dtype, QKNR_INT8 or QKNR_FP8_E4M3FN.
+ *   k_cache_strides[3], ckv_cache_strides[3]: element strides of the cache's
+ *       leading axes: NORM (batch, row, head); PA_BNSD (block, slot in block,
+ *       head). The channel axis is contiguous.
+ *   k_scale, k_offset, v_scale, v_offset   fp32 device arrays or NULL; the
+ *       *_qshape fields give their shapes (QKNR_QSHAPE_*). A scale is required
+ *       exactly when the cache dtype differs from dtype; an offset needs its
+ *       scale. V1 allows SCALAR/CHANNEL shapes, V2 HEAD_CHANNEL.
+ *   eps              default on the page 1e-5.
+ *   is_output_kv     1: write k_rope and c_kv (allowed in PA_BNSD, and in
+ *       NORM only for V2 with quantisation).
+ */
+typedef struct qknr_kv_args {
+    int32_t dtype;
+    int32_t heads;
+    int64_t batch;
+    int64_t seq;
+    int32_t kv_dim;
+    int32_t rms_size;
+    int32_t rope_size;
+    int32_t v_dim;
+    const void *kv;
+    const void *v_optional;
+    const void *gamma;
+    const void *cos;
+    const void *sin;
+    int64_t kv_strides[3];
+    int64_t v_strides[3];
+    int64_t rope_strides[3];
+    const int64_t *index;
+    int32_t cache_mode;
+    int32_t block_size;
+    int64_t cache_rows;
+    void *k_cache;
+    void *ckv_cache;
+    int32_t k_cache_dtype;
+    int32_t ckv_cache_dtype;
+    int64_t k_cache_strides[3];
+    int64_t ckv_cache_strides[3];
+    const float *k_scale;
+    const float *k_offset;
+    const float *v_scale;
+    const float *v_offset;
+    int32_t k_qshape;
+    int32_t v_qshape;
+    float eps;
+    int32_t is_output_kv;
+    void *k_rope;
+    void *c_kv;
+    int64_t k_rope_strides[3];
+    int64_t c_kv_strides[3];
+} qknr_kv_args;
+
+int32_t qknr_kv_rmsnorm_rope_cache(const qknr_kv_args *args, hipStream_t stream);
+
+/* Host-only validation of (b)'s arguments (no device access). */
+int32_t qknr_kv_validate(const qknr_kv_args *args);
+
+/* Message for the last non-zero status returned on the calling thread
+ * (empty string if none). The pointer stays valid until the next call on
+ * this thread. */
+const char *qknr_last_error(void);
+
+/* QKNR_ABI_VERSION of the loaded library. */
+int32_t qknr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKNR_H */

@@ -110,12 +110,13 @@ def encode(dtype: int, values) -> np.ndarray:
 
 def qk_norm_rope_across_heads(q, k, q_gamma, k_gamma, cos, sin, eps, n_q_heads,
                               n_k_heads, head_dim, dtype, apply_norm=True,
-                              apply_rope=True, nthreads=None):
+                              apply_rope=True, nthreads=None, values=True):
     """Across-heads RMSNorm + rotate-half RoPE of T tokens.
 
     q: [T, n_q*d], k: [T, n_k*d] or None, gammas [n*d], cos/sin [T, d], all in
     storage form of ``dtype`` (F32 float32 arrays, BF16/F16 uint16 bits).
-    Returns (q_out, k_out, q_val, k_val): encoded outputs and exact fp64 values.
+    Returns (q_out, k_out, q_val, k_val): encoded outputs and exact fp64 values
+    (None when ``values`` is false).
     """
     st = STORAGE[dtype]
     q = _c(q, st)
@@ -129,8 +130,8 @@ def qk_norm_rope_across_heads(q, k, q_gamma, k_gamma, cos, sin, eps, n_q_heads,
     cos, sin = _c(cos, st), _c(sin, st)
     q_out = np.empty((T, cq), st)
     k_out = np.empty((T, ck), st) if k is not None else None
-    q_val = np.empty((T, cq), np.float64)
-    k_val = np.empty((T, ck), np.float64) if k is not None else None
+    q_val = np.empty((T, cq), np.float64) if values else None
+    k_val = np.empty((T, ck), np.float64) if (k is not None and values) else None
     rc = _load().oracle_qk_norm_rope_across_heads(
         T, n_q_heads, n_k_heads, head_dim, dtype, _ptr(q), _ptr(k), _ptr(q_gamma),
         _ptr(k_gamma), _ptr(cos), _ptr(sin), float(eps), int(bool(apply_norm)),
@@ -157,13 +158,14 @@ def kv_rmsnorm_rope_cache(kv, v, gamma, cos, sin, index, k_cache, ckv_cache, *,
                           rms_size, rope_size, eps, cache_mode, in_dtype, k_dtype,
                           ckv_dtype, block_size=0, k_scale=None, k_offset=None,
                           v_scale=None, v_offset=None, is_output_kv=False,
-                          nthreads=None):
+                          nthreads=None, copy_caches=True):
     """The KvRmsNormRopeCache operator on host arrays.
 
     kv [B, N, S, Dkv] and v [B, N, S, Dv] (or None for V1), gamma, cos/sin
     [B, N, S or 1, rope] in storage form of ``in_dtype``; index int64; the caches
     (storage arrays, Norm [B, N, Scache, D] or paged [blocks, bs, N, D]) are
-    copied and the copies updated. Returns a dict with k_cache, ckv_cache,
+    copied and the copies updated (``copy_caches=False`` updates the given
+    C-contiguous arrays in place). Returns a dict with k_cache, ckv_cache,
     k_rope, c_kv (None unless is_output_kv), and the exact values k_x, c_x
     (fed to quantisation) and k_t, c_t (right before rounding).
     """
@@ -175,8 +177,12 @@ def kv_rmsnorm_rope_cache(kv, v, gamma, cos, sin, index, k_cache, ckv_cache, *,
     gamma, cos, sin = _c(gamma, st), _c(cos, st), _c(sin, st)
     rope_S = cos.shape[2]
     index = _c(index, np.int64)
-    k_cache = np.array(k_cache, copy=True, order="C")
-    ckv_cache = np.array(ckv_cache, copy=True, order="C")
+    if copy_caches:
+        k_cache = np.array(k_cache, copy=True, order="C")
+        ckv_cache = np.array(ckv_cache, copy=True, order="C")
+    elif not (k_cache.flags.c_contiguous and ckv_cache.flags.c_contiguous
+              and k_cache.flags.writeable and ckv_cache.flags.writeable):
+        raise ValueError("in-place caches must be writeable C-contiguous arrays")
     if k_cache.dtype != STORAGE[k_dtype] or ckv_cache.dtype != STORAGE[ckv_dtype]:
         raise TypeError("cache storage does not match its dtype code")
     dk = Dkv if v is not None else rope_size

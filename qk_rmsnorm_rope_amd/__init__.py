@@ -1,0 +1,372 @@
+"""Python binding of the qknr C ABI (include/qknr.h): fused QK / KV RMSNorm +
+RoPE (+ KV-cache scatter) on AMD MI355X (gfx950).
+
+This module only marshals torch tensors into the ABI's argument structs
+(pointers, element strides, dtype codes) and passes torch's current HIP stream.
+Every step of both operators runs in the HIP kernels of libqknr.so; there is
+no fallback: importing fails loudly if the library has not been built
+(``python -m qk_rmsnorm_rope_amd._build``).
+
+Entry points (same names as the C ABI, without the ``qknr_`` prefix):
+
+* :func:`qk_norm_rope_across_heads` -- across-heads RMSNorm + rotate-half RoPE
+  ("Kernel reference: qkv_cte", Design sections 1-2).
+* :func:`kv_rmsnorm_rope_cache` -- the KvRmsNormRopeCache operator (CANN page,
+  formulas 1-5), argument names as on that page's parameter table.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqknr.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m qk_rmsnorm_rope_amd._build, or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR = 0, 1, 2, 3
+F32, BF16, F16, INT8, FP8_E4M3FN = 0, 1, 2, 3, 4
+CACHE_NORM, CACHE_PA_BNSD = 0, 1
+QSHAPE_SCALAR, QSHAPE_CHANNEL, QSHAPE_HEAD_CHANNEL = 0, 1, 2
+
+_DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16,
+          torch.int8: INT8, torch.float8_e4m3fn: FP8_E4M3FN}
+_CACHE_MODE = {"Norm": CACHE_NORM, "PA": CACHE_PA_BNSD, "PA_BNSD": CACHE_PA_BNSD}
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class QkArgs(ctypes.Structure):
+    """Mirror of ``qknr_qk_args``."""
+    _fields_ = [
+        ("dtype", _i32), ("n_q_heads", _i32), ("n_k_heads", _i32), ("head_dim", _i32),
+        ("batch", _i64), ("seq", _i64),
+        ("q_in", _p), ("k_in", _p), ("q_out", _p), ("k_out", _p),
+        ("in_batch_stride", _i64), ("in_token_stride", _i64), ("in_head_stride", _i64),
+        ("out_batch_stride", _i64), ("out_token_stride", _i64), ("out_head_stride", _i64),
+        ("q_gamma", _p), ("k_gamma", _p), ("cos", _p), ("sin", _p),
+        ("rope_batch_stride", _i64), ("rope_token_stride", _i64),
+        ("eps", ctypes.c_float), ("apply_norm", _i32), ("apply_rope", _i32), ("reserved", _i32),
+    ]
+
+
+class KvArgs(ctypes.Structure):
+    """Mirror of ``qknr_kv_args``."""
+    _fields_ = [
+        ("dtype", _i32), ("heads", _i32), ("batch", _i64), ("seq", _i64),
+        ("kv_dim", _i32), ("rms_size", _i32), ("rope_size", _i32), ("v_dim", _i32),
+        ("kv", _p), ("v_optional", _p), ("gamma", _p), ("cos", _p), ("sin", _p),
+        ("kv_strides", _i64 * 3), ("v_strides", _i64 * 3), ("rope_strides", _i64 * 3),
+        ("index", _p), ("cache_mode", _i32), ("block_size", _i32), ("cache_rows", _i64),
+        ("k_cache", _p), ("ckv_cache", _p), ("k_cache_dtype", _i32), ("ckv_cache_dtype", _i32),
+        ("k_cache_strides", _i64 * 3), ("ckv_cache_strides", _i64 * 3),
+        ("k_scale", _p), ("k_offset", _p), ("v_scale", _p), ("v_offset", _p),
+        ("k_qshape", _i32), ("v_qshape", _i32), ("eps", ctypes.c_float), ("is_output_kv", _i32),
+        ("k_rope", _p), ("c_kv", _p), ("k_rope_strides", _i64 * 3), ("c_kv_strides", _i64 * 3),
+    ]
+
+
+_lib.qknr_qk_norm_rope_across_heads.argtypes = [ctypes.POINTER(QkArgs), _p]
+_lib.qknr_qk_norm_rope_across_heads.restype = _i32
+_lib.qknr_qk_validate.argtypes = [ctypes.POINTER(QkArgs)]
+_lib.qknr_qk_validate.restype = _i32
+_lib.qknr_kv_rmsnorm_rope_cache.argtypes = [ctypes.POINTER(KvArgs), _p]
+_lib.qknr_kv_rmsnorm_rope_cache.restype = _i32
+_lib.qknr_kv_validate.argtypes = [ctypes.POINTER(KvArgs)]
+_lib.qknr_kv_validate.restype = _i32
+_lib.qknr_last_error.argtypes = []
+_lib.qknr_last_error.restype = ctypes.c_char_p
+_lib.qknr_version.argtypes = []
+_lib.qknr_version.restype = _i32
+
+EXPORTED = ("qknr_qk_norm_rope_across_heads", "qknr_qk_validate", "qknr_kv_rmsnorm_rope_cache",
+            "qknr_kv_validate", "qknr_last_error", "qknr_version")
+
+
+class QknrError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"qknr status {code}: {message}")
+        self.code = code
+
+
+def last_error() -> str:
+    return _lib.qknr_last_error().decode()
+
+
+def version() -> int:
+    return int(_lib.qknr_version())
+
+
+def _check(code: int):
+    if code != OK:
+        raise QknrError(code, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t) -> int:
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _last_dim_contiguous(name, t):
+    if t is not None and t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+
+
+# ----------------------------------------------------------------------------
+# (a) across-heads QK RMSNorm + rotate-half RoPE
+# ----------------------------------------------------------------------------
+
+def qk_args(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
+            apply_norm=True, apply_rope=True) -> QkArgs:
+    """Fill ``qknr_qk_args`` from tensors.
+
+    q: [B, S, n_q_heads, d] (any strides, d contiguous) -- e.g. a BSD projection
+    ``qkv[..., :nq*d].unflatten(-1, (nq, d))`` or an NBSd buffer permuted to
+    (B, S, N, d). k: [B, S, n_k_heads, d] with the same strides, or None.
+    cos, sin: [B or 1, S, d] (a batch of 1 is shared). Outputs default to the
+    inputs (in place).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, S, n_q_heads, head_dim]")
+    B, S, nq, d = q.shape
+    q_out = q if q_out is None else q_out
+    nk = 0
+    if k is not None:
+        if k.dim() != 4 or k.shape[0] != B or k.shape[1] != S or k.shape[3] != d:
+            raise ValueError("k must be [B, S, n_k_heads, head_dim] like q")
+        if k.stride() != q.stride():
+            raise ValueError("q and k must share strides")
+        nk = k.shape[2]
+        k_out = k if k_out is None else k_out
+        if k_out.stride() != q_out.stride():
+            raise ValueError("q_out and k_out must share strides")
+    if q_out.shape != q.shape:
+        raise ValueError("q_out must have q's shape")
+    for name, t in (("q", q), ("k", k), ("q_out", q_out), ("k_out", k_out), ("cos", cos), ("sin", sin)):
+        _last_dim_contiguous(name, t)
+    a = QkArgs()
+    a.dtype = _dtype(q)
+    for t in (k, q_out, k_out, q_gamma, k_gamma, cos, sin):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("all tensors of (a) share one dtype")
+    a.n_q_heads, a.n_k_heads, a.head_dim = nq, nk, d
+    a.batch, a.seq = B, S
+    a.q_in, a.k_in, a.q_out, a.k_out = _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out)
+    a.in_batch_stride, a.in_token_stride, a.in_head_stride = q.stride(0), q.stride(1), q.stride(2)
+    a.out_batch_stride, a.out_token_stride, a.out_head_stride = q_out.stride(0), q_out.stride(1), q_out.stride(2)
+    if apply_norm:
+        if q_gamma is None or q_gamma.numel() != nq * d or (nk and (k_gamma is None or k_gamma.numel() != nk * d)):
+            raise ValueError("gammas must be [n_heads * head_dim] (segment-wide)")
+        a.q_gamma, a.k_gamma = _ptr(q_gamma.contiguous()), _ptr(k_gamma.contiguous() if nk else None)
+    if apply_rope:
+        if (cos.dim() != 3 or cos.shape[0] not in (1, B) or cos.shape[1] != S or cos.shape[2] != d
+                or sin.shape != cos.shape or cos.stride() != sin.stride()):
+            raise ValueError("cos/sin must be [B or 1, S, head_dim] with equal strides")
+        a.cos, a.sin = _ptr(cos), _ptr(sin)
+        a.rope_batch_stride = 0 if cos.shape[0] == 1 else cos.stride(0)
+        a.rope_token_stride = cos.stride(1)
+    a.eps = float(eps)
+    a.apply_norm, a.apply_rope = int(bool(apply_norm)), int(bool(apply_rope))
+    a._keep = (q_gamma, k_gamma)  # keep contiguous copies alive
+    return a
+
+
+def qk_norm_rope_across_heads(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
+                              apply_norm=True, apply_rope=True, stream=None):
+    """Across-heads RMSNorm + rotate-half RoPE of Q and K (see :func:`qk_args`).
+    Returns (q_out, k_out)."""
+    if q_out is None:
+        q_out = q
+    if k is not None and k_out is None:
+        k_out = k
+    a = qk_args(q, k, q_gamma, k_gamma, cos, sin, eps=eps, q_out=q_out, k_out=k_out,
+                apply_norm=apply_norm, apply_rope=apply_rope)
+    with torch.cuda.device(q.device):
+        _check(_lib.qknr_qk_norm_rope_across_heads(ctypes.byref(a), _stream(q.device, stream)))
+    return q_out, k_out
+
+
+def qk_validate(a: QkArgs) -> int:
+    """Host-only validation of filled arguments; returns the status code."""
+    return int(_lib.qknr_qk_validate(ctypes.byref(a)))
+
+
+# ----------------------------------------------------------------------------
+# (b) KvRmsNormRopeCache
+# ----------------------------------------------------------------------------
+
+def _qshape(t, heads, width, v2):
+    """Shape code of a quantisation parameter tensor: [1] -> SCALAR, [D] or
+    [1, D] -> CHANNEL ([1, D] is [N, D] when V2 has N = 1), [N, D] -> HEAD_CHANNEL."""
+    if t is None:
+        return QSHAPE_SCALAR
+    shape = tuple(t.shape)
+    if shape == (1,):
+        return QSHAPE_SCALAR
+    if shape == (width,):
+        return QSHAPE_CHANNEL
+    if shape == (1, width):
+        return QSHAPE_HEAD_CHANNEL if (v2 and heads == 1) else QSHAPE_CHANNEL
+    if shape == (heads, width):
+        return QSHAPE_HEAD_CHANNEL
+    raise ValueError(f"quantisation parameter shape {shape} is not [1], [{width}], [1, {width}] "
+                     f"or [{heads}, {width}]")
+
+
+def _strides3(t):
+    return (_i64 * 3)(*(t.stride()[:3] if t is not None else (0, 0, 0)))
+
+
+def kv_args(kv, gamma, cos, sin, index, k_cache, ckv_cache, *, k_rope_scale=None, c_kv_scale=None,
+            k_rope_offset=None, c_kv_offset=None, v=None, epsilon=1e-5, cache_mode="Norm",
+            is_output_kv=False, k_rope=None, c_kv=None) -> KvArgs:
+    """Fill ``qknr_kv_args`` from tensors named as on the KvRmsNormRopeCache
+    parameter table.
+
+    kv [Bkv, N, Skv, D]; v (v_optional) [Bkv, N, Skv, Dv] or None; gamma
+    [rms_size]; cos/sin [Bkv, N, Skv or 1, rope]; index int64 ([Bkv, Skv] for
+    Norm, [Bkv*Skv] for PA/PA_BNSD); caches Norm [Bkv, N, Scache, D] or paged
+    [block_num, block_size, N, D]; scales/offsets fp32 [1], [D], [1, D] (V1) or
+    [N, D] (V2). V1 takes rope_size = cos.shape[-1] and rms_size = D - rope_size.
+    """
+    if kv.dim() != 4:
+        raise ValueError("kv must be [Bkv, N, Skv, D]")
+    B, N, S, D = kv.shape
+    v2 = v is not None
+    R = cos.shape[-1]
+    a = KvArgs()
+    a.dtype = _dtype(kv)
+    for t in (gamma, cos, sin, v, k_rope, c_kv):
+        if t is not None and t.dtype != kv.dtype:
+            raise TypeError("kv, gamma, cos, sin, v_optional, k_rope and c_kv share one dtype")
+    a.heads, a.batch, a.seq = N, B, S
+    a.kv_dim, a.rope_size = D, R
+    a.rms_size = D if v2 else D - R
+    a.v_dim = v.shape[-1] if v2 else 0
+    if cos.dim() != 4 or sin.shape != cos.shape or cos.stride() != sin.stride():
+        raise ValueError("cos/sin must be 4-D with equal shapes and strides")
+    for name, t in (("kv", kv), ("v_optional", v), ("cos", cos), ("sin", sin), ("k_cache", k_cache),
+                    ("ckv_cache", ckv_cache), ("k_rope", k_rope), ("c_kv", c_kv)):
+        _last_dim_contiguous(name, t)
+    if gamma.numel() != a.rms_size:
+        raise ValueError(f"gamma must have rms_size = {a.rms_size} elements")
+    if index.dtype != torch.int64:
+        raise TypeError("index must be int64")
+    if cos.shape[0] != B or cos.shape[1] != N or cos.shape[2] not in (1, S):
+        raise ValueError("cos/sin must be [Bkv, N, Skv or 1, rope_size]")
+    if v2 and tuple(v.shape[:3]) != (B, N, S):
+        raise ValueError("v_optional must be [Bkv, N, Skv, Dv]")
+    dk_w = D if v2 else R
+    dc_w = v.shape[-1] if v2 else D - R
+    if cache_mode == "Norm":
+        if index.numel() != B * S or (index.dim() == 2 and tuple(index.shape) != (B, S)):
+            raise ValueError("Norm index must be [Bkv, Skv]")
+        lead_ok = (k_cache.dim() == 4 and ckv_cache.dim() == 4 and k_cache.shape[0] == B
+                   and k_cache.shape[1] == N and tuple(ckv_cache.shape[:3]) == tuple(k_cache.shape[:3]))
+    else:
+        if index.numel() != B * S:
+            raise ValueError("paged index must be [Bkv * Skv]")
+        lead_ok = (k_cache.dim() == 4 and ckv_cache.dim() == 4 and k_cache.shape[2] == N
+                   and tuple(ckv_cache.shape[:3]) == tuple(k_cache.shape[:3]))
+    if not lead_ok or k_cache.shape[3] != dk_w or ckv_cache.shape[3] != dc_w:
+        raise ValueError(f"caches must be Norm [Bkv, N, Scache, D] or paged [block_num, block_size, N, D] "
+                         f"with k width {dk_w} and ckv width {dc_w}, and agree in their leading dims")
+    for name, t, w in (("k_rope", k_rope, dk_w), ("c_kv", c_kv, dc_w)):
+        if t is not None and tuple(t.shape) != (B, N, S, w):
+            raise ValueError(f"{name} must be [Bkv, N, Skv, {w}]")
+    a.kv, a.v_optional = _ptr(kv), _ptr(v)
+    gamma = gamma.contiguous()
+    index = index.contiguous()
+    a.gamma, a.cos, a.sin, a.index = _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(index)
+    a.kv_strides = _strides3(kv)
+    a.v_strides = _strides3(v)
+    rs = list(cos.stride()[:3])
+    if cos.shape[2] == 1:
+        rs[2] = 0  # S-axis broadcast (Srope = 1)
+    a.rope_strides = (_i64 * 3)(*rs)
+    try:
+        a.cache_mode = _CACHE_MODE[cache_mode]
+    except KeyError:
+        raise ValueError(f"cache_mode {cache_mode!r} is not built (Norm, PA, PA_BNSD)") from None
+    a.k_cache, a.ckv_cache = _ptr(k_cache), _ptr(ckv_cache)
+    a.k_cache_dtype, a.ckv_cache_dtype = _dtype(k_cache), _dtype(ckv_cache)
+    if a.cache_mode == CACHE_NORM:
+        # [Bkv, N, Scache, D] -> (batch, row, head)
+        a.cache_rows = k_cache.shape[2]
+        a.block_size = 0
+        a.k_cache_strides = (_i64 * 3)(k_cache.stride(0), k_cache.stride(2), k_cache.stride(1))
+        a.ckv_cache_strides = (_i64 * 3)(ckv_cache.stride(0), ckv_cache.stride(2), ckv_cache.stride(1))
+    else:
+        # [block_num, block_size, N, D] -> (block, slot in block, head)
+        a.cache_rows = k_cache.shape[0]
+        a.block_size = k_cache.shape[1]
+        a.k_cache_strides = (_i64 * 3)(*k_cache.stride()[:3])
+        a.ckv_cache_strides = (_i64 * 3)(*ckv_cache.stride()[:3])
+    qp = [None if t is None else t.contiguous() for t in (k_rope_scale, k_rope_offset, c_kv_scale, c_kv_offset)]
+    for t in qp:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("quantisation parameters are float32")
+    a.k_scale, a.k_offset, a.v_scale, a.v_offset = (_ptr(t) for t in qp)
+    dk = D if v2 else R
+    dc = a.v_dim if v2 else a.rms_size
+    a.k_qshape, a.v_qshape = _qshape(qp[0], N, dk, v2), _qshape(qp[2], N, dc, v2)
+    for scale, offset in ((qp[0], qp[1]), (qp[2], qp[3])):
+        if scale is not None and offset is not None and scale.shape != offset.shape:
+            raise ValueError("a scale and its offset must have the same shape")
+    a.eps = float(epsilon)
+    a.is_output_kv = int(bool(is_output_kv))
+    a.k_rope, a.c_kv = _ptr(k_rope), _ptr(c_kv)
+    a.k_rope_strides = _strides3(k_rope)
+    a.c_kv_strides = _strides3(c_kv)
+    a._keep = (gamma, index, qp)
+    return a
+
+
+def kv_rmsnorm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, *, k_rope_scale=None,
+                          c_kv_scale=None, k_rope_offset=None, c_kv_offset=None, v=None,
+                          epsilon=1e-5, cache_mode="Norm", is_output_kv=False, k_rope=None,
+                          c_kv=None, stream=None):
+    """KvRmsNormRopeCache: caches are updated in place; returns (k_rope, c_kv)
+    when is_output_kv (allocating them if not given), else (None, None)."""
+    if is_output_kv and (k_rope is None or c_kv is None):
+        B, N, S, D = kv.shape
+        R = cos.shape[-1]
+        dk = D if v is not None else R
+        dc = v.shape[-1] if v is not None else D - R
+        if k_rope is None:
+            k_rope = torch.empty((B, N, S, dk), dtype=kv.dtype, device=kv.device)
+        if c_kv is None:
+            c_kv = torch.empty((B, N, S, dc), dtype=kv.dtype, device=kv.device)
+    a = kv_args(kv, gamma, cos, sin, index, k_cache, ckv_cache, k_rope_scale=k_rope_scale,
+                c_kv_scale=c_kv_scale, k_rope_offset=k_rope_offset, c_kv_offset=c_kv_offset, v=v,
+                epsilon=epsilon, cache_mode=cache_mode, is_output_kv=is_output_kv, k_rope=k_rope,
+                c_kv=c_kv)
+    with torch.cuda.device(kv.device):
+        _check(_lib.qknr_kv_rmsnorm_rope_cache(ctypes.byref(a), _stream(kv.device, stream)))
+    return (k_rope, c_kv) if is_output_kv else (None, None)
+
+
+def kv_validate(a: KvArgs) -> int:
+    """Host-only validation of filled arguments; returns the status code."""
+    return int(_lib.qknr_kv_validate(ctypes.byref(a)))

@@ -1,0 +1,365 @@
+// api.cpp -- the extern "C" entry points declared in include/qknr.h: argument
+// validation (host only), vector-width selection and kernel dispatch.
+//
+// Validation follows the constraint sections of the "KvRmsNormRopeCache" page
+// (dtype equalities, the scale/offset legality table, cache/index shapes,
+// block_size alignment, V1/V2 head counts, no empty tensors, is_output_kv
+// validity) and the argument list of the qkv_cte page's interface (segment
+// widths, gammas, rotate-half tables).
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "qknr.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int32_t ok() {
+    return QKNR_OK;
+}
+
+int elem_size(int32_t dtype) {
+    switch (dtype) {
+    case QKNR_F32: return 4;
+    case QKNR_BF16: case QKNR_F16: return 2;
+    case QKNR_INT8: case QKNR_FP8_E4M3FN: return 1;
+    }
+    return 0;
+}
+
+bool aligned(const void *p, int bytes) {
+    return p == nullptr || (reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes) == 0;
+}
+
+// ---------------------------------------------------------------- (a)
+
+struct QkPlan {
+    qknr::QkParams p;
+    int elem_type;
+    int vec;
+};
+
+int32_t qk_check(const qknr_qk_args *a, QkPlan *out) {
+    if (!a) return fail(QKNR_INVALID_ARGUMENT, "args is NULL");
+    if (a->dtype != QKNR_F32 && a->dtype != QKNR_BF16 && a->dtype != QKNR_F16)
+        return fail(QKNR_INVALID_ARGUMENT, "dtype must be QKNR_F32, QKNR_BF16 or QKNR_F16 (got %d)", a->dtype);
+    if (a->n_q_heads < 1) return fail(QKNR_INVALID_ARGUMENT, "n_q_heads must be >= 1");
+    if (a->n_k_heads < 0) return fail(QKNR_INVALID_ARGUMENT, "n_k_heads must be >= 0");
+    if (a->head_dim < 2 || (a->head_dim & 1))
+        return fail(QKNR_INVALID_ARGUMENT, "head_dim must be even and >= 2 (rotate-half pairs i, i+d/2)");
+    if (a->batch < 0 || a->seq < 0) return fail(QKNR_INVALID_ARGUMENT, "batch and seq must be >= 0");
+    if (!(a->eps >= 0.0f) || a->eps == __builtin_inff())
+        return fail(QKNR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    const int64_t tokens = a->batch * a->seq;
+    const bool has_k = a->n_k_heads > 0;
+    if (tokens > 0) {
+        if (!a->q_in || !a->q_out) return fail(QKNR_INVALID_ARGUMENT, "q_in and q_out are required");
+        if (has_k && (!a->k_in || !a->k_out))
+            return fail(QKNR_INVALID_ARGUMENT, "k_in and k_out are required when n_k_heads > 0");
+        if (a->apply_norm && (!a->q_gamma || (has_k && !a->k_gamma)))
+            return fail(QKNR_INVALID_ARGUMENT, "apply_norm needs q_gamma (and k_gamma when n_k_heads > 0)");
+        if (a->apply_rope && (!a->cos || !a->sin))
+            return fail(QKNR_INVALID_ARGUMENT, "apply_rope needs cos and sin");
+    }
+    if (a->in_batch_stride < 0 || a->in_token_stride < 0 || a->out_batch_stride < 0 ||
+        a->out_token_stride < 0 || a->rope_batch_stride < 0 || a->rope_token_stride < 0)
+        return fail(QKNR_INVALID_ARGUMENT, "strides must be >= 0");
+    if (a->in_head_stride < a->head_dim || a->out_head_stride < a->head_dim)
+        return fail(QKNR_INVALID_ARGUMENT, "head strides must be >= head_dim (heads may not overlap)");
+    const bool q_alias = a->q_out == a->q_in, k_alias = has_k && a->k_out == a->k_in;
+    if ((q_alias || k_alias) && (a->in_batch_stride != a->out_batch_stride ||
+                                 a->in_token_stride != a->out_token_stride ||
+                                 a->in_head_stride != a->out_head_stride))
+        return fail(QKNR_INVALID_ARGUMENT, "in-place use needs identical input and output strides");
+
+    const int es = elem_size(a->dtype);
+    const int half = a->head_dim / 2;
+    const void *ptrs[] = {a->q_in, a->q_out, has_k ? a->k_in : nullptr, has_k ? a->k_out : nullptr,
+                          a->apply_norm ? a->q_gamma : nullptr,
+                          (a->apply_norm && has_k) ? a->k_gamma : nullptr,
+                          a->apply_rope ? a->cos : nullptr, a->apply_rope ? a->sin : nullptr};
+    const int64_t strides[] = {a->in_batch_stride, a->in_token_stride, a->in_head_stride,
+                               a->out_batch_stride, a->out_token_stride, a->out_head_stride,
+                               a->apply_rope ? a->rope_batch_stride : 0,
+                               a->apply_rope ? a->rope_token_stride : 0};
+    auto fits = [&](int vec) {
+        if (half % vec) return false;
+        for (const void *p : ptrs)
+            if (!aligned(p, vec * es)) return false;
+        for (int64_t s : strides)
+            if (s % vec) return false;
+        return true;
+    };
+    const int wide = 16 / es, narrow = 4 / es;
+    int vec = fits(wide) ? wide : (fits(narrow) ? narrow : 0);
+    if (!vec)
+        return fail(QKNR_UNSUPPORTED, "pointers/strides are not aligned to 4 bytes for this dtype");
+
+    QkPlan plan;
+    qknr::QkParams &p = plan.p;
+    p = qknr::QkParams{};
+    p.q_in = a->q_in; p.k_in = a->k_in; p.q_out = a->q_out; p.k_out = a->k_out;
+    p.q_gamma = a->q_gamma; p.k_gamma = a->k_gamma; p.cos = a->cos; p.sin = a->sin;
+    p.tokens = tokens;
+    p.seq = a->seq > 0 ? a->seq : 1;
+    p.in_batch_stride = a->in_batch_stride; p.in_token_stride = a->in_token_stride;
+    p.in_head_stride = a->in_head_stride;
+    p.out_batch_stride = a->out_batch_stride; p.out_token_stride = a->out_token_stride;
+    p.out_head_stride = a->out_head_stride;
+    p.rope_batch_stride = a->rope_batch_stride; p.rope_token_stride = a->rope_token_stride;
+    p.n_q = a->n_q_heads; p.n_k = a->n_k_heads; p.head_dim = a->head_dim;
+    p.apply_norm = a->apply_norm ? 1 : 0; p.apply_rope = a->apply_rope ? 1 : 0;
+    p.q_channels = (float)a->n_q_heads * (float)a->head_dim;
+    p.k_channels = (float)(has_k ? a->n_k_heads : 1) * (float)a->head_dim;
+    p.eps = a->eps;
+    int J = qknr::qk_plan(p, vec);
+    if (J < 0 && vec == wide && fits(narrow)) {
+        vec = narrow;
+        J = qknr::qk_plan(p, vec);
+    }
+    if (J < 0)
+        return fail(QKNR_UNSUPPORTED, "head_dim %d with %d heads exceeds one block's register plan",
+                    a->head_dim, a->n_q_heads > a->n_k_heads ? a->n_q_heads : a->n_k_heads);
+    const int64_t blocks = (tokens + (4 / p.waves_per_token) - 1) / (4 / p.waves_per_token);
+    if (blocks > 0x7FFFFFFFLL) return fail(QKNR_UNSUPPORTED, "too many tokens for one launch");
+    plan.elem_type = a->dtype == QKNR_F32 ? 0 : (a->dtype == QKNR_BF16 ? 1 : 2);
+    plan.vec = vec;
+    if (out) *out = plan;
+    return ok();
+}
+
+// ---------------------------------------------------------------- (b)
+
+struct KvPlan {
+    qknr::KvParams p;
+    int elem_type;
+    int vec;
+    bool v2;
+};
+
+int32_t cache_code(int32_t cache_dtype, int32_t dtype, const char *which, int32_t *code) {
+    if (cache_dtype == dtype) { *code = qknr::CODE_SAME; return QKNR_OK; }
+    if (cache_dtype == QKNR_INT8) { *code = qknr::CODE_INT8; return QKNR_OK; }
+    if (cache_dtype == QKNR_FP8_E4M3FN) { *code = qknr::CODE_E4M3FN; return QKNR_OK; }
+    if (cache_dtype == QKNR_F32 || cache_dtype == QKNR_BF16 || cache_dtype == QKNR_F16)
+        return fail(QKNR_INVALID_ARGUMENT, "%s: an unquantised cache must have the kv dtype", which);
+    return fail(QKNR_UNSUPPORTED, "%s: cache dtype %d is not built (INT8 and FP8_E4M3FN are)", which,
+                cache_dtype);
+}
+
+int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
+    if (!a) return fail(QKNR_INVALID_ARGUMENT, "args is NULL");
+    if (a->dtype != QKNR_BF16 && a->dtype != QKNR_F16)
+        return fail(QKNR_INVALID_ARGUMENT, "dtype must be QKNR_BF16 or QKNR_F16 (got %d)", a->dtype);
+    if (a->batch < 1 || a->heads < 1 || a->seq < 1)
+        return fail(QKNR_INVALID_ARGUMENT, "empty tensors are not supported (batch, heads, seq >= 1)");
+    if (!a->kv || !a->gamma || !a->cos || !a->sin || !a->index || !a->k_cache || !a->ckv_cache)
+        return fail(QKNR_INVALID_ARGUMENT, "kv, gamma, cos, sin, index, k_cache and ckv_cache are required");
+    if (a->rope_size < 2 || (a->rope_size & 1))
+        return fail(QKNR_INVALID_ARGUMENT, "rope_size must be even and >= 2");
+    if (a->rms_size < 1) return fail(QKNR_INVALID_ARGUMENT, "rms_size must be >= 1");
+    if (!(a->eps >= 0.0f) || a->eps == __builtin_inff())
+        return fail(QKNR_INVALID_ARGUMENT, "epsilon must be finite and >= 0");
+    const bool v2 = a->v_optional != nullptr;
+    int32_t k_dim, c_dim;
+    if (!v2) {
+        if (a->heads != 1) return fail(QKNR_INVALID_ARGUMENT, "V1 (merged kv) supports N = 1 only");
+        if (a->kv_dim != a->rms_size + a->rope_size)
+            return fail(QKNR_INVALID_ARGUMENT, "V1: kv_dim must equal rms_size + rope_size");
+        k_dim = a->rope_size;
+        c_dim = a->rms_size;
+    } else {
+        if (a->heads != 1 && a->heads != 2 && a->heads != 4 && a->heads != 8)
+            return fail(QKNR_INVALID_ARGUMENT, "V2 (split k/v) supports N in {1, 2, 4, 8}");
+        if (a->rms_size != a->kv_dim) return fail(QKNR_INVALID_ARGUMENT, "V2: rms_size must equal kv_dim");
+        if (a->rope_size > a->kv_dim) return fail(QKNR_INVALID_ARGUMENT, "V2: rope_size must be <= kv_dim");
+        if (a->v_dim < 1) return fail(QKNR_INVALID_ARGUMENT, "V2: v_dim must be >= 1");
+        k_dim = a->kv_dim;
+        c_dim = a->v_dim;
+    }
+
+    int32_t k_code, c_code, rc;
+    if ((rc = cache_code(a->k_cache_dtype, a->dtype, "k_cache", &k_code)) != QKNR_OK) return rc;
+    if ((rc = cache_code(a->ckv_cache_dtype, a->dtype, "ckv_cache", &c_code)) != QKNR_OK) return rc;
+    // scale/offset legality table: no scale + no offset -> cache has the kv dtype;
+    // offset without scale is illegal; a quantised cache needs its scale.
+    if (a->k_offset && !a->k_scale) return fail(QKNR_INVALID_ARGUMENT, "k_offset given without k_scale");
+    if (a->v_offset && !a->v_scale) return fail(QKNR_INVALID_ARGUMENT, "v_offset given without v_scale");
+    if (k_code == qknr::CODE_SAME && (a->k_scale || a->k_offset))
+        return fail(QKNR_INVALID_ARGUMENT, "k_cache is unquantised (kv dtype): k_scale/k_offset must be NULL");
+    if (c_code == qknr::CODE_SAME && (a->v_scale || a->v_offset))
+        return fail(QKNR_INVALID_ARGUMENT, "ckv_cache is unquantised (kv dtype): v_scale/v_offset must be NULL");
+    if (k_code != qknr::CODE_SAME && !a->k_scale)
+        return fail(QKNR_INVALID_ARGUMENT, "a quantised k_cache needs k_scale");
+    if (c_code != qknr::CODE_SAME && !a->v_scale)
+        return fail(QKNR_INVALID_ARGUMENT, "a quantised ckv_cache needs v_scale");
+    const bool k_quant = k_code != qknr::CODE_SAME, c_quant = c_code != qknr::CODE_SAME;
+    for (int which = 0; which < 2; which++) {
+        const bool q = which == 0 ? k_quant : c_quant;
+        const int32_t shape = which == 0 ? a->k_qshape : a->v_qshape;
+        if (!q) continue;
+        if (!v2 && shape != QKNR_QSHAPE_SCALAR && shape != QKNR_QSHAPE_CHANNEL)
+            return fail(QKNR_INVALID_ARGUMENT, "V1 quantisation parameters are [1], [D] or [1, D]");
+        if (v2 && shape != QKNR_QSHAPE_HEAD_CHANNEL)
+            return fail(QKNR_INVALID_ARGUMENT, "V2 quantisation parameters are [N, D]");
+    }
+
+    // cache modes and index ranges
+    int64_t capacity;
+    if (a->cache_mode == QKNR_CACHE_NORM) {
+        if (a->cache_rows < a->seq) return fail(QKNR_INVALID_ARGUMENT, "Norm cache: Scache must be >= Skv");
+        capacity = a->cache_rows;
+    } else if (a->cache_mode == QKNR_CACHE_PA_BNSD) {
+        if (a->block_size <= 1) return fail(QKNR_INVALID_ARGUMENT, "paged cache: block_size must be > 1");
+        const int kb = k_quant ? 1 : elem_size(a->dtype), cb = c_quant ? 1 : elem_size(a->dtype);
+        if (((int64_t)a->block_size * kb) % 32 || ((int64_t)a->block_size * cb) % 32)
+            return fail(QKNR_INVALID_ARGUMENT,
+                        "paged cache: block_size must be 32-byte aligned for each cache dtype");
+        if (a->cache_rows < (a->seq / a->block_size) * a->batch)
+            return fail(QKNR_INVALID_ARGUMENT, "paged cache: block_num must be >= floor(Skv/block_size)*Bkv");
+        capacity = a->cache_rows * (int64_t)a->block_size;
+    } else {
+        return fail(QKNR_UNSUPPORTED, "cache_mode %d is not built (Norm and PA/PA_BNSD are)", a->cache_mode);
+    }
+
+    // S-axis broadcast of cos/sin (Srope = 1): allowed for Norm and for an
+    // unquantised paged cache
+    const bool s_bcast = a->rope_strides[2] == 0 && a->seq > 1;
+    if (s_bcast && a->cache_mode == QKNR_CACHE_PA_BNSD && (k_quant || c_quant))
+        return fail(QKNR_INVALID_ARGUMENT, "S-axis broadcast of cos/sin is not allowed with quantised paged caches");
+
+    // is_output_kv: effective for paged caches, and for Norm only in V2 with quantisation
+    const bool out_kv = a->is_output_kv &&
+                        (a->cache_mode == QKNR_CACHE_PA_BNSD || (v2 && (k_quant || c_quant)));
+    if (out_kv && (!a->k_rope || !a->c_kv))
+        return fail(QKNR_INVALID_ARGUMENT, "is_output_kv needs k_rope and c_kv");
+
+    for (int i = 0; i < 3; i++) {
+        if (a->kv_strides[i] < 0 || a->rope_strides[i] < 0 || (v2 && a->v_strides[i] < 0) ||
+            a->k_cache_strides[i] < 0 || a->ckv_cache_strides[i] < 0 ||
+            (out_kv && (a->k_rope_strides[i] < 0 || a->c_kv_strides[i] < 0)))
+            return fail(QKNR_INVALID_ARGUMENT, "strides must be >= 0");
+    }
+
+    // vector width: 8 elements (16-byte accesses) or 4 (8-byte)
+    const int es = elem_size(a->dtype);
+    auto fits = [&](int vec) {
+        const int h = vec / 2;
+        if (a->rms_size % vec || a->rope_size % vec || (v2 && a->v_dim % vec)) return false;
+        const void *full[] = {a->kv, v2 ? a->v_optional : nullptr, a->gamma, out_kv ? a->c_kv : nullptr};
+        for (const void *p : full)
+            if (!aligned(p, vec * es)) return false;
+        if (!aligned(a->cos, h * es) || !aligned(a->sin, h * es)) return false;
+        // k rows take half-chunk stores (the rotated part); V2 k rows also take
+        // whole chunks (the unrotated normed part)
+        const int kw = v2 ? vec : h;
+        if (out_kv && !aligned(a->k_rope, kw * es)) return false;
+        const int kb = k_quant ? 1 : es, cb = c_quant ? 1 : es;
+        if (!aligned(a->k_cache, kw * kb) || !aligned(a->ckv_cache, vec * cb)) return false;
+        const float *qp[] = {a->k_scale, a->k_offset, a->v_scale, a->v_offset};
+        for (const float *p : qp)
+            if (!aligned(p, 16)) return false;
+        for (int i = 0; i < 3; i++) {
+            if (a->kv_strides[i] % vec || (v2 && a->v_strides[i] % vec) || a->rope_strides[i] % h ||
+                a->k_cache_strides[i] % kw || a->ckv_cache_strides[i] % vec ||
+                (out_kv && (a->k_rope_strides[i] % kw || a->c_kv_strides[i] % vec)))
+                return false;
+        }
+        return true;
+    };
+    const int vec = fits(8) ? 8 : (fits(4) ? 4 : 0);
+    if (!vec)
+        return fail(QKNR_UNSUPPORTED,
+                    "sizes, pointers or strides are not multiples of 4 elements (8-byte accesses)");
+
+    KvPlan plan;
+    qknr::KvParams &p = plan.p;
+    p = qknr::KvParams{};
+    p.kv = a->kv; p.v = a->v_optional; p.gamma = a->gamma; p.cos = a->cos; p.sin = a->sin;
+    p.index = a->index; p.k_cache = a->k_cache; p.ckv_cache = a->ckv_cache;
+    p.k_scale = a->k_scale; p.k_offset = a->k_offset; p.v_scale = a->v_scale; p.v_offset = a->v_offset;
+    p.k_rope = a->k_rope; p.c_kv = a->c_kv;
+    p.rows = a->batch * a->heads * a->seq;
+    p.seq = a->seq;
+    p.kv_b = a->kv_strides[0]; p.kv_n = a->kv_strides[1]; p.kv_s = a->kv_strides[2];
+    p.v_b = a->v_strides[0]; p.v_n = a->v_strides[1]; p.v_s = a->v_strides[2];
+    p.rope_b = a->rope_strides[0]; p.rope_n = a->rope_strides[1]; p.rope_s = a->rope_strides[2];
+    p.kr_b = a->k_rope_strides[0]; p.kr_n = a->k_rope_strides[1]; p.kr_s = a->k_rope_strides[2];
+    p.ck_b = a->c_kv_strides[0]; p.ck_n = a->c_kv_strides[1]; p.ck_s = a->c_kv_strides[2];
+    p.kc0 = a->k_cache_strides[0]; p.kc1 = a->k_cache_strides[1]; p.kc2 = a->k_cache_strides[2];
+    p.cc0 = a->ckv_cache_strides[0]; p.cc1 = a->ckv_cache_strides[1]; p.cc2 = a->ckv_cache_strides[2];
+    p.capacity = capacity;
+    p.heads = a->heads;
+    p.mode = a->cache_mode == QKNR_CACHE_NORM ? 0 : 1;
+    p.block_size = a->cache_mode == QKNR_CACHE_NORM ? 1 : a->block_size;
+    p.rms_size = a->rms_size; p.rope_size = a->rope_size; p.half_rope = a->rope_size / 2;
+    p.k_dim = k_dim; p.c_dim = c_dim;
+    p.k_code = k_code; p.c_code = c_code;
+    p.k_qshape = a->k_qshape; p.v_qshape = a->v_qshape;
+    p.out_kv = out_kv ? 1 : 0;
+    p.eps = a->eps;
+    int cr = 0, cx = 0;
+    if (qknr::kv_plan(p, vec, v2, cr, cx) != 0)
+        return fail(QKNR_UNSUPPORTED, "row too wide for one block's register plan");
+    const int64_t blocks = (p.rows + (256 / p.lanes_per_row) - 1) / (256 / p.lanes_per_row);
+    if (blocks > 0x7FFFFFFFLL) return fail(QKNR_UNSUPPORTED, "too many rows for one launch");
+    plan.elem_type = a->dtype == QKNR_BF16 ? 1 : 2;
+    plan.vec = vec;
+    plan.v2 = v2;
+    if (out) *out = plan;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qknr_qk_validate(const qknr_qk_args *args) {
+    return qk_check(args, nullptr);
+}
+
+int32_t qknr_qk_norm_rope_across_heads(const qknr_qk_args *args, hipStream_t stream) {
+    QkPlan plan;
+    int32_t rc = qk_check(args, &plan);
+    if (rc != QKNR_OK) return rc;
+    hipError_t e = qknr::qk_launch(plan.p, plan.elem_type, plan.vec, stream);
+    if (e != hipSuccess) return fail(QKNR_DEVICE_ERROR, "launch failed: %s", hipGetErrorString(e));
+    return QKNR_OK;
+}
+
+int32_t qknr_kv_validate(const qknr_kv_args *args) {
+    return kv_check(args, nullptr);
+}
+
+int32_t qknr_kv_rmsnorm_rope_cache(const qknr_kv_args *args, hipStream_t stream) {
+    KvPlan plan;
+    int32_t rc = kv_check(args, &plan);
+    if (rc != QKNR_OK) return rc;
+    hipError_t e = qknr::kv_launch(plan.p, plan.elem_type, plan.vec, plan.v2, stream);
+    if (e != hipSuccess) return fail(QKNR_DEVICE_ERROR, "launch failed: %s", hipGetErrorString(e));
+    return QKNR_OK;
+}
+
+const char *qknr_last_error(void) {
+    return g_last_error.c_str();
+}
+
+int32_t qknr_version(void) {
+    return QKNR_ABI_VERSION;
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// launch.h -- flat kernel parameter blocks and launcher entry points shared by
+// the C-ABI layer (api.cpp) and the two kernels. Host and device code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qknr {
+
+// (a) across-heads QK RMSNorm + rotate-half RoPE
+struct QkParams {
+    const void *q_in;
+    const void *k_in;
+    void *q_out;
+    void *k_out;
+    const void *q_gamma;
+    const void *k_gamma;
+    const void *cos;
+    const void *sin;
+    int64_t tokens;            // B*S
+    int64_t seq;
+    int64_t in_batch_stride, in_token_stride, in_head_stride;
+    int64_t out_batch_stride, out_token_stride, out_head_stride;
+    int64_t rope_batch_stride, rope_token_stride;
+    int32_t n_q, n_k, head_dim, half;
+    int32_t chunks_per_half;   // half / VEC
+    int32_t heads_per_step;    // 64 / chunks_per_half
+    int32_t waves_per_token;   // 1, 2 or 4
+    int32_t apply_norm, apply_rope;
+    float q_channels, k_channels, eps;
+};
+
+// Fills the lane geometry of p for chunk width `vec`; returns J > 0 or -1.
+int qk_plan(QkParams &p, int vec);
+// elem_type: 0 f32, 1 bf16, 2 f16. vec: 16-byte chunk width, or the narrow fallback.
+hipError_t qk_launch(QkParams &p, int elem_type, int vec, hipStream_t stream);
+
+// (b) KvRmsNormRopeCache
+enum CacheCode : int32_t { CODE_SAME = 0, CODE_INT8 = 1, CODE_E4M3FN = 2 };
+enum QShape : int32_t { QS_SCALAR = 0, QS_CHANNEL = 1, QS_HEAD_CHANNEL = 2 };
+
+struct KvParams {
+    const void *kv;
+    const void *v;
+    const void *gamma;
+    const void *cos;
+    const void *sin;
+    const int64_t *index;
+    void *k_cache;
+    void *ckv_cache;
+    const float *k_scale, *k_offset, *v_scale, *v_offset;
+    void *k_rope;
+    void *c_kv;
+    int64_t rows;              // B*N*S
+    int64_t seq;
+    int64_t kv_b, kv_n, kv_s;
+    int64_t v_b, v_n, v_s;
+    int64_t rope_b, rope_n, rope_s;
+    int64_t kr_b, kr_n, kr_s;  // k_rope strides
+    int64_t ck_b, ck_n, ck_s;  // c_kv strides
+    int64_t kc0, kc1, kc2;     // k_cache strides (NORM: batch,row,head; PA: block,slot,head)
+    int64_t cc0, cc1, cc2;     // ckv_cache strides
+    int64_t capacity;          // NORM: Scache; PA: block_num*block_size
+    int32_t heads;
+    int32_t mode;              // 0 NORM, 1 PA_BNSD
+    int32_t block_size;
+    int32_t rms_size, rope_size, half_rope;
+    int32_t k_dim, c_dim;      // widths of the k and ckv rows
+    int32_t nr;                // rms chunks per row
+    int32_t nx;                // V1: raw rope chunks; V2: v chunks
+    int32_t n_rope_chunks;     // V2: rope_size / VEC (normed chunks that are rotated)
+    int32_t lanes_per_row;     // G: 8, 16, 32 or 64
+    int32_t k_code, c_code;    // CacheCode
+    int32_t k_qshape, v_qshape;
+    int32_t out_kv;
+    float eps;
+};
+
+// Picks VEC-independent geometry (lanes per row and the register slots);
+// returns 0 and sets cr/cx, or -1 if the row is too wide.
+int kv_plan(KvParams &p, int vec, bool v2, int &cr, int &cx);
+// elem_type: 1 bf16, 2 f16. vec: 8 or 4.
+hipError_t kv_launch(KvParams &p, int elem_type, int vec, bool v2, hipStream_t stream);
+
+}  // namespace qknr

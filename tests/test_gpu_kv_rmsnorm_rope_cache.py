@@ -1,0 +1,120 @@
+"""GPU parity of qknr_kv_rmsnorm_rope_cache against the fp64 oracle.
+
+Cases: the three MLA workloads at their full sizes (V1 prefill into bf16 paged
+caches with k_rope/c_kv; V1 decode into int8 / fp8-e4m3fn Norm caches of 8192
+rows, plus the same with k scales large enough to exercise rounding and
+clamping; V2 split mode with asymmetric int8 per-head parameters, with and
+without k_rope/c_kv) and variants at reduced size: index -1 entries, several
+tokens per batch in a Norm cache, fp16 inputs, fp8 ckv in V2, scalar and
+[1, D] scale shapes, S-axis broadcast of cos/sin, the 8-byte access path, and
+determinism. Untouched cache rows must keep their pre-filled bytes exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.parity import check_kv, run_gpu_kv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import qk_rmsnorm_rope_amd as lib
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return lib
+
+
+def test_mla_v1_prefill_full(Q):
+    d = W.make_kv_cache(W.MLA_V1_PREFILL, device="cuda")
+    rep, _ = check_kv(Q, d, "v1-prefill")
+    print(rep)
+
+
+def test_mla_v1_decode_quant_full(Q):
+    d = W.make_kv_cache(W.MLA_V1_DECODE_QUANT, device="cuda")
+    rep, r = check_kv(Q, d, "v1-decode", big_cache=True)
+    print(rep)
+
+
+def test_mla_v1_decode_quant_large_k_scale(Q):
+    """k scale ~U(20, 100): k codes span the int8 range and clamp."""
+    d = W.make_kv_cache(W.MLA_V1_DECODE_QUANT, device="cuda", k_scale=(20.0, 100.0, "D"))
+    rep, r = check_kv(Q, d, "v1-decode-bigscale", big_cache=True)
+    codes = np.rint(np.clip(r["k_t"], -128, 127))
+    assert (np.abs(codes) == 127).sum() + (codes == -128).sum() > 0, "clamping not exercised"
+    assert len(np.unique(codes)) > 100
+    print(rep)
+
+
+@pytest.mark.parametrize("out_kv", [False, True])
+def test_mla_v2_split_full(Q, out_kv):
+    d = W.make_kv_cache(W.MLA_V2_SPLIT, device="cuda", is_output_kv=out_kv)
+    rep, _ = check_kv(Q, d, f"v2-split-outkv{int(out_kv)}")
+    print(rep)
+
+
+VARIANTS = {
+    "v1_pa_invalid_index": (W.MLA_V1_PREFILL, dict(seq=300, block_num=24, invalid_every=7)),
+    "v1_norm_multi_token": (W.MLA_V1_DECODE_QUANT, dict(batch=5, seq=37, cache_rows=64, index_kind="perm",
+                                                        rope_pos="seq", invalid_every=11)),
+    "v1_norm_bf16_caches": (W.MLA_V1_DECODE_QUANT, dict(batch=9, seq=3, cache_rows=16, index_kind="perm",
+                                                        k_cache_dtype=torch.bfloat16,
+                                                        ckv_cache_dtype=torch.bfloat16, k_scale=None,
+                                                        v_scale=None, rope_pos="seq")),
+    "v1_fp16": (W.MLA_V1_PREFILL, dict(seq=130, block_num=12, dtype=torch.float16,
+                                       k_cache_dtype=torch.float16, ckv_cache_dtype=torch.float16)),
+    "v1_scalar_scale_pa": (W.MLA_V1_PREFILL, dict(seq=96, block_num=8, k_cache_dtype=torch.int8,
+                                                  ckv_cache_dtype=torch.int8, k_scale=(20.0, 40.0, "1"),
+                                                  v_scale=(20.0, 40.0, "1D"), is_output_kv=True)),
+    "v1_e4m3_both": (W.MLA_V1_PREFILL, dict(seq=64, block_num=8, k_cache_dtype=torch.float8_e4m3fn,
+                                            ckv_cache_dtype=torch.float8_e4m3fn, k_scale=(50.0, 400.0, "D"),
+                                            v_scale=(0.5, 2.0, "D"))),
+    "v2_e4m3_ckv": (W.MLA_V2_SPLIT, dict(batch=2, seq=256, block_num=8, ckv_cache_dtype=torch.float8_e4m3fn,
+                                         v_offset=None, v_scale=(1.0, 8.0, "ND"), is_output_kv=True)),
+    "v2_bf16_caches_n4": (W.MLA_V2_SPLIT, dict(batch=3, heads=4, seq=100, block_num=8,
+                                               k_cache_dtype=torch.bfloat16, ckv_cache_dtype=torch.bfloat16,
+                                               k_scale=None, k_offset=None, v_scale=None, v_offset=None,
+                                               is_output_kv=True)),
+    "v2_norm_quant_outkv": (W.MLA_V2_SPLIT, dict(batch=2, heads=2, seq=40, cache_mode=W.NORM, cache_rows=64,
+                                                 is_output_kv=True, invalid_every=5)),
+    "v2_symmetric_n1": (W.MLA_V2_SPLIT, dict(batch=4, heads=1, seq=128, block_num=8, k_offset=None,
+                                             v_offset=None)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+def test_variants(Q, name):
+    cfg, over = VARIANTS[name]
+    d = W.make_kv_cache(cfg, device="cuda", **over)
+    rep, _ = check_kv(Q, d, name)
+    print(name, rep)
+
+
+def test_s_axis_broadcast_cos_sin(Q):
+    """cos/sin [B, N, 1, rope] shared by every position (Norm cache)."""
+    d = W.make_kv_cache(W.MLA_V1_DECODE_QUANT, device="cuda", batch=4, seq=20, cache_rows=32,
+                        index_kind="perm", rope_pos="seq")
+    d["cos"] = d["cos"][:, :, 5:6].contiguous()
+    d["sin"] = d["sin"][:, :, 5:6].contiguous()
+    rep, _ = check_kv(Q, d, "s-broadcast")
+    print(rep)
+
+
+def test_narrow_access_path(Q):
+    """rms_size 12 (not a multiple of 8): the 4-element (8-byte) path."""
+    d = W.make_kv_cache(W.MLA_V1_PREFILL, device="cuda", seq=64, block_num=8, kv_dim=12 + 16, rms_size=12,
+                        rope_size=16, is_output_kv=True)
+    rep, _ = check_kv(Q, d, "narrow")
+    print(rep)
+
+
+def test_deterministic(Q):
+    d1 = W.make_kv_cache(W.MLA_V2_SPLIT, device="cuda", batch=2, seq=512, block_num=16)
+    d2 = W.make_kv_cache(W.MLA_V2_SPLIT, device="cuda", batch=2, seq=512, block_num=16)
+    run_gpu_kv(Q, d1)
+    run_gpu_kv(Q, d2)
+    torch.cuda.synchronize()
+    assert torch.equal(d1["k_cache"], d2["k_cache"]) and torch.equal(d1["ckv_cache"], d2["ckv_cache"])

@@ -287,7 +287,7 @@ def make_kv_cache(cfg: KvCacheConfig, device="cpu", prefill=True, **override):
     def _cache(shape, dt):
         if not prefill:
             return torch.zeros(shape, dtype=dt, device=device)
-        raw = torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        raw = torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.uint8)
         if dt.itemsize == 1:
             return raw.view(dt)
         # 16-bit caches: fill with random finite values (exponent field kept small)
