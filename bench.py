@@ -16,6 +16,9 @@ write before every launch) and hot.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv]
        python bench.py --profile {across,kv_v1_prefill,kv_v1_decode,kv_v2,copy}
        (a short fixed run of one kernel, for rocprofv3 counter collection)
+       python bench.py --summarize DIR
+       (turn the rocprofv3 CSVs under DIR into the text summaries and the
+       traffic record under profiles/; CPU only)
 """
 from __future__ import annotations
 
@@ -71,6 +74,7 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=30)
     ap.add_argument("--profile", default=None,
                     choices=["across", "kv_v1_prefill", "kv_v1_decode", "kv_v2", "copy"])
+    ap.add_argument("--summarize", default=None, metavar="DIR")
     return ap.parse_args()
 
 
@@ -216,8 +220,105 @@ def profile_run(torch, W, Q, which):
     print(json.dumps({"profile": which, "launches": 5}))
 
 
+PROFILE_WORKLOADS = {
+    "across": ("qk_across_heads", "wan22_self_attn"),
+    "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill"),
+    "kv_v1_decode": ("kv_rmsnorm_rope_cache", "mla_v1_decode_quant"),
+    "kv_v2": ("kv_rmsnorm_rope_cache", "mla_v2_split"),
+}
+
+
+def summarize(prof_dir):
+    """Write profiles/*.txt and profiles/pmc_traffic.json from rocprofv3 CSVs:
+    <dir>/trace/*_kernel_trace.csv (kernel durations of a bench run) and
+    <dir>/pmc_{fetch,write}_<workload>/*_counter_collection.csv."""
+    import csv
+    import glob
+    import statistics
+    import workloads as W
+
+    def counters(kind, w):
+        files = glob.glob(os.path.join(prof_dir, f"pmc_{kind}_{w}", "*counter_collection.csv"))
+        vals = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    def pick(vals, needle):
+        hits = [v for k, v in vals.items() if needle in k]
+        return statistics.mean(hits[0]) if hits else None
+
+    # calibration: the same counters on a plain 1 GiB copy (read 1 GiB, write 1 GiB)
+    cf, cw = pick(counters("fetch", "copy"), "copy"), pick(counters("write", "copy"), "copy")
+    kib = (1 << 30) / 1024
+    f_scale, w_scale = kib / cf, kib / cw
+    trace = glob.glob(os.path.join(prof_dir, "trace", "*kernel_trace.csv"))
+    durs = {}
+    for f in trace:
+        for r in csv.DictReader(open(f)):
+            if "qknr::" in r["Kernel_Name"]:
+                key = (r["Kernel_Name"], r["Grid_Size_X"])
+                durs.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    cfgs = {"wan22_self_attn": W.WAN22_SELF_ATTN, "mla_v1_prefill": W.MLA_V1_PREFILL,
+            "mla_v1_decode_quant": W.MLA_V1_DECODE_QUANT, "mla_v2_split": W.MLA_V2_SPLIT}
+    record = {"calibration": {"copy_bytes": 1 << 30, "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
+                              "fetch_scale": f_scale, "write_scale": w_scale},
+              "kernels": {}}
+    lines_by_kernel = {}
+    for prof, (kernel, wname) in PROFILE_WORKLOADS.items():
+        fv, wv = counters("fetch", prof), counters("write", prof)
+        f, w = pick(fv, "qknr::"), pick(wv, "qknr::")
+        if f is None or w is None:
+            continue
+        cfg = cfgs[wname]
+        alg = (W.algorithmic_bytes_across_heads(cfg) if kernel == "qk_across_heads"
+               else W.algorithmic_bytes_kv_cache(cfg))
+        hbm = f * 1024 * f_scale + w * 1024 * w_scale
+        record["kernels"][wname] = {"kernel": kernel, "source_hash": source_hash(kernel),
+                                    "FETCH_SIZE_KiB": f, "WRITE_SIZE_KiB": w,
+                                    "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes": alg,
+                                    "traffic_over_algorithmic": round(hbm / alg, 4)}
+        kname = [k for k in fv if "qknr::" in k][0]
+        grids = set()
+        for fpath in glob.glob(os.path.join(prof_dir, f"pmc_fetch_{prof}", "*counter_collection.csv")):
+            grids |= {r["Grid_Size"] for r in csv.DictReader(open(fpath)) if r["Kernel_Name"] == kname}
+        lines = lines_by_kernel.setdefault(kernel, [])
+        lines.append(f"workload {wname}: kernel {kname}")
+        for (k, g), v in sorted(durs.items()):
+            if k == kname and g in grids:
+                lines.append(f"  trace grid {g}: {len(v)} dispatches, median {statistics.median(v):.2f} us, "
+                             f"mean {statistics.mean(v):.2f} us, min {min(v):.2f} us, max {max(v):.2f} us")
+        lines.append(f"  FETCH_SIZE {f:.1f} KiB x {f_scale:.4f} + WRITE_SIZE {w:.1f} KiB x {w_scale:.4f} "
+                     f"= {hbm / 1e6:.3f} MB per launch; algorithmic {alg / 1e6:.3f} MB "
+                     f"(ratio {hbm / alg:.4f})")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as fjs:
+        json.dump(record, fjs, indent=1)
+    cmds = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o bench -- "
+            "python -u bench.py --steps 100 --warmup 10 --no-cpu\n"
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_fetch_<w> -o p -- "
+            "python -u bench.py --profile <w>\n"
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write_<w> -o p -- "
+            "python -u bench.py --profile <w>\n"
+            "  for <w> in across kv_v1_prefill kv_v1_decode kv_v2 copy; then "
+            "python bench.py --summarize <dir>\n")
+    calib = (f"calibration (copy of 1 GiB, __amd_rocclr_copyBuffer): FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE "
+             f"{cw:.1f} KiB -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}\n")
+    names = {"qk_across_heads": "qk_across_heads_wan22_s75600.txt",
+             "kv_rmsnorm_rope_cache": "kv_rmsnorm_rope_cache_mla_workloads.txt"}
+    for kernel, lines in lines_by_kernel.items():
+        with open(os.path.join(ROOT, "profiles", names[kernel]), "w") as ftxt:
+            ftxt.write(f"MI355X (gfx950), rocprofv3 summaries for {kernel}\n\ncommands:\n{cmds}\n{calib}\n")
+            ftxt.write("\n".join(lines) + "\n")
+    print(json.dumps(record, indent=1))
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is described, not built)"}))
@@ -255,6 +356,10 @@ def main():
 
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
     cold_us = time_cold(torch, step, args.cold_iters, flush)
+    copy_src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    copy_dst = torch.empty_like(copy_src)
+    copy_us = time_hot(torch, lambda: copy_dst.copy_(copy_src), 20)
+    del copy_src, copy_dst
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -270,6 +375,9 @@ def main():
                      "kernel": "qk_across_heads_kernel", "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": round(launch_us, 3), "cold_launch_us_median": round(cold_us, 3),
                      "frac_cold": round(nbytes / cold_us / 1e3 / PEAK_HBM_GBS, 4)},
+        "copy_reference": {"what": "1 GiB device-to-device copy (hipMemcpy), read + write bytes / time",
+                           "gbs": round(2 * (1 << 30) / copy_us / 1e3, 1),
+                           "frac": round(2 * (1 << 30) / copy_us / 1e3 / PEAK_HBM_GBS, 4)},
     }
     if not args.no_kv:
         result["kv_rmsnorm_rope_cache"] = kv_measure(torch, W, Q, flush, args.cold_iters)
