@@ -109,19 +109,28 @@ int32_t qk_check(const qknr_qk_args *a, QkPlan *out) {
     if (!vec)
         return fail(QKNR_UNSUPPORTED, "pointers/strides are not aligned to 4 bytes for this dtype");
 
+    // 32-bit index ranges used inside the kernel
+    const int64_t max_heads = a->n_q_heads > a->n_k_heads ? a->n_q_heads : a->n_k_heads;
+    const int64_t span_in = ((max_heads - 1) * a->in_head_stride + a->head_dim) * es;
+    const int64_t span_out = ((max_heads - 1) * a->out_head_stride + a->head_dim) * es;
+    if (tokens >= (1LL << 31) || span_in >= (1LL << 32) || span_out >= (1LL << 32))
+        return fail(QKNR_UNSUPPORTED, "more than 2^31 tokens, or one token's heads span 4 GiB or more");
+
     QkPlan plan;
     qknr::QkParams &p = plan.p;
     p = qknr::QkParams{};
     p.q_in = a->q_in; p.k_in = a->k_in; p.q_out = a->q_out; p.k_out = a->k_out;
     p.q_gamma = a->q_gamma; p.k_gamma = a->k_gamma; p.cos = a->cos; p.sin = a->sin;
-    p.tokens = tokens;
-    p.seq = a->seq > 0 ? a->seq : 1;
+    p.tokens = (uint32_t)tokens;
+    p.seq = (uint32_t)(a->seq > 0 ? a->seq : 1);
+    p.seq_div = qknr::make_fastdiv(p.seq);
     p.in_batch_stride = a->in_batch_stride; p.in_token_stride = a->in_token_stride;
-    p.in_head_stride = a->in_head_stride;
+    p.in_head_stride = (uint32_t)a->in_head_stride;
     p.out_batch_stride = a->out_batch_stride; p.out_token_stride = a->out_token_stride;
-    p.out_head_stride = a->out_head_stride;
+    p.out_head_stride = (uint32_t)a->out_head_stride;
     p.rope_batch_stride = a->rope_batch_stride; p.rope_token_stride = a->rope_token_stride;
     p.n_q = a->n_q_heads; p.n_k = a->n_k_heads; p.head_dim = a->head_dim;
+    p.segs = has_k ? 2 : 1;
     p.apply_norm = a->apply_norm ? 1 : 0; p.apply_rope = a->apply_rope ? 1 : 0;
     p.q_channels = (float)a->n_q_heads * (float)a->head_dim;
     p.k_channels = (float)(has_k ? a->n_k_heads : 1) * (float)a->head_dim;
@@ -133,9 +142,7 @@ int32_t qk_check(const qknr_qk_args *a, QkPlan *out) {
     }
     if (J < 0)
         return fail(QKNR_UNSUPPORTED, "head_dim %d with %d heads exceeds one block's register plan",
-                    a->head_dim, a->n_q_heads > a->n_k_heads ? a->n_q_heads : a->n_k_heads);
-    const int64_t blocks = (tokens + (4 / p.waves_per_token) - 1) / (4 / p.waves_per_token);
-    if (blocks > 0x7FFFFFFFLL) return fail(QKNR_UNSUPPORTED, "too many tokens for one launch");
+                    a->head_dim, (int)max_heads);
     plan.elem_type = a->dtype == QKNR_F32 ? 0 : (a->dtype == QKNR_BF16 ? 1 : 2);
     plan.vec = vec;
     if (out) *out = plan;
@@ -293,8 +300,15 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
     p.index = a->index; p.k_cache = a->k_cache; p.ckv_cache = a->ckv_cache;
     p.k_scale = a->k_scale; p.k_offset = a->k_offset; p.v_scale = a->v_scale; p.v_offset = a->v_offset;
     p.k_rope = a->k_rope; p.c_kv = a->c_kv;
-    p.rows = a->batch * a->heads * a->seq;
-    p.seq = a->seq;
+    const int64_t rows = a->batch * a->heads * a->seq;
+    if (rows >= (1LL << 31) || capacity >= (1LL << 31) || a->batch * a->seq >= (1LL << 31))
+        return fail(QKNR_UNSUPPORTED, "more than 2^31 rows, tokens or cache slots in one call");
+    p.rows = (uint32_t)rows;
+    p.seq = (uint32_t)a->seq;
+    p.seq_div = qknr::make_fastdiv(p.seq);
+    p.heads_div = qknr::make_fastdiv((uint32_t)a->heads);
+    p.block_div = qknr::make_fastdiv((uint32_t)(a->cache_mode == QKNR_CACHE_NORM ? 1 : a->block_size));
+    p.stream_rope = s_bcast ? 0 : 1;
     p.kv_b = a->kv_strides[0]; p.kv_n = a->kv_strides[1]; p.kv_s = a->kv_strides[2];
     p.v_b = a->v_strides[0]; p.v_n = a->v_strides[1]; p.v_s = a->v_strides[2];
     p.rope_b = a->rope_strides[0]; p.rope_n = a->rope_strides[1]; p.rope_s = a->rope_strides[2];
@@ -315,8 +329,6 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
     int cr = 0, cx = 0;
     if (qknr::kv_plan(p, vec, v2, cr, cx) != 0)
         return fail(QKNR_UNSUPPORTED, "row too wide for one block's register plan");
-    const int64_t blocks = (p.rows + (256 / p.lanes_per_row) - 1) / (256 / p.lanes_per_row);
-    if (blocks > 0x7FFFFFFFLL) return fail(QKNR_UNSUPPORTED, "too many rows for one launch");
     plan.elem_type = a->dtype == QKNR_BF16 ? 1 : 2;
     plan.vec = vec;
     plan.v2 = v2;

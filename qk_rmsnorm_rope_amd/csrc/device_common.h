@@ -71,6 +71,40 @@ template <> struct Storage<f16_t> {
 
 template <int WORDS> struct Words { uint32_t w[WORDS]; };
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) accesses: data read or written exactly once is
+// marked so that it does not displace reused lines (gammas, tables, scales)
+// in the caches.
+template <int WORDS>
+__device__ __forceinline__ Words<WORDS> load_words_nt(const void *p) {
+    Words<WORDS> r;
+    if constexpr (WORDS == 4) {
+        u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else if constexpr (WORDS == 2) {
+        u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+        r.w[0] = v.x; r.w[1] = v.y;
+    } else {
+        r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+    }
+    return r;
+}
+
+template <int WORDS>
+__device__ __forceinline__ void store_words_nt(void *p, const Words<WORDS> &r) {
+    if constexpr (WORDS == 4) {
+        u32x4_t v = {r.w[0], r.w[1], r.w[2], r.w[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+    } else if constexpr (WORDS == 2) {
+        u32x2_t v = {r.w[0], r.w[1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(p));
+    } else {
+        __builtin_nontemporal_store(r.w[0], reinterpret_cast<uint32_t *>(p));
+    }
+}
+
 template <int WORDS>
 __device__ __forceinline__ Words<WORDS> load_words(const void *p) {
     Words<WORDS> r;
@@ -112,6 +146,17 @@ struct Chunk {
         Words<kWords> r = load_words<kWords>(p);
 #pragma unroll
         for (int i = 0; i < kWords; i++) w[i] = r.w[i];
+    }
+    __device__ __forceinline__ void load_nt(const T *p) {
+        Words<kWords> r = load_words_nt<kWords>(p);
+#pragma unroll
+        for (int i = 0; i < kWords; i++) w[i] = r.w[i];
+    }
+    __device__ __forceinline__ void store_nt(T *p) const {
+        Words<kWords> r;
+#pragma unroll
+        for (int i = 0; i < kWords; i++) r.w[i] = w[i];
+        store_words_nt<kWords>(p, r);
     }
     __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -176,6 +221,15 @@ __device__ __forceinline__ void store_vec(T *p, const float *in) {
 #pragma unroll
     for (int i = 0; i < W; i++) r.w[i] = Storage<T>::encode(in + i * Storage<T>::kPerWord);
     store_words<W>(p, r);
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void store_vec_nt(T *p, const float *in) {
+    constexpr int W = VEC * (int)sizeof(T) / 4;
+    Words<W> r;
+#pragma unroll
+    for (int i = 0; i < W; i++) r.w[i] = Storage<T>::encode(in + i * Storage<T>::kPerWord);
+    store_words_nt<W>(p, r);
 }
 
 // ---------------------------------------------------------------------------

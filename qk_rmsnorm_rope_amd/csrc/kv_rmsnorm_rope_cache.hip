@@ -20,13 +20,18 @@
 //   * quantisation (int8 RNE + clamp, or FP8 E4M3FN RNE saturating) is fused
 //     into the stores; each cache row is written by whole-chunk vector stores
 //     to its slot, so there are no atomics and each output byte has one writer;
-//   * an index of -1 (or, defensively, outside the cache) writes no cache row.
+//   * an index of -1 (or, defensively, outside the cache) writes no cache row;
+//   * data touched once (kv, v, per-row cos/sin, cache rows, k_rope, c_kv) moves
+//     with non-temporal loads and stores; gamma and the quantisation
+//     parameters, reused by every row, stay cached;
+//   * row -> (b, n, s) and slot -> (block, offset) use multiply-high division
+//     by the invariant sizes instead of 64-bit divides.
 #include "device_common.h"
 #include "launch.h"
 
 namespace qknr {
 
-// Store n = NB bytes of codes (one byte per element) at p (naturally aligned).
+// Store N codes (one byte each) at p (naturally aligned), streaming.
 template <int N>
 __device__ __forceinline__ void store_codes(void *p, const uint32_t *code) {
     if constexpr (N >= 4) {
@@ -35,7 +40,7 @@ __device__ __forceinline__ void store_codes(void *p, const uint32_t *code) {
 #pragma unroll
         for (int i = 0; i < W; i++)
             r.w[i] = code[4 * i] | (code[4 * i + 1] << 8) | (code[4 * i + 2] << 16) | (code[4 * i + 3] << 24);
-        store_words<W>(p, r);
+        store_words_nt<W>(p, r);
     } else if constexpr (N == 2) {
         *reinterpret_cast<uint16_t *>(p) = (uint16_t)(code[0] | (code[1] << 8));
     } else {
@@ -78,7 +83,7 @@ __device__ __forceinline__ void put_cache(void *row, int code, int c, const floa
                                           const float *scale, const float *offset, int qshape,
                                           int n, int width) {
     if (code == CODE_SAME) {
-        store_vec<T, N>(reinterpret_cast<T *>(row) + c, x);
+        store_vec_nt<T, N>(reinterpret_cast<T *>(row) + c, x);
         return;
     }
     float sc[N], of[N];
@@ -100,9 +105,6 @@ __device__ __forceinline__ void put_cache(void *row, int code, int c, const floa
     store_codes<N>(reinterpret_cast<uint8_t *>(row) + c, q);
 }
 
-template <int G>
-__device__ __forceinline__ float row_sum_g(float v) { return group_sum<G>(v); }
-
 __device__ __forceinline__ float row_sum(float v, int G) {
     switch (G) {
     case 8: return group_sum<8>(v);
@@ -117,13 +119,16 @@ __device__ __forceinline__ float row_sum(float v, int G) {
 // to half_rope + j0.. .
 template <typename T, int VEC>
 __device__ __forceinline__ void rope_chunk(const float *z, const T *cs, const T *sn, int j0, int half,
-                                           float *o1, float *o2) {
+                                           bool streaming, float *o1, float *o2) {
     constexpr int H = VEC / 2;
     float c1[H], c2[H], s1[H], s2[H];
-    load_vec<T, H>(cs + j0, c1);
-    load_vec<T, H>(cs + half + j0, c2);
-    load_vec<T, H>(sn + j0, s1);
-    load_vec<T, H>(sn + half + j0, s2);
+    Chunk<T, H> a, b2, c, d;
+    if (streaming) {
+        a.load_nt(cs + j0); b2.load_nt(cs + half + j0); c.load_nt(sn + j0); d.load_nt(sn + half + j0);
+    } else {
+        a.load(cs + j0); b2.load(cs + half + j0); c.load(sn + j0); d.load(sn + half + j0);
+    }
+    a.decode(c1); b2.decode(c2); c.decode(s1); d.decode(s2);
 #pragma unroll
     for (int m = 0; m < H; m++) {
         o1[m] = fmaf(z[2 * m], c1[m], -(z[2 * m + 1] * s1[m]));
@@ -135,15 +140,15 @@ template <typename T, int VEC, bool V2, int CR, int CX>
 __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) {
     const int G = p.lanes_per_row;
     const int gl = threadIdx.x & (G - 1);
-    const int64_t row = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
+    const uint32_t row = blockIdx.x * (uint32_t)(256 / G) + threadIdx.x / (uint32_t)G;
     const bool row_ok = row < p.rows;
 
-    int64_t b = 0, n = 0, s = 0;
+    uint32_t b = 0, n = 0, s = 0;
     if (row_ok) {
-        s = row % p.seq;
-        const int64_t bn = row / p.seq;
-        n = bn % p.heads;
-        b = bn / p.heads;
+        const uint32_t bn = fastdiv(row, p.seq_div);
+        s = row - bn * p.seq;
+        b = fastdiv(bn, p.heads_div);
+        n = bn - b * (uint32_t)p.heads;
     }
     const T *kv = reinterpret_cast<const T *>(p.kv) + b * p.kv_b + n * p.kv_n + s * p.kv_s;
 
@@ -152,16 +157,16 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
 #pragma unroll
     for (int i = 0; i < CR; i++) {
         const int c = gl + i * G;
-        if (row_ok && c < p.nr) x[i].load(kv + c * VEC); else x[i].zero();
+        if (row_ok && c < p.nr) x[i].load_nt(kv + c * VEC); else x[i].zero();
     }
     const T *zrow = V2 ? reinterpret_cast<const T *>(p.v) + b * p.v_b + n * p.v_n + s * p.v_s
                        : kv + p.rms_size;
 #pragma unroll
     for (int i = 0; i < CX; i++) {
         const int c = gl + i * G;
-        if (row_ok && c < p.nx) z[i].load(zrow + c * VEC); else z[i].zero();
+        if (row_ok && c < p.nx) z[i].load_nt(zrow + c * VEC); else z[i].zero();
     }
-    const int64_t slot = row_ok ? p.index[b * p.seq + s] : -1;
+    const int64_t slot = row_ok ? p.index[(uint64_t)b * p.seq + s] : -1;
 
     // ---- (1) RmsNorm statistic over rms_size values, reduced over the group
     float ss = 0.0f;
@@ -180,7 +185,8 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
             ko = b * p.kc0 + slot * p.kc1 + n * p.kc2;
             co = b * p.cc0 + slot * p.cc1 + n * p.cc2;
         } else {
-            const int64_t blk = slot / p.block_size, off = slot - blk * p.block_size;
+            const uint32_t blk = fastdiv((uint32_t)slot, p.block_div);     // slot < capacity < 2^31
+            const uint32_t off = (uint32_t)slot - blk * (uint32_t)p.block_size;
             ko = blk * p.kc0 + off * p.kc1 + n * p.kc2;
             co = blk * p.cc0 + off * p.cc1 + n * p.cc2;
         }
@@ -196,6 +202,7 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
     const T *cs = reinterpret_cast<const T *>(p.cos) + b * p.rope_b + n * p.rope_n + s * p.rope_s;
     const T *sn = reinterpret_cast<const T *>(p.sin) + b * p.rope_b + n * p.rope_n + s * p.rope_s;
     constexpr int H = VEC / 2;
+    const bool stream_rope = p.stream_rope != 0;
 
     // ---- normed chunks: y = x * inv_rms * gamma
 #pragma unroll
@@ -211,26 +218,26 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
             // V1: the normed row goes to the ckv cache and c_kv
             if (to_cache)
                 put_cache<T, VEC>(crow, p.c_code, c * VEC, y, p.v_scale, p.v_offset, p.v_qshape, (int)n, p.c_dim);
-            if (out_kv) store_vec<T, VEC>(c_kv + c * VEC, y);
+            if (out_kv) store_vec_nt<T, VEC>(c_kv + c * VEC, y);
         } else {
             if (c < p.n_rope_chunks) {
                 // V2: rotate the first rope_size normed values in place
                 float o1[H], o2[H];
                 const int j0 = c * H;
-                rope_chunk<T, VEC>(y, cs, sn, j0, p.half_rope, o1, o2);
+                rope_chunk<T, VEC>(y, cs, sn, j0, p.half_rope, stream_rope, o1, o2);
                 if (to_cache) {
                     put_cache<T, H>(krow, p.k_code, j0, o1, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim);
                     put_cache<T, H>(krow, p.k_code, p.half_rope + j0, o2, p.k_scale, p.k_offset, p.k_qshape,
                                     (int)n, p.k_dim);
                 }
                 if (out_kv) {
-                    store_vec<T, H>(k_rope + j0, o1);
-                    store_vec<T, H>(k_rope + p.half_rope + j0, o2);
+                    store_vec_nt<T, H>(k_rope + j0, o1);
+                    store_vec_nt<T, H>(k_rope + p.half_rope + j0, o2);
                 }
             } else {
                 if (to_cache)
                     put_cache<T, VEC>(krow, p.k_code, c * VEC, y, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim);
-                if (out_kv) store_vec<T, VEC>(k_rope + c * VEC, y);
+                if (out_kv) store_vec_nt<T, VEC>(k_rope + c * VEC, y);
             }
         }
     }
@@ -244,22 +251,21 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
             float zv[VEC], o1[H], o2[H];
             z[i].decode(zv);
             const int j0 = c * H;
-            rope_chunk<T, VEC>(zv, cs, sn, j0, p.half_rope, o1, o2);
+            rope_chunk<T, VEC>(zv, cs, sn, j0, p.half_rope, stream_rope, o1, o2);
             if (to_cache) {
                 put_cache<T, H>(krow, p.k_code, j0, o1, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim);
                 put_cache<T, H>(krow, p.k_code, p.half_rope + j0, o2, p.k_scale, p.k_offset, p.k_qshape, (int)n,
                                 p.k_dim);
             }
             if (out_kv) {
-                store_vec<T, H>(k_rope + j0, o1);
-                store_vec<T, H>(k_rope + p.half_rope + j0, o2);
+                store_vec_nt<T, H>(k_rope + j0, o1);
+                store_vec_nt<T, H>(k_rope + p.half_rope + j0, o2);
             }
         } else {
             // V2: v_optional goes to the ckv cache (quantised or copied) and to c_kv unchanged
             if (to_cache) {
                 if (p.c_code == CODE_SAME) {
-                    store_words<Chunk<T, VEC>::kWords>(reinterpret_cast<T *>(crow) + c * VEC,
-                                                       *reinterpret_cast<const Words<Chunk<T, VEC>::kWords> *>(z[i].w));
+                    z[i].store_nt(reinterpret_cast<T *>(crow) + c * VEC);
                 } else {
                     float zv[VEC];
                     z[i].decode(zv);
@@ -267,9 +273,7 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
                                       p.c_dim);
                 }
             }
-            if (out_kv)
-                store_words<Chunk<T, VEC>::kWords>(c_kv + c * VEC,
-                                                   *reinterpret_cast<const Words<Chunk<T, VEC>::kWords> *>(z[i].w));
+            if (out_kv) z[i].store_nt(c_kv + c * VEC);
         }
     }
 }
@@ -306,8 +310,8 @@ int kv_plan(KvParams &p, int vec, bool v2, int &cr, int &cx) {
 
 template <typename T, int VEC, bool V2>
 static hipError_t launch_t(const KvParams &p, int cr, int cx, hipStream_t stream) {
-    const int rows_per_block = 256 / p.lanes_per_row;
-    const int64_t blocks = (p.rows + rows_per_block - 1) / rows_per_block;
+    const uint32_t rows_per_block = 256 / p.lanes_per_row;
+    const uint32_t blocks = (p.rows + rows_per_block - 1) / rows_per_block;
     dim3 grid((unsigned)blocks), block(256);
 #define QKNR_KV(CRV, CXV)                                                                              \
     if (cr == CRV && cx == CXV) {                                                                      \

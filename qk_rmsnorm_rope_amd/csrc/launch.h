@@ -7,6 +7,36 @@
 
 namespace qknr {
 
+// Unsigned 32-bit division by a runtime-invariant divisor d >= 1 with a
+// multiply-high and two shifts: for l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (t + ((n - t) >> 1)) >> (l - 1)
+// with t = mulhi(n, m) (the round-up method of Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994); d = 1 uses
+// m = 0 and zero shifts. Exact for every n < 2^32.
+struct FastDiv {
+    uint32_t d, m, sh1, sh2;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f{d, 0u, 0u, 0u};
+    if (d <= 1) return f;
+    uint32_t l = 0;
+    while ((1ull << l) < d) l++;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    f.sh1 = 1;
+    f.sh2 = l - 1;
+    return f;
+}
+
+__host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv &f) {
+#ifdef __HIP_DEVICE_COMPILE__
+    const uint32_t t = __umulhi(n, f.m);
+#else
+    const uint32_t t = (uint32_t)(((uint64_t)n * f.m) >> 32);
+#endif
+    return (t + ((n - t) >> f.sh1)) >> f.sh2;
+}
+
 // (a) across-heads QK RMSNorm + rotate-half RoPE
 struct QkParams {
     const void *q_in;
@@ -17,15 +47,18 @@ struct QkParams {
     const void *k_gamma;
     const void *cos;
     const void *sin;
-    int64_t tokens;            // B*S
-    int64_t seq;
-    int64_t in_batch_stride, in_token_stride, in_head_stride;
-    int64_t out_batch_stride, out_token_stride, out_head_stride;
+    int64_t in_batch_stride, in_token_stride;
+    int64_t out_batch_stride, out_token_stride;
     int64_t rope_batch_stride, rope_token_stride;
+    uint32_t tokens;           // B*S (< 2^31)
+    uint32_t seq;
+    FastDiv seq_div;           // token -> (b, s)
+    uint32_t in_head_stride, out_head_stride;   // elements; head offsets fit 32 bits
     int32_t n_q, n_k, head_dim, half;
     int32_t chunks_per_half;   // half / VEC
     int32_t heads_per_step;    // 64 / chunks_per_half
-    int32_t waves_per_token;   // 1, 2 or 4
+    int32_t waves_per_unit;    // W: waves sharing one (token, segment), 1, 2 or 4
+    int32_t segs;              // 2 with a K segment, 1 for Q only
     int32_t apply_norm, apply_rope;
     float q_channels, k_channels, eps;
 };
@@ -51,8 +84,9 @@ struct KvParams {
     const float *k_scale, *k_offset, *v_scale, *v_offset;
     void *k_rope;
     void *c_kv;
-    int64_t rows;              // B*N*S
-    int64_t seq;
+    uint32_t rows;             // B*N*S (< 2^31)
+    uint32_t seq;
+    FastDiv seq_div, heads_div, block_div;   // row -> (b, n, s); slot -> (block, offset)
     int64_t kv_b, kv_n, kv_s;
     int64_t v_b, v_n, v_s;
     int64_t rope_b, rope_n, rope_s;
@@ -73,6 +107,7 @@ struct KvParams {
     int32_t k_code, c_code;    // CacheCode
     int32_t k_qshape, v_qshape;
     int32_t out_kv;
+    int32_t stream_rope;       // cos/sin read once (no S-axis broadcast): streaming loads
     float eps;
 };
 

@@ -7,186 +7,185 @@
 // one GPU so step b's all-reduce disappears (tp = 1).
 //
 // MI355X design (not the Trainium one): the pass is HBM-bound (about 2 flops
-// per byte), so the kernel is one read and one write of Q|K:
-//   * one wavefront per token (W = 1) or W waves per token for very wide
-//     segments; each lane owns the chunk pair (i, i + d/2) of J heads, so the
-//     rotate-half partner of every element is in the same lane and no
-//     cross-lane shuffle is needed;
+// per byte), so the kernel is exactly one read and one write of Q|K:
+//   * one wavefront per (token, segment) unit -- the Q segment and the K
+//     segment of a token are independent reductions, so splitting them halves
+//     the registers a wave holds and doubles the waves in flight; very wide
+//     segments use W = 2 or 4 waves per unit, joined through LDS;
+//   * each lane owns the chunk pair (i, i + d/2) of J heads, so the
+//     rotate-half partner of every element is in the same lane: no shuffles;
 //   * lane k of every head group reads the same cos/sin chunks, so each lane
-//     loads its cos/sin once per token and reuses it for all its heads and
-//     for both segments;
-//   * 16-byte loads and stores (8 bf16 or 4 fp32 per access); consecutive
-//     lanes cover whole 128-byte lines;
-//   * the sum of squares is fp32 in registers, reduced across the wave with
-//     DPP (no LDS), across waves through LDS when W > 1;
-//   * inv_rms is multiplied into cos and sin once per lane
-//     (r*cos, r*sin), so the per-element work is
-//     y = x*gamma; out = y*rc - y_partner*rs.
+//     loads its cos/sin once per unit and reuses them for all its heads;
+//   * 16-byte non-temporal loads and stores for Q/K (read once, written once),
+//     ordinary cached loads for the reused gammas and position tables;
+//   * addresses are a wave-uniform 64-bit base (scalar registers) plus a
+//     32-bit per-lane offset, and the head geometry is a compile-time constant
+//     for the usual head sizes, so address arithmetic costs few VGPRs;
+//   * the sum of squares is fp32 (v_dot2 on packed 16-bit pairs), reduced with
+//     DPP inside the wave, and inv_rms is folded into cos/sin once per lane:
+//     per element y = x*gamma; out = y*(r*cos) -/+ y_partner*(r*sin).
 #include "device_common.h"
 #include "launch.h"
 
+#ifndef QKNR_QK_STREAMING
+#define QKNR_QK_STREAMING 1   // non-temporal Q/K loads and stores
+#endif
+
 namespace qknr {
 
-template <typename T, int VEC, int J>
+template <typename T, int VEC>
+__device__ __forceinline__ void load_stream(Chunk<T, VEC> &c, const T *p) {
+#if QKNR_QK_STREAMING
+    c.load_nt(p);
+#else
+    c.load(p);
+#endif
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void store_stream(T *p, const float *v) {
+#if QKNR_QK_STREAMING
+    store_vec_nt<T, VEC>(p, v);
+#else
+    store_vec<T, VEC>(p, v);
+#endif
+}
+
+// KC: chunks per half head known at compile time (0: read p.chunks_per_half).
+template <typename T, int VEC, int KC, int J>
 __global__ __launch_bounds__(256) void qk_across_heads_kernel(QkParams p) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;                 // 0..3
-    const int W = p.waves_per_token;                   // 1, 2 or 4
-    const int token_in_block = wave / W;
-    const int wave_in_token = wave - token_in_block * W;
-    const int64_t t = (int64_t)blockIdx.x * (4 / W) + token_in_block;
-    const bool token_ok = t < p.tokens;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..3, wave-uniform
+    const int W = p.waves_per_unit;
+    const int unit_in_block = wave / W;
+    const int wave_in_unit = wave - unit_in_block * W;
+    const uint32_t unit = blockIdx.x * (uint32_t)(4 / W) + unit_in_block;
+    const uint32_t t = p.segs == 2 ? unit >> 1 : unit;
+    const int seg = p.segs == 2 ? (int)(unit & 1u) : 0;
+    const bool unit_ok = t < p.tokens;
+    if (W == 1 && !unit_ok) return;                     // no barrier follows when W == 1
 
-    const int kc = p.chunks_per_half;                  // d/2 / VEC
-    const int hpw = p.heads_per_step;                  // 64 / kc
+    const int kc = KC ? KC : p.chunks_per_half;
+    const int hpw = 64 / kc;                            // heads covered by one wave step
+    const int half = kc * VEC;
     const int k = lane % kc;
     const int hsub = lane / kc;
-    const bool lane_ok = token_ok && hsub < hpw;
-    const int half = p.half;
+    const bool lane_ok = unit_ok && hsub < hpw;
 
-    int64_t b = 0, s = 0;
-    if (token_ok) { b = t / p.seq; s = t - b * p.seq; }
-    const int64_t in_base = b * p.in_batch_stride + s * p.in_token_stride;
-    const int64_t out_base = b * p.out_batch_stride + s * p.out_token_stride;
-    const int64_t rope_base = b * p.rope_batch_stride + s * p.rope_token_stride;
+    uint32_t b = 0, s = 0;
+    if (unit_ok) {
+        b = fastdiv(t, p.seq_div);
+        s = t - b * p.seq;
+    }
+    const int nh = seg ? p.n_k : p.n_q;
+    const T *x = reinterpret_cast<const T *>(seg ? p.k_in : p.q_in) + b * p.in_batch_stride +
+                 s * p.in_token_stride;
+    // per-lane byte offset inside the token (32-bit; checked on the host)
+    const uint32_t lane_in = ((uint32_t)hsub * p.in_head_stride + (uint32_t)(k * VEC)) * (uint32_t)sizeof(T);
 
-    const T *qi = reinterpret_cast<const T *>(p.q_in);
-    const T *ki = reinterpret_cast<const T *>(p.k_in);
-
-    // Raw (packed) chunks of this lane's heads: (lo, hi) = lanes [kVEC, kVEC+VEC)
-    // and their rotate-half partners d/2 further on.
-    Chunk<T, VEC> qlo[J], qhi[J], klo[J], khi[J];
+    Chunk<T, VEC> lo[J], hi[J];
 #pragma unroll
     for (int j = 0; j < J; j++) {
-        const int h = (j * W + wave_in_token) * hpw + hsub;
-        const int64_t off = in_base + (int64_t)h * p.in_head_stride + k * VEC;
-        if (lane_ok && h < p.n_q) {
-            qlo[j].load(qi + off);
-            qhi[j].load(qi + off + half);
+        const int hb = (j * W + wave_in_unit) * hpw;    // first head of this step (uniform)
+        const char *xj = reinterpret_cast<const char *>(x + (uint64_t)hb * p.in_head_stride) + lane_in;
+        if (lane_ok && hb + hsub < nh) {
+            load_stream<T, VEC>(lo[j], reinterpret_cast<const T *>(xj));
+            load_stream<T, VEC>(hi[j], reinterpret_cast<const T *>(xj) + half);
         } else {
-            qlo[j].zero();
-            qhi[j].zero();
-        }
-        if (lane_ok && h < p.n_k) {
-            klo[j].load(ki + off);
-            khi[j].load(ki + off + half);
-        } else {
-            klo[j].zero();
-            khi[j].zero();
+            lo[j].zero();
+            hi[j].zero();
         }
     }
 
     Chunk<T, VEC> c_lo, c_hi, s_lo, s_hi;
     const bool rope = p.apply_rope != 0;
     if (rope && lane_ok) {
-        const T *cs = reinterpret_cast<const T *>(p.cos) + rope_base + k * VEC;
-        const T *sn = reinterpret_cast<const T *>(p.sin) + rope_base + k * VEC;
+        const int64_t rb = b * p.rope_batch_stride + s * p.rope_token_stride + k * VEC;
+        const T *cs = reinterpret_cast<const T *>(p.cos) + rb;
+        const T *sn = reinterpret_cast<const T *>(p.sin) + rb;
         c_lo.load(cs);
         c_hi.load(cs + half);
         s_lo.load(sn);
         s_hi.load(sn + half);
     }
 
-    float rq = 1.0f, rk = 1.0f;
+    float r = 1.0f;
     if (p.apply_norm) {
-        float sq = 0.0f, sk = 0.0f;
+        float ss = 0.0f;
 #pragma unroll
-        for (int j = 0; j < J; j++) {
-            sq = qhi[j].sumsq(qlo[j].sumsq(sq));
-            sk = khi[j].sumsq(klo[j].sumsq(sk));
-        }
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
+        for (int j = 0; j < J; j++) ss = hi[j].sumsq(lo[j].sumsq(ss));
+        ss = wave_sum(ss);
         if (W > 1) {
-            __shared__ float part[4][2];
-            if (lane == 0) { part[wave][0] = sq; part[wave][1] = sk; }
+            __shared__ float part[4];
+            if (lane == 0) part[wave] = ss;
             __syncthreads();
-            sq = 0.0f;
-            sk = 0.0f;
-            for (int w = 0; w < W; w++) {                 // fixed order: deterministic
-                sq += part[token_in_block * W + w][0];
-                sk += part[token_in_block * W + w][1];
-            }
+            ss = 0.0f;
+            for (int w = 0; w < W; w++) ss += part[unit_in_block * W + w];   // fixed order
         }
-        rq = rsqrtf(sq / p.q_channels + p.eps);
-        rk = rsqrtf(sk / p.k_channels + p.eps);
+        r = rsqrtf(ss / (seg ? p.k_channels : p.q_channels) + p.eps);
     }
     if (!lane_ok) return;
 
-    // inv_rms folded into the rotation coefficients, one set per segment:
-    //   out_lo = y_lo*(r*cos_lo) - y_hi*(r*sin_lo),  out_hi = y_hi*(r*cos_hi) + y_lo*(r*sin_hi)
-    float qc_lo[VEC], qc_hi[VEC], qs_lo[VEC], qs_hi[VEC];
-    float kc_lo[VEC], kc_hi[VEC], ks_lo[VEC], ks_hi[VEC];
-    {
-        float clo[VEC], chi[VEC], slo[VEC], shi[VEC];
-        if (rope) {
-            c_lo.decode(clo); c_hi.decode(chi); s_lo.decode(slo); s_hi.decode(shi);
-        } else {
+    // inv_rms folded into the rotation coefficients
+    float rc_lo[VEC], rc_hi[VEC], rs_lo[VEC], rs_hi[VEC];
+    if (rope) {
+        c_lo.decode(rc_lo);
+        c_hi.decode(rc_hi);
+        s_lo.decode(rs_lo);
+        s_hi.decode(rs_hi);
 #pragma unroll
-            for (int e = 0; e < VEC; e++) { clo[e] = 1.0f; chi[e] = 1.0f; slo[e] = 0.0f; shi[e] = 0.0f; }
-        }
+        for (int e = 0; e < VEC; e++) { rc_lo[e] *= r; rc_hi[e] *= r; rs_lo[e] *= r; rs_hi[e] *= r; }
+    } else {
 #pragma unroll
-        for (int e = 0; e < VEC; e++) {
-            qc_lo[e] = rq * clo[e]; qc_hi[e] = rq * chi[e]; qs_lo[e] = rq * slo[e]; qs_hi[e] = rq * shi[e];
-            kc_lo[e] = rk * clo[e]; kc_hi[e] = rk * chi[e]; ks_lo[e] = rk * slo[e]; ks_hi[e] = rk * shi[e];
-        }
+        for (int e = 0; e < VEC; e++) { rc_lo[e] = r; rc_hi[e] = r; rs_lo[e] = 0.0f; rs_hi[e] = 0.0f; }
     }
 
-    T *qo = reinterpret_cast<T *>(p.q_out);
-    T *ko = reinterpret_cast<T *>(p.k_out);
-    const T *qg = reinterpret_cast<const T *>(p.q_gamma);
-    const T *kg = reinterpret_cast<const T *>(p.k_gamma);
+    T *o = reinterpret_cast<T *>(seg ? p.k_out : p.q_out) + b * p.out_batch_stride + s * p.out_token_stride;
+    const uint32_t lane_out = ((uint32_t)hsub * p.out_head_stride + (uint32_t)(k * VEC)) * (uint32_t)sizeof(T);
+    const T *g = reinterpret_cast<const T *>(seg ? p.k_gamma : p.q_gamma);
+    const uint32_t lane_g = (uint32_t)(hsub * p.head_dim + k * VEC) * (uint32_t)sizeof(T);
     const bool norm = p.apply_norm != 0;
 
 #pragma unroll
     for (int j = 0; j < J; j++) {
-        const int h = (j * W + wave_in_token) * hpw + hsub;
-        const int64_t off = out_base + (int64_t)h * p.out_head_stride + k * VEC;
-        const int64_t goff = (int64_t)h * p.head_dim + k * VEC;
+        const int hb = (j * W + wave_in_unit) * hpw;
+        if (hb + hsub >= nh) continue;
+        float xl[VEC], xh[VEC], gl[VEC], gh[VEC], ol[VEC], oh[VEC];
+        lo[j].decode(xl);
+        hi[j].decode(xh);
+        if (norm) {
+            const T *gj = reinterpret_cast<const T *>(reinterpret_cast<const char *>(g + (uint64_t)hb * p.head_dim) +
+                                                      lane_g);
+            load_vec<T, VEC>(gj, gl);
+            load_vec<T, VEC>(gj + half, gh);
+        } else {
 #pragma unroll
-        for (int seg = 0; seg < 2; seg++) {
-            const int nh = seg == 0 ? p.n_q : p.n_k;
-            if (h >= nh) continue;
-            const T *g = seg == 0 ? qg : kg;
-            T *o = seg == 0 ? qo : ko;
-            const float *cl = seg == 0 ? qc_lo : kc_lo;
-            const float *ch = seg == 0 ? qc_hi : kc_hi;
-            const float *sl = seg == 0 ? qs_lo : ks_lo;
-            const float *sh = seg == 0 ? qs_hi : ks_hi;
-            float xlo[VEC], xhi[VEC], glo[VEC], ghi[VEC], olo[VEC], ohi[VEC];
-            (seg == 0 ? qlo[j] : klo[j]).decode(xlo);
-            (seg == 0 ? qhi[j] : khi[j]).decode(xhi);
-            if (norm) {
-                load_vec<T, VEC>(g + goff, glo);
-                load_vec<T, VEC>(g + goff + half, ghi);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; e++) { glo[e] = 1.0f; ghi[e] = 1.0f; }
-            }
-#pragma unroll
-            for (int e = 0; e < VEC; e++) {
-                const float ylo = xlo[e] * glo[e];
-                const float yhi = xhi[e] * ghi[e];
-                olo[e] = fmaf(ylo, cl[e], -(yhi * sl[e]));
-                ohi[e] = fmaf(yhi, ch[e], ylo * sh[e]);
-            }
-            store_vec<T, VEC>(o + off, olo);
-            store_vec<T, VEC>(o + off + half, ohi);
+            for (int e = 0; e < VEC; e++) { gl[e] = 1.0f; gh[e] = 1.0f; }
         }
+#pragma unroll
+        for (int e = 0; e < VEC; e++) {
+            const float yl = xl[e] * gl[e];
+            const float yh = xh[e] * gh[e];
+            ol[e] = fmaf(yl, rc_lo[e], -(yh * rs_lo[e]));
+            oh[e] = fmaf(yh, rc_hi[e], yl * rs_hi[e]);
+        }
+        T *oj = reinterpret_cast<T *>(reinterpret_cast<char *>(o + (uint64_t)hb * p.out_head_stride) + lane_out);
+        store_stream<T, VEC>(oj, ol);
+        store_stream<T, VEC>(oj + half, oh);
     }
 }
 
 // ---------------------------------------------------------------------------
-// launcher: picks VEC (16-byte or scalar access), W and J
+// launcher: picks the head-geometry specialisation, W and J
 // ---------------------------------------------------------------------------
 
-template <typename T, int VEC>
-static hipError_t launch_vec(const QkParams &p, int J, hipStream_t stream) {
-    const int tokens_per_block = 4 / p.waves_per_token;
-    const int64_t blocks = (p.tokens + tokens_per_block - 1) / tokens_per_block;
-    dim3 grid((unsigned)blocks), block(256);
+template <typename T, int VEC, int KC>
+static hipError_t launch_kc(const QkParams &p, int J, hipStream_t stream) {
+    const uint32_t units = p.tokens * (uint32_t)p.segs;
+    const uint32_t per_block = 4 / p.waves_per_unit;
+    dim3 grid((units + per_block - 1) / per_block), block(256);
 #define QKNR_CASE(JJ) \
-    case JJ: hipLaunchKernelGGL((qk_across_heads_kernel<T, VEC, JJ>), grid, block, 0, stream, p); break;
+    case JJ: hipLaunchKernelGGL((qk_across_heads_kernel<T, VEC, KC, JJ>), grid, block, 0, stream, p); break;
     switch (J) {
         QKNR_CASE(1) QKNR_CASE(2) QKNR_CASE(3) QKNR_CASE(4) QKNR_CASE(5) QKNR_CASE(6) QKNR_CASE(8)
         default: return hipErrorInvalidValue;
@@ -195,15 +194,22 @@ static hipError_t launch_vec(const QkParams &p, int J, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename T, int VEC>
+static hipError_t launch_vec(const QkParams &p, int J, hipStream_t stream) {
+    switch (p.chunks_per_half) {
+    case 4: return launch_kc<T, VEC, 4>(p, J, stream);
+    case 8: return launch_kc<T, VEC, 8>(p, J, stream);
+    case 16: return launch_kc<T, VEC, 16>(p, J, stream);
+    default: return launch_kc<T, VEC, 0>(p, J, stream);
+    }
+}
+
 static int round_up_j(int j) {
     if (j <= 6) return j;
     if (j <= 8) return 8;
     return -1;
 }
 
-// Geometry only (host side, no device access): fills chunks_per_half,
-// heads_per_step, waves_per_token and returns J (> 0), or -1 if the shape does
-// not fit the register budget of one 256-thread block.
 int qk_plan(QkParams &p, int vec) {
     const int half = p.head_dim / 2;
     if (half % vec) return -1;
@@ -212,13 +218,12 @@ int qk_plan(QkParams &p, int vec) {
     const int hpw = 64 / kc;
     const int heads = p.n_q > p.n_k ? p.n_q : p.n_k;
     for (int W = 1; W <= 4; W *= 2) {
-        int J = (heads + hpw * W - 1) / (hpw * W);
-        J = round_up_j(J);
+        const int J = round_up_j((heads + hpw * W - 1) / (hpw * W));
         if (J > 0) {
             p.half = half;
             p.chunks_per_half = kc;
             p.heads_per_step = hpw;
-            p.waves_per_token = W;
+            p.waves_per_unit = W;
             return J;
         }
     }
@@ -231,11 +236,11 @@ hipError_t qk_launch(QkParams &p, int elem_type, int vec, hipStream_t stream) {
     if (p.tokens == 0) return hipSuccess;
     switch (elem_type) {
     case 0:  // f32: 16-byte chunks, or single elements
-        return vec == 4 ? launch_vec<float, 4>(p, J, stream) : launch_vec<float, 1>(p, J, stream);
+        return vec == 4 ? launch_vec<float, 4>(p, J, stream) : launch_kc<float, 1, 0>(p, J, stream);
     case 1:  // bf16: 16-byte chunks, or pairs
-        return vec == 8 ? launch_vec<bf16_t, 8>(p, J, stream) : launch_vec<bf16_t, 2>(p, J, stream);
+        return vec == 8 ? launch_vec<bf16_t, 8>(p, J, stream) : launch_kc<bf16_t, 2, 0>(p, J, stream);
     case 2:  // f16
-        return vec == 8 ? launch_vec<f16_t, 8>(p, J, stream) : launch_vec<f16_t, 2>(p, J, stream);
+        return vec == 8 ? launch_vec<f16_t, 8>(p, J, stream) : launch_kc<f16_t, 2, 0>(p, J, stream);
     }
     return hipErrorInvalidValue;
 }
