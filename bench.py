@@ -10,8 +10,8 @@ the timed steps), tokens/s, the roofline of the kernel (bytes it must move /
 its average launch time, measured with HIP events on the launch stream, vs
 MI355X's 8 TB/s), the fp64 CPU oracle timed on a bounded sample of the same
 workload, and the KvRmsNormRopeCache workloads (MLA V1 prefill, V1 decode
-quantised, V2 split) timed the same way, cold (L2 and MALL flushed by a 1 GiB
-write before every launch) and hot.
+quantised, V2 split) timed the same way, cold (L2 and MALL evicted by reading
+1 GiB before every launch) and hot.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv]
        python bench.py --profile {across,kv_v1_prefill,kv_v1_decode,kv_v2,copy}
@@ -89,9 +89,8 @@ def across_setup(torch, W, Q):
     qo = out[..., : nq * hd].unflatten(-1, (nq, hd))
     ko = out[..., nq * hd:].unflatten(-1, (nk, hd))
 
-    def step():
-        Q.qk_norm_rope_across_heads(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"], eps=cfg.eps,
-                                    q_out=qo, k_out=ko)
+    step = Q.prepare_qk_norm_rope_across_heads(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"],
+                                               eps=cfg.eps, q_out=qo, k_out=ko)
     return cfg, d, step
 
 
@@ -99,12 +98,11 @@ def kv_setup(torch, W, Q, cfg):
     d = W.make_kv_cache(cfg, device="cuda", prefill=False)
     mode = "Norm" if cfg.cache_mode == W.NORM else "PA_BNSD"
 
-    def step():
-        Q.kv_rmsnorm_rope_cache(d["kv"], d["gamma"], d["cos"], d["sin"], d["index"], d["k_cache"],
-                                d["ckv_cache"], k_rope_scale=d["k_scale"], k_rope_offset=d["k_offset"],
-                                c_kv_scale=d["v_scale"], c_kv_offset=d["v_offset"], v=d["v"],
-                                epsilon=cfg.eps, cache_mode=mode, is_output_kv=cfg.is_output_kv,
-                                k_rope=d["k_rope"], c_kv=d["c_kv"])
+    step = Q.prepare_kv_rmsnorm_rope_cache(
+        d["kv"], d["gamma"], d["cos"], d["sin"], d["index"], d["k_cache"], d["ckv_cache"],
+        k_rope_scale=d["k_scale"], k_rope_offset=d["k_offset"], c_kv_scale=d["v_scale"],
+        c_kv_offset=d["v_offset"], v=d["v"], epsilon=cfg.eps, cache_mode=mode,
+        is_output_kv=cfg.is_output_kv, k_rope=d["k_rope"], c_kv=d["c_kv"])
     return d, step
 
 
@@ -122,11 +120,14 @@ def time_hot(torch, step, iters):
 
 
 def time_cold(torch, step, iters, flush):
-    """Each launch timed alone after a 1 GiB write evicts L2 and the MALL."""
+    """Each launch timed alone after reading 1 GiB, which evicts L2 and the
+    256 MB MALL with clean lines (a write would leave dirty lines whose
+    write-back then overlaps the timed launch)."""
     s = torch.cuda.current_stream()
+    sink = torch.zeros((), dtype=flush.dtype, device=flush.device)
     times = []
     for _ in range(iters):
-        flush.add_(1)
+        sink.copy_(flush.sum())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
         step()
@@ -354,7 +355,7 @@ def main():
     achieved = nbytes / launch_us / 1e3          # GB/s per launch
     value = nbytes * args.steps / wall / 1e9
 
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
     cold_us = time_cold(torch, step, args.cold_iters, flush)
     copy_src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
     copy_dst = torch.empty_like(copy_src)

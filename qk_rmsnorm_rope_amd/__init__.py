@@ -207,6 +207,29 @@ def qk_norm_rope_across_heads(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=No
     return q_out, k_out
 
 
+def prepare_qk_norm_rope_across_heads(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
+                                      apply_norm=True, apply_rope=True, stream=None):
+    """Marshal the arguments once and return a zero-argument callable that
+    launches (a) on the chosen stream (torch's current stream at preparation
+    time by default). The tensors must stay alive and unmoved while the
+    callable is used; each call re-validates on the host (a few microseconds)."""
+    if q_out is None:
+        q_out = q
+    if k is not None and k_out is None:
+        k_out = k
+    a = qk_args(q, k, q_gamma, k_gamma, cos, sin, eps=eps, q_out=q_out, k_out=k_out,
+                apply_norm=apply_norm, apply_rope=apply_rope)
+    st = _stream(q.device, stream)
+    ref = ctypes.byref(a)
+    fn = _lib.qknr_qk_norm_rope_across_heads
+    keep = (q, k, q_out, k_out, q_gamma, k_gamma, cos, sin)
+
+    def launch():
+        _check(fn(ref, st))
+    launch.args, launch.tensors = a, keep
+    return launch
+
+
 def qk_validate(a: QkArgs) -> int:
     """Host-only validation of filled arguments; returns the status code."""
     return int(_lib.qknr_qk_validate(ctypes.byref(a)))
@@ -365,6 +388,30 @@ def kv_rmsnorm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, *, k_r
     with torch.cuda.device(kv.device):
         _check(_lib.qknr_kv_rmsnorm_rope_cache(ctypes.byref(a), _stream(kv.device, stream)))
     return (k_rope, c_kv) if is_output_kv else (None, None)
+
+
+def prepare_kv_rmsnorm_rope_cache(kv, gamma, cos, sin, index, k_cache, ckv_cache, *, k_rope_scale=None,
+                                  c_kv_scale=None, k_rope_offset=None, c_kv_offset=None, v=None,
+                                  epsilon=1e-5, cache_mode="Norm", is_output_kv=False, k_rope=None,
+                                  c_kv=None, stream=None):
+    """Marshal the arguments of :func:`kv_rmsnorm_rope_cache` once and return a
+    zero-argument callable that launches the operator (for decode loops and
+    timing, where per-call Python marshalling would dominate a few-microsecond
+    kernel). The tensors must stay alive and unmoved while it is used."""
+    a = kv_args(kv, gamma, cos, sin, index, k_cache, ckv_cache, k_rope_scale=k_rope_scale,
+                c_kv_scale=c_kv_scale, k_rope_offset=k_rope_offset, c_kv_offset=c_kv_offset, v=v,
+                epsilon=epsilon, cache_mode=cache_mode, is_output_kv=is_output_kv, k_rope=k_rope,
+                c_kv=c_kv)
+    st = _stream(kv.device, stream)
+    ref = ctypes.byref(a)
+    fn = _lib.qknr_kv_rmsnorm_rope_cache
+    keep = (kv, gamma, cos, sin, index, k_cache, ckv_cache, k_rope_scale, c_kv_scale, k_rope_offset,
+            c_kv_offset, v, k_rope, c_kv)
+
+    def launch():
+        _check(fn(ref, st))
+    launch.args, launch.tensors = a, keep
+    return launch
 
 
 def kv_validate(a: KvArgs) -> int:

@@ -21,9 +21,12 @@
 //     into the stores; each cache row is written by whole-chunk vector stores
 //     to its slot, so there are no atomics and each output byte has one writer;
 //   * an index of -1 (or, defensively, outside the cache) writes no cache row;
-//   * data touched once (kv, v, per-row cos/sin, cache rows, k_rope, c_kv) moves
-//     with non-temporal loads and stores; gamma and the quantisation
-//     parameters, reused by every row, stay cached;
+//   * data read once (kv, v, per-row cos/sin) moves with non-temporal loads;
+//     k_rope / c_kv and cache rows made of whole 128-byte lines with
+//     non-temporal stores; cache rows that cover lines only in part (e.g. 192-
+//     or 64-byte int8 rows) with ordinary stores, so that neighbouring rows
+//     written by other waves merge in L2 before they reach HBM; gamma and the
+//     quantisation parameters, reused by every row, stay cached;
 //   * row -> (b, n, s) and slot -> (block, offset) use multiply-high division
 //     by the invariant sizes instead of 64-bit divides.
 #include "device_common.h"
@@ -31,16 +34,16 @@
 
 namespace qknr {
 
-// Store N codes (one byte each) at p (naturally aligned), streaming.
+// Store N codes (one byte each) at p (naturally aligned).
 template <int N>
-__device__ __forceinline__ void store_codes(void *p, const uint32_t *code) {
+__device__ __forceinline__ void store_codes(void *p, const uint32_t *code, bool nt) {
     if constexpr (N >= 4) {
         constexpr int W = N / 4;
         Words<W> r;
 #pragma unroll
         for (int i = 0; i < W; i++)
             r.w[i] = code[4 * i] | (code[4 * i + 1] << 8) | (code[4 * i + 2] << 16) | (code[4 * i + 3] << 24);
-        store_words_nt<W>(p, r);
+        if (nt) store_words_nt<W>(p, r); else store_words<W>(p, r);
     } else if constexpr (N == 2) {
         *reinterpret_cast<uint16_t *>(p) = (uint16_t)(code[0] | (code[1] << 8));
     } else {
@@ -81,9 +84,10 @@ __device__ __forceinline__ void load_qparam(const float *p, int shape, int n, in
 template <typename T, int N>
 __device__ __forceinline__ void put_cache(void *row, int code, int c, const float *x,
                                           const float *scale, const float *offset, int qshape,
-                                          int n, int width) {
+                                          int n, int width, bool nt) {
     if (code == CODE_SAME) {
-        store_vec_nt<T, N>(reinterpret_cast<T *>(row) + c, x);
+        if (nt) store_vec_nt<T, N>(reinterpret_cast<T *>(row) + c, x);
+        else store_vec<T, N>(reinterpret_cast<T *>(row) + c, x);
         return;
     }
     float sc[N], of[N];
@@ -102,7 +106,7 @@ __device__ __forceinline__ void put_cache(void *row, int code, int c, const floa
 #pragma unroll
         for (int i = 0; i < N; i++) q[i] = enc_e4m3fn(fmaf(x[i], sc[i], of[i]));
     }
-    store_codes<N>(reinterpret_cast<uint8_t *>(row) + c, q);
+    store_codes<N>(reinterpret_cast<uint8_t *>(row) + c, q, nt);
 }
 
 __device__ __forceinline__ float row_sum(float v, int G) {
@@ -136,8 +140,11 @@ __device__ __forceinline__ void rope_chunk(const float *z, const T *cs, const T 
     }
 }
 
+// The occupancy hint (at least 6 waves per SIMD, 4 for the widest rows) keeps register use low enough
+// for many rows in flight; the planner's shapes fit without spilling.
 template <typename T, int VEC, bool V2, int CR, int CX>
-__global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CR >= 4 ? 4 : 6, 8))) void kv_rmsnorm_rope_cache_kernel(
+    KvParams p) {
     const int G = p.lanes_per_row;
     const int gl = threadIdx.x & (G - 1);
     const uint32_t row = blockIdx.x * (uint32_t)(256 / G) + threadIdx.x / (uint32_t)G;
@@ -203,6 +210,7 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
     const T *sn = reinterpret_cast<const T *>(p.sin) + b * p.rope_b + n * p.rope_n + s * p.rope_s;
     constexpr int H = VEC / 2;
     const bool stream_rope = p.stream_rope != 0;
+    const bool k_nt = p.k_rows_whole_lines != 0, c_nt = p.c_rows_whole_lines != 0;
 
     // ---- normed chunks: y = x * inv_rms * gamma
 #pragma unroll
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
         if constexpr (!V2) {
             // V1: the normed row goes to the ckv cache and c_kv
             if (to_cache)
-                put_cache<T, VEC>(crow, p.c_code, c * VEC, y, p.v_scale, p.v_offset, p.v_qshape, (int)n, p.c_dim);
+                put_cache<T, VEC>(crow, p.c_code, c * VEC, y, p.v_scale, p.v_offset, p.v_qshape, (int)n, p.c_dim, c_nt);
             if (out_kv) store_vec_nt<T, VEC>(c_kv + c * VEC, y);
         } else {
             if (c < p.n_rope_chunks) {
@@ -226,9 +234,9 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
                 const int j0 = c * H;
                 rope_chunk<T, VEC>(y, cs, sn, j0, p.half_rope, stream_rope, o1, o2);
                 if (to_cache) {
-                    put_cache<T, H>(krow, p.k_code, j0, o1, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim);
+                    put_cache<T, H>(krow, p.k_code, j0, o1, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim, k_nt);
                     put_cache<T, H>(krow, p.k_code, p.half_rope + j0, o2, p.k_scale, p.k_offset, p.k_qshape,
-                                    (int)n, p.k_dim);
+                                    (int)n, p.k_dim, k_nt);
                 }
                 if (out_kv) {
                     store_vec_nt<T, H>(k_rope + j0, o1);
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
                 }
             } else {
                 if (to_cache)
-                    put_cache<T, VEC>(krow, p.k_code, c * VEC, y, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim);
+                    put_cache<T, VEC>(krow, p.k_code, c * VEC, y, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim, k_nt);
                 if (out_kv) store_vec_nt<T, VEC>(k_rope + c * VEC, y);
             }
         }
@@ -253,9 +261,9 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
             const int j0 = c * H;
             rope_chunk<T, VEC>(zv, cs, sn, j0, p.half_rope, stream_rope, o1, o2);
             if (to_cache) {
-                put_cache<T, H>(krow, p.k_code, j0, o1, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim);
+                put_cache<T, H>(krow, p.k_code, j0, o1, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim, k_nt);
                 put_cache<T, H>(krow, p.k_code, p.half_rope + j0, o2, p.k_scale, p.k_offset, p.k_qshape, (int)n,
-                                p.k_dim);
+                                p.k_dim, k_nt);
             }
             if (out_kv) {
                 store_vec_nt<T, H>(k_rope + j0, o1);
@@ -265,12 +273,19 @@ __global__ __launch_bounds__(256) void kv_rmsnorm_rope_cache_kernel(KvParams p) 
             // V2: v_optional goes to the ckv cache (quantised or copied) and to c_kv unchanged
             if (to_cache) {
                 if (p.c_code == CODE_SAME) {
-                    z[i].store_nt(reinterpret_cast<T *>(crow) + c * VEC);
+                    if (c_nt) {
+                        z[i].store_nt(reinterpret_cast<T *>(crow) + c * VEC);
+                    } else {
+                        Words<Chunk<T, VEC>::kWords> rw;
+#pragma unroll
+                        for (int q = 0; q < Chunk<T, VEC>::kWords; q++) rw.w[q] = z[i].w[q];
+                        store_words<Chunk<T, VEC>::kWords>(reinterpret_cast<T *>(crow) + c * VEC, rw);
+                    }
                 } else {
                     float zv[VEC];
                     z[i].decode(zv);
                     put_cache<T, VEC>(crow, p.c_code, c * VEC, zv, p.v_scale, p.v_offset, p.v_qshape, (int)n,
-                                      p.c_dim);
+                                      p.c_dim, c_nt);
                 }
             }
             if (out_kv) z[i].store_nt(c_kv + c * VEC);
@@ -291,10 +306,15 @@ static int round_slots(int c, const int *allowed, int n_allowed) {
 static const int kCR[] = {1, 2, 3, 4};
 static const int kCX[] = {1, 2};
 
+// Lane-group size: the smallest G whose register slots hold the row (fewest
+// lanes per row, most rows per wave), unless that leaves fewer than 2048
+// wavefronts (two per SIMD on 256 CUs); then larger groups spread few rows
+// over more waves (a decode batch of 512 rows runs on 512 waves at G = 64).
 int kv_plan(KvParams &p, int vec, bool v2, int &cr, int &cx) {
     p.nr = p.rms_size / vec;
     p.nx = (v2 ? p.c_dim : p.rope_size) / vec;
     p.n_rope_chunks = v2 ? p.rope_size / vec : 0;
+    int found = -1;
     for (int G = 8; G <= 64; G *= 2) {
         int r = round_slots((p.nr + G - 1) / G, kCR, 4);
         int x = round_slots((p.nx + G - 1) / G, kCX, 2);
@@ -302,10 +322,11 @@ int kv_plan(KvParams &p, int vec, bool v2, int &cr, int &cx) {
             p.lanes_per_row = G;
             cr = r;
             cx = x;
-            return 0;
+            found = 0;
+            if ((uint64_t)p.rows * (uint64_t)G >= 2048ull * 64ull) return 0;
         }
     }
-    return -1;
+    return found;
 }
 
 template <typename T, int VEC, bool V2>

@@ -17,7 +17,9 @@
 //   * lane k of every head group reads the same cos/sin chunks, so each lane
 //     loads its cos/sin once per unit and reuses them for all its heads;
 //   * 16-byte non-temporal loads and stores for Q/K (read once, written once),
-//     ordinary cached loads for the reused gammas and position tables;
+//     ordinary cached loads for the reused gammas and position tables; the
+//     gammas of all of a lane's heads are requested with the data, so their
+//     latency hides under the HBM latency;
 //   * addresses are a wave-uniform 64-bit base (scalar registers) plus a
 //     32-bit per-lane offset, and the head geometry is a compile-time constant
 //     for the usual head sizes, so address arithmetic costs few VGPRs;
@@ -97,6 +99,27 @@ __global__ __launch_bounds__(256) void qk_across_heads_kernel(QkParams p) {
         }
     }
 
+    // Gammas of all J heads are requested together with the data: their cached
+    // (L2) latency then overlaps the HBM latency instead of serialising one
+    // round trip per head in the apply loop.
+    const T *g = reinterpret_cast<const T *>(seg ? p.k_gamma : p.q_gamma);
+    const uint32_t lane_g = (uint32_t)(hsub * p.head_dim + k * VEC) * (uint32_t)sizeof(T);
+    const bool norm = p.apply_norm != 0;
+    Chunk<T, VEC> glo[J], ghi[J];
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        const int hb = (j * W + wave_in_unit) * hpw;
+        if (norm && lane_ok && hb + hsub < nh) {
+            const T *gj = reinterpret_cast<const T *>(reinterpret_cast<const char *>(g + (uint64_t)hb * p.head_dim) +
+                                                      lane_g);
+            glo[j].load(gj);
+            ghi[j].load(gj + half);
+        } else {
+            glo[j].zero();
+            ghi[j].zero();
+        }
+    }
+
     Chunk<T, VEC> c_lo, c_hi, s_lo, s_hi;
     const bool rope = p.apply_rope != 0;
     if (rope && lane_ok) {
@@ -142,9 +165,6 @@ __global__ __launch_bounds__(256) void qk_across_heads_kernel(QkParams p) {
 
     T *o = reinterpret_cast<T *>(seg ? p.k_out : p.q_out) + b * p.out_batch_stride + s * p.out_token_stride;
     const uint32_t lane_out = ((uint32_t)hsub * p.out_head_stride + (uint32_t)(k * VEC)) * (uint32_t)sizeof(T);
-    const T *g = reinterpret_cast<const T *>(seg ? p.k_gamma : p.q_gamma);
-    const uint32_t lane_g = (uint32_t)(hsub * p.head_dim + k * VEC) * (uint32_t)sizeof(T);
-    const bool norm = p.apply_norm != 0;
 
 #pragma unroll
     for (int j = 0; j < J; j++) {
@@ -154,10 +174,8 @@ __global__ __launch_bounds__(256) void qk_across_heads_kernel(QkParams p) {
         lo[j].decode(xl);
         hi[j].decode(xh);
         if (norm) {
-            const T *gj = reinterpret_cast<const T *>(reinterpret_cast<const char *>(g + (uint64_t)hb * p.head_dim) +
-                                                      lane_g);
-            load_vec<T, VEC>(gj, gl);
-            load_vec<T, VEC>(gj + half, gh);
+            glo[j].decode(gl);
+            ghi[j].decode(gh);
         } else {
 #pragma unroll
             for (int e = 0; e < VEC; e++) { gl[e] = 1.0f; gh[e] = 1.0f; }

@@ -118,3 +118,20 @@ def test_deterministic(Q):
     run_gpu_kv(Q, d2)
     torch.cuda.synchronize()
     assert torch.equal(d1["k_cache"], d2["k_cache"]) and torch.equal(d1["ckv_cache"], d2["ckv_cache"])
+
+
+def test_prepared_call_matches_direct_call(Q):
+    """The prepared launcher (arguments marshalled once) writes what a direct call writes."""
+    d1 = W.make_kv_cache(W.MLA_V1_PREFILL, device="cuda", seq=256, block_num=16)
+    d2 = W.make_kv_cache(W.MLA_V1_PREFILL, device="cuda", seq=256, block_num=16)
+    run_gpu_kv(Q, d1)
+    cfg = d2["cfg"]
+    launch = Q.prepare_kv_rmsnorm_rope_cache(d2["kv"], d2["gamma"], d2["cos"], d2["sin"], d2["index"],
+                                             d2["k_cache"], d2["ckv_cache"], cache_mode="PA_BNSD",
+                                             epsilon=cfg.eps, is_output_kv=True, k_rope=d2["k_rope"],
+                                             c_kv=d2["c_kv"])
+    launch()
+    launch()                                         # idempotent: same inputs, same slots
+    torch.cuda.synchronize()
+    for key in ("k_cache", "ckv_cache", "k_rope", "c_kv"):
+        assert torch.equal(d1[key].view(torch.int16), d2[key].view(torch.int16)), key

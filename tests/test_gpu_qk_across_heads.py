@@ -175,3 +175,18 @@ def test_zero_tokens_is_a_noop(Q):
     Q.qk_norm_rope_across_heads(q[:, :0], k[:, :0], d["q_gamma"], d["k_gamma"], d["cos"][:, :0], d["sin"][:, :0],
                                 eps=1e-6)
     torch.cuda.synchronize()
+
+
+def test_prepared_call_matches_direct_call(Q):
+    d = W.make_across_heads(W.WAN22_SELF_ATTN, device="cuda", seq=333, table="1d")
+    q, k = qk_views(d)
+    o1, o2 = torch.empty_like(d["qkv"]), torch.empty_like(d["qkv"])
+    q1, k1 = qk_views(dict(d, qkv=o1))
+    q2, k2 = qk_views(dict(d, qkv=o2))
+    _run(Q, d, q, k, q1, k1)
+    launch = Q.prepare_qk_norm_rope_across_heads(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"],
+                                                 eps=d["eps"], q_out=q2, k_out=k2)
+    launch()
+    torch.cuda.synchronize()
+    assert torch.equal(q1.reshape(-1).view(torch.int16), q2.reshape(-1).view(torch.int16))
+    assert torch.equal(k1.reshape(-1).view(torch.int16), k2.reshape(-1).view(torch.int16))
