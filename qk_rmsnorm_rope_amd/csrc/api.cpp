@@ -339,8 +339,8 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
     p.k_qshape = a->k_qshape; p.v_qshape = a->v_qshape;
     p.out_kv = out_kv ? 1 : 0;
     p.eps = a->eps;
-    int cr = 0, cx = 0;
-    if (qknr::kv_plan(p, vec, v2, cr, cx) != 0)
+    int ca = 0, cb = 0;
+    if (qknr::kv_plan(p, vec, v2, ca, cb) != 0)
         return fail(QKNR_UNSUPPORTED, "row too wide for one block's register plan");
     plan.elem_type = a->dtype == QKNR_BF16 ? 1 : 2;
     plan.vec = vec;

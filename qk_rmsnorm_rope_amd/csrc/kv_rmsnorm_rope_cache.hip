@@ -8,9 +8,15 @@
 //
 // MI355X design: the operator is HBM-bound, so each row is read once and every
 // output row is written once, in one pass:
-//   * a group of G lanes (8..64, a power of two) owns one row; 64/G rows per
-//     wavefront, 256/G per block. Lane l of a group owns the 8-element chunks
-//     l, l+G, l+2G, ... of the row (16-byte loads of bf16/f16);
+//   * each row splits into two independent parts with their own waves (blocks
+//     are typed): part A is the normed part (V1: RmsNorm of kv[:Dv] -> ckv
+//     cache and c_kv; V2: RmsNorm of kv, RoPE on its head -> k cache and
+//     k_rope), part B the other (V1: RoPE of the raw kv[Dv:] -> k cache and
+//     k_rope; V2: v_optional -> ckv cache and c_kv). Splitting halves the
+//     registers a wave holds and leaves part B without any reduction;
+//   * in each part a group of G lanes (8..64, a power of two) owns one row; 64/G
+//     rows per wavefront, 256/G per block. Lane l of a group owns the 8-element
+//     chunks l, l+G, l+2G, ... of its part (16-byte loads of bf16/f16);
 //   * the sum of squares reduces inside the group with DPP / ds_swizzle (no
 //     LDS, no barrier); the result is bit-identical in every lane of the group;
 //   * an interleaved input chunk (pairs 2j, 2j+1) produces half a chunk of the
@@ -28,7 +34,9 @@
 //     written by other waves merge in L2 before they reach HBM; gamma and the
 //     quantisation parameters, reused by every row, stay cached;
 //   * row -> (b, n, s) and slot -> (block, offset) use multiply-high division
-//     by the invariant sizes instead of 64-bit divides.
+//     by the invariant sizes instead of 64-bit divides;
+//   * gamma and the cos/sin of rotated chunks are requested together with the
+//     row data, so their latency overlaps the HBM latency.
 #include "device_common.h"
 #include "launch.h"
 
@@ -79,34 +87,41 @@ __device__ __forceinline__ void load_qparam(const float *p, int shape, int n, in
     }
 }
 
-// Write N values of one cache row starting at channel c: quantised (int8 /
-// E4M3FN, t = x*scale (+offset) in fp32 with one rounding) or rounded to T.
+// One destination row (a cache row, with its encoding and parameters).
+struct CacheRow {
+    uint8_t *row;            // nullptr: no cache write for this token
+    int code;                // CacheCode
+    const float *scale, *offset;
+    int qshape, n, width;
+    bool nt;                 // the row covers whole 128-byte lines: streaming stores
+};
+
+// Write N values starting at channel c: quantised (int8 / E4M3FN, t =
+// x*scale (+offset) in fp32 with one rounding) or rounded to T.
 template <typename T, int N>
-__device__ __forceinline__ void put_cache(void *row, int code, int c, const float *x,
-                                          const float *scale, const float *offset, int qshape,
-                                          int n, int width, bool nt) {
-    if (code == CODE_SAME) {
-        if (nt) store_vec_nt<T, N>(reinterpret_cast<T *>(row) + c, x);
-        else store_vec<T, N>(reinterpret_cast<T *>(row) + c, x);
+__device__ __forceinline__ void put_cache(const CacheRow &d, int c, const float *x) {
+    if (d.code == CODE_SAME) {
+        if (d.nt) store_vec_nt<T, N>(reinterpret_cast<T *>(d.row) + c, x);
+        else store_vec<T, N>(reinterpret_cast<T *>(d.row) + c, x);
         return;
     }
     float sc[N], of[N];
-    load_qparam<N>(scale, qshape, n, width, c, sc);
-    if (offset) {
-        load_qparam<N>(offset, qshape, n, width, c, of);
+    load_qparam<N>(d.scale, d.qshape, d.n, d.width, c, sc);
+    if (d.offset) {
+        load_qparam<N>(d.offset, d.qshape, d.n, d.width, c, of);
     } else {
 #pragma unroll
         for (int i = 0; i < N; i++) of[i] = 0.0f;
     }
     uint32_t q[N];
-    if (code == CODE_INT8) {
+    if (d.code == CODE_INT8) {
 #pragma unroll
         for (int i = 0; i < N; i++) q[i] = enc_int8(fmaf(x[i], sc[i], of[i]));
     } else {
 #pragma unroll
         for (int i = 0; i < N; i++) q[i] = enc_e4m3fn(fmaf(x[i], sc[i], of[i]));
     }
-    store_codes<N>(reinterpret_cast<uint8_t *>(row) + c, q, nt);
+    store_codes<N>(d.row + c, q, d.nt);
 }
 
 __device__ __forceinline__ float row_sum(float v, int G) {
@@ -118,179 +133,232 @@ __device__ __forceinline__ float row_sum(float v, int G) {
     }
 }
 
-// Interleave RoPE of one input chunk (VEC elements = VEC/2 pairs starting at
-// pair j0): the even-lane results go to positions j0.., the odd-lane results
-// to half_rope + j0.. .
-template <typename T, int VEC>
-__device__ __forceinline__ void rope_chunk(const float *z, const T *cs, const T *sn, int j0, int half,
-                                           bool streaming, float *o1, float *o2) {
-    constexpr int H = VEC / 2;
-    float c1[H], c2[H], s1[H], s2[H];
-    Chunk<T, H> a, b2, c, d;
-    if (streaming) {
-        a.load_nt(cs + j0); b2.load_nt(cs + half + j0); c.load_nt(sn + j0); d.load_nt(sn + half + j0);
-    } else {
-        a.load(cs + j0); b2.load(cs + half + j0); c.load(sn + j0); d.load(sn + half + j0);
+// cos/sin of one interleaved input chunk (VEC elements = H = VEC/2 pairs
+// starting at pair j0): the even-lane results go to positions j0.., the
+// odd-lane results to half + j0.. .
+template <typename T, int H>
+struct RopeCoef {
+    Chunk<T, H> c1, c2, s1, s2;
+    __device__ __forceinline__ void load(const T *cs, const T *sn, int j0, int half, bool streaming) {
+        if (streaming) {
+            c1.load_nt(cs + j0); c2.load_nt(cs + half + j0); s1.load_nt(sn + j0); s2.load_nt(sn + half + j0);
+        } else {
+            c1.load(cs + j0); c2.load(cs + half + j0); s1.load(sn + j0); s2.load(sn + half + j0);
+        }
     }
-    a.decode(c1); b2.decode(c2); c.decode(s1); d.decode(s2);
+    // o1[m] = z[2m] cos[j0+m] - z[2m+1] sin[j0+m]; o2[m] = z[2m+1] cos[h+j0+m] + z[2m] sin[h+j0+m]
+    __device__ __forceinline__ void apply(const float *z, float *o1, float *o2) const {
+        float a[H], b[H], c[H], d[H];
+        c1.decode(a); c2.decode(b); s1.decode(c); s2.decode(d);
 #pragma unroll
-    for (int m = 0; m < H; m++) {
-        o1[m] = fmaf(z[2 * m], c1[m], -(z[2 * m + 1] * s1[m]));
-        o2[m] = fmaf(z[2 * m + 1], c2[m], z[2 * m] * s2[m]);
+        for (int m = 0; m < H; m++) {
+            o1[m] = fmaf(z[2 * m], a[m], -(z[2 * m + 1] * c[m]));
+            o2[m] = fmaf(z[2 * m + 1], b[m], z[2 * m] * d[m]);
+        }
     }
+};
+
+struct RowPos {
+    uint32_t b, n, s;
+    bool ok;
+};
+
+__device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t row) {
+    RowPos r{0, 0, 0, row < p.rows};
+    if (r.ok) {
+        const uint32_t bn = fastdiv(row, p.seq_div);
+        r.s = row - bn * p.seq;
+        r.b = fastdiv(bn, p.heads_div);
+        r.n = bn - r.b * (uint32_t)p.heads;
+    }
+    return r;
 }
 
-// The occupancy hint (at least 6 waves per SIMD, 4 for the widest rows) keeps register use low enough
-// for many rows in flight; the planner's shapes fit without spilling.
-template <typename T, int VEC, bool V2, int CR, int CX>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CR >= 4 ? 4 : 6, 8))) void kv_rmsnorm_rope_cache_kernel(
-    KvParams p) {
-    const int G = p.lanes_per_row;
-    const int gl = threadIdx.x & (G - 1);
-    const uint32_t row = blockIdx.x * (uint32_t)(256 / G) + threadIdx.x / (uint32_t)G;
-    const bool row_ok = row < p.rows;
-
-    uint32_t b = 0, n = 0, s = 0;
-    if (row_ok) {
-        const uint32_t bn = fastdiv(row, p.seq_div);
-        s = row - bn * p.seq;
-        b = fastdiv(bn, p.heads_div);
-        n = bn - b * (uint32_t)p.heads;
-    }
-    const T *kv = reinterpret_cast<const T *>(p.kv) + b * p.kv_b + n * p.kv_n + s * p.kv_s;
-
-    // ---- loads: rms chunks, then the raw rope tail (V1) or the v row (V2)
-    Chunk<T, VEC> x[CR], z[CX];
-#pragma unroll
-    for (int i = 0; i < CR; i++) {
-        const int c = gl + i * G;
-        if (row_ok && c < p.nr) x[i].load_nt(kv + c * VEC); else x[i].zero();
-    }
-    const T *zrow = V2 ? reinterpret_cast<const T *>(p.v) + b * p.v_b + n * p.v_n + s * p.v_s
-                       : kv + p.rms_size;
-#pragma unroll
-    for (int i = 0; i < CX; i++) {
-        const int c = gl + i * G;
-        if (row_ok && c < p.nx) z[i].load_nt(zrow + c * VEC); else z[i].zero();
-    }
-    const int64_t slot = row_ok ? p.index[(uint64_t)b * p.seq + s] : -1;
-
-    // ---- (1) RmsNorm statistic over rms_size values, reduced over the group
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < CR; i++) ss = x[i].sumsq(ss);
-    ss = row_sum(ss, G);
-    const float inv_rms = rsqrtf(ss / (float)p.rms_size + p.eps);
-    if (!row_ok) return;
-
-    // ---- destinations
-    const bool to_cache = slot >= 0 && slot < p.capacity;
-    uint8_t *krow = nullptr, *crow = nullptr;
-    if (to_cache) {
-        int64_t ko, co;
+// The cache row of token (b, s), head n, for the k cache (is_k) or the ckv cache.
+template <typename T>
+__device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int64_t slot, const RowPos &r) {
+    CacheRow d;
+    d.code = is_k ? p.k_code : p.c_code;
+    d.scale = is_k ? p.k_scale : p.v_scale;
+    d.offset = is_k ? p.k_offset : p.v_offset;
+    d.qshape = is_k ? p.k_qshape : p.v_qshape;
+    d.n = (int)r.n;
+    d.width = is_k ? p.k_dim : p.c_dim;
+    d.nt = (is_k ? p.k_rows_whole_lines : p.c_rows_whole_lines) != 0;
+    d.row = nullptr;
+    if (slot >= 0 && slot < p.capacity) {
+        const int64_t s0 = is_k ? p.kc0 : p.cc0, s1 = is_k ? p.kc1 : p.cc1, s2 = is_k ? p.kc2 : p.cc2;
+        int64_t off;
         if (p.mode == 0) {
-            ko = b * p.kc0 + slot * p.kc1 + n * p.kc2;
-            co = b * p.cc0 + slot * p.cc1 + n * p.cc2;
+            off = r.b * s0 + slot * s1 + r.n * s2;
         } else {
             const uint32_t blk = fastdiv((uint32_t)slot, p.block_div);     // slot < capacity < 2^31
-            const uint32_t off = (uint32_t)slot - blk * (uint32_t)p.block_size;
-            ko = blk * p.kc0 + off * p.kc1 + n * p.kc2;
-            co = blk * p.cc0 + off * p.cc1 + n * p.cc2;
+            const uint32_t in_blk = (uint32_t)slot - blk * (uint32_t)p.block_size;
+            off = blk * s0 + in_blk * s1 + r.n * s2;
         }
-        const int kbytes = p.k_code == CODE_SAME ? (int)sizeof(T) : 1;
-        const int cbytes = p.c_code == CODE_SAME ? (int)sizeof(T) : 1;
-        krow = reinterpret_cast<uint8_t *>(p.k_cache) + ko * kbytes;
-        crow = reinterpret_cast<uint8_t *>(p.ckv_cache) + co * cbytes;
+        const int eb = d.code == CODE_SAME ? (int)sizeof(T) : 1;
+        d.row = reinterpret_cast<uint8_t *>(is_k ? p.k_cache : p.ckv_cache) + off * eb;
     }
-    const bool out_kv = p.out_kv != 0;
-    T *k_rope = out_kv ? reinterpret_cast<T *>(p.k_rope) + b * p.kr_b + n * p.kr_n + s * p.kr_s : nullptr;
-    T *c_kv = out_kv ? reinterpret_cast<T *>(p.c_kv) + b * p.ck_b + n * p.ck_n + s * p.ck_s : nullptr;
-    const T *gamma = reinterpret_cast<const T *>(p.gamma);
-    const T *cs = reinterpret_cast<const T *>(p.cos) + b * p.rope_b + n * p.rope_n + s * p.rope_s;
-    const T *sn = reinterpret_cast<const T *>(p.sin) + b * p.rope_b + n * p.rope_n + s * p.rope_s;
-    constexpr int H = VEC / 2;
-    const bool stream_rope = p.stream_rope != 0;
-    const bool k_nt = p.k_rows_whole_lines != 0, c_nt = p.c_rows_whole_lines != 0;
+    return d;
+}
 
-    // ---- normed chunks: y = x * inv_rms * gamma
+// Part A: the normed part of a row. V1: y = RmsNorm(kv[:Dv]) -> ckv cache,
+// c_kv. V2: y = RmsNorm(kv); the first rope_size values rotated -> k cache,
+// k_rope (the planner keeps every rotated chunk in slot 0).
+template <typename T, int VEC, bool V2, int CA>
+__device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
+    constexpr int H = VEC / 2;
+    const int G = p.ga;
+    const int gl = threadIdx.x & (G - 1);
+    const RowPos r = row_pos(p, blk * (uint32_t)(256 / G) + threadIdx.x / (uint32_t)G);
+    const T *kv = reinterpret_cast<const T *>(p.kv) + r.b * p.kv_b + r.n * p.kv_n + r.s * p.kv_s;
+    const T *gamma = reinterpret_cast<const T *>(p.gamma);
+
+    Chunk<T, VEC> x[CA], gm[CA];
+    RopeCoef<T, H> rc;
 #pragma unroll
-    for (int i = 0; i < CR; i++) {
+    for (int i = 0; i < CA; i++) {
+        const int c = gl + i * G;
+        if (r.ok && c < p.nr) {
+            x[i].load_nt(kv + c * VEC);
+            gm[i].load(gamma + c * VEC);
+        } else {
+            x[i].zero();
+        }
+    }
+    if (V2 && r.ok && gl < p.n_rope_chunks) {
+        const int64_t ro = r.b * p.rope_b + r.n * p.rope_n + r.s * p.rope_s;
+        rc.load(reinterpret_cast<const T *>(p.cos) + ro, reinterpret_cast<const T *>(p.sin) + ro, gl * H,
+                p.half_rope, p.stream_rope != 0);
+    }
+    const int64_t slot = r.ok ? p.index[(uint64_t)r.b * p.seq + r.s] : -1;
+
+    // (1) RmsNorm statistic over rms_size values, reduced over the group
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CA; i++) ss = x[i].sumsq(ss);
+    ss = row_sum(ss, G);
+    const float inv_rms = rsqrtf(ss / (float)p.rms_size + p.eps);
+    if (!r.ok) return;
+
+    const CacheRow d = cache_row<T>(p, V2, slot, r);
+    const bool out_kv = p.out_kv != 0;
+    T *raw = nullptr;   // c_kv (V1) or k_rope (V2)
+    if (out_kv)
+        raw = V2 ? reinterpret_cast<T *>(p.k_rope) + r.b * p.kr_b + r.n * p.kr_n + r.s * p.kr_s
+                 : reinterpret_cast<T *>(p.c_kv) + r.b * p.ck_b + r.n * p.ck_n + r.s * p.ck_s;
+#pragma unroll
+    for (int i = 0; i < CA; i++) {
         const int c = gl + i * G;
         if (c >= p.nr) continue;
         float xv[VEC], g[VEC], y[VEC];
         x[i].decode(xv);
-        load_vec<T, VEC>(gamma + c * VEC, g);
+        gm[i].decode(g);
 #pragma unroll
         for (int e = 0; e < VEC; e++) y[e] = xv[e] * inv_rms * g[e];
-        if constexpr (!V2) {
-            // V1: the normed row goes to the ckv cache and c_kv
-            if (to_cache)
-                put_cache<T, VEC>(crow, p.c_code, c * VEC, y, p.v_scale, p.v_offset, p.v_qshape, (int)n, p.c_dim, c_nt);
-            if (out_kv) store_vec_nt<T, VEC>(c_kv + c * VEC, y);
-        } else {
-            if (c < p.n_rope_chunks) {
-                // V2: rotate the first rope_size normed values in place
-                float o1[H], o2[H];
-                const int j0 = c * H;
-                rope_chunk<T, VEC>(y, cs, sn, j0, p.half_rope, stream_rope, o1, o2);
-                if (to_cache) {
-                    put_cache<T, H>(krow, p.k_code, j0, o1, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim, k_nt);
-                    put_cache<T, H>(krow, p.k_code, p.half_rope + j0, o2, p.k_scale, p.k_offset, p.k_qshape,
-                                    (int)n, p.k_dim, k_nt);
-                }
-                if (out_kv) {
-                    store_vec_nt<T, H>(k_rope + j0, o1);
-                    store_vec_nt<T, H>(k_rope + p.half_rope + j0, o2);
-                }
-            } else {
-                if (to_cache)
-                    put_cache<T, VEC>(krow, p.k_code, c * VEC, y, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim, k_nt);
-                if (out_kv) store_vec_nt<T, VEC>(k_rope + c * VEC, y);
+        if (V2 && i == 0 && c < p.n_rope_chunks) {
+            // (2) interleaveRope on the normed head: rope_out replaces y there
+            float o1[H], o2[H];
+            const int j0 = c * H;
+            rc.apply(y, o1, o2);
+            if (d.row) {
+                put_cache<T, H>(d, j0, o1);
+                put_cache<T, H>(d, p.half_rope + j0, o2);
             }
+            if (out_kv) {
+                store_vec_nt<T, H>(raw + j0, o1);
+                store_vec_nt<T, H>(raw + p.half_rope + j0, o2);
+            }
+        } else {
+            if (d.row) put_cache<T, VEC>(d, c * VEC, y);
+            if (out_kv) store_vec_nt<T, VEC>(raw + c * VEC, y);
         }
     }
+}
 
-    // ---- second part of the row: V1 raw rope tail -> k; V2 v row -> ckv
+// Part B: V1: interleaveRope of the raw kv[Dv:] -> k cache, k_rope.
+//         V2: v_optional -> ckv cache (quantised or copied), c_kv (copied).
+template <typename T, int VEC, bool V2, int CB>
+__device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
+    constexpr int H = VEC / 2;
+    const int G = p.gb;
+    const int gl = threadIdx.x & (G - 1);
+    const RowPos r = row_pos(p, blk * (uint32_t)(256 / G) + threadIdx.x / (uint32_t)G);
+    const T *src = V2 ? reinterpret_cast<const T *>(p.v) + r.b * p.v_b + r.n * p.v_n + r.s * p.v_s
+                      : reinterpret_cast<const T *>(p.kv) + r.b * p.kv_b + r.n * p.kv_n + r.s * p.kv_s + p.rms_size;
+    const int64_t ro = r.b * p.rope_b + r.n * p.rope_n + r.s * p.rope_s;
+    const T *cs = reinterpret_cast<const T *>(p.cos) + ro;
+    const T *sn = reinterpret_cast<const T *>(p.sin) + ro;
+
+    Chunk<T, VEC> z[CB];
+    RopeCoef<T, H> rc[V2 ? 1 : CB];
 #pragma unroll
-    for (int i = 0; i < CX; i++) {
+    for (int i = 0; i < CB; i++) {
+        const int c = gl + i * G;
+        if (r.ok && c < p.nx) {
+            z[i].load_nt(src + c * VEC);
+            if (!V2) rc[i].load(cs, sn, c * H, p.half_rope, p.stream_rope != 0);
+        } else {
+            z[i].zero();
+        }
+    }
+    const int64_t slot = r.ok ? p.index[(uint64_t)r.b * p.seq + r.s] : -1;
+    if (!r.ok) return;
+
+    const CacheRow d = cache_row<T>(p, !V2, slot, r);
+    const bool out_kv = p.out_kv != 0;
+    T *raw = nullptr;   // k_rope (V1) or c_kv (V2)
+    if (out_kv)
+        raw = V2 ? reinterpret_cast<T *>(p.c_kv) + r.b * p.ck_b + r.n * p.ck_n + r.s * p.ck_s
+                 : reinterpret_cast<T *>(p.k_rope) + r.b * p.kr_b + r.n * p.kr_n + r.s * p.kr_s;
+#pragma unroll
+    for (int i = 0; i < CB; i++) {
         const int c = gl + i * G;
         if (c >= p.nx) continue;
         if constexpr (!V2) {
             float zv[VEC], o1[H], o2[H];
             z[i].decode(zv);
             const int j0 = c * H;
-            rope_chunk<T, VEC>(zv, cs, sn, j0, p.half_rope, stream_rope, o1, o2);
-            if (to_cache) {
-                put_cache<T, H>(krow, p.k_code, j0, o1, p.k_scale, p.k_offset, p.k_qshape, (int)n, p.k_dim, k_nt);
-                put_cache<T, H>(krow, p.k_code, p.half_rope + j0, o2, p.k_scale, p.k_offset, p.k_qshape, (int)n,
-                                p.k_dim, k_nt);
+            rc[i].apply(zv, o1, o2);
+            if (d.row) {
+                put_cache<T, H>(d, j0, o1);
+                put_cache<T, H>(d, p.half_rope + j0, o2);
             }
             if (out_kv) {
-                store_vec_nt<T, H>(k_rope + j0, o1);
-                store_vec_nt<T, H>(k_rope + p.half_rope + j0, o2);
+                store_vec_nt<T, H>(raw + j0, o1);
+                store_vec_nt<T, H>(raw + p.half_rope + j0, o2);
             }
         } else {
-            // V2: v_optional goes to the ckv cache (quantised or copied) and to c_kv unchanged
-            if (to_cache) {
-                if (p.c_code == CODE_SAME) {
-                    if (c_nt) {
-                        z[i].store_nt(reinterpret_cast<T *>(crow) + c * VEC);
+            if (d.row) {
+                if (d.code == CODE_SAME) {
+                    T *dst = reinterpret_cast<T *>(d.row) + c * VEC;
+                    if (d.nt) {
+                        z[i].store_nt(dst);
                     } else {
                         Words<Chunk<T, VEC>::kWords> rw;
 #pragma unroll
                         for (int q = 0; q < Chunk<T, VEC>::kWords; q++) rw.w[q] = z[i].w[q];
-                        store_words<Chunk<T, VEC>::kWords>(reinterpret_cast<T *>(crow) + c * VEC, rw);
+                        store_words<Chunk<T, VEC>::kWords>(dst, rw);
                     }
                 } else {
                     float zv[VEC];
                     z[i].decode(zv);
-                    put_cache<T, VEC>(crow, p.c_code, c * VEC, zv, p.v_scale, p.v_offset, p.v_qshape, (int)n,
-                                      p.c_dim, c_nt);
+                    put_cache<T, VEC>(d, c * VEC, zv);
                 }
             }
-            if (out_kv) z[i].store_nt(c_kv + c * VEC);
+            if (out_kv) z[i].store_nt(raw + c * VEC);
         }
     }
+}
+
+// Blocks [0, blocks_a) run part A, the rest part B. The occupancy hint keeps
+// register use low enough for many rows in flight (lower for the widest rows,
+// so that no instantiation spills).
+template <typename T, int VEC, bool V2, int CA, int CB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CA >= 4 ? 6 : (CA == 3 ? 7 : 8), 8))) void kv_rmsnorm_rope_cache_kernel(
+    KvParams p) {
+    if (blockIdx.x < p.blocks_a) part_a<T, VEC, V2, CA>(p, blockIdx.x);
+    else part_b<T, VEC, V2, CB>(p, blockIdx.x - p.blocks_a);
 }
 
 // ---------------------------------------------------------------------------
@@ -303,41 +371,50 @@ static int round_slots(int c, const int *allowed, int n_allowed) {
     return -1;
 }
 
-static const int kCR[] = {1, 2, 3, 4};
-static const int kCX[] = {1, 2};
+static const int kCA[] = {1, 2, 3, 4};
+static const int kCB[] = {1, 2};
 
-// Lane-group size: the smallest G whose register slots hold the row (fewest
-// lanes per row, most rows per wave), unless that leaves fewer than 2048
-// wavefronts (two per SIMD on 256 CUs); then larger groups spread few rows
-// over more waves (a decode batch of 512 rows runs on 512 waves at G = 64).
-int kv_plan(KvParams &p, int vec, bool v2, int &cr, int &cx) {
-    p.nr = p.rms_size / vec;
-    p.nx = (v2 ? p.c_dim : p.rope_size) / vec;
-    p.n_rope_chunks = v2 ? p.rope_size / vec : 0;
+// Lane-group size of one part: the smallest G whose register slots hold the
+// part (fewest lanes per row, most rows per wave), unless that leaves fewer
+// than 2048 wavefronts (two per SIMD on 256 CUs); then larger groups spread few
+// rows over more waves (a decode batch of 512 rows runs on 512 waves at G = 64).
+static int pick_group(uint32_t rows, int chunks, const int *allowed, int n_allowed, int min_g, int &slots) {
     int found = -1;
     for (int G = 8; G <= 64; G *= 2) {
-        int r = round_slots((p.nr + G - 1) / G, kCR, 4);
-        int x = round_slots((p.nx + G - 1) / G, kCX, 2);
-        if (r > 0 && x > 0) {
-            p.lanes_per_row = G;
-            cr = r;
-            cx = x;
-            found = 0;
-            if ((uint64_t)p.rows * (uint64_t)G >= 2048ull * 64ull) return 0;
+        if (G < min_g) continue;
+        const int k = round_slots((chunks + G - 1) / G, allowed, n_allowed);
+        if (k > 0) {
+            found = G;
+            slots = k;
+            if ((uint64_t)rows * (uint64_t)G >= 2048ull * 64ull) break;
         }
     }
     return found;
 }
 
+int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
+    p.nr = p.rms_size / vec;
+    p.nx = (v2 ? p.c_dim : p.rope_size) / vec;
+    p.n_rope_chunks = v2 ? p.rope_size / vec : 0;
+    // V2: rotated chunks 0..n_rope_chunks-1 must all sit in slot 0 (G >= their count)
+    const int ga = pick_group(p.rows, p.nr, kCA, 4, v2 ? p.n_rope_chunks : 8, ca);
+    const int gb = pick_group(p.rows, p.nx, kCB, 2, 8, cb);
+    if (ga < 0 || gb < 0) return -1;
+    p.ga = ga;
+    p.gb = gb;
+    p.blocks_a = (p.rows + (256 / ga) - 1) / (256 / ga);
+    p.blocks_b = (p.rows + (256 / gb) - 1) / (256 / gb);
+    if ((uint64_t)p.blocks_a + p.blocks_b >= (1ull << 31)) return -1;
+    return 0;
+}
+
 template <typename T, int VEC, bool V2>
-static hipError_t launch_t(const KvParams &p, int cr, int cx, hipStream_t stream) {
-    const uint32_t rows_per_block = 256 / p.lanes_per_row;
-    const uint32_t blocks = (p.rows + rows_per_block - 1) / rows_per_block;
-    dim3 grid((unsigned)blocks), block(256);
-#define QKNR_KV(CRV, CXV)                                                                              \
-    if (cr == CRV && cx == CXV) {                                                                      \
-        hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CRV, CXV>), grid, block, 0, stream, p); \
-        return hipGetLastError();                                                                      \
+static hipError_t launch_t(const KvParams &p, int ca, int cb, hipStream_t stream) {
+    dim3 grid(p.blocks_a + p.blocks_b), block(256);
+#define QKNR_KV(CAV, CBV)                                                                                 \
+    if (ca == CAV && cb == CBV) {                                                                         \
+        hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CAV, CBV>), grid, block, 0, stream, p); \
+        return hipGetLastError();                                                                         \
     }
     QKNR_KV(1, 1) QKNR_KV(2, 1) QKNR_KV(3, 1) QKNR_KV(4, 1)
     QKNR_KV(1, 2) QKNR_KV(2, 2) QKNR_KV(3, 2) QKNR_KV(4, 2)
@@ -346,17 +423,17 @@ static hipError_t launch_t(const KvParams &p, int cr, int cx, hipStream_t stream
 }
 
 template <typename T>
-static hipError_t launch_elem(const KvParams &p, int vec, bool v2, int cr, int cx, hipStream_t stream) {
-    if (vec == 8) return v2 ? launch_t<T, 8, true>(p, cr, cx, stream) : launch_t<T, 8, false>(p, cr, cx, stream);
-    return v2 ? launch_t<T, 4, true>(p, cr, cx, stream) : launch_t<T, 4, false>(p, cr, cx, stream);
+static hipError_t launch_elem(const KvParams &p, int vec, bool v2, int ca, int cb, hipStream_t stream) {
+    if (vec == 8) return v2 ? launch_t<T, 8, true>(p, ca, cb, stream) : launch_t<T, 8, false>(p, ca, cb, stream);
+    return v2 ? launch_t<T, 4, true>(p, ca, cb, stream) : launch_t<T, 4, false>(p, ca, cb, stream);
 }
 
 hipError_t kv_launch(KvParams &p, int elem_type, int vec, bool v2, hipStream_t stream) {
-    int cr = 0, cx = 0;
-    if (kv_plan(p, vec, v2, cr, cx) != 0) return hipErrorInvalidValue;
+    int ca = 0, cb = 0;
+    if (kv_plan(p, vec, v2, ca, cb) != 0) return hipErrorInvalidValue;
     if (p.rows == 0) return hipSuccess;
-    if (elem_type == 1) return launch_elem<bf16_t>(p, vec, v2, cr, cx, stream);
-    if (elem_type == 2) return launch_elem<f16_t>(p, vec, v2, cr, cx, stream);
+    if (elem_type == 1) return launch_elem<bf16_t>(p, vec, v2, ca, cb, stream);
+    if (elem_type == 2) return launch_elem<f16_t>(p, vec, v2, ca, cb, stream);
     return hipErrorInvalidValue;
 }
 

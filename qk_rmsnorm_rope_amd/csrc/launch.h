@@ -100,10 +100,11 @@ struct KvParams {
     int32_t block_size;
     int32_t rms_size, rope_size, half_rope;
     int32_t k_dim, c_dim;      // widths of the k and ckv rows
-    int32_t nr;                // rms chunks per row
-    int32_t nx;                // V1: raw rope chunks; V2: v chunks
+    int32_t nr;                // part A chunks per row (the normed part)
+    int32_t nx;                // part B chunks per row (V1: raw rope tail; V2: v row)
     int32_t n_rope_chunks;     // V2: rope_size / VEC (normed chunks that are rotated)
-    int32_t lanes_per_row;     // G: 8, 16, 32 or 64
+    int32_t ga, gb;            // lanes per row in part A / part B: 8, 16, 32 or 64
+    uint32_t blocks_a, blocks_b;   // blocks of part A, then of part B
     int32_t k_code, c_code;    // CacheCode
     int32_t k_qshape, v_qshape;
     int32_t out_kv;
@@ -112,9 +113,9 @@ struct KvParams {
     float eps;
 };
 
-// Picks VEC-independent geometry (lanes per row and the register slots);
-// returns 0 and sets cr/cx, or -1 if the row is too wide.
-int kv_plan(KvParams &p, int vec, bool v2, int &cr, int &cx);
+// Lane geometry of the two row parts and their register slots; returns 0 and
+// sets ca/cb, or -1 if a row is too wide.
+int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb);
 // elem_type: 1 bf16, 2 f16. vec: 8 or 4.
 hipError_t kv_launch(KvParams &p, int elem_type, int vec, bool v2, hipStream_t stream);
 
