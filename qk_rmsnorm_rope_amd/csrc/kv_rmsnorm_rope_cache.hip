@@ -35,8 +35,10 @@
 //     quantisation parameters, reused by every row, stay cached;
 //   * row -> (b, n, s) and slot -> (block, offset) use multiply-high division
 //     by the invariant sizes instead of 64-bit divides;
-//   * gamma and the cos/sin of rotated chunks are requested together with the
-//     row data, so their latency overlaps the HBM latency.
+//   * gamma, the cos/sin of rotated chunks and (in part B) the quantisation
+//     parameters are requested together with the row data, so their latency
+//     overlaps the HBM latency (part A loads its quantisation parameters at
+//     the store: holding them from the start would cost occupancy).
 #include "device_common.h"
 #include "launch.h"
 
@@ -96,23 +98,27 @@ struct CacheRow {
     bool nt;                 // the row covers whole 128-byte lines: streaming stores
 };
 
-// Write N values starting at channel c: quantised (int8 / E4M3FN, t =
-// x*scale (+offset) in fp32 with one rounding) or rounded to T.
-template <typename T, int N>
-__device__ __forceinline__ void put_cache(const CacheRow &d, int c, const float *x) {
-    if (d.code == CODE_SAME) {
-        if (d.nt) store_vec_nt<T, N>(reinterpret_cast<T *>(d.row) + c, x);
-        else store_vec<T, N>(reinterpret_cast<T *>(d.row) + c, x);
-        return;
-    }
+// The scale and offset (0 if absent) of N consecutive channels from c.
+template <int N>
+struct QuantParams {
     float sc[N], of[N];
-    load_qparam<N>(d.scale, d.qshape, d.n, d.width, c, sc);
-    if (d.offset) {
-        load_qparam<N>(d.offset, d.qshape, d.n, d.width, c, of);
-    } else {
+    __device__ __forceinline__ void load(const float *scale, const float *offset, int qshape, int n, int width,
+                                         int c) {
+        load_qparam<N>(scale, qshape, n, width, c, sc);
+        if (offset) {
+            load_qparam<N>(offset, qshape, n, width, c, of);
+        } else {
 #pragma unroll
-        for (int i = 0; i < N; i++) of[i] = 0.0f;
+            for (int i = 0; i < N; i++) of[i] = 0.0f;
+        }
     }
+};
+
+// Write N quantised values starting at channel c (int8 / E4M3FN, t =
+// x*scale (+offset) in fp32 with one rounding), parameters already loaded.
+template <int N>
+__device__ __forceinline__ void put_codes(const CacheRow &d, int c, const float *x, const QuantParams<N> &qp) {
+    const float *sc = qp.sc, *of = qp.of;
     uint32_t q[N];
     if (d.code == CODE_INT8) {
 #pragma unroll
@@ -122,6 +128,19 @@ __device__ __forceinline__ void put_cache(const CacheRow &d, int c, const float 
         for (int i = 0; i < N; i++) q[i] = enc_e4m3fn(fmaf(x[i], sc[i], of[i]));
     }
     store_codes<N>(d.row + c, q, d.nt);
+}
+
+// Write N values starting at channel c: quantised, or rounded to T.
+template <typename T, int N>
+__device__ __forceinline__ void put_cache(const CacheRow &d, int c, const float *x) {
+    if (d.code == CODE_SAME) {
+        if (d.nt) store_vec_nt<T, N>(reinterpret_cast<T *>(d.row) + c, x);
+        else store_vec<T, N>(reinterpret_cast<T *>(d.row) + c, x);
+        return;
+    }
+    QuantParams<N> qp;
+    qp.load(d.scale, d.offset, d.qshape, d.n, d.width, c);
+    put_codes<N>(d, c, x, qp);
 }
 
 __device__ __forceinline__ float row_sum(float v, int G) {
@@ -292,12 +311,15 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
 
     Chunk<T, VEC> z[CB];
     RopeCoef<T, H> rc[V2 ? 1 : CB];
+    QuantParams<VEC> qp[V2 ? CB : 1];     // V2 quantised ckv: requested with the data
+    const bool quant = V2 && p.c_code != CODE_SAME;
 #pragma unroll
     for (int i = 0; i < CB; i++) {
         const int c = gl + i * G;
         if (r.ok && c < p.nx) {
             z[i].load_nt(src + c * VEC);
             if (!V2) rc[i].load(cs, sn, c * H, p.half_rope, p.stream_rope != 0);
+            if (quant) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r.n, p.c_dim, c * VEC);
         } else {
             z[i].zero();
         }
@@ -343,7 +365,7 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
                 } else {
                     float zv[VEC];
                     z[i].decode(zv);
-                    put_cache<T, VEC>(d, c * VEC, zv);
+                    put_codes<VEC>(d, c * VEC, zv, qp[i]);
                 }
             }
             if (out_kv) z[i].store_nt(raw + c * VEC);
@@ -352,10 +374,11 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
 }
 
 // Blocks [0, blocks_a) run part A, the rest part B. The occupancy hint keeps
-// register use low enough for many rows in flight (lower for the widest rows,
-// so that no instantiation spills).
+// register use low enough for many rows in flight (lower for the widest rows
+// and for two V2 value chunks with their parameters, so that no instantiation
+// spills).
 template <typename T, int VEC, bool V2, int CA, int CB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CA >= 4 ? 6 : (CA == 3 ? 7 : 8), 8))) void kv_rmsnorm_rope_cache_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CA >= 4 ? 6 : ((CA == 3 || (V2 && CB == 2)) ? 7 : 8), 8))) void kv_rmsnorm_rope_cache_kernel(
     KvParams p) {
     if (blockIdx.x < p.blocks_a) part_a<T, VEC, V2, CA>(p, blockIdx.x);
     else part_b<T, VEC, V2, CB>(p, blockIdx.x - p.blocks_a);
