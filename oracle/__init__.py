@@ -23,12 +23,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F64, F32, BF16, F16, INT8, E4M3FN = 0, 1, 2, 3, 4, 5
-NORM, PA_BNSD = 0, 1
+F64, F32, BF16, F16, INT8, E4M3FN, E5M2 = 0, 1, 2, 3, 4, 5, 6
+NORM, PA_BNSD, PA_BLK_BNSD = 0, 1, 2
 
 # numpy storage views: 16-bit floats travel as uint16 bit patterns, fp8 as uint8
 STORAGE = {F64: np.float64, F32: np.float32, BF16: np.uint16, F16: np.uint16,
-           INT8: np.int8, E4M3FN: np.uint8}
+           INT8: np.int8, E4M3FN: np.uint8, E5M2: np.uint8}
 
 _lib = None
 
@@ -101,7 +101,7 @@ def decode(dtype: int, bits: np.ndarray) -> np.ndarray:
 
 
 def encode(dtype: int, values) -> np.ndarray:
-    """Round fp64 values once to the storage type (RNE; E4M3FN saturating)."""
+    """Round fp64 values once to the storage type (RNE; the FP8 formats saturating)."""
     src = np.ascontiguousarray(values, dtype=np.float64)
     out = np.empty(src.shape, STORAGE[dtype])
     _load().oracle_encode(dtype, _ptr(src), _ptr(out), src.size)
@@ -162,8 +162,9 @@ def kv_rmsnorm_rope_cache(kv, v, gamma, cos, sin, index, k_cache, ckv_cache, *,
     """The KvRmsNormRopeCache operator on host arrays.
 
     kv [B, N, S, Dkv] and v [B, N, S, Dv] (or None for V1), gamma, cos/sin
-    [B, N, S or 1, rope] in storage form of ``in_dtype``; index int64; the caches
-    (storage arrays, Norm [B, N, Scache, D] or paged [blocks, bs, N, D]) are
+    [B, N, S or 1, rope] in storage form of ``in_dtype``; index int64 (Norm
+    [B, S], PA_BNSD [B*S], PA_BLK_BNSD [B*ceil(S/block_size)] block starts); the
+    caches (storage arrays, Norm [B, N, Scache, D] or paged [blocks, bs, N, D]) are
     copied and the copies updated (``copy_caches=False`` updates the given
     C-contiguous arrays in place). Returns a dict with k_cache, ckv_cache,
     k_rope, c_kv (None unless is_output_kv), and the exact values k_x, c_x
@@ -177,6 +178,11 @@ def kv_rmsnorm_rope_cache(kv, v, gamma, cos, sin, index, k_cache, ckv_cache, *,
     gamma, cos, sin = _c(gamma, st), _c(cos, st), _c(sin, st)
     rope_S = cos.shape[2]
     index = _c(index, np.int64)
+    if cache_mode != NORM and block_size < 1:
+        raise ValueError("paged caches need block_size >= 1")
+    entries = B * (-(-S // block_size) if cache_mode == PA_BLK_BNSD else S)
+    if index.size != entries:
+        raise ValueError(f"index holds {index.size} entries, the cache mode needs {entries}")
     if copy_caches:
         k_cache = np.array(k_cache, copy=True, order="C")
         ckv_cache = np.array(ckv_cache, copy=True, order="C")

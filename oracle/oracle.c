@@ -35,8 +35,8 @@
 #include <string.h>
 
 /* storage type codes used by the oracle's own wrapper (oracle/__init__.py) */
-enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2, ORC_F16 = 3, ORC_INT8 = 4, ORC_E4M3FN = 5 };
-enum { ORC_NORM = 0, ORC_PA_BNSD = 1 };
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2, ORC_F16 = 3, ORC_INT8 = 4, ORC_E4M3FN = 5, ORC_E5M2 = 6 };
+enum { ORC_NORM = 0, ORC_PA_BNSD = 1, ORC_PA_BLK_BNSD = 2 };
 
 /* ------------------------------------------------------------------------ */
 /* Format definitions: decode (exact) and encode (round to nearest, ties to  */
@@ -68,6 +68,17 @@ static double dec_e4m3fn(uint8_t c) {
     if (e == 15 && m == 7) v = NAN;
     else if (e == 0) v = ldexp((double)m, -9);
     else v = ldexp(8.0 + m, e - 10);
+    return s ? -v : v;
+}
+
+/* OCP FP8 E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa; IEEE-like: exponent
+ * 31 holds inf (mantissa 0) and NaN */
+static double dec_e5m2(uint8_t c) {
+    int s = c >> 7, e = (c >> 2) & 31, m = c & 3;
+    double v;
+    if (e == 31) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)m, -16);
+    else v = ldexp(4.0 + m, e - 17);
     return s ? -v : v;
 }
 
@@ -131,6 +142,22 @@ static uint8_t enc_e4m3fn(double x) {
     return s | (uint8_t)((E + 7) << 3) | mant;
 }
 
+/* saturating E5M2 encoder: |x| at or above the largest finite (57344) -> 57344 */
+static uint8_t enc_e5m2(double x) {
+    if (isnan(x)) return 0x7F;
+    uint8_t s = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a >= 57344.0) return s | 0x7B;
+    double r = round_to_format(a, 3, -14);
+    if (r >= 57344.0) return s | 0x7B;
+    if (r < ldexp(1.0, -14)) return s | (uint8_t)(r / ldexp(1.0, -16));  /* subnormal field */
+    int e;
+    double m = frexp(r, &e);
+    int E = e - 1;
+    uint8_t mant = (uint8_t)((m * 2.0 - 1.0) * 4.0);
+    return s | (uint8_t)((E + 15) << 2) | mant;
+}
+
 static double load(int dtype, const void *p, int64_t i) {
     switch (dtype) {
     case ORC_F64: return ((const double *)p)[i];
@@ -139,6 +166,7 @@ static double load(int dtype, const void *p, int64_t i) {
     case ORC_F16: return dec_f16(((const uint16_t *)p)[i]);
     case ORC_INT8: return (double)((const int8_t *)p)[i];
     case ORC_E4M3FN: return dec_e4m3fn(((const uint8_t *)p)[i]);
+    case ORC_E5M2: return dec_e5m2(((const uint8_t *)p)[i]);
     }
     return NAN;
 }
@@ -162,6 +190,7 @@ void oracle_decode(int dtype, const void *src, double *dst, int64_t n) {
 void oracle_encode(int dtype, const double *src, void *dst, int64_t n) {
     for (int64_t i = 0; i < n; i++) {
         if (dtype == ORC_E4M3FN) ((uint8_t *)dst)[i] = enc_e4m3fn(src[i]);
+        else if (dtype == ORC_E5M2) ((uint8_t *)dst)[i] = enc_e5m2(src[i]);
         else store(dtype, dst, i, src[i]);
     }
 }
@@ -269,9 +298,10 @@ int oracle_qk_norm_rope_across_heads(int64_t T, int64_t n_q, int64_t n_k, int64_
  * [KVRNRC] formula (3): x*scale if a scale is given, then +offset if an
  * offset is given; with any quantisation the value is rounded (half to even,
  * as torch.round does) and clamped to [-128, 127] for INT8. For FLOAT8E4M3FN
- * the pages give no separate formula; the value is cast to E4M3FN with round
- * to nearest even, saturating at +-448. The rounding decision is taken on the
- * fp32 value of t, the precision the GPU kernel computes t in.
+ * and FLOAT8E5M2 the pages give no separate formula; the value is cast to the
+ * format with round to nearest even, saturating at its largest finite value
+ * (+-448, +-57344). The rounding decision is taken on the fp32 value of t,
+ * the precision the GPU kernel computes t in.
  * Returns t (the exact pre-rounding value) and writes the code.
  */
 static double quantise(int cdtype, void *cache, int64_t pos, double x,
@@ -286,6 +316,8 @@ static double quantise(int cdtype, void *cache, int64_t pos, double x,
         ((int8_t *)cache)[pos] = (int8_t)r;
     } else if (cdtype == ORC_E4M3FN) {
         ((uint8_t *)cache)[pos] = enc_e4m3fn((double)(float)t);
+    } else if (cdtype == ORC_E5M2) {
+        ((uint8_t *)cache)[pos] = enc_e5m2((double)(float)t);
     } else {
         store(cdtype, cache, pos, t);
     }
@@ -301,14 +333,18 @@ static double quantise(int cdtype, void *cache, int64_t pos, double x,
  *   gamma [rms_size]; cos/sin [B, N, rope_S, rope_size], rope_S == S (or 1:
  *   the S-axis broadcast the constraint tables allow).
  *   index: Norm [B, S] rows of batch b's cache slab, in [-1, Scache);
- *          PA_BNSD [B*S] global slots in [-1, block_num*block_size).
- *   Caches: Norm [B, N, Scache, D]; PA_BNSD [block_num, block_size, N, D]
- *   (the shape the cache/index table gives for PA/PA_BNSD).
+ *          PA_BNSD [B*S] global slots in [-1, block_num*block_size);
+ *          PA_BLK_BNSD [B*ceil(S/block_size)]: the starting slot of each run
+ *          of block_size consecutive tokens of a batch; token s of batch b
+ *          goes to slot index[b*ceil(S/bs) + s/bs] + s%bs.
+ *   Caches: Norm [B, N, Scache, D]; PA_BNSD and PA_BLK_BNSD
+ *   [block_num, block_size, N, D] (the shape the cache/index table gives).
  *   k width Dk_out = rope_size (V1) or Dkv (V2); ckv width Dc = rms_size (V1)
  *   or Dv (V2).
  *   k_scale/k_offset [N, Dk_out], v_scale/v_offset [N, Dc] fp64 or NULL (the
  *   wrapper broadcasts [1], [D], [1, D] to [N, D]).
- *   index == -1: the token writes no cache row (reading in the design doc).
+ *   index == -1, or a slot outside the cache: the token writes no cache row
+ *   (reading in the design doc).
  * Outputs: caches updated in place; k_rope/c_kv (if out_kv) in in_dtype;
  * optional exact values: k_x/c_x (the values fed to Quant) and k_t/c_t (the
  * values right before rounding, = x*scale+offset, or x without quantisation).
@@ -328,6 +364,7 @@ int oracle_kv_rmsnorm_rope_cache(
     if (!v2 && rms_size + rope_size != Dkv) return -1;
     if (v2 && (rms_size != Dkv || rope_size > Dkv || Dv < 1)) return -1;
     if (rope_S != S && rope_S != 1) return -1;
+    if (cache_mode != ORC_NORM && block_size < 1) return -1;
     int64_t Dk_out = v2 ? Dkv : rope_size;
     int64_t Dc = v2 ? Dv : rms_size;
     int64_t half = rope_size / 2;
@@ -374,10 +411,19 @@ int oracle_kv_rmsnorm_rope_cache(
                 c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : y[i];
 
             /* (4) scatter slot for token (b, s): Norm's index is [B, S] and
-             * PA_BNSD's is [B*S], the same flat position b*S + s */
-            int64_t slot = index[b * S + s];
+             * PA_BNSD's is [B*S], the same flat position b*S + s; PA_BLK_BNSD
+             * holds one starting slot per block_size tokens of a batch */
+            int64_t slot, capacity;
+            if (cache_mode == ORC_PA_BLK_BNSD) {
+                int64_t nblk = (S + block_size - 1) / block_size;
+                int64_t start = index[b * nblk + s / block_size];
+                slot = start < 0 ? -1 : start + s % block_size;
+            } else {
+                slot = index[b * S + s];
+            }
+            capacity = cache_mode == ORC_NORM ? cache_dim0 : cache_dim0 * block_size;
             int64_t krow = -1, crow = -1;   /* first element of the cache row */
-            if (slot >= 0) {
+            if (slot >= 0 && slot < capacity) {
                 if (cache_mode == ORC_NORM) {
                     int64_t r = (b * N + n) * cache_dim0 + slot;      /* [B, N, Scache, D] */
                     krow = r * Dk_out;

@@ -39,6 +39,17 @@ def e4m3fn_value(code: int) -> float:
     return s * (1 + m / 8) * 2.0 ** (e - 7)
 
 
+def e5m2_value(code: int) -> float:
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 2) & 0x1F
+    m = code & 3
+    if e == 0x1F:
+        return s * math.inf if m == 0 else math.nan
+    if e == 0:
+        return s * m * 2.0 ** -16
+    return s * (1 + m / 4) * 2.0 ** (e - 15)
+
+
 @functools.lru_cache(maxsize=None)
 def _codebook(fmt: str):
     """Sorted (value, code) pairs of every finite non-negative value."""
@@ -51,6 +62,9 @@ def _codebook(fmt: str):
     elif fmt == "e4m3fn":
         codes = range(0, 0x7F)
         val = e4m3fn_value
+    elif fmt == "e5m2":
+        codes = range(0, 0x7C)
+        val = e5m2_value
     else:
         raise ValueError(fmt)
     pairs = sorted((val(c), c) for c in codes)
@@ -59,9 +73,9 @@ def _codebook(fmt: str):
 
 def encode_nearest(fmt: str, x: float, saturate: bool = False) -> int:
     """Nearest representable value, ties to the even code; overflow past the
-    largest finite value goes to inf (bf16/f16) or saturates (e4m3fn)."""
+    largest finite value goes to inf (bf16/f16) or saturates (the FP8 formats)."""
     vals, codes = _codebook(fmt)
-    sign = {"bf16": 0x8000, "f16": 0x8000, "e4m3fn": 0x80}[fmt]
+    sign = {"bf16": 0x8000, "f16": 0x8000, "e4m3fn": 0x80, "e5m2": 0x80}[fmt]
     neg = math.copysign(1.0, x) < 0
     a = abs(x)
     top = vals[-1]
@@ -92,7 +106,7 @@ def encode_nearest(fmt: str, x: float, saturate: bool = False) -> int:
 
 
 def decode(fmt: str, code: int) -> float:
-    return {"bf16": bf16_value, "f16": f16_value, "e4m3fn": e4m3fn_value}[fmt](code)
+    return {"bf16": bf16_value, "f16": f16_value, "e4m3fn": e4m3fn_value, "e5m2": e5m2_value}[fmt](code)
 
 
 def to_fp32(x: float) -> float:
@@ -151,7 +165,7 @@ def interleave_rope(z, cos, sin):
 
 
 def quant_code(x, scale, offset, fmt):
-    """Returns (code, t). fmt in {"int8", "e4m3fn", "bf16", "f16"}."""
+    """Returns (code, t). fmt in {"int8", "e4m3fn", "e5m2", "bf16", "f16"}."""
     t = x
     if scale is not None:
         t = t * scale
@@ -160,8 +174,8 @@ def quant_code(x, scale, offset, fmt):
     if fmt == "int8":
         r = round_half_even(to_fp32(t))
         return max(-128, min(127, r)), t
-    if fmt == "e4m3fn":
-        return encode_nearest("e4m3fn", to_fp32(t), saturate=True), t
+    if fmt in ("e4m3fn", "e5m2"):
+        return encode_nearest(fmt, to_fp32(t), saturate=True), t
     return encode_nearest(fmt, t), t
 
 
@@ -176,11 +190,30 @@ def kv_row(kv_row_vals, v_row_vals, gamma, cos, sin, rms_size, rope_size, eps):
     return rope + y[rope_size:], list(v_row_vals)
 
 
+def token_slot(mode, index, b, s, S, block_size):
+    """The cache slot of token (b, s), or None when it writes no cache row.
+
+    Norm: index[b][s]; PA_BNSD: index[b*S + s]; PA_BLK_BNSD: the tokens of
+    batch b are cut into runs of block_size (the last run may be shorter) and
+    run j fills consecutive slots from its start index[b*runs + j].
+    """
+    if mode == "norm":
+        v = index[b][s]
+    elif mode == "pa":
+        v = index[b * S + s]
+    else:
+        runs = -(-S // block_size)
+        j, k = divmod(s, block_size)
+        start = index[b * runs + j]
+        v = -1 if start < 0 else start + k
+    return None if v < 0 else int(v)
+
+
 def cache_row_address(mode, b, n, slot, N, Scache, block_size):
     """Row number of the cache row for token (b, ., s) and head n.
 
     Norm: [B, N, Scache, D] -> (b*N + n)*Scache + slot.
-    PA_BNSD: [block_num, block_size, N, D] -> ((slot//bs)*bs + slot%bs)*N + n.
+    PA_BNSD, PA_BLK_BNSD: [block_num, block_size, N, D] -> ((slot//bs)*bs + slot%bs)*N + n.
     """
     if mode == "norm":
         return (b * N + n) * Scache + slot

@@ -32,6 +32,12 @@ MUTANTS = {
                             "    if (offset) t = t + offset[qi];\n    if (scale) t = t * scale[qi];"),
     "e4m3_no_saturation": ("if (a >= 448.0) return s | 0x7E;", "if (a >= 464.0) return s | 0x7F;"),
     "bf16_truncates": ("return nearbyint(a / q) * q;", "return floor(a / q) * q;"),
+    "e5m2_no_saturation": ("if (a >= 57344.0) return s | 0x7B;", "if (a >= 61440.0) return s | 0x7C;"),
+    "e5m2_wrong_bias": ("return s | (uint8_t)((E + 15) << 2) | mant;", "return s | (uint8_t)((E + 16) << 2) | mant;"),
+    "pa_blk_start_not_offset": ("slot = start < 0 ? -1 : start + s % block_size;", "slot = start;"),
+    "pa_blk_per_token_index": ("int64_t start = index[b * nblk + s / block_size];",
+                               "int64_t start = index[(b * S + s) / block_size];"),
+    "no_capacity_check": ("if (slot >= 0 && slot < capacity) {", "if (slot >= 0) {"),
     "c_kv_from_raw_in_v1": ("c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : y[i];",
                             "c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : load(in_dtype, kv, kv0 + i);"),
 }

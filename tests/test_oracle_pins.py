@@ -223,6 +223,33 @@ def test_e4m3fn_codebook_exhaustive():
     np.testing.assert_array_equal(oracle.encode(oracle.E4M3FN, t.astype(np.float32).astype(np.float64)), ref)
 
 
+def test_e5m2_codebook_exhaustive():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode(oracle.E5M2, codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    for c in range(256):
+        bv = brute.e5m2_value(c)
+        if math.isnan(bv):
+            assert math.isnan(vals[c]) and math.isnan(ref[c])
+            continue
+        assert vals[c] == bv == ref[c], c
+        if math.isfinite(bv):
+            assert oracle.encode(oracle.E5M2, [bv])[0] == c
+    # inf and values past the largest finite saturate (57344 = 0x7B)
+    assert oracle.encode(oracle.E5M2, [math.inf])[0] == 0x7B
+    assert oracle.encode(oracle.E5M2, [-1e30])[0] == 0xFB
+    finite = sorted(brute.e5m2_value(c) for c in range(0, 0x7C))
+    for lo, hi in zip(finite[:-1], finite[1:]):
+        mid = (lo + hi) / 2
+        for x in (mid, math.nextafter(mid, 0), math.nextafter(mid, 1e9), -mid):
+            assert oracle.encode(oracle.E5M2, [x])[0] == brute.encode_nearest("e5m2", x, saturate=True), x
+    # torch's cast is a library RNE cast below the saturation point
+    rng = np.random.default_rng(10)
+    t = rng.uniform(-57343, 57343, 20000) * 10.0 ** rng.integers(-8, 1, 20000)
+    ref = torch.from_numpy(t.astype(np.float32)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.encode(oracle.E5M2, t.astype(np.float32).astype(np.float64)), ref)
+
+
 def test_quant_golden_hand_cases():
     g = _golden("quant_hand.json")
     for c in g["int8"]:
@@ -233,6 +260,9 @@ def test_quant_golden_hand_cases():
     for c in g["e4m3fn"]:
         assert oracle.encode(oracle.E4M3FN, [c["t"]])[0] == c["code"], c
         assert brute.encode_nearest("e4m3fn", c["t"], saturate=True) == c["code"]
+    for c in g["e5m2"]:
+        assert oracle.encode(oracle.E5M2, [c["t"]])[0] == c["code"], c
+        assert brute.encode_nearest("e5m2", c["t"], saturate=True) == c["code"], c
 
 
 def _run_single_quant(x, scale, offset, kdtype):
@@ -357,6 +387,62 @@ def test_scatter_golden_norm_and_pa():
         assert (r["k_cache"][i, j, n] == -7).all() and (r["ckv_cache"][i, j, n] == -7).all()
 
 
+@pytest.mark.parametrize("key", ["pa_blk_bnsd", "pa_blk_bnsd_unaligned"])
+def test_scatter_golden_pa_blk(key):
+    c = _golden("scatter_hand.json")[key]
+    B, S, N, bs, nb, R = c["B"], c["S"], c["N"], c["block_size"], c["block_num"], 2
+    kv = np.arange(B * N * S * (2 + R), dtype=float).reshape(B, N, S, 2 + R) + 1.0
+    pre_k = np.full((nb, bs, N, R), -7.0)
+    pre_c = np.full((nb, bs, N, 2), -7.0)
+    r = oracle.kv_rmsnorm_rope_cache(
+        kv, None, np.ones(2), np.ones((B, N, S, R)), np.zeros((B, N, S, R)),
+        np.array(c["index"], np.int64), pre_k, pre_c, rms_size=2, rope_size=R, eps=0.0,
+        cache_mode=oracle.PA_BLK_BNSD, in_dtype=oracle.F64, k_dtype=oracle.F64, ckv_dtype=oracle.F64,
+        block_size=bs, nthreads=1)
+    written = set()
+    for b, s, n, blk, off in c["written"]:
+        written.add((blk, off, n))
+        np.testing.assert_array_equal(r["k_cache"][blk, off, n], r["k_x"][b, n, s])
+        np.testing.assert_array_equal(r["ckv_cache"][blk, off, n], r["c_x"][b, n, s])
+    for i in range(nb):
+        for j in range(bs):
+            for n in range(N):
+                if (i, j, n) not in written:
+                    assert (r["k_cache"][i, j, n] == -7).all() and (r["ckv_cache"][i, j, n] == -7).all()
+
+
+def test_pa_blk_with_block_size_one_is_pa_bnsd():
+    """With runs of one token the block starts are per-token slots: PA_BLK_BNSD
+    reduces to PA_BNSD (a special case the constraint table's two rows share)."""
+    B, N, S, R = 2, 1, 3, 2
+    kv = np.random.default_rng(3).standard_normal((B, N, S, 2 + R))
+    idx = np.array([4, -1, 0, 5, 2, 1], np.int64)
+    outs = []
+    for mode in (oracle.PA_BNSD, oracle.PA_BLK_BNSD):
+        outs.append(oracle.kv_rmsnorm_rope_cache(
+            kv, None, np.ones(2), np.ones((B, N, S, R)), np.zeros((B, N, S, R)), idx,
+            np.zeros((6, 1, N, R)), np.zeros((6, 1, N, 2)), rms_size=2, rope_size=R, eps=1e-6,
+            cache_mode=mode, in_dtype=oracle.F64, k_dtype=oracle.F64, ckv_dtype=oracle.F64,
+            block_size=1, nthreads=1))
+    np.testing.assert_array_equal(outs[0]["k_cache"], outs[1]["k_cache"])
+    np.testing.assert_array_equal(outs[0]["ckv_cache"], outs[1]["ckv_cache"])
+
+
+def test_kv_slot_past_the_cache_writes_nothing():
+    """Each cache is the leading part of a larger buffer; the rest is a guard
+    region that a write past the cache would land in."""
+    kv = np.ones((1, 1, 2, 4))
+    for mode, idx, buf_shape in ((oracle.NORM, [[3, 0]], (2, 1, 3, 2)), (oracle.PA_BNSD, [6, 1], (4, 2, 1, 2))):
+        kbuf, cbuf = np.full(buf_shape, 5.0), np.full(buf_shape, 5.0)
+        oracle.kv_rmsnorm_rope_cache(
+            kv, None, np.ones(2), np.ones((1, 1, 2, 2)), np.zeros((1, 1, 2, 2)), np.array(idx, np.int64),
+            kbuf[:buf_shape[0] - 1], cbuf[:buf_shape[0] - 1], rms_size=2, rope_size=2, eps=0.0,
+            cache_mode=mode, in_dtype=oracle.F64, k_dtype=oracle.F64, ckv_dtype=oracle.F64,
+            block_size=0 if mode == oracle.NORM else 2, nthreads=1, copy_caches=False)
+        assert (kbuf[-1] == 5).all() and (cbuf[-1] == 5).all(), "wrote past the cache"
+        assert (kbuf != 5).sum() == 2 and (cbuf != 5).sum() == 2     # only the in-range token
+
+
 # ---------------------------------------------------------------- (b) brute force
 
 def _bits(t):
@@ -371,10 +457,14 @@ KV_CASES = [
     ("v2_pa_int8_asym", True, "pa", "int8", "int8", ("ND", True), ("ND", True), True),
     ("v2_norm_bf16", True, "norm", "bf16", "bf16", None, None, True),
     ("v2_pa_mixed", True, "pa", "e4m3fn", "bf16", ("ND", True), None, False),
+    ("v1_pablk_e5m2", False, "pablk", "e5m2", "e5m2", ("D", False), ("1D", False), True),
+    ("v2_pablk_e5m2_int8", True, "pablk", "int8", "e5m2", ("ND", True), ("ND", False), True),
+    ("v1_norm_e5m2", False, "norm", "e5m2", "e4m3fn", ("1", False), ("D", False), False),
 ]
 
-_FMT = {"bf16": oracle.BF16, "int8": oracle.INT8, "e4m3fn": oracle.E4M3FN}
-_NP = {"bf16": np.uint16, "int8": np.int8, "e4m3fn": np.uint8}
+_FMT = {"bf16": oracle.BF16, "int8": oracle.INT8, "e4m3fn": oracle.E4M3FN, "e5m2": oracle.E5M2}
+_NP = {"bf16": np.uint16, "int8": np.int8, "e4m3fn": np.uint8, "e5m2": np.uint8}
+_MODE = {"norm": oracle.NORM, "pa": oracle.PA_BNSD, "pablk": oracle.PA_BLK_BNSD}
 
 
 @pytest.mark.parametrize("case", KV_CASES, ids=[c[0] for c in KV_CASES])
@@ -411,6 +501,11 @@ def test_kv_brute_force_tiny(case):
         k_cache = np.random.default_rng(1).integers(0, 200, (B, N, Sc, dk)).astype(_NP[kf])
         c_cache = np.random.default_rng(2).integers(0, 200, (B, N, Sc, dc)).astype(_NP[cf])
         bs = 0
+    elif mode == "pablk":
+        bs, nb = 2, 4
+        index = np.array([6, 0, -1, 3], np.int64)     # runs {0,1}, {2} of each batch
+        k_cache = np.random.default_rng(1).integers(0, 200, (nb, bs, N, dk)).astype(_NP[kf])
+        c_cache = np.random.default_rng(2).integers(0, 200, (nb, bs, N, dc)).astype(_NP[cf])
     else:
         bs, nb = 2, 4
         index = np.array([7, 0, -1, 3, 4, 1], np.int64)
@@ -419,7 +514,7 @@ def test_kv_brute_force_tiny(case):
     r = oracle.kv_rmsnorm_rope_cache(
         _bits(kv), _bits(v) if v2 else None, _bits(gamma), _bits(cos), _bits(sin), index,
         k_cache, c_cache, rms_size=rms, rope_size=R, eps=1e-5,
-        cache_mode=oracle.NORM if mode == "norm" else oracle.PA_BNSD, in_dtype=oracle.BF16,
+        cache_mode=_MODE[mode], in_dtype=oracle.BF16,
         k_dtype=_FMT[kf], ckv_dtype=_FMT[cf], block_size=bs, k_scale=ks, k_offset=ko,
         v_scale=vs, v_offset=vo, is_output_kv=out_kv, nthreads=2)
 
@@ -444,11 +539,11 @@ def test_kv_brute_force_tiny(case):
                                               gd, cd[b, n, s].tolist(), sd[b, n, s].tolist(), rms, R, 1e-5)
                 np.testing.assert_allclose(r["k_x"][b, n, s], rope_out, rtol=1e-13, atol=1e-15)
                 np.testing.assert_allclose(r["c_x"][b, n, s], csrc, rtol=1e-13, atol=1e-15)
-                slot = int(index[b, s] if mode == "norm" else index[b * S + s])
+                slot = brute.token_slot(mode, index.tolist(), b, s, S, bs)
                 if out_kv:
                     assert r["k_rope"][b, n, s].tolist() == [brute.encode_nearest("bf16", x) for x in rope_out]
                     assert r["c_kv"][b, n, s].tolist() == [brute.encode_nearest("bf16", x) for x in csrc]
-                if slot < 0:
+                if slot is None:
                     continue
                 row = brute.cache_row_address(mode, b, n, slot, N, 5, bs)
                 krow = [brute.quant_code(x, at(ks, n, j), at(ko, n, j), kf)[0] for j, x in enumerate(rope_out)]
