@@ -66,10 +66,13 @@ extern "C" {
 #define QKNR_F16 2
 #define QKNR_INT8 3
 #define QKNR_FP8_E4M3FN 4
+#define QKNR_FP8_E5M2 5
 
 /* cache modes (KvRmsNormRopeCache, cache_mode attribute) */
 #define QKNR_CACHE_NORM 0      /* "Norm": [Bkv, N, Scache, D], index [Bkv, Skv] */
 #define QKNR_CACHE_PA_BNSD 1   /* "PA" / "PA_BNSD": [block_num, block_size, N, D], index [Bkv*Skv] */
+#define QKNR_CACHE_PA_BLK_BNSD 2 /* "PA_BLK_BNSD": PA_BNSD's layout, index [Bkv*ceil(Skv/block_size)]
+                                    of block starting slots */
 
 /* shapes of a quantisation parameter (constraint table for k_rope_scale etc.) */
 #define QKNR_QSHAPE_SCALAR 0       /* [1]                 */
@@ -157,14 +160,23 @@ int32_t qknr_qk_validate(const qknr_qk_args *args);
  *       out[j+R/2] = z[2j+1]*cos[j+R/2] + z[2j]*sin[j+R/2], j < R/2 (the even
  *       lanes' results first, then the odd lanes'; cos/sin indexed by output lane).
  *   Quant (per cache): t = x*scale (+offset); INT8: round half to even, clamp to
- *       [-128, 127]; FP8_E4M3FN: round to nearest even, saturate at +-448;
+ *       [-128, 127]; FP8_E4M3FN / FP8_E5M2: round to nearest even, saturate at
+ *       the largest finite value (+-448 / +-57344);
  *       cache dtype == dtype: round the value to dtype (no scale/offset allowed).
  *       Rounding decisions are taken on the fp32 value of t.
  *   Scatter: NORM: row index[b*Skv + s] (index is [Bkv, Skv]) inside batch b:
  *       k_cache[b*kc_stride0 + n*kc_stride2 + row*kc_stride1];
  *       PA_BNSD: slot = index[b*Skv + s] (index is [Bkv*Skv]):
  *       k_cache[(slot/block_size)*kc_stride0 + (slot%block_size)*kc_stride1 + n*kc_stride2];
- *       likewise ckv_cache with the ckv strides. index -1: no cache write.
+ *       PA_BLK_BNSD: the tokens of batch b form runs of block_size (the last
+ *       may be shorter); run j fills consecutive slots from its starting slot
+ *       index[b*ceil(Skv/block_size) + j] (the cache/index constraint table
+ *       gives one entry per block of tokens, the block's starting offset), so
+ *       token s goes to slot index[b*ceil(Skv/bs) + s/bs] + s%bs, addressed as
+ *       in PA_BNSD. Starts need not be multiples of block_size.
+ *       The ckv cache is addressed likewise with the ckv strides. index -1: no
+ *       cache write (PA_BLK_BNSD: for the whole run); a slot outside the cache
+ *       (undefined on the page) writes nothing.
  *   Raw outputs (is_output_kv): k_rope[b,n,s,:] = rope_out and
  *       c_kv[b,n,s,:] = y (V1) or v_optional row (V2), in `dtype`, unquantised.
  *
@@ -178,21 +190,22 @@ int32_t qknr_qk_validate(const qknr_qk_args *args);
  *   kv_strides[3], v_strides[3], rope_strides[3], k_rope_strides[3],
  *   c_kv_strides[3]: element strides of the (b, n, s) axes; the channel axis is
  *       contiguous. rope_strides[2] == 0 is the S-axis broadcast (Srope = 1).
- *   index            int64 device array (see Scatter).
- *   cache_mode       QKNR_CACHE_NORM or QKNR_CACHE_PA_BNSD.
- *   cache_rows       NORM: Scache (>= Skv). PA_BNSD: block_num.
- *   block_size       PA_BNSD: > 1 and block_size*sizeof(cache element) a multiple of 32.
- *   k_cache_dtype, ckv_cache_dtype   dtype, QKNR_INT8 or QKNR_FP8_E4M3FN.
+ *   index            int64 device array (see Scatter): Bkv*Skv entries (NORM,
+ *       PA_BNSD) or Bkv*ceil(Skv/block_size) (PA_BLK_BNSD).
+ *   cache_mode       QKNR_CACHE_NORM, QKNR_CACHE_PA_BNSD or QKNR_CACHE_PA_BLK_BNSD.
+ *   cache_rows       NORM: Scache (>= Skv). Paged: block_num (>= floor(Skv/bs)*Bkv).
+ *   block_size       paged: > 1 and block_size*sizeof(cache element) a multiple of 32.
+ *   k_cache_dtype, ckv_cache_dtype   dtype, QKNR_INT8, QKNR_FP8_E4M3FN or QKNR_FP8_E5M2.
  *   k_cache_strides[3], ckv_cache_strides[3]: element strides of the cache's
- *       leading axes: NORM (batch, row, head); PA_BNSD (block, slot in block,
+ *       leading axes: NORM (batch, row, head); paged (block, slot in block,
  *       head). The channel axis is contiguous.
  *   k_scale, k_offset, v_scale, v_offset   fp32 device arrays or NULL; the
  *       *_qshape fields give their shapes (QKNR_QSHAPE_*). A scale is required
  *       exactly when the cache dtype differs from dtype; an offset needs its
  *       scale. V1 allows SCALAR/CHANNEL shapes, V2 HEAD_CHANNEL.
  *   eps              default on the page 1e-5.
- *   is_output_kv     1: write k_rope and c_kv (allowed in PA_BNSD, and in
- *       NORM only for V2 with quantisation).
+ *   is_output_kv     1: write k_rope and c_kv (effective in the paged modes,
+ *       and in NORM only for V2 with quantisation; ignored elsewhere).
  */
 typedef struct qknr_kv_args {
     int32_t dtype;

@@ -32,13 +32,14 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR = 0, 1, 2, 3
-F32, BF16, F16, INT8, FP8_E4M3FN = 0, 1, 2, 3, 4
-CACHE_NORM, CACHE_PA_BNSD = 0, 1
+F32, BF16, F16, INT8, FP8_E4M3FN, FP8_E5M2 = 0, 1, 2, 3, 4, 5
+CACHE_NORM, CACHE_PA_BNSD, CACHE_PA_BLK_BNSD = 0, 1, 2
 QSHAPE_SCALAR, QSHAPE_CHANNEL, QSHAPE_HEAD_CHANNEL = 0, 1, 2
 
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16,
-          torch.int8: INT8, torch.float8_e4m3fn: FP8_E4M3FN}
-_CACHE_MODE = {"Norm": CACHE_NORM, "PA": CACHE_PA_BNSD, "PA_BNSD": CACHE_PA_BNSD}
+          torch.int8: INT8, torch.float8_e4m3fn: FP8_E4M3FN, torch.float8_e5m2: FP8_E5M2}
+_CACHE_MODE = {"Norm": CACHE_NORM, "PA": CACHE_PA_BNSD, "PA_BNSD": CACHE_PA_BNSD,
+               "PA_BLK_BNSD": CACHE_PA_BLK_BNSD}
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -269,7 +270,8 @@ def kv_args(kv, gamma, cos, sin, index, k_cache, ckv_cache, *, k_rope_scale=None
 
     kv [Bkv, N, Skv, D]; v (v_optional) [Bkv, N, Skv, Dv] or None; gamma
     [rms_size]; cos/sin [Bkv, N, Skv or 1, rope]; index int64 ([Bkv, Skv] for
-    Norm, [Bkv*Skv] for PA/PA_BNSD); caches Norm [Bkv, N, Scache, D] or paged
+    Norm, [Bkv*Skv] for PA/PA_BNSD, [Bkv*ceil(Skv/block_size)] block starts for
+    PA_BLK_BNSD); caches Norm [Bkv, N, Scache, D] or paged
     [block_num, block_size, N, D]; scales/offsets fp32 [1], [D], [1, D] (V1) or
     [N, D] (V2). V1 takes rope_size = cos.shape[-1] and rms_size = D - rope_size.
     """
@@ -302,14 +304,20 @@ def kv_args(kv, gamma, cos, sin, index, k_cache, ckv_cache, *, k_rope_scale=None
         raise ValueError("v_optional must be [Bkv, N, Skv, Dv]")
     dk_w = D if v2 else R
     dc_w = v.shape[-1] if v2 else D - R
+    if cache_mode not in _CACHE_MODE:
+        raise ValueError(f"cache_mode {cache_mode!r} is not built ({', '.join(_CACHE_MODE)})")
     if cache_mode == "Norm":
         if index.numel() != B * S or (index.dim() == 2 and tuple(index.shape) != (B, S)):
             raise ValueError("Norm index must be [Bkv, Skv]")
         lead_ok = (k_cache.dim() == 4 and ckv_cache.dim() == 4 and k_cache.shape[0] == B
                    and k_cache.shape[1] == N and tuple(ckv_cache.shape[:3]) == tuple(k_cache.shape[:3]))
     else:
-        if index.numel() != B * S:
-            raise ValueError("paged index must be [Bkv * Skv]")
+        if k_cache.dim() != 4 or k_cache.shape[1] < 1:
+            raise ValueError("paged caches must be [block_num, block_size, N, D]")
+        entries = B * (-(-S // k_cache.shape[1]) if cache_mode == "PA_BLK_BNSD" else S)
+        if index.numel() != entries:
+            raise ValueError(f"{cache_mode} index must hold {entries} entries "
+                             f"({'Bkv * ceil(Skv / block_size)' if cache_mode == 'PA_BLK_BNSD' else 'Bkv * Skv'})")
         lead_ok = (k_cache.dim() == 4 and ckv_cache.dim() == 4 and k_cache.shape[2] == N
                    and tuple(ckv_cache.shape[:3]) == tuple(k_cache.shape[:3]))
     if not lead_ok or k_cache.shape[3] != dk_w or ckv_cache.shape[3] != dc_w:
@@ -328,10 +336,7 @@ def kv_args(kv, gamma, cos, sin, index, k_cache, ckv_cache, *, k_rope_scale=None
     if cos.shape[2] == 1:
         rs[2] = 0  # S-axis broadcast (Srope = 1)
     a.rope_strides = (_i64 * 3)(*rs)
-    try:
-        a.cache_mode = _CACHE_MODE[cache_mode]
-    except KeyError:
-        raise ValueError(f"cache_mode {cache_mode!r} is not built (Norm, PA, PA_BNSD)") from None
+    a.cache_mode = _CACHE_MODE[cache_mode]
     a.k_cache, a.ckv_cache = _ptr(k_cache), _ptr(ckv_cache)
     a.k_cache_dtype, a.ckv_cache_dtype = _dtype(k_cache), _dtype(ckv_cache)
     if a.cache_mode == CACHE_NORM:

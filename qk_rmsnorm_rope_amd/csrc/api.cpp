@@ -162,9 +162,10 @@ int32_t cache_code(int32_t cache_dtype, int32_t dtype, const char *which, int32_
     if (cache_dtype == dtype) { *code = qknr::CODE_SAME; return QKNR_OK; }
     if (cache_dtype == QKNR_INT8) { *code = qknr::CODE_INT8; return QKNR_OK; }
     if (cache_dtype == QKNR_FP8_E4M3FN) { *code = qknr::CODE_E4M3FN; return QKNR_OK; }
+    if (cache_dtype == QKNR_FP8_E5M2) { *code = qknr::CODE_E5M2; return QKNR_OK; }
     if (cache_dtype == QKNR_F32 || cache_dtype == QKNR_BF16 || cache_dtype == QKNR_F16)
         return fail(QKNR_INVALID_ARGUMENT, "%s: an unquantised cache must have the kv dtype", which);
-    return fail(QKNR_UNSUPPORTED, "%s: cache dtype %d is not built (INT8 and FP8_E4M3FN are)", which,
+    return fail(QKNR_UNSUPPORTED, "%s: cache dtype %d is not built (INT8, FP8_E4M3FN and FP8_E5M2 are)", which,
                 cache_dtype);
 }
 
@@ -230,7 +231,7 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
     if (a->cache_mode == QKNR_CACHE_NORM) {
         if (a->cache_rows < a->seq) return fail(QKNR_INVALID_ARGUMENT, "Norm cache: Scache must be >= Skv");
         capacity = a->cache_rows;
-    } else if (a->cache_mode == QKNR_CACHE_PA_BNSD) {
+    } else if (a->cache_mode == QKNR_CACHE_PA_BNSD || a->cache_mode == QKNR_CACHE_PA_BLK_BNSD) {
         if (a->block_size <= 1) return fail(QKNR_INVALID_ARGUMENT, "paged cache: block_size must be > 1");
         const int kb = k_quant ? 1 : elem_size(a->dtype), cb = c_quant ? 1 : elem_size(a->dtype);
         if (((int64_t)a->block_size * kb) % 32 || ((int64_t)a->block_size * cb) % 32)
@@ -240,18 +241,20 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
             return fail(QKNR_INVALID_ARGUMENT, "paged cache: block_num must be >= floor(Skv/block_size)*Bkv");
         capacity = a->cache_rows * (int64_t)a->block_size;
     } else {
-        return fail(QKNR_UNSUPPORTED, "cache_mode %d is not built (Norm and PA/PA_BNSD are)", a->cache_mode);
+        return fail(QKNR_UNSUPPORTED, "cache_mode %d is not built (Norm, PA/PA_BNSD and PA_BLK_BNSD are)",
+                    a->cache_mode);
     }
 
     // S-axis broadcast of cos/sin (Srope = 1): allowed for Norm and for an
     // unquantised paged cache
     const bool s_bcast = a->rope_strides[2] == 0 && a->seq > 1;
-    if (s_bcast && a->cache_mode == QKNR_CACHE_PA_BNSD && (k_quant || c_quant))
+    const bool paged = a->cache_mode != QKNR_CACHE_NORM;
+    if (s_bcast && paged && (k_quant || c_quant))
         return fail(QKNR_INVALID_ARGUMENT, "S-axis broadcast of cos/sin is not allowed with quantised paged caches");
 
     // is_output_kv: effective for paged caches, and for Norm only in V2 with quantisation
     const bool out_kv = a->is_output_kv &&
-                        (a->cache_mode == QKNR_CACHE_PA_BNSD || (v2 && (k_quant || c_quant)));
+                        (paged || (v2 && (k_quant || c_quant)));
     if (out_kv && (!a->k_rope || !a->c_kv))
         return fail(QKNR_INVALID_ARGUMENT, "is_output_kv needs k_rope and c_kv");
 
@@ -331,7 +334,9 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
     p.cc0 = a->ckv_cache_strides[0]; p.cc1 = a->ckv_cache_strides[1]; p.cc2 = a->ckv_cache_strides[2];
     p.capacity = capacity;
     p.heads = a->heads;
-    p.mode = a->cache_mode == QKNR_CACHE_NORM ? 0 : 1;
+    p.mode = a->cache_mode;     // 0 Norm, 1 PA_BNSD, 2 PA_BLK_BNSD
+    p.runs = a->cache_mode == QKNR_CACHE_PA_BLK_BNSD
+                 ? (uint32_t)((a->seq + a->block_size - 1) / a->block_size) : 0;
     p.block_size = a->cache_mode == QKNR_CACHE_NORM ? 1 : a->block_size;
     p.rms_size = a->rms_size; p.rope_size = a->rope_size; p.half_rope = a->rope_size / 2;
     p.k_dim = k_dim; p.c_dim = c_dim;

@@ -269,6 +269,32 @@ __device__ __forceinline__ uint32_t enc_e4m3fn(float t) {
     return sign | code;
 }
 
+// OCP FP8 E5M2 (bias 15, 2 mantissa bits, largest finite 57344 = 0x7B, inf and
+// NaN at exponent 31), round to nearest even, saturating at +-57344:
+//   |t| >= 57344 -> 0x7B (everything that would round past it, and inf);
+//   |t| < 2^-14 (below the smallest normal) -> the subnormal field, the
+//   integer rint(|t| * 2^16) (0..4; 4 is the smallest normal, code 0x04);
+//   otherwise drop 21 mantissa bits with round-to-nearest-even and rebias the
+//   exponent from 127 to 15.
+__device__ __forceinline__ uint32_t enc_e5m2(float t) {
+    uint32_t u = __float_as_uint(t);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    float af = __uint_as_float(a);
+    uint32_t code;
+    if (a > 0x7F800000u) {
+        code = 0x7Fu;                                    // NaN
+    } else if (af >= 57344.0f) {
+        code = 0x7Bu;                                    // saturate
+    } else if (af < 6.103515625e-05f) {                  // 2^-14
+        code = (uint32_t)__builtin_rintf(af * 65536.0f); // subnormal field (exact scaling)
+    } else {
+        uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);    // RNE at mantissa bit 21
+        code = (r >> 21) - (112u << 2);                  // exponent 127 -> 15
+    }
+    return sign | code;
+}
+
 // ---------------------------------------------------------------------------
 // wavefront reductions (wave64). Every lane of a group ends with the same
 // bits: each step adds a lane's value to its partner's, and both partners

@@ -3,8 +3,10 @@
 // Computes, per (b, n, s) row, the CANN page's formulas: (1) RmsNorm over the
 // first rms_size values, (2) interleaveRope (V1: on the raw tail; V2: on the
 // first rope_size normed values, which it replaces), (3) static quantisation
-// per cache, (4) scatter of the k and ckv rows to the slot index(b, s) of a
-// Norm or paged (PA_BNSD) cache, (5) optional raw outputs k_rope / c_kv.
+// per cache (int8, FP8 E4M3FN or E5M2), (4) scatter of the k and ckv rows to
+// the slot of token (b, s) in a Norm or paged cache (PA_BNSD: one index entry
+// per token; PA_BLK_BNSD: one starting slot per run of block_size tokens),
+// (5) optional raw outputs k_rope / c_kv.
 //
 // MI355X design: the operator is HBM-bound, so each row is read once and every
 // output row is written once, in one pass:
@@ -23,7 +25,7 @@
 //     even-lane outputs (positions j) and half a chunk of the odd-lane outputs
 //     (positions j + R/2), so the rotation needs no data exchange between
 //     lanes: each lane writes two half-chunks;
-//   * quantisation (int8 RNE + clamp, or FP8 E4M3FN RNE saturating) is fused
+//   * quantisation (int8 RNE + clamp, or FP8 E4M3FN / E5M2 RNE saturating) is fused
 //     into the stores; each cache row is written by whole-chunk vector stores
 //     to its slot, so there are no atomics and each output byte has one writer;
 //   * an index of -1 (or, defensively, outside the cache) writes no cache row;
@@ -123,9 +125,12 @@ __device__ __forceinline__ void put_codes(const CacheRow &d, int c, const float 
     if (d.code == CODE_INT8) {
 #pragma unroll
         for (int i = 0; i < N; i++) q[i] = enc_int8(fmaf(x[i], sc[i], of[i]));
-    } else {
+    } else if (d.code == CODE_E4M3FN) {
 #pragma unroll
         for (int i = 0; i < N; i++) q[i] = enc_e4m3fn(fmaf(x[i], sc[i], of[i]));
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i++) q[i] = enc_e5m2(fmaf(x[i], sc[i], of[i]));
     }
     store_codes<N>(d.row + c, q, d.nt);
 }
@@ -193,6 +198,17 @@ __device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t row) {
     return r;
 }
 
+// The cache slot of token (b, s), or -1. Norm and PA_BNSD: index[b*S + s].
+// PA_BLK_BNSD: the run s / block_size of batch b starts at index[b*runs + run]
+// and the token takes the slot s % block_size places after that start.
+__device__ __forceinline__ int64_t token_slot(const KvParams &p, const RowPos &r) {
+    if (!r.ok) return -1;
+    if (p.mode != 2) return p.index[(uint64_t)r.b * p.seq + r.s];
+    const uint32_t run = fastdiv(r.s, p.block_div);
+    const int64_t start = p.index[(uint64_t)r.b * p.runs + run];
+    return start < 0 ? -1 : start + (int64_t)(r.s - run * (uint32_t)p.block_size);
+}
+
 // The cache row of token (b, s), head n, for the k cache (is_k) or the ckv cache.
 template <typename T>
 __device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int64_t slot, const RowPos &r) {
@@ -250,7 +266,7 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
         rc.load(reinterpret_cast<const T *>(p.cos) + ro, reinterpret_cast<const T *>(p.sin) + ro, gl * H,
                 p.half_rope, p.stream_rope != 0);
     }
-    const int64_t slot = r.ok ? p.index[(uint64_t)r.b * p.seq + r.s] : -1;
+    const int64_t slot = token_slot(p, r);
 
     // (1) RmsNorm statistic over rms_size values, reduced over the group
     float ss = 0.0f;
@@ -324,7 +340,7 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
             z[i].zero();
         }
     }
-    const int64_t slot = r.ok ? p.index[(uint64_t)r.b * p.seq + r.s] : -1;
+    const int64_t slot = token_slot(p, r);
     if (!r.ok) return;
 
     const CacheRow d = cache_row<T>(p, !V2, slot, r);

@@ -69,7 +69,7 @@ int qk_plan(QkParams &p, int vec);
 hipError_t qk_launch(QkParams &p, int elem_type, int vec, hipStream_t stream);
 
 // (b) KvRmsNormRopeCache
-enum CacheCode : int32_t { CODE_SAME = 0, CODE_INT8 = 1, CODE_E4M3FN = 2 };
+enum CacheCode : int32_t { CODE_SAME = 0, CODE_INT8 = 1, CODE_E4M3FN = 2, CODE_E5M2 = 3 };
 enum QShape : int32_t { QS_SCALAR = 0, QS_CHANNEL = 1, QS_HEAD_CHANNEL = 2 };
 
 struct KvParams {
@@ -96,7 +96,8 @@ struct KvParams {
     int64_t cc0, cc1, cc2;     // ckv_cache strides
     int64_t capacity;          // NORM: Scache; PA: block_num*block_size
     int32_t heads;
-    int32_t mode;              // 0 NORM, 1 PA_BNSD
+    int32_t mode;              // 0 NORM, 1 PA_BNSD, 2 PA_BLK_BNSD
+    uint32_t runs;             // PA_BLK_BNSD: index entries per batch, ceil(seq / block_size)
     int32_t block_size;
     int32_t rms_size, rope_size, half_rope;
     int32_t k_dim, c_dim;      // widths of the k and ckv rows

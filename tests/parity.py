@@ -10,8 +10,8 @@ Tolerances (stated by the operator's specification of this build):
   1-ulp rsqrt; the oracle is exact);
 * INT8 codes: equal, or one apart where the oracle's pre-rounding value t lies
   within 1e-3 of a .5 boundary;
-* FP8 E4M3FN codes: equal, or adjacent where t lies within 1e-3 of the code
-  spacing from the midpoint between the two values;
+* FP8 E4M3FN / E5M2 codes: equal, or adjacent where t lies within 1e-3 of the
+  code spacing from the midpoint between the two values;
 * cache bytes the operator must not write, and scatter positions: bit-exact.
 """
 from __future__ import annotations
@@ -22,7 +22,8 @@ import torch
 import oracle
 
 ORC = {torch.float32: oracle.F32, torch.bfloat16: oracle.BF16, torch.float16: oracle.F16,
-       torch.int8: oracle.INT8, torch.float8_e4m3fn: oracle.E4M3FN}
+       torch.int8: oracle.INT8, torch.float8_e4m3fn: oracle.E4M3FN, torch.float8_e5m2: oracle.E5M2}
+_FP8 = {torch.float8_e4m3fn: oracle.E4M3FN, torch.float8_e5m2: oracle.E5M2}
 
 
 def host(t):
@@ -32,7 +33,7 @@ def host(t):
     t = t.detach().contiguous().cpu()
     if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in _FP8:
         return t.view(torch.uint8).numpy()
     return t.numpy()
 
@@ -73,31 +74,33 @@ def check_int8(gpu_codes, ref_codes, t, what):
     return int(diff.sum())
 
 
-def check_e4m3(gpu_codes, ref_codes, t, what):
+def check_fp8(gpu_codes, ref_codes, t, what, fmt=oracle.E4M3FN):
+    """FP8 codes of format `fmt` (oracle.E4M3FN or oracle.E5M2)."""
     g = np.asarray(gpu_codes, np.uint8).reshape(ref_codes.shape)
     r = np.asarray(ref_codes, np.uint8)
     diff = g != r
     if diff.any():
-        gv = oracle.decode(oracle.E4M3FN, g[diff])
-        rv = oracle.decode(oracle.E4M3FN, r[diff])
+        gv = oracle.decode(fmt, g[diff])
+        rv = oracle.decode(fmt, r[diff])
         tt = np.asarray(t, np.float64)[diff]
         spacing = np.abs(gv - rv)
         mid = (gv + rv) / 2
         # adjacent: no representable value strictly between them
-        adjacent = np.array([_adjacent(a, b) for a, b in zip(g[diff], r[diff])])
+        adjacent = np.array([_adjacent(a, b, fmt) for a, b in zip(g[diff], r[diff])])
         ok = adjacent & (np.abs(tt - mid) <= 1e-3 * spacing)
         if not ok.all():
             j = int(np.flatnonzero(~ok)[0])
-            raise AssertionError(f"{what}: {int((~ok).sum())} e4m3fn codes differ outside the tie window; "
+            raise AssertionError(f"{what}: {int((~ok).sum())} fp8 codes differ outside the tie window; "
                                  f"gpu {gv[j]} ref {rv[j]} t {tt[j]!r}")
     return int(diff.sum())
 
 
-def _adjacent(a, b):
-    va, vb = oracle.decode(oracle.E4M3FN, np.array([a, b], np.uint8))
+
+def _adjacent(a, b, fmt=oracle.E4M3FN):
+    va, vb = oracle.decode(fmt, np.array([a, b], np.uint8))
     lo, hi = min(va, vb), max(va, vb)
-    allv = oracle.decode(oracle.E4M3FN, np.arange(256, dtype=np.uint8))
-    allv = allv[~np.isnan(allv)]
+    allv = oracle.decode(fmt, np.arange(256, dtype=np.uint8))
+    allv = allv[np.isfinite(allv)]
     return not np.any((allv > lo) & (allv < hi))
 
 
@@ -135,18 +138,28 @@ def cache_rows(d):
     """Flat cache row (of [rows, D]) written by each (b, n, s), -1 if none.
 
     Norm [B, N, Scache, D]: (b*N + n)*Scache + index[b, s];
-    PA_BNSD [block_num, block_size, N, D]: slot*N + n with slot = index[b*S + s].
+    PA_BNSD [block_num, block_size, N, D]: slot*N + n with slot = index[b*S + s];
+    PA_BLK_BNSD: the same with slot = index[b, s // bs] + s % bs (one starting
+    slot per run of bs tokens). A slot outside the cache writes nothing.
     """
     cfg = d["cfg"]
     B, N, S = cfg.batch, cfg.heads, cfg.seq
-    idx = d["index"].cpu().numpy().reshape(B, S).astype(np.int64)
     n = np.arange(N).reshape(1, N, 1)
-    slot = idx.reshape(B, 1, S)
+    if cfg.cache_mode == "pa_blk_bnsd":
+        bs = cfg.block_size
+        starts = d["index"].cpu().numpy().reshape(B, -1).astype(np.int64)
+        s = np.arange(S)
+        st = starts[:, s // bs]
+        slot = np.where(st >= 0, st + s % bs, -1).reshape(B, 1, S)
+    else:
+        slot = d["index"].cpu().numpy().reshape(B, 1, S).astype(np.int64)
     if cfg.cache_mode == "norm":
+        capacity = cfg.cache_rows
         rows = (np.arange(B).reshape(B, 1, 1) * N + n) * cfg.cache_rows + slot
     else:
+        capacity = cfg.block_num * cfg.block_size
         rows = slot * N + n
-    return np.where(slot >= 0, rows, -1)
+    return np.where((slot >= 0) & (slot < capacity), rows, -1)
 
 
 def run_oracle_kv(d, inplace_zero_caches=False):
@@ -162,16 +175,20 @@ def run_oracle_kv(d, inplace_zero_caches=False):
     return oracle.kv_rmsnorm_rope_cache(
         host(d["kv"]), host(d["v"]), host(d["gamma"]), host(d["cos"]), host(d["sin"]),
         d["index"].cpu().numpy(), kh, ch, rms_size=cfg.rms_size, rope_size=cfg.rope_size,
-        eps=cfg.eps, cache_mode=oracle.NORM if cfg.cache_mode == "norm" else oracle.PA_BNSD,
+        eps=cfg.eps, cache_mode=_ORC_MODE[cfg.cache_mode],
         in_dtype=ORC[cfg.dtype], k_dtype=ORC[k_cache.dtype], ckv_dtype=ORC[c_cache.dtype],
         block_size=cfg.block_size, k_scale=np32(d["k_scale"]), k_offset=np32(d["k_offset"]),
         v_scale=np32(d["v_scale"]), v_offset=np32(d["v_offset"]), is_output_kv=cfg.is_output_kv,
         copy_caches=not inplace_zero_caches)
 
 
+_ORC_MODE = {"norm": oracle.NORM, "pa_bnsd": oracle.PA_BNSD, "pa_blk_bnsd": oracle.PA_BLK_BNSD}
+LIB_MODE = {"norm": "Norm", "pa_bnsd": "PA_BNSD", "pa_blk_bnsd": "PA_BLK_BNSD"}
+
+
 def run_gpu_kv(Q, d):
     cfg = d["cfg"]
-    mode = "Norm" if cfg.cache_mode == "norm" else "PA_BNSD"
+    mode = LIB_MODE[cfg.cache_mode]
     return Q.kv_rmsnorm_rope_cache(
         d["kv"], d["gamma"], d["cos"], d["sin"], d["index"], d["k_cache"], d["ckv_cache"],
         k_rope_scale=d["k_scale"], k_rope_offset=d["k_offset"], c_kv_scale=d["v_scale"],
@@ -212,8 +229,8 @@ def check_kv(Q, d, what, big_cache=False):
         xv = x[valid]
         if cache.dtype == torch.int8:
             report[name + "_pm1"] = check_int8(host(got), ref_rows, tv, f"{what}/{name}")
-        elif cache.dtype == torch.float8_e4m3fn:
-            report[name + "_adjacent"] = check_e4m3(host(got), ref_rows, tv, f"{what}/{name}")
+        elif cache.dtype in _FP8:
+            report[name + "_adjacent"] = check_fp8(host(got), ref_rows, tv, f"{what}/{name}", _FP8[cache.dtype])
         else:
             report[name + "_rel"] = check_float(got, xv, f"{what}/{name}")
     if cfg.is_output_kv and d["k_rope"] is not None:

@@ -43,7 +43,9 @@ def test_header_constants_match_binding():
     assert consts["QKNR_UNSUPPORTED"] == Q.UNSUPPORTED and consts["QKNR_DEVICE_ERROR"] == Q.DEVICE_ERROR
     assert consts["QKNR_BF16"] == Q.BF16 and consts["QKNR_F16"] == Q.F16 and consts["QKNR_F32"] == Q.F32
     assert consts["QKNR_INT8"] == Q.INT8 and consts["QKNR_FP8_E4M3FN"] == Q.FP8_E4M3FN
+    assert consts["QKNR_FP8_E5M2"] == Q.FP8_E5M2
     assert consts["QKNR_CACHE_NORM"] == Q.CACHE_NORM and consts["QKNR_CACHE_PA_BNSD"] == Q.CACHE_PA_BNSD
+    assert consts["QKNR_CACHE_PA_BLK_BNSD"] == Q.CACHE_PA_BLK_BNSD
     assert consts["QKNR_QSHAPE_HEAD_CHANNEL"] == Q.QSHAPE_HEAD_CHANNEL
 
 
@@ -153,7 +155,7 @@ def _kv(v2=False, mode="PA_BNSD", kdt=torch.bfloat16, cdt=torch.bfloat16, B=2, N
     else:
         kc = torch.zeros(nb, bs, N, dk, dtype=kdt)
         cc = torch.zeros(nb, bs, N, dc, dtype=cdt)
-        idx = torch.zeros(B * S, dtype=torch.int64)
+        idx = torch.zeros(B * (-(-S // bs) if mode == "PA_BLK_BNSD" else S), dtype=torch.int64)
     kr = torch.zeros(B, N, S, dk, dtype=dtype) if out_kv else None
     ck = torch.zeros(B, N, S, dc, dtype=dtype) if out_kv else None
     return Q.kv_args(kv, g, cs, cs, idx, kc, cc, k_rope_scale=ks, k_rope_offset=ko, c_kv_scale=vs,
@@ -172,6 +174,10 @@ def test_kv_valid_arguments_pass():
                              vs=f32(8, 128), vo=f32(8, 128), bs=128)) == Q.OK
     assert Q.kv_validate(_kv(mode="Norm", srope=1)) == Q.OK        # S-axis broadcast
     assert Q.kv_validate(_kv(kdt=torch.int8, ks=f32(1), bs=32)) == Q.OK   # scalar scale, V1
+    assert Q.kv_validate(_kv(kdt=torch.float8_e5m2, cdt=torch.float8_e5m2, ks=f32(64), vs=f32(1, 512))) == Q.OK
+    assert Q.kv_validate(_kv(mode="PA_BLK_BNSD", S=70, nb=6, out_kv=True)) == Q.OK
+    assert Q.kv_validate(_kv(mode="PA_BLK_BNSD", v2=True, N=4, kdt=torch.int8, cdt=torch.float8_e5m2,
+                             ks=f32(4, 192), vs=f32(4, 128), bs=128, S=300, nb=8)) == Q.OK
 
 
 @pytest.mark.parametrize("kw, code", [
@@ -187,6 +193,10 @@ def test_kv_valid_arguments_pass():
     (dict(v2=True, N=2, kdt=torch.int8, ks=f32(192)), Q.INVALID_ARGUMENT),      # V2 needs [N, D]
     (dict(kdt=torch.int8, ks=f32(1, 64), srope=1, S=8), Q.INVALID_ARGUMENT),    # broadcast + quant paged
     (dict(dtype=torch.float32, kdt=torch.float32, cdt=torch.float32), Q.INVALID_ARGUMENT),  # kv must be 16-bit
+    (dict(mode="PA_BLK_BNSD", S=70, nb=3), Q.INVALID_ARGUMENT),                 # block_num < floor(S/bs)*B
+    (dict(mode="PA_BLK_BNSD", kdt=torch.float8_e5m2, ks=f32(64), bs=16), Q.INVALID_ARGUMENT),  # 32-B blocks
+    (dict(mode="PA_BLK_BNSD", kdt=torch.int8, ks=f32(1, 64), srope=1), Q.INVALID_ARGUMENT),  # bcast + quant
+    (dict(kdt=torch.float8_e5m2, ko=f32(64)), Q.INVALID_ARGUMENT),              # e5m2 offset without scale
 ])
 def test_kv_invalid_arguments(kw, code):
     a = _kv(**kw)
@@ -207,6 +217,15 @@ def test_kv_output_kv_needs_buffers_when_effective():
     b = _kv(mode="Norm")
     b.is_output_kv = 1
     assert Q.kv_validate(b) == Q.OK
+
+
+def test_kv_binding_checks_pa_blk_index_length():
+    with pytest.raises(ValueError, match="ceil"):
+        kv = torch.zeros(2, 1, 70, 576, dtype=torch.bfloat16)
+        cs = torch.ones(2, 1, 70, 64, dtype=torch.bfloat16)
+        Q.kv_args(kv, torch.ones(512, dtype=torch.bfloat16), cs, cs, torch.zeros(140, dtype=torch.int64),
+                  torch.zeros(6, 32, 1, 64, dtype=torch.bfloat16), torch.zeros(6, 32, 1, 512, dtype=torch.bfloat16),
+                  cache_mode="PA_BLK_BNSD")
 
 
 def test_kv_unbuilt_modes_and_types_are_unsupported():

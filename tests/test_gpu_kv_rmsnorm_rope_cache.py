@@ -7,7 +7,10 @@ clamping; V2 split mode with asymmetric int8 per-head parameters, with and
 without k_rope/c_kv) and variants at reduced size: index -1 entries, several
 tokens per batch in a Norm cache, fp16 inputs, fp8 ckv in V2, scalar and
 [1, D] scale shapes, S-axis broadcast of cos/sin, the 8-byte access path, and
-determinism. Untouched cache rows must keep their pre-filled bytes exactly.
+determinism; FP8 E5M2 caches (with and without saturation) and PA_BLK_BNSD
+block-start indexing (full V1 prefill size; ragged runs; starts off block
+boundaries; runs marked -1). Untouched cache rows must keep their pre-filled
+bytes exactly.
 """
 import numpy as np
 import pytest
@@ -30,6 +33,23 @@ def Q():
 def test_mla_v1_prefill_full(Q):
     d = W.make_kv_cache(W.MLA_V1_PREFILL, device="cuda")
     rep, _ = check_kv(Q, d, "v1-prefill")
+    print(rep)
+
+
+def test_mla_v1_prefill_pa_blk_full(Q):
+    """The V1 prefill workload with block-start indexing: 256 runs of 128 tokens."""
+    d = W.make_kv_cache(W.MLA_V1_PREFILL, device="cuda", cache_mode=W.PA_BLK_BNSD)
+    assert d["index"].numel() == 8 * 32
+    rep, _ = check_kv(Q, d, "v1-prefill-pablk")
+    print(rep)
+
+
+def test_e5m2_saturation_exercised(Q):
+    """Scales of 1e4..5e4 push |t| past 57344: saturated codes must match."""
+    cfg, over = VARIANTS["v1_e5m2_saturating"]
+    d = W.make_kv_cache(cfg, device="cuda", **over)
+    rep, r = check_kv(Q, d, "e5m2-sat")
+    assert (np.abs(r["c_t"]) > 57344).any() and (np.abs(r["k_t"]) > 57344).any()
     print(rep)
 
 
@@ -82,6 +102,27 @@ VARIANTS = {
                                                  is_output_kv=True, invalid_every=5)),
     "v2_symmetric_n1": (W.MLA_V2_SPLIT, dict(batch=4, heads=1, seq=128, block_num=8, k_offset=None,
                                              v_offset=None)),
+    "v1_e5m2_norm": (W.MLA_V1_DECODE_QUANT, dict(batch=9, seq=3, cache_rows=16, index_kind="perm",
+                                                 k_cache_dtype=torch.float8_e5m2,
+                                                 ckv_cache_dtype=torch.float8_e5m2, k_scale=(20.0, 100.0, "D"),
+                                                 rope_pos="seq")),
+    "v1_e5m2_saturating": (W.MLA_V1_PREFILL, dict(seq=64, block_num=8, k_cache_dtype=torch.float8_e5m2,
+                                                  ckv_cache_dtype=torch.float8_e5m2, k_scale=(1e4, 5e4, "D"),
+                                                  v_scale=(1e4, 5e4, "1D"))),
+    "v1_pablk_ragged": (W.MLA_V1_PREFILL, dict(cache_mode=W.PA_BLK_BNSD, seq=300, block_num=24,
+                                               invalid_every=5)),
+    "v1_pablk_unaligned_int8": (W.MLA_V1_PREFILL, dict(cache_mode=W.PA_BLK_BNSD, batch=3, seq=200, block_num=16,
+                                                       index_kind="blocks_unaligned", k_cache_dtype=torch.int8,
+                                                       ckv_cache_dtype=torch.int8, k_scale=(20.0, 40.0, "D"),
+                                                       v_scale=(20.0, 40.0, "D"))),
+    "v2_pablk_unaligned_e5m2": (W.MLA_V2_SPLIT, dict(cache_mode=W.PA_BLK_BNSD, batch=2, seq=200, block_num=16,
+                                                     index_kind="blocks_unaligned",
+                                                     ckv_cache_dtype=torch.float8_e5m2, v_offset=None,
+                                                     v_scale=(1.0, 8.0, "ND"), is_output_kv=True)),
+    "v2_pablk_bf16_n2": (W.MLA_V2_SPLIT, dict(cache_mode=W.PA_BLK_BNSD, batch=3, heads=2, seq=129, block_num=12,
+                                              k_cache_dtype=torch.bfloat16, ckv_cache_dtype=torch.bfloat16,
+                                              k_scale=None, k_offset=None, v_scale=None, v_offset=None,
+                                              invalid_every=4)),
 }
 
 
@@ -91,6 +132,15 @@ def test_variants(Q, name):
     d = W.make_kv_cache(cfg, device="cuda", **over)
     rep, _ = check_kv(Q, d, name)
     print(name, rep)
+
+
+def test_pa_blk_run_past_the_cache_end(Q):
+    """A run that starts 3 slots before the end of the cache writes 3 rows; the
+    other 125 tokens of the run write nothing."""
+    d = W.make_kv_cache(W.MLA_V1_PREFILL, device="cuda", cache_mode=W.PA_BLK_BNSD, batch=2, seq=256, block_num=8)
+    d["index"].copy_(torch.tensor([0, 256, 512, 8 * 128 - 3], dtype=torch.int64))
+    rep, _ = check_kv(Q, d, "pablk-past-end")
+    print(rep)
 
 
 def test_s_axis_broadcast_cos_sin(Q):

@@ -41,6 +41,7 @@ THETA = 10000.0
 # Cache / mode names used in the generated dictionaries (plain strings, not an ABI).
 NORM = "norm"
 PA_BNSD = "pa_bnsd"
+PA_BLK_BNSD = "pa_blk_bnsd"
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -175,7 +176,7 @@ class KvCacheConfig:
     dtype: torch.dtype
     eps: float
     seed: int
-    cache_mode: str      # NORM or PA_BNSD
+    cache_mode: str      # NORM, PA_BNSD or PA_BLK_BNSD
     k_cache_dtype: torch.dtype
     ckv_cache_dtype: torch.dtype
     block_size: int = 0
@@ -267,6 +268,19 @@ def make_kv_cache(cfg: KvCacheConfig, device="cpu", prefill=True, **override):
         else:
             index = torch.stack([torch.randperm(cfg.cache_rows, generator=_gen(cfg.seed + 7 + b, "cpu"))[:S]
                                  for b in range(B)])
+    elif cfg.cache_mode == PA_BLK_BNSD:
+        # one starting slot per run of block_size tokens of a batch: distinct
+        # blocks, block-aligned starts ("blocks"), or starts at a random offset
+        # inside even-numbered blocks so that a run spills into the unused odd
+        # block after it ("blocks_unaligned")
+        bs = cfg.block_size
+        runs = B * -(-S // bs)
+        gi = _gen(cfg.seed + 7, "cpu")
+        if cfg.index_kind == "blocks_unaligned":
+            blocks = torch.randperm(cfg.block_num // 2, generator=gi)[:runs] * 2
+            index = blocks * bs + torch.randint(0, bs, (runs,), generator=gi)
+        else:
+            index = torch.randperm(cfg.block_num, generator=gi)[:runs] * bs
     else:
         slots = cfg.block_num * cfg.block_size
         index = torch.randperm(slots, generator=_gen(cfg.seed + 7, "cpu"))[: B * S].clone()
@@ -328,7 +342,8 @@ def algorithmic_bytes_kv_cache(cfg: KvCacheConfig) -> int:
     _, _, dk, dc = cache_shapes(cfg)
     ek = torch.tensor([], dtype=cfg.k_cache_dtype).element_size()
     ec = torch.tensor([], dtype=cfg.ckv_cache_dtype).element_size()
-    rd = rows * e * (cfg.kv_dim + cfg.v_dim + 2 * cfg.rope_size) + tokens * 8
+    entries = cfg.batch * -(-cfg.seq // cfg.block_size) if cfg.cache_mode == PA_BLK_BNSD else tokens
+    rd = rows * e * (cfg.kv_dim + cfg.v_dim + 2 * cfg.rope_size) + entries * 8
     wr = rows * (dk * ek + dc * ec)
     if cfg.is_output_kv:
         wr += rows * e * (dk + dc)
