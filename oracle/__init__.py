@@ -64,6 +64,11 @@ def _load():
         lib.oracle_qk_norm_rope_across_heads.argtypes = (
             [i64, i64, i64, i64, i32] + [p] * 6 + [f64, i32, i32] + [p] * 4 + [i32])
         lib.oracle_qk_norm_rope_across_heads.restype = i32
+        lib.oracle_qk_norm_rope.argtypes = (
+            [i64, i64, i64, i64, i32] + [p] * 6 + [f64, i32, i32, i32, p, p, f64, f64] + [p] * 4 + [i32])
+        lib.oracle_qk_norm_rope.restype = i32
+        lib.oracle_qk_sumsq.argtypes = [i64, i64, i64, i32, p, p]
+        lib.oracle_qk_sumsq.restype = i32
         lib.oracle_kv_rmsnorm_rope_cache.argtypes = (
             [i64] * 7 + [i32] + [p] * 5 + [i64, p, i32, i64, i64, i32, i32, p, p]
             + [p] * 4 + [f64, i32] + [p] * 6 + [i32])
@@ -140,6 +145,95 @@ def qk_norm_rope_across_heads(q, k, q_gamma, k_gamma, cos, sin, eps, n_q_heads,
     if rc != 0:
         raise ValueError("oracle rejected the dimensions")
     return q_out, k_out, q_val, k_val
+
+
+def qk_norm_rope(q, k, q_gamma, k_gamma, cos, sin, eps, n_q_heads, n_k_heads, head_dim,
+                 dtype, apply_norm=True, apply_rope=True, per_head=False, q_sumsq=None,
+                 k_sumsq=None, q_channels=0, k_channels=0, nthreads=None, values=True):
+    """QK RMSNorm + rotate-half RoPE in its three forms:
+
+    * across heads (default): one RMS per token over the whole segment,
+      gammas [n*d];
+    * per head (``per_head``): one RMS per head over d channels, gammas [d]
+      shared by every head;
+    * the apply step of a split over ranks: ``q_sumsq``/``k_sumsq`` [T] are the
+      summed squares of the whole segment (all ranks) and ``q_channels`` /
+      ``k_channels`` its channel count; q/k hold this rank's heads only.
+
+    Arguments otherwise as :func:`qk_norm_rope_across_heads`.
+    """
+    st = STORAGE[dtype]
+    q = _c(q, st)
+    T = q.shape[0]
+    cq, ck = n_q_heads * head_dim, n_k_heads * head_dim
+    assert q.shape == (T, cq)
+    k = _c(k, st) if n_k_heads else None
+    if k is not None:
+        assert k.shape == (T, ck)
+    gw = (head_dim, head_dim) if per_head else (cq, ck)
+    q_gamma = _c(q_gamma, st)
+    k_gamma = _c(k_gamma, st) if n_k_heads else None
+    if apply_norm:
+        assert q_gamma.size == gw[0] and (k_gamma is None or k_gamma.size == gw[1]), "gamma size"
+    cos, sin = _c(cos, st), _c(sin, st)
+    qs = _c(q_sumsq, np.float64)
+    ks = _c(k_sumsq, np.float64) if n_k_heads else None
+    for a in (qs, ks):
+        assert a is None or a.shape == (T,)
+    q_out = np.empty((T, cq), st)
+    k_out = np.empty((T, ck), st) if k is not None else None
+    q_val = np.empty((T, cq), np.float64) if values else None
+    k_val = np.empty((T, ck), np.float64) if (k is not None and values) else None
+    rc = _load().oracle_qk_norm_rope(
+        T, n_q_heads, n_k_heads, head_dim, dtype, _ptr(q), _ptr(k), _ptr(q_gamma),
+        _ptr(k_gamma), _ptr(cos), _ptr(sin), float(eps), int(bool(apply_norm)),
+        int(bool(apply_rope)), int(bool(per_head)), _ptr(qs), _ptr(ks), float(q_channels),
+        float(k_channels), _ptr(q_out), _ptr(k_out), _ptr(q_val), _ptr(k_val),
+        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the dimensions")
+    return q_out, k_out, q_val, k_val
+
+
+def qk_sumsq(x, n_heads, head_dim, dtype):
+    """Per-token sum of squares over one segment: x [T, n*d] -> fp64 [T]."""
+    x = _c(x, STORAGE[dtype])
+    T = x.shape[0]
+    assert x.shape == (T, n_heads * head_dim)
+    out = np.empty(T, np.float64)
+    if _load().oracle_qk_sumsq(T, n_heads, head_dim, dtype, _ptr(x), _ptr(out)) != 0:
+        raise ValueError("oracle rejected the dimensions")
+    return out
+
+
+def rotate_half_permutation(head_dim):
+    """Lane j of a rotate-half head holds interleaved lane perm[j]: the even
+    lanes 0, 2, ..., d-2 first, then the odd lanes 1, 3, ..., d-1, so that the
+    interleaved pair (2j, 2j+1) becomes the rotate-half pair (j, j + d/2)."""
+    return np.concatenate([np.arange(0, head_dim, 2), np.arange(1, head_dim, 2)])
+
+
+def interleaved_to_rotate_half(a, head_dim, axis=-1, first=0, n_heads=None, inverse=False):
+    """Permute `n_heads` blocks of `head_dim` lanes, starting at index `first`
+    of `axis`, from the interleaved-pair layout to the rotate-half layout
+    (``inverse``: back). Indices outside those blocks keep their values.
+    Returns a new array."""
+    a = np.asarray(a)
+    axis = axis % a.ndim
+    L = a.shape[axis]
+    if n_heads is None:
+        n_heads = (L - first) // head_dim
+    if head_dim % 2 or first < 0 or first + n_heads * head_dim > L:
+        raise ValueError("blocks outside the axis, or odd head_dim")
+    dst = first + np.arange(n_heads * head_dim)
+    src = first + (np.arange(n_heads)[:, None] * head_dim
+                   + rotate_half_permutation(head_dim)[None, :]).ravel()
+    idx = np.arange(L)
+    if inverse:
+        idx[src] = dst
+    else:
+        idx[dst] = src
+    return np.take(a, idx, axis=axis)
 
 
 def _expand_quant(p, heads, width):

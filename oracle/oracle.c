@@ -203,33 +203,53 @@ void oracle_encode(int dtype, const double *src, void *dst, int64_t n) {
  * One segment (all heads of Q, or all heads of K) of one token.
  *
  * [qkv_cte] section 1: one RMS over the whole segment of n_heads*d_head
- * channels (step b: inv_rms = 1/sqrt(sum(x^2)/(n_heads*d_head*tp) + eps) with
- * tp = 1, all heads resident), then the per-channel segment-wide gamma
- * (step c). [CP] forward listing: the norm runs before the rotary embedding.
+ * channels (step b: inv_rms = 1/sqrt(sum(x^2)/(n_heads*d_head*tp) + eps);
+ * with all heads resident tp = 1 and the sum is this segment's own), then the
+ * per-channel segment-wide gamma (step c). When the heads are split over tp
+ * ranks, step a gives each rank the sum over its own heads, step b adds the
+ * ranks' sums, and step c applies with the added sum and the whole segment's
+ * channel count: `given_ss` / `channels` are that sum and count.
+ * [qkv_cte] "Upstream behavior" and section 1: the upstream qk-norm is per
+ * head instead -- each head's d_head slice normalised by its own RMS, with a
+ * per-head [d_head] gamma shared by every head (`per_head`).
+ * [CP] forward listing: the norm runs before the rotary embedding.
  * [qkv_cte] section 2: rotate-half RoPE per head, lanes i and i+d/2 paired,
  * out = y*cos + [-y_hi, y_lo]*sin with cos/sin indexed by the output lane
  * and shared by every head of the token. Folding inv_rms into the cos/sin
  * products is an evaluation order, not a different result, so the
  * definition is written here as norm-then-rotate.
  */
-static void across_heads_segment(int64_t nh, int64_t d, int dtype,
-                                 const void *x, int64_t x0,
-                                 const void *gamma, const void *cs, const void *sn,
-                                 int64_t r0, double eps, int apply_norm,
-                                 int apply_rope, double *y, double *out) {
+static void qk_segment(int64_t nh, int64_t d, int dtype, const void *x, int64_t x0,
+                       const void *gamma, const void *cs, const void *sn, int64_t r0,
+                       double eps, int apply_norm, int apply_rope, int per_head,
+                       const double *given_ss, double channels, double *y, double *out) {
     int64_t C = nh * d, h2 = d / 2;
-    double inv_rms = 1.0;
-    if (apply_norm) {
-        double ss = 0.0;
-        for (int64_t c = 0; c < C; c++) {
-            double v = load(dtype, x, x0 + c);
-            ss += v * v;
+    if (!apply_norm) {
+        for (int64_t c = 0; c < C; c++) y[c] = load(dtype, x, x0 + c);
+    } else if (per_head) {
+        for (int64_t h = 0; h < nh; h++) {
+            double ss = 0.0;
+            for (int64_t i = 0; i < d; i++) {
+                double v = load(dtype, x, x0 + h * d + i);
+                ss += v * v;
+            }
+            double inv_rms = 1.0 / sqrt(ss / (double)d + eps);
+            for (int64_t i = 0; i < d; i++)
+                y[h * d + i] = load(dtype, x, x0 + h * d + i) * inv_rms * load(dtype, gamma, i);
         }
-        inv_rms = 1.0 / sqrt(ss / (double)C + eps);
-    }
-    for (int64_t c = 0; c < C; c++) {
-        double v = load(dtype, x, x0 + c);
-        y[c] = apply_norm ? v * inv_rms * load(dtype, gamma, c) : v;
+    } else {
+        double ss = 0.0;
+        if (given_ss) {
+            ss = *given_ss;
+        } else {
+            for (int64_t c = 0; c < C; c++) {
+                double v = load(dtype, x, x0 + c);
+                ss += v * v;
+            }
+        }
+        double inv_rms = 1.0 / sqrt(ss / (channels > 0 ? channels : (double)C) + eps);
+        for (int64_t c = 0; c < C; c++)
+            y[c] = load(dtype, x, x0 + c) * inv_rms * load(dtype, gamma, c);
     }
     for (int64_t h = 0; h < nh; h++) {
         const double *yh = y + h * d;
@@ -246,19 +266,23 @@ static void across_heads_segment(int64_t nh, int64_t d, int dtype,
 }
 
 /*
- * q: [T, n_q*d], k: [T, n_k*d] (NULL when n_k == 0), contiguous rows;
- * q_gamma [n_q*d], k_gamma [n_k*d]; cos/sin [T, d]. Writes q_out/k_out in
- * `dtype` (rounded once) and, if given, the exact results q_val/k_val.
- * Returns 0, or -1 on bad dimensions.
+ * q: [T, n_q*d], k: [T, n_k*d] (NULL when n_k == 0), contiguous rows; gammas
+ * [n*d] (across heads) or [d] (per head); cos/sin [T, d]. q_sumsq/k_sumsq [T]
+ * (or NULL): sums of squares to use instead of this call's own (the apply
+ * step of a split over ranks), with q_channels/k_channels the whole
+ * segment's channel count (<= 0: n*d). Writes q_out/k_out in `dtype` (rounded
+ * once) and, if given, the exact results q_val/k_val. Returns 0, or -1 on bad
+ * dimensions.
  */
-int oracle_qk_norm_rope_across_heads(int64_t T, int64_t n_q, int64_t n_k, int64_t d,
-                                     int dtype, const void *q, const void *k,
-                                     const void *q_gamma, const void *k_gamma,
-                                     const void *cs, const void *sn, double eps,
-                                     int apply_norm, int apply_rope, void *q_out,
-                                     void *k_out, double *q_val, double *k_val,
-                                     int nthreads) {
+int oracle_qk_norm_rope(int64_t T, int64_t n_q, int64_t n_k, int64_t d, int dtype,
+                        const void *q, const void *k, const void *q_gamma,
+                        const void *k_gamma, const void *cs, const void *sn, double eps,
+                        int apply_norm, int apply_rope, int per_head,
+                        const double *q_sumsq, const double *k_sumsq, double q_channels,
+                        double k_channels, void *q_out, void *k_out, double *q_val,
+                        double *k_val, int nthreads) {
     if (T < 0 || n_q < 1 || n_k < 0 || d < 2 || (d & 1)) return -1;
+    if (per_head && (q_sumsq || k_sumsq)) return -1;
     int64_t cq = n_q * d, ck = n_k * d;
     int64_t cmax = cq > ck ? cq : ck;
     if (nthreads < 1) nthreads = 1;
@@ -274,10 +298,12 @@ int oracle_qk_norm_rope_across_heads(int64_t T, int64_t n_q, int64_t n_k, int64_
                 int64_t C = nh * d;
                 const void *x = seg == 0 ? q : k;
                 const void *g = seg == 0 ? q_gamma : k_gamma;
+                const double *given = seg == 0 ? q_sumsq : k_sumsq;
+                double channels = seg == 0 ? q_channels : k_channels;
                 void *dst = seg == 0 ? q_out : k_out;
                 double *val = seg == 0 ? q_val : k_val;
-                across_heads_segment(nh, d, dtype, x, t * C, g, cs, sn, t * d, eps,
-                                     apply_norm, apply_rope, y, o);
+                qk_segment(nh, d, dtype, x, t * C, g, cs, sn, t * d, eps, apply_norm,
+                           apply_rope, per_head, given ? given + t : NULL, channels, y, o);
                 for (int64_t c = 0; c < C; c++) {
                     if (dst) store(dtype, dst, t * C + c, o[c]);
                     if (val) val[t * C + c] = o[c];
@@ -286,6 +312,37 @@ int oracle_qk_norm_rope_across_heads(int64_t T, int64_t n_q, int64_t n_k, int64_
         }
         free(y);
         free(o);
+    }
+    return 0;
+}
+
+/* The across-heads operator with every head on one device (tp = 1). */
+int oracle_qk_norm_rope_across_heads(int64_t T, int64_t n_q, int64_t n_k, int64_t d,
+                                     int dtype, const void *q, const void *k,
+                                     const void *q_gamma, const void *k_gamma,
+                                     const void *cs, const void *sn, double eps,
+                                     int apply_norm, int apply_rope, void *q_out,
+                                     void *k_out, double *q_val, double *k_val,
+                                     int nthreads) {
+    return oracle_qk_norm_rope(T, n_q, n_k, d, dtype, q, k, q_gamma, k_gamma, cs, sn, eps,
+                               apply_norm, apply_rope, 0, NULL, NULL, 0.0, 0.0, q_out, k_out,
+                               q_val, k_val, nthreads);
+}
+
+/*
+ * [qkv_cte] section 1, step a: each token's sum of x^2 over one segment of
+ * n*d channels, x: [T, n*d] contiguous. Writes sumsq[T].
+ */
+int oracle_qk_sumsq(int64_t T, int64_t n, int64_t d, int dtype, const void *x,
+                    double *sumsq) {
+    if (T < 0 || n < 1 || d < 1) return -1;
+    for (int64_t t = 0; t < T; t++) {
+        double ss = 0.0;
+        for (int64_t c = 0; c < n * d; c++) {
+            double v = load(dtype, x, t * n * d + c);
+            ss += v * v;
+        }
+        sumsq[t] = ss;
     }
     return 0;
 }

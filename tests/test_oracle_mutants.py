@@ -11,9 +11,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 MUTANTS = {
-    "rms_divides_by_head_dim": ("ss / (double)C + eps", "ss / (double)d + eps"),
-    "eps_outside_sqrt": ("1.0 / sqrt(ss / (double)C + eps)", "1.0 / (sqrt(ss / (double)C) + eps)"),
-    "gamma_dropped": ("v * inv_rms * load(dtype, gamma, c)", "v * inv_rms"),
+    "rms_divides_by_head_dim": ("ss / (channels > 0 ? channels : (double)C) + eps",
+                                "ss / (channels > 0 ? channels : (double)d) + eps"),
+    "eps_outside_sqrt": ("1.0 / sqrt(ss / (channels > 0 ? channels : (double)C) + eps)",
+                         "1.0 / (sqrt(ss / (channels > 0 ? channels : (double)C)) + eps)"),
+    "gamma_dropped": ("y[c] = load(dtype, x, x0 + c) * inv_rms * load(dtype, gamma, c);",
+                      "y[c] = load(dtype, x, x0 + c) * inv_rms;"),
     "rotate_half_sign": ("(i < h2) ? -yh[i + h2] : yh[i - h2]", "(i < h2) ? yh[i + h2] : -yh[i - h2]"),
     "rotate_half_partner": ("(i < h2) ? -yh[i + h2] : yh[i - h2]", "(i < h2) ? -yh[h2 - 1 - i] : yh[d - 1 - i]"),
     "cos_half_index": ("yh[i] * load(dtype, cs, r0 + i)", "yh[i] * load(dtype, cs, r0 + i % h2)"),
@@ -38,6 +41,15 @@ MUTANTS = {
     "pa_blk_per_token_index": ("int64_t start = index[b * nblk + s / block_size];",
                                "int64_t start = index[(b * S + s) / block_size];"),
     "no_capacity_check": ("if (slot >= 0 && slot < capacity) {", "if (slot >= 0) {"),
+    "per_head_denominator": ("double inv_rms = 1.0 / sqrt(ss / (double)d + eps);",
+                             "double inv_rms = 1.0 / sqrt(ss / (double)(nh * d) + eps);"),
+    "per_head_gamma_dropped": ("y[h * d + i] = load(dtype, x, x0 + h * d + i) * inv_rms * load(dtype, gamma, i);",
+                               "y[h * d + i] = load(dtype, x, x0 + h * d + i) * inv_rms;"),
+    "split_ignores_given_sum": ("            ss = *given_ss;\n", "            ss = 0.0 * *given_ss + 1.0;\n"),
+    "split_ignores_total_channels": ("ss / (channels > 0 ? channels : (double)C) + eps",
+                                     "ss / (double)C + eps"),
+    "sumsq_not_squared": ("            double v = load(dtype, x, t * n * d + c);\n            ss += v * v;",
+                          "            double v = load(dtype, x, t * n * d + c);\n            ss += fabs(v);"),
     "c_kv_from_raw_in_v1": ("c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : y[i];",
                             "c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : load(in_dtype, kv, kv0 + i);"),
 }

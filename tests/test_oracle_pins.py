@@ -120,6 +120,140 @@ def test_across_heads_rotate_half_equals_permuted_interleaved():
     np.testing.assert_allclose(out.reshape(T, nh, d), inter[:, :, perm], rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- (a) per head, split, permutation
+
+def _qk(x, g, cos, sin, nh, d, eps, **kw):
+    qv = oracle.qk_norm_rope(np.asarray(x, np.float64), None, np.asarray(g, np.float64), None,
+                             np.asarray(cos, np.float64), np.asarray(sin, np.float64), eps, nh, 0, d,
+                             oracle.F64, nthreads=1, **kw)[2]
+    return qv
+
+
+def test_per_head_golden_hand_cases():
+    for c in _golden("across_heads_hand.json")["per_head_cases"]:
+        out = _qk([c["x"]], c["gamma"], [c["cos"]], [c["sin"]], c["n_heads"], c["d"], c["eps"], per_head=True)
+        np.testing.assert_allclose(out[0], c["out"], rtol=0, atol=1e-14)
+
+
+def test_per_head_matches_torch_rms_norm_per_head_and_complex_rotation():
+    rng = np.random.default_rng(12)
+    T, nh, d, eps = 7, 4, 16, 1e-6
+    x = rng.standard_normal((T, nh * d)) * rng.uniform(0.1, 10, (1, nh * d))
+    g = rng.uniform(0.5, 1.5, d)
+    theta = rng.uniform(-4, 4, (T, d // 2))
+    out = _qk(x, g, np.cos(np.hstack([theta, theta])), np.sin(np.hstack([theta, theta])), nh, d, eps,
+              per_head=True)
+    y = torch.nn.functional.rms_norm(torch.from_numpy(x).reshape(T, nh, d), [d], torch.from_numpy(g), eps)
+    z = torch.complex(y[..., : d // 2], y[..., d // 2:]) * torch.polar(
+        torch.ones(T, 1, d // 2, dtype=torch.float64), torch.from_numpy(theta)[:, None, :])
+    ref = torch.cat([z.real, z.imag], -1).reshape(T, nh * d).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_per_head_closed_form_and_one_head_equals_across():
+    rng = np.random.default_rng(13)
+    T, nh, d, eps = 5, 3, 8, 0.25
+    x = rng.standard_normal((T, nh * d)) * rng.uniform(0.1, 5, (T, nh * d))
+    out = _qk(x, np.ones(d), np.ones((T, d)), np.zeros((T, d)), nh, d, eps, per_head=True)
+    ms = (x.reshape(T, nh, d) ** 2).mean(-1)
+    rms_out = np.sqrt((out.reshape(T, nh, d) ** 2).mean(-1))
+    np.testing.assert_allclose(rms_out, 1 / np.sqrt(1 + eps / ms), rtol=1e-13)
+    x1 = x[:, :d]
+    g1 = rng.uniform(0.5, 1.5, d)
+    th = rng.uniform(-3, 3, (T, d))
+    a = _qk(x1, g1, np.cos(th), np.sin(th), 1, d, eps, per_head=True)
+    b = _qk(x1, g1, np.cos(th), np.sin(th), 1, d, eps)
+    np.testing.assert_allclose(a, b, rtol=1e-15, atol=0)
+
+
+def test_sumsq_brute_force_and_rms_identity():
+    rng = np.random.default_rng(14)
+    T, nh, d, eps = 6, 3, 4, 1e-3
+    x = rng.standard_normal((T, nh * d))
+    ss = oracle.qk_sumsq(x, nh, d, oracle.F64)
+    for t in range(T):
+        assert abs(ss[t] - sum(v * v for v in x[t].tolist())) <= 1e-13 * ss[t]
+    # with gamma = 1, cos = 1, sin = 0 the fused operator scales x by 1/sqrt(ss/C + eps)
+    out = _qk(x, np.ones(nh * d), np.ones((T, d)), np.zeros((T, d)), nh, d, eps)
+    inv = out[:, 0] / x[:, 0]
+    np.testing.assert_allclose(inv, 1 / np.sqrt(ss / (nh * d) + eps), rtol=1e-13)
+
+
+@pytest.mark.parametrize("tp", [2, 4, 5])
+def test_split_over_ranks_reproduces_the_fused_operator(tp):
+    """Steps a-c of the page with the heads split over tp ranks: each rank's
+    sum over its own heads, the sums added (the all-reduce), each rank applying
+    with the total over n_heads*d*tp channels -- equals every head on one
+    device."""
+    rng = np.random.default_rng(20 + tp)
+    T, nh, d, eps = 5, 20, 8, 1e-6
+    q = rng.standard_normal((T, nh * d))
+    k = rng.standard_normal((T, nh * d)) * 3
+    gq, gk = rng.uniform(0.5, 1.5, nh * d), rng.uniform(0.5, 1.5, nh * d)
+    th = rng.uniform(-3, 3, (T, d // 2))
+    cos, sin = np.cos(np.hstack([th, th])), np.sin(np.hstack([th, th]))
+    full_q, full_k = oracle.qk_norm_rope(q, k, gq, gk, cos, sin, eps, nh, nh, d, oracle.F64, nthreads=1)[2:]
+    lh = nh // tp
+    sl = [slice(r * lh * d, (r + 1) * lh * d) for r in range(tp)]
+    sq = sum(oracle.qk_sumsq(np.ascontiguousarray(q[:, s]), lh, d, oracle.F64) for s in sl)
+    sk = sum(oracle.qk_sumsq(np.ascontiguousarray(k[:, s]), lh, d, oracle.F64) for s in sl)
+    for s in sl:
+        oq, ok_ = oracle.qk_norm_rope(np.ascontiguousarray(q[:, s]), np.ascontiguousarray(k[:, s]), gq[s], gk[s],
+                                      cos, sin, eps, lh, lh, d, oracle.F64, q_sumsq=sq, k_sumsq=sk,
+                                      q_channels=nh * d, k_channels=nh * d, nthreads=1)[2:]
+        np.testing.assert_allclose(oq, full_q[:, s], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(ok_, full_k[:, s], rtol=1e-13, atol=1e-15)
+    # a rank that used only its own sum would be wrong
+    own = oracle.qk_norm_rope(np.ascontiguousarray(q[:, sl[0]]), None, gq[sl[0]], None, cos, sin, eps, lh, 0,
+                              d, oracle.F64, nthreads=1)[2]
+    assert not np.allclose(own, full_q[:, sl[0]], rtol=1e-6)
+
+
+def test_permutation_closed_form_inverse_and_untouched_lanes():
+    np.testing.assert_array_equal(oracle.rotate_half_permutation(8), [0, 2, 4, 6, 1, 3, 5, 7])
+    a = np.arange(3 * 26).reshape(3, 26)
+    p = oracle.interleaved_to_rotate_half(a, 6, axis=1, first=5, n_heads=3)
+    np.testing.assert_array_equal(p[:, :5], a[:, :5])
+    np.testing.assert_array_equal(p[:, 23:], a[:, 23:])
+    np.testing.assert_array_equal(p[0, 5:23], [5, 7, 9, 6, 8, 10, 11, 13, 15, 12, 14, 16, 17, 19, 21, 18, 20, 22])
+    back = oracle.interleaved_to_rotate_half(p, 6, axis=1, first=5, n_heads=3, inverse=True)
+    np.testing.assert_array_equal(back, a)
+    # a weight [H, I]: permuting output columns permutes the projection's outputs
+    rng = np.random.default_rng(15)
+    x, w = rng.standard_normal((4, 7)), rng.standard_normal((7, 24))
+    wp = oracle.interleaved_to_rotate_half(w, 8, axis=1, first=0, n_heads=2)   # Q|K blocks, V (last 8) untouched
+    np.testing.assert_allclose(x @ wp, oracle.interleaved_to_rotate_half(x @ w, 8, first=0, n_heads=2), rtol=1e-13)
+    np.testing.assert_array_equal(wp[:, 16:], w[:, 16:])
+
+
+def test_permutation_makes_rotate_half_equal_interleaved_rope_and_keeps_scores():
+    """The offline conversion of [qkv_cte] Design section 2: with q, k, the
+    interleaved cos/sin tables (each angle at lanes 2j and 2j+1) and gammas
+    permuted, rotate-half RoPE gives the permuted interleaved result, and the
+    attention scores q.k per head do not change."""
+    rng = np.random.default_rng(16)
+    T, nh, d, eps = 5, 3, 8, 1e-6
+    q, k = rng.standard_normal((T, nh * d)), rng.standard_normal((T, nh * d))
+    gq, gk = rng.uniform(0.5, 1.5, nh * d), rng.uniform(0.5, 1.5, nh * d)
+    th = rng.uniform(-3, 3, (T, d // 2))
+    cos_i, sin_i = np.repeat(np.cos(th), 2, axis=1), np.repeat(np.sin(th), 2, axis=1)   # interleaved tables
+
+    def interleaved(x, g):
+        y = _qk(x, g, np.ones((T, d)), np.zeros((T, d)), nh, d, eps)   # across-heads norm, no rotation
+        z = (y.reshape(T, nh, d // 2, 2) @ np.array([1, 1j])) * np.exp(1j * th)[:, None, :]
+        return np.stack([z.real, z.imag], -1).reshape(T, nh * d)
+
+    P = lambda a, n=nh: oracle.interleaved_to_rotate_half(a, d, n_heads=n)
+    rq = oracle.qk_norm_rope(P(q), P(k), P(gq), P(gk), P(cos_i, 1), P(sin_i, 1), eps, nh, nh, d, oracle.F64,
+                             nthreads=1)
+    iq, ik = interleaved(q, gq), interleaved(k, gk)
+    np.testing.assert_allclose(rq[2], P(iq), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(rq[3], P(ik), rtol=1e-12, atol=1e-14)
+    s_int = np.einsum("thd,uhd->htu", iq.reshape(T, nh, d), ik.reshape(T, nh, d))
+    s_rh = np.einsum("thd,uhd->htu", rq[2].reshape(T, nh, d), rq[3].reshape(T, nh, d))
+    np.testing.assert_allclose(s_rh, s_int, rtol=1e-12, atol=1e-13)
+
+
 def test_across_heads_brute_force_tiny():
     rng = np.random.default_rng(5)
     for (T, nq, nk, d, norm, rope) in [(3, 2, 2, 4, 1, 1), (2, 3, 1, 6, 1, 1), (2, 1, 0, 2, 1, 1),
