@@ -2,7 +2,7 @@
  * qknr.h -- C ABI of the fused QK / KV RMSNorm + RoPE (+ KV-cache scatter)
  * library for AMD Instinct MI355X (gfx950).
  *
- * Two operators, each one kernel launch on the caller's HIP stream:
+ * Operators, each one kernel launch on the caller's HIP stream:
  *
  *   qknr_qk_norm_rope_across_heads  -- per-token RMSNorm over the whole Q
  *       segment (and, separately, the whole K segment) of n_heads*d_head
@@ -13,6 +13,15 @@
  *       RMSNorm, steps a-c, here with every head on one GPU) and section 2
  *       (bundled rotate-half RoPE), and by the WanSelfAttention forward of
  *       "Context Parallelism in vLLM Omni Neuron" (norm before rotary).
+ *   qknr_qk_sumsq_across_heads / qknr_qk_apply_across_heads  -- the same
+ *       operator when a segment's heads are split over ranks: step a (sums of
+ *       squares over this rank's heads) and step c (apply with the sums added
+ *       over every rank); the caller adds the sums in between (all-reduce).
+ *   qknr_qk_norm_rope_per_head  -- the upstream per-head qk-norm the same page
+ *       contrasts with ("Upstream behavior"): one RMS per head, [d_head] gamma.
+ *   qknr_interleaved_to_rotate_half  -- the offline lane permutation that turns
+ *       an interleaved-pair checkpoint (weights, bias, gamma, cos/sin) into the
+ *       rotate-half layout the kernels use (qkv_cte Design section 2).
  *
  *   qknr_kv_rmsnorm_rope_cache  -- the MLA operator of the CANN page
  *       "KvRmsNormRopeCache": RmsNorm (formula 1), interleaveRope (formula 2),
@@ -52,7 +61,7 @@
 extern "C" {
 #endif
 
-#define QKNR_ABI_VERSION 1
+#define QKNR_ABI_VERSION 2
 
 /* status codes */
 #define QKNR_OK 0
@@ -108,6 +117,8 @@ extern "C" {
  *   head_dim         even, 2..1024.
  *   q_gamma [n_q_heads*head_dim], k_gamma [n_k_heads*head_dim] (segment-wide gammas).
  *   eps              added to the mean of squares inside the square root.
+ *   q_norm_channels, k_norm_channels   0, except in qknr_qk_apply_across_heads
+ *       (the channel count of the whole segment over every rank).
  */
 typedef struct qknr_qk_args {
     int32_t dtype;
@@ -136,6 +147,8 @@ typedef struct qknr_qk_args {
     int32_t apply_norm;
     int32_t apply_rope;
     int32_t reserved;
+    int64_t q_norm_channels;
+    int64_t k_norm_channels;
 } qknr_qk_args;
 
 int32_t qknr_qk_norm_rope_across_heads(const qknr_qk_args *args, hipStream_t stream);
@@ -143,6 +156,70 @@ int32_t qknr_qk_norm_rope_across_heads(const qknr_qk_args *args, hipStream_t str
 /* Host-only validation of (a)'s arguments: the same checks the launch call
  * makes, without touching a device. Returns a status code. */
 int32_t qknr_qk_validate(const qknr_qk_args *args);
+
+/*
+ * (a) split over ranks, step a ("Kernel reference: qkv_cte", Design section 1:
+ * each rank accumulates sum(x^2) of its own heads for every token).
+ *   sumsq[seg*B*S + b*S + s] = sum over this call's heads and channels of x^2
+ * for seg 0 = Q and seg 1 = K (K only when n_k_heads > 0), fp32, written by the
+ * call; sumsq is a caller-owned device array of (n_k_heads > 0 ? 2 : 1)*B*S
+ * floats, 4-byte aligned. Only q_in/k_in, the input strides, dtype and the
+ * sizes of `args` are read (gammas, tables, outputs, apply_* are ignored).
+ * The caller then adds the arrays of all ranks (an all-reduce; on one GPU, the
+ * array itself) before step c.
+ */
+int32_t qknr_qk_sumsq_across_heads(const qknr_qk_args *args, float *sumsq, hipStream_t stream);
+
+/*
+ * (a) split over ranks, step c: as qknr_qk_norm_rope_across_heads on this
+ * rank's heads, but with
+ *   r = 1 / sqrt( sumsq[seg*B*S + b*S + s] / norm_channels + eps )
+ * where sumsq holds the sums added over every rank (layout of step a) and
+ * norm_channels = args->q_norm_channels (Q) / k_norm_channels (K), the
+ * channel count of the whole segment (n_heads*d_head*tp, below 2^24); 0 means
+ * this call's own n*d_head. apply_norm must be 1.
+ */
+int32_t qknr_qk_apply_across_heads(const qknr_qk_args *args, const float *sumsq, hipStream_t stream);
+
+/*
+ * (a) per head: as qknr_qk_norm_rope_across_heads, but with one RMS per
+ * (token, head) over head_dim channels,
+ *   r_h = 1 / sqrt( sum_i x[h,i]^2 / head_dim + eps ),   y[h,i] = x[h,i]*gamma_i,
+ * and q_gamma, k_gamma of head_dim elements shared by every head (the per-head
+ * [1, d_head] gamma of the upstream qk-norm, qkv_cte "Upstream behavior").
+ */
+int32_t qknr_qk_norm_rope_per_head(const qknr_qk_args *args, hipStream_t stream);
+
+/*
+ * Interleaved-pair -> rotate-half lane permutation (qkv_cte Design section 2:
+ * an interleaved checkpoint is converted once, offline, by permuting the Q/K
+ * weights, bias, gamma and cos/sin caches).
+ *
+ * The tensor is viewed as [outer, axis_len, inner] (row-major, contiguous,
+ * `elem_bytes`-byte elements). Along the middle axis, the n_heads blocks of
+ * head_dim indices starting at `first` are permuted:
+ *   dst[o, first + h*d + j, :] = src[o, first + h*d + (j < d/2 ? 2j : 2(j - d/2) + 1), :]
+ * (inverse = 1 applies the inverse permutation); every other index is copied.
+ * Examples: a fused QKV weight [H, I] -> outer H, axis I, inner 1, first 0,
+ * n_heads = n_q + n_k (V's blocks stay); an MX weight [H/4, I, 4] -> inner 4;
+ * interleaved cos/sin tables [S, d] (each angle at lanes 2j and 2j+1) -> outer S,
+ * axis d, n_heads 1, giving rotate-half tables.
+ * src and dst are caller-owned device memory and must not overlap.
+ */
+typedef struct qknr_permute_args {
+    int32_t elem_bytes;     /* 1, 2, 4 or 8 */
+    int32_t inverse;        /* 0: interleaved -> rotate-half; 1: rotate-half -> interleaved */
+    int64_t outer;          /* >= 0 */
+    int64_t axis_len;       /* >= 1 */
+    int64_t inner;          /* >= 1 elements per axis index */
+    int64_t first;          /* >= 0 */
+    int64_t n_heads;        /* >= 0; first + n_heads*head_dim <= axis_len */
+    int64_t head_dim;       /* even, >= 2 */
+    const void *src;
+    void *dst;
+} qknr_permute_args;
+
+int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream_t stream);
 
 /*
  * (b) KvRmsNormRopeCache.

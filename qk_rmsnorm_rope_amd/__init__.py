@@ -11,6 +11,11 @@ Entry points (same names as the C ABI, without the ``qknr_`` prefix):
 
 * :func:`qk_norm_rope_across_heads` -- across-heads RMSNorm + rotate-half RoPE
   ("Kernel reference: qkv_cte", Design sections 1-2).
+* :func:`qk_sumsq_across_heads`, :func:`qk_apply_across_heads` -- the same
+  operator split over ranks (step a, then step c with the added sums).
+* :func:`qk_norm_rope_per_head` -- the upstream per-head qk-norm + RoPE.
+* :func:`interleaved_to_rotate_half` -- the offline lane permutation of an
+  interleaved-pair checkpoint (qkv_cte Design section 2).
 * :func:`kv_rmsnorm_rope_cache` -- the KvRmsNormRopeCache operator (CANN page,
   formulas 1-5), argument names as on that page's parameter table.
 """
@@ -57,6 +62,15 @@ class QkArgs(ctypes.Structure):
         ("q_gamma", _p), ("k_gamma", _p), ("cos", _p), ("sin", _p),
         ("rope_batch_stride", _i64), ("rope_token_stride", _i64),
         ("eps", ctypes.c_float), ("apply_norm", _i32), ("apply_rope", _i32), ("reserved", _i32),
+        ("q_norm_channels", _i64), ("k_norm_channels", _i64),
+    ]
+
+
+class PermuteArgs(ctypes.Structure):
+    """Mirror of ``qknr_permute_args``."""
+    _fields_ = [
+        ("elem_bytes", _i32), ("inverse", _i32), ("outer", _i64), ("axis_len", _i64), ("inner", _i64),
+        ("first", _i64), ("n_heads", _i64), ("head_dim", _i64), ("src", _p), ("dst", _p),
     ]
 
 
@@ -80,6 +94,14 @@ _lib.qknr_qk_norm_rope_across_heads.argtypes = [ctypes.POINTER(QkArgs), _p]
 _lib.qknr_qk_norm_rope_across_heads.restype = _i32
 _lib.qknr_qk_validate.argtypes = [ctypes.POINTER(QkArgs)]
 _lib.qknr_qk_validate.restype = _i32
+_lib.qknr_qk_sumsq_across_heads.argtypes = [ctypes.POINTER(QkArgs), _p, _p]
+_lib.qknr_qk_sumsq_across_heads.restype = _i32
+_lib.qknr_qk_apply_across_heads.argtypes = [ctypes.POINTER(QkArgs), _p, _p]
+_lib.qknr_qk_apply_across_heads.restype = _i32
+_lib.qknr_qk_norm_rope_per_head.argtypes = [ctypes.POINTER(QkArgs), _p]
+_lib.qknr_qk_norm_rope_per_head.restype = _i32
+_lib.qknr_interleaved_to_rotate_half.argtypes = [ctypes.POINTER(PermuteArgs), _p]
+_lib.qknr_interleaved_to_rotate_half.restype = _i32
 _lib.qknr_kv_rmsnorm_rope_cache.argtypes = [ctypes.POINTER(KvArgs), _p]
 _lib.qknr_kv_rmsnorm_rope_cache.restype = _i32
 _lib.qknr_kv_validate.argtypes = [ctypes.POINTER(KvArgs)]
@@ -89,8 +111,9 @@ _lib.qknr_last_error.restype = ctypes.c_char_p
 _lib.qknr_version.argtypes = []
 _lib.qknr_version.restype = _i32
 
-EXPORTED = ("qknr_qk_norm_rope_across_heads", "qknr_qk_validate", "qknr_kv_rmsnorm_rope_cache",
-            "qknr_kv_validate", "qknr_last_error", "qknr_version")
+EXPORTED = ("qknr_qk_norm_rope_across_heads", "qknr_qk_validate", "qknr_qk_sumsq_across_heads",
+            "qknr_qk_apply_across_heads", "qknr_qk_norm_rope_per_head", "qknr_interleaved_to_rotate_half",
+            "qknr_kv_rmsnorm_rope_cache", "qknr_kv_validate", "qknr_last_error", "qknr_version")
 
 
 class QknrError(RuntimeError):
@@ -139,14 +162,17 @@ def _last_dim_contiguous(name, t):
 # ----------------------------------------------------------------------------
 
 def qk_args(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
-            apply_norm=True, apply_rope=True) -> QkArgs:
+            apply_norm=True, apply_rope=True, per_head=False, q_norm_channels=0,
+            k_norm_channels=0) -> QkArgs:
     """Fill ``qknr_qk_args`` from tensors.
 
     q: [B, S, n_q_heads, d] (any strides, d contiguous) -- e.g. a BSD projection
     ``qkv[..., :nq*d].unflatten(-1, (nq, d))`` or an NBSd buffer permuted to
     (B, S, N, d). k: [B, S, n_k_heads, d] with the same strides, or None.
     cos, sin: [B or 1, S, d] (a batch of 1 is shared). Outputs default to the
-    inputs (in place).
+    inputs (in place). Gammas are [n_heads * d] (segment-wide) or, with
+    ``per_head``, [d]. ``*_norm_channels``: the whole segment's channel count
+    for the apply pass of a split norm (0 otherwise).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, S, n_q_heads, head_dim]")
@@ -177,8 +203,10 @@ def qk_args(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
     a.in_batch_stride, a.in_token_stride, a.in_head_stride = q.stride(0), q.stride(1), q.stride(2)
     a.out_batch_stride, a.out_token_stride, a.out_head_stride = q_out.stride(0), q_out.stride(1), q_out.stride(2)
     if apply_norm:
-        if q_gamma is None or q_gamma.numel() != nq * d or (nk and (k_gamma is None or k_gamma.numel() != nk * d)):
-            raise ValueError("gammas must be [n_heads * head_dim] (segment-wide)")
+        gq, gk = (d, d) if per_head else (nq * d, nk * d)
+        if q_gamma is None or q_gamma.numel() != gq or (nk and (k_gamma is None or k_gamma.numel() != gk)):
+            raise ValueError("gammas must be [head_dim] (per head)" if per_head else
+                             "gammas must be [n_heads * head_dim] (segment-wide)")
         a.q_gamma, a.k_gamma = _ptr(q_gamma.contiguous()), _ptr(k_gamma.contiguous() if nk else None)
     if apply_rope:
         if (cos.dim() != 3 or cos.shape[0] not in (1, B) or cos.shape[1] != S or cos.shape[2] != d
@@ -189,6 +217,7 @@ def qk_args(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
         a.rope_token_stride = cos.stride(1)
     a.eps = float(eps)
     a.apply_norm, a.apply_rope = int(bool(apply_norm)), int(bool(apply_rope))
+    a.q_norm_channels, a.k_norm_channels = int(q_norm_channels), int(k_norm_channels)
     a._keep = (q_gamma, k_gamma)  # keep contiguous copies alive
     return a
 
@@ -234,6 +263,95 @@ def prepare_qk_norm_rope_across_heads(q, k, q_gamma, k_gamma, cos, sin, *, eps, 
 def qk_validate(a: QkArgs) -> int:
     """Host-only validation of filled arguments; returns the status code."""
     return int(_lib.qknr_qk_validate(ctypes.byref(a)))
+
+
+def qk_norm_rope_per_head(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
+                          apply_norm=True, apply_rope=True, stream=None):
+    """Per-head RMSNorm (gammas [head_dim] shared by every head) + rotate-half
+    RoPE; arguments as :func:`qk_args`. Returns (q_out, k_out)."""
+    if q_out is None:
+        q_out = q
+    if k is not None and k_out is None:
+        k_out = k
+    a = qk_args(q, k, q_gamma, k_gamma, cos, sin, eps=eps, q_out=q_out, k_out=k_out,
+                apply_norm=apply_norm, apply_rope=apply_rope, per_head=True)
+    with torch.cuda.device(q.device):
+        _check(_lib.qknr_qk_norm_rope_per_head(ctypes.byref(a), _stream(q.device, stream)))
+    return q_out, k_out
+
+
+def qk_sumsq_across_heads(q, k=None, *, sumsq=None, stream=None):
+    """Step a of a split across-heads norm: per token and segment, the sum of
+    squares over the given heads. Returns fp32 [segs, B*S] (segs = 2 with k)."""
+    B, S = q.shape[0], q.shape[1]
+    segs = 2 if k is not None else 1
+    if sumsq is None:
+        sumsq = torch.empty(segs, B * S, dtype=torch.float32, device=q.device)
+    if sumsq.dtype != torch.float32 or sumsq.numel() != segs * B * S or not sumsq.is_contiguous():
+        raise ValueError(f"sumsq must be a contiguous float32 tensor of {segs}*B*S elements")
+    a = qk_args(q, k, None, None, None, None, eps=0.0, apply_norm=False, apply_rope=False)
+    a.q_out = a.k_out = None
+    with torch.cuda.device(q.device):
+        _check(_lib.qknr_qk_sumsq_across_heads(ctypes.byref(a), _ptr(sumsq), _stream(q.device, stream)))
+    return sumsq
+
+
+def qk_apply_across_heads(q, k, q_gamma, k_gamma, cos, sin, sumsq, *, eps, q_norm_channels,
+                          k_norm_channels=0, q_out=None, k_out=None, apply_rope=True, stream=None):
+    """Step c of a split across-heads norm on this rank's heads: ``sumsq``
+    [segs, B*S] holds the sums added over every rank, ``*_norm_channels`` the
+    whole segment's channel count (n_heads*d*tp). Gammas are this rank's slice
+    of the segment-wide gamma. Returns (q_out, k_out)."""
+    if q_out is None:
+        q_out = q
+    if k is not None and k_out is None:
+        k_out = k
+    segs = 2 if k is not None else 1
+    if sumsq.dtype != torch.float32 or sumsq.numel() != segs * q.shape[0] * q.shape[1] or not sumsq.is_contiguous():
+        raise ValueError("sumsq must be the contiguous float32 [segs, B*S] array of the sum pass")
+    a = qk_args(q, k, q_gamma, k_gamma, cos, sin, eps=eps, q_out=q_out, k_out=k_out, apply_norm=True,
+                apply_rope=apply_rope, q_norm_channels=q_norm_channels, k_norm_channels=k_norm_channels)
+    with torch.cuda.device(q.device):
+        _check(_lib.qknr_qk_apply_across_heads(ctypes.byref(a), _ptr(sumsq), _stream(q.device, stream)))
+    return q_out, k_out
+
+
+def permute_args(src, dst, head_dim, *, dim=-1, first=0, n_heads=None, inverse=False) -> PermuteArgs:
+    """Fill ``qknr_permute_args`` for contiguous tensors src/dst of one shape."""
+    if not (src.is_contiguous() and dst.is_contiguous()) or src.shape != dst.shape or src.dtype != dst.dtype:
+        raise ValueError("src and dst must be contiguous tensors of one shape and dtype")
+    dim = dim % src.dim()
+    L = src.shape[dim]
+    if n_heads is None:
+        n_heads = (L - first) // head_dim
+    outer = 1
+    for n in src.shape[:dim]:
+        outer *= n
+    inner = 1
+    for n in src.shape[dim + 1:]:
+        inner *= n
+    a = PermuteArgs()
+    a.elem_bytes, a.inverse = src.element_size(), int(bool(inverse))
+    a.outer, a.axis_len, a.inner = outer, L, inner
+    a.first, a.n_heads, a.head_dim = first, n_heads, head_dim
+    a.src, a.dst = _ptr(src), _ptr(dst)
+    return a
+
+
+def interleaved_to_rotate_half(src, head_dim, *, dim=-1, first=0, n_heads=None, inverse=False, out=None,
+                               stream=None):
+    """Permute `n_heads` blocks of `head_dim` indices of dimension `dim`,
+    starting at `first`, from interleaved pairs (2j, 2j+1) to rotate-half
+    pairs (j, j + d/2) (``inverse``: back); other indices are copied. For a
+    fused QKV weight [H, I] use dim=1, n_heads = n_q + n_k; for interleaved
+    cos/sin tables [.., d] the defaults. Returns the new tensor."""
+    src = src.contiguous()
+    if out is None:
+        out = torch.empty_like(src)
+    a = permute_args(src, out, head_dim, dim=dim, first=first, n_heads=n_heads, inverse=inverse)
+    with torch.cuda.device(src.device):
+        _check(_lib.qknr_interleaved_to_rotate_half(ctypes.byref(a), _stream(src.device, stream)))
+    return out
 
 
 # ----------------------------------------------------------------------------

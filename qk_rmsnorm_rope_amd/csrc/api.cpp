@@ -8,6 +8,7 @@
 // widths, gammas, rotate-half tables).
 #include <cstdarg>
 #include <cstdint>
+#include <climits>
 #include <cstdio>
 #include <string>
 
@@ -36,7 +37,7 @@ int elem_size(int32_t dtype) {
     switch (dtype) {
     case QKNR_F32: return 4;
     case QKNR_BF16: case QKNR_F16: return 2;
-    case QKNR_INT8: case QKNR_FP8_E4M3FN: return 1;
+    case QKNR_INT8: case QKNR_FP8_E4M3FN: case QKNR_FP8_E5M2: return 1;
     }
     return 0;
 }
@@ -53,8 +54,10 @@ struct QkPlan {
     int vec;
 };
 
-int32_t qk_check(const qknr_qk_args *a, QkPlan *out) {
+// mode: qknr::QkMode (which entry point); sumsq: step a's output / step c's input.
+int32_t qk_check(const qknr_qk_args *a, int mode, const float *sumsq, QkPlan *out) {
     if (!a) return fail(QKNR_INVALID_ARGUMENT, "args is NULL");
+    const bool sums_only = mode == qknr::QK_SUMSQ;
     if (a->dtype != QKNR_F32 && a->dtype != QKNR_BF16 && a->dtype != QKNR_F16)
         return fail(QKNR_INVALID_ARGUMENT, "dtype must be QKNR_F32, QKNR_BF16 or QKNR_F16 (got %d)", a->dtype);
     if (a->n_q_heads < 1) return fail(QKNR_INVALID_ARGUMENT, "n_q_heads must be >= 1");
@@ -66,21 +69,37 @@ int32_t qk_check(const qknr_qk_args *a, QkPlan *out) {
         return fail(QKNR_INVALID_ARGUMENT, "eps must be finite and >= 0");
     const int64_t tokens = a->batch * a->seq;
     const bool has_k = a->n_k_heads > 0;
+    const bool use_norm = !sums_only && a->apply_norm, use_rope = !sums_only && a->apply_rope;
+    if (mode == qknr::QK_APPLY && !a->apply_norm)
+        return fail(QKNR_INVALID_ARGUMENT, "the apply pass of a split norm needs apply_norm = 1");
     if (tokens > 0) {
-        if (!a->q_in || !a->q_out) return fail(QKNR_INVALID_ARGUMENT, "q_in and q_out are required");
-        if (has_k && (!a->k_in || !a->k_out))
+        if (!a->q_in || (!sums_only && !a->q_out))
+            return fail(QKNR_INVALID_ARGUMENT, "q_in and q_out are required");
+        if (has_k && (!a->k_in || (!sums_only && !a->k_out)))
             return fail(QKNR_INVALID_ARGUMENT, "k_in and k_out are required when n_k_heads > 0");
-        if (a->apply_norm && (!a->q_gamma || (has_k && !a->k_gamma)))
+        if (use_norm && (!a->q_gamma || (has_k && !a->k_gamma)))
             return fail(QKNR_INVALID_ARGUMENT, "apply_norm needs q_gamma (and k_gamma when n_k_heads > 0)");
-        if (a->apply_rope && (!a->cos || !a->sin))
+        if (use_rope && (!a->cos || !a->sin))
             return fail(QKNR_INVALID_ARGUMENT, "apply_rope needs cos and sin");
+        if ((mode == qknr::QK_SUMSQ || mode == qknr::QK_APPLY) && !sumsq)
+            return fail(QKNR_INVALID_ARGUMENT, "sumsq is required");
+        if (!aligned(sumsq, 4)) return fail(QKNR_INVALID_ARGUMENT, "sumsq must be 4-byte aligned");
     }
+    // total channel counts belong to the apply pass; elsewhere 0 (or the call's own count)
+    const int64_t own_q = (int64_t)a->n_q_heads * a->head_dim, own_k = (int64_t)a->n_k_heads * a->head_dim;
+    const int64_t q_total = a->q_norm_channels ? a->q_norm_channels : own_q;
+    const int64_t k_total = a->k_norm_channels ? a->k_norm_channels : own_k;
+    if (mode != qknr::QK_APPLY && (q_total != own_q || (has_k && k_total != own_k)))
+        return fail(QKNR_INVALID_ARGUMENT, "q_norm_channels/k_norm_channels are for the apply pass only (else 0)");
+    if (q_total < own_q || (has_k && k_total < own_k) || q_total >= (1LL << 24) || k_total >= (1LL << 24))
+        return fail(QKNR_INVALID_ARGUMENT,
+                    "norm channel counts must cover this call's heads and stay below 2^24");
     if (a->in_batch_stride < 0 || a->in_token_stride < 0 || a->out_batch_stride < 0 ||
         a->out_token_stride < 0 || a->rope_batch_stride < 0 || a->rope_token_stride < 0)
         return fail(QKNR_INVALID_ARGUMENT, "strides must be >= 0");
-    if (a->in_head_stride < a->head_dim || a->out_head_stride < a->head_dim)
+    if (a->in_head_stride < a->head_dim || (!sums_only && a->out_head_stride < a->head_dim))
         return fail(QKNR_INVALID_ARGUMENT, "head strides must be >= head_dim (heads may not overlap)");
-    const bool q_alias = a->q_out == a->q_in, k_alias = has_k && a->k_out == a->k_in;
+    const bool q_alias = !sums_only && a->q_out == a->q_in, k_alias = !sums_only && has_k && a->k_out == a->k_in;
     if ((q_alias || k_alias) && (a->in_batch_stride != a->out_batch_stride ||
                                  a->in_token_stride != a->out_token_stride ||
                                  a->in_head_stride != a->out_head_stride))
@@ -88,14 +107,16 @@ int32_t qk_check(const qknr_qk_args *a, QkPlan *out) {
 
     const int es = elem_size(a->dtype);
     const int half = a->head_dim / 2;
-    const void *ptrs[] = {a->q_in, a->q_out, has_k ? a->k_in : nullptr, has_k ? a->k_out : nullptr,
-                          a->apply_norm ? a->q_gamma : nullptr,
-                          (a->apply_norm && has_k) ? a->k_gamma : nullptr,
-                          a->apply_rope ? a->cos : nullptr, a->apply_rope ? a->sin : nullptr};
+    const void *ptrs[] = {a->q_in, sums_only ? nullptr : a->q_out, has_k ? a->k_in : nullptr,
+                          (has_k && !sums_only) ? a->k_out : nullptr,
+                          use_norm ? a->q_gamma : nullptr,
+                          (use_norm && has_k) ? a->k_gamma : nullptr,
+                          use_rope ? a->cos : nullptr, use_rope ? a->sin : nullptr};
     const int64_t strides[] = {a->in_batch_stride, a->in_token_stride, a->in_head_stride,
-                               a->out_batch_stride, a->out_token_stride, a->out_head_stride,
-                               a->apply_rope ? a->rope_batch_stride : 0,
-                               a->apply_rope ? a->rope_token_stride : 0};
+                               sums_only ? 0 : a->out_batch_stride, sums_only ? 0 : a->out_token_stride,
+                               sums_only ? 0 : a->out_head_stride,
+                               use_rope ? a->rope_batch_stride : 0,
+                               use_rope ? a->rope_token_stride : 0};
     auto fits = [&](int vec) {
         if (half % vec) return false;
         for (const void *p : ptrs)
@@ -112,7 +133,7 @@ int32_t qk_check(const qknr_qk_args *a, QkPlan *out) {
     // 32-bit index ranges used inside the kernel
     const int64_t max_heads = a->n_q_heads > a->n_k_heads ? a->n_q_heads : a->n_k_heads;
     const int64_t span_in = ((max_heads - 1) * a->in_head_stride + a->head_dim) * es;
-    const int64_t span_out = ((max_heads - 1) * a->out_head_stride + a->head_dim) * es;
+    const int64_t span_out = sums_only ? 0 : ((max_heads - 1) * a->out_head_stride + a->head_dim) * es;
     if (tokens >= (1LL << 31) || span_in >= (1LL << 32) || span_out >= (1LL << 32))
         return fail(QKNR_UNSUPPORTED, "more than 2^31 tokens, or one token's heads span 4 GiB or more");
 
@@ -131,10 +152,11 @@ int32_t qk_check(const qknr_qk_args *a, QkPlan *out) {
     p.rope_batch_stride = a->rope_batch_stride; p.rope_token_stride = a->rope_token_stride;
     p.n_q = a->n_q_heads; p.n_k = a->n_k_heads; p.head_dim = a->head_dim;
     p.segs = has_k ? 2 : 1;
-    p.apply_norm = a->apply_norm ? 1 : 0; p.apply_rope = a->apply_rope ? 1 : 0;
-    p.q_channels = (float)a->n_q_heads * (float)a->head_dim;
-    p.k_channels = (float)(has_k ? a->n_k_heads : 1) * (float)a->head_dim;
+    p.apply_norm = use_norm ? 1 : 0; p.apply_rope = use_rope ? 1 : 0;
+    p.q_channels = (float)q_total;
+    p.k_channels = (float)(has_k ? k_total : a->head_dim);
     p.eps = a->eps;
+    p.sumsq = const_cast<float *>(sumsq);
     int J = qknr::qk_plan(p, vec);
     if (J < 0 && vec == wide && fits(narrow)) {
         vec = narrow;
@@ -359,16 +381,69 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
 extern "C" {
 
 int32_t qknr_qk_validate(const qknr_qk_args *args) {
-    return qk_check(args, nullptr);
+    return qk_check(args, qknr::QK_ACROSS, nullptr, nullptr);
+}
+
+static int32_t qk_run(const qknr_qk_args *args, int mode, const float *sumsq, hipStream_t stream) {
+    QkPlan plan;
+    int32_t rc = qk_check(args, mode, sumsq, &plan);
+    if (rc != QKNR_OK) return rc;
+    hipError_t e = qknr::qk_launch(plan.p, plan.elem_type, plan.vec, mode, stream);
+    if (e != hipSuccess) return fail(QKNR_DEVICE_ERROR, "launch failed: %s", hipGetErrorString(e));
+    return QKNR_OK;
 }
 
 int32_t qknr_qk_norm_rope_across_heads(const qknr_qk_args *args, hipStream_t stream) {
-    QkPlan plan;
-    int32_t rc = qk_check(args, &plan);
-    if (rc != QKNR_OK) return rc;
-    hipError_t e = qknr::qk_launch(plan.p, plan.elem_type, plan.vec, stream);
+    return qk_run(args, qknr::QK_ACROSS, nullptr, stream);
+}
+
+int32_t qknr_qk_sumsq_across_heads(const qknr_qk_args *args, float *sumsq, hipStream_t stream) {
+    return qk_run(args, qknr::QK_SUMSQ, sumsq, stream);
+}
+
+int32_t qknr_qk_apply_across_heads(const qknr_qk_args *args, const float *sumsq, hipStream_t stream) {
+    return qk_run(args, qknr::QK_APPLY, sumsq, stream);
+}
+
+int32_t qknr_qk_norm_rope_per_head(const qknr_qk_args *args, hipStream_t stream) {
+    return qk_run(args, qknr::QK_PER_HEAD, nullptr, stream);
+}
+
+int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *a, hipStream_t stream) {
+    if (!a) return fail(QKNR_INVALID_ARGUMENT, "args is NULL");
+    if (a->elem_bytes != 1 && a->elem_bytes != 2 && a->elem_bytes != 4 && a->elem_bytes != 8)
+        return fail(QKNR_INVALID_ARGUMENT, "elem_bytes must be 1, 2, 4 or 8");
+    if (a->outer < 0 || a->axis_len < 1 || a->inner < 1 || a->first < 0 || a->n_heads < 0)
+        return fail(QKNR_INVALID_ARGUMENT, "outer >= 0, axis_len >= 1, inner >= 1, first >= 0, n_heads >= 0");
+    if (a->head_dim < 2 || (a->head_dim & 1)) return fail(QKNR_INVALID_ARGUMENT, "head_dim must be even and >= 2");
+    if (a->first > a->axis_len || a->n_heads > (a->axis_len - a->first) / a->head_dim)
+        return fail(QKNR_INVALID_ARGUMENT, "first + n_heads*head_dim exceeds axis_len");
+    if (a->inner > (1LL << 40) || a->axis_len > (1LL << 40))
+        return fail(QKNR_INVALID_ARGUMENT, "tensor too large");
+    const int64_t index_bytes = a->inner * a->elem_bytes;
+    if (a->outer && a->axis_len * index_bytes > (INT64_MAX / 2) / a->outer)
+        return fail(QKNR_INVALID_ARGUMENT, "tensor too large");
+    const int64_t bytes = a->outer * a->axis_len * index_bytes;
+    if (bytes == 0) return ok();
+    if (!a->src || !a->dst) return fail(QKNR_INVALID_ARGUMENT, "src and dst are required");
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(a->src), d0 = reinterpret_cast<uintptr_t>(a->dst);
+    if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes)
+        return fail(QKNR_INVALID_ARGUMENT, "src and dst overlap");
+    int unit = 16;
+    while (unit > 1 && (index_bytes % unit || !aligned(a->src, unit) || !aligned(a->dst, unit))) unit /= 2;
+    qknr::PermuteParams p;
+    p.src = a->src;
+    p.dst = a->dst;
+    p.outer = (uint64_t)a->outer;
+    p.axis_len = (uint64_t)a->axis_len;
+    p.units_per_index = (uint64_t)(index_bytes / unit);
+    p.first = (uint64_t)a->first;
+    p.n_heads = (uint64_t)a->n_heads;
+    p.head_dim = (uint64_t)a->head_dim;
+    p.inverse = a->inverse ? 1 : 0;
+    hipError_t e = qknr::permute_launch(p, unit, stream);
     if (e != hipSuccess) return fail(QKNR_DEVICE_ERROR, "launch failed: %s", hipGetErrorString(e));
-    return QKNR_OK;
+    return ok();
 }
 
 int32_t qknr_kv_validate(const qknr_kv_args *args) {

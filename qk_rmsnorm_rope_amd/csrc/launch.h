@@ -37,7 +37,15 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv &f) {
     return (t + ((n - t) >> f.sh1)) >> f.sh2;
 }
 
-// (a) across-heads QK RMSNorm + rotate-half RoPE
+// (a) QK RMSNorm + rotate-half RoPE. The kernel has four forms:
+//   QK_ACROSS    one RMS per (token, segment) over all its heads, then RoPE;
+//   QK_PER_HEAD  one RMS per (token, head), gamma [head_dim] shared by heads;
+//   QK_SUMSQ     first pass of a split over ranks: each (token, segment)'s sum
+//                of squares over this call's heads -> sumsq[seg*tokens + t];
+//   QK_APPLY     second pass: RMS from sumsq (the sum over every rank) and
+//                q_channels / k_channels (the whole segment), then as QK_ACROSS.
+enum QkMode : int32_t { QK_ACROSS = 0, QK_PER_HEAD = 1, QK_SUMSQ = 2, QK_APPLY = 3 };
+
 struct QkParams {
     const void *q_in;
     const void *k_in;
@@ -60,13 +68,31 @@ struct QkParams {
     int32_t waves_per_unit;    // W: waves sharing one (token, segment), 1, 2 or 4
     int32_t segs;              // 2 with a K segment, 1 for Q only
     int32_t apply_norm, apply_rope;
-    float q_channels, k_channels, eps;
+    float q_channels, k_channels, eps;   // RMS denominators (QK_PER_HEAD: head_dim)
+    float *sumsq;              // QK_SUMSQ output / QK_APPLY input, fp32 [segs, tokens]
 };
 
 // Fills the lane geometry of p for chunk width `vec`; returns J > 0 or -1.
 int qk_plan(QkParams &p, int vec);
 // elem_type: 0 f32, 1 bf16, 2 f16. vec: 16-byte chunk width, or the narrow fallback.
-hipError_t qk_launch(QkParams &p, int elem_type, int vec, hipStream_t stream);
+hipError_t qk_launch(QkParams &p, int elem_type, int vec, int mode, hipStream_t stream);
+// One translation unit per form (compiled in parallel); J from qk_plan.
+hipError_t qk_launch_across(const QkParams &p, int elem_type, int vec, int J, hipStream_t stream);
+hipError_t qk_launch_per_head(const QkParams &p, int elem_type, int vec, int J, hipStream_t stream);
+hipError_t qk_launch_split(const QkParams &p, int elem_type, int vec, int J, int mode, hipStream_t stream);
+
+// Interleaved-pair -> rotate-half lane permutation of a tensor viewed as
+// [outer, axis_len, inner]: along the axis, n_heads blocks of head_dim starting
+// at `first` are permuted (inverse: back); every other index is copied.
+struct PermuteParams {
+    const void *src;
+    void *dst;
+    uint64_t outer, axis_len, units_per_index;   // units of `unit` bytes per axis index
+    uint64_t first, n_heads, head_dim;
+    int32_t inverse;
+};
+// unit: bytes moved per access (1, 2, 4, 8 or 16), dividing the bytes per index.
+hipError_t permute_launch(const PermuteParams &p, int unit, hipStream_t stream);
 
 // (b) KvRmsNormRopeCache
 enum CacheCode : int32_t { CODE_SAME = 0, CODE_INT8 = 1, CODE_E4M3FN = 2, CODE_E5M2 = 3 };

@@ -51,7 +51,8 @@ def test_header_constants_match_binding():
 
 def test_struct_layouts_match_c(tmp_path):
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "qknr.h"', "int main(void) {"]
-    for cname, py in (("qknr_qk_args", Q.QkArgs), ("qknr_kv_args", Q.KvArgs)):
+    structs = (("qknr_qk_args", Q.QkArgs), ("qknr_kv_args", Q.KvArgs), ("qknr_permute_args", Q.PermuteArgs))
+    for cname, py in structs:
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
         for f, _ in py._fields_:
             lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
@@ -68,7 +69,7 @@ def test_struct_layouts_match_c(tmp_path):
         if not line:
             continue
         cname, field, val = line.split()
-        py = Q.QkArgs if cname == "qknr_qk_args" else Q.KvArgs
+        py = dict(structs)[cname]
         expect = ctypes.sizeof(py) if field == "sizeof" else getattr(py, field).offset
         assert int(val) == expect, (cname, field)
 
@@ -129,6 +130,57 @@ def test_qk_alignment_falls_back_or_is_unsupported():
     assert Q.qk_validate(a) == Q.OK
     a.q_in = a.q_in + 2            # 2-byte offset: no 4-byte access possible
     assert Q.qk_validate(a) == Q.UNSUPPORTED
+
+
+def _call(fn, a, *extra):
+    return int(getattr(Q._lib, fn)(ctypes.byref(a), *extra, None))
+
+
+def test_qk_new_entry_points_reject_invalid_arguments_on_the_host():
+    """Each failing check returns before any device call."""
+    fake = ctypes.c_void_p(0x100000)          # never dereferenced: validation fails first
+    a = _qk()
+    a.q_norm_channels = 4096                  # only the apply pass takes a total channel count
+    assert _call("qknr_qk_norm_rope_across_heads", a) == Q.INVALID_ARGUMENT
+    assert _call("qknr_qk_norm_rope_per_head", a) == Q.INVALID_ARGUMENT
+    assert _call("qknr_qk_sumsq_across_heads", a, fake) == Q.INVALID_ARGUMENT
+    b = _qk()
+    assert _call("qknr_qk_sumsq_across_heads", b, None) == Q.INVALID_ARGUMENT      # sums buffer missing
+    assert _call("qknr_qk_apply_across_heads", b, None) == Q.INVALID_ARGUMENT
+    assert _call("qknr_qk_apply_across_heads", b, ctypes.c_void_p(0x100002)) == Q.INVALID_ARGUMENT  # misaligned
+    c = _qk(apply_norm=False)
+    assert _call("qknr_qk_apply_across_heads", c, fake) == Q.INVALID_ARGUMENT      # apply needs the norm
+    d = _qk()
+    d.q_norm_channels = 8                     # smaller than this call's own 2*8 channels
+    assert _call("qknr_qk_apply_across_heads", d, fake) == Q.INVALID_ARGUMENT
+    d.q_norm_channels = 1 << 24
+    assert _call("qknr_qk_apply_across_heads", d, fake) == Q.INVALID_ARGUMENT
+    e = _qk()
+    e.q_gamma = None                          # per head still needs its gamma
+    assert _call("qknr_qk_norm_rope_per_head", e) == Q.INVALID_ARGUMENT
+
+
+def _perm(**kw):
+    a = Q.PermuteArgs()
+    a.elem_bytes, a.inverse, a.outer, a.axis_len, a.inner = 2, 0, 4, 24, 1
+    a.first, a.n_heads, a.head_dim = 0, 3, 8
+    a.src, a.dst = 0x100000, 0x200000
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw", [dict(elem_bytes=3), dict(head_dim=7), dict(n_heads=4), dict(first=1),
+                                dict(axis_len=0), dict(inner=0), dict(outer=-1), dict(dst=0x100010),
+                                dict(src=None)])
+def test_permute_rejects_invalid_arguments(kw):
+    assert int(Q._lib.qknr_interleaved_to_rotate_half(ctypes.byref(_perm(**kw)), None)) == Q.INVALID_ARGUMENT
+    assert Q.last_error() != ""
+
+
+def test_permute_empty_tensor_is_a_noop():
+    assert int(Q._lib.qknr_interleaved_to_rotate_half(ctypes.byref(_perm(outer=0, src=None, dst=None)),
+                                                       None)) == Q.OK
 
 
 def test_qk_too_many_heads_is_unsupported():
