@@ -9,12 +9,16 @@ Printed: ONE JSON line with the headline throughput (algorithmic HBM GB/s over
 the timed steps), tokens/s, the roofline of the kernel (bytes it must move /
 its average launch time, measured with HIP events on the launch stream, vs
 MI355X's 8 TB/s), the fp64 CPU oracle timed on a bounded sample of the same
-workload, and the KvRmsNormRopeCache workloads (MLA V1 prefill, V1 decode
-quantised, V2 split) timed the same way, cold (L2 and MALL evicted by reading
-1 GiB before every launch) and hot.
+workload, the KvRmsNormRopeCache workloads (MLA V1 prefill, also with
+PA_BLK_BNSD indexing, V1 decode quantised, also as a HIP-graph replay, V2
+split) timed the same way, cold (L2 and MALL evicted by reading 1 GiB before
+every launch) and hot, and the other forms of the QK operator on the Wan2.2
+shape: per-head norm, and the two passes of the across-heads norm split over
+tp = 4 ranks at one rank's share (10 + 10 heads).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv]
-       python bench.py --profile {across,kv_v1_prefill,kv_v1_decode,kv_v2,copy}
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv] [--no-forms]
+       python bench.py --profile {across,per_head,split_sumsq,split_apply,kv_v1_prefill,
+                                  kv_v1_decode,kv_v2,copy}
        (a short fixed run of one kernel, for rocprofv3 counter collection)
        python bench.py --summarize DIR
        (turn the rocprofv3 CSVs under DIR into the text summaries and the
@@ -35,8 +39,12 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "achieved HBM GB/s (% of MI355X peak) + tokens/s for fused norm+RoPE(+cache)"
 KERNEL_SOURCES = {
-    "qk_across_heads": ["qk_rmsnorm_rope_amd/csrc/qk_across_heads.hip",
+    "qk_across_heads": ["qk_rmsnorm_rope_amd/csrc/qk_across_heads.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
                         "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+    "qk_per_head": ["qk_rmsnorm_rope_amd/csrc/qk_per_head.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
+                    "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+    "qk_split": ["qk_rmsnorm_rope_amd/csrc/qk_split.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
+                 "qk_rmsnorm_rope_amd/csrc/device_common.h"],
     "kv_rmsnorm_rope_cache": ["qk_rmsnorm_rope_amd/csrc/kv_rmsnorm_rope_cache.hip",
                               "qk_rmsnorm_rope_amd/csrc/device_common.h"],
 }
@@ -71,9 +79,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-kv", action="store_true", help="skip the KvRmsNormRopeCache workloads")
+    ap.add_argument("--no-forms", action="store_true", help="skip the per-head and split forms of (a)")
     ap.add_argument("--cold-iters", type=int, default=30)
     ap.add_argument("--profile", default=None,
-                    choices=["across", "kv_v1_prefill", "kv_v1_decode", "kv_v2", "copy"])
+                    choices=["across", "per_head", "split_sumsq", "split_apply", "kv_v1_prefill",
+                             "kv_v1_decode", "kv_v2", "copy"])
     ap.add_argument("--summarize", default=None, metavar="DIR")
     return ap.parse_args()
 
@@ -94,15 +104,80 @@ def across_setup(torch, W, Q):
     return cfg, d, step
 
 
-def kv_setup(torch, W, Q, cfg):
-    d = W.make_kv_cache(cfg, device="cuda", prefill=False)
-    mode = "Norm" if cfg.cache_mode == W.NORM else "PA_BNSD"
+def forms_setup(torch, W, Q, which, d=None):
+    """Launchers of the other forms of (a) on the Wan2.2 shape: 'per_head'
+    (all 40 + 40 heads, [128] gammas) and the split over tp = 4 ranks at one
+    rank's share, 'split_sumsq' and 'split_apply' (10 + 10 heads)."""
+    cfg = W.WAN22_SELF_ATTN
+    if d is None:
+        d = W.make_across_heads(cfg, device="cuda")
+    nq, nk, hd = cfg.n_q_heads, cfg.n_k_heads, cfg.head_dim
+    qkv = d["qkv"]
+    q = qkv[..., : nq * hd].unflatten(-1, (nq, hd))
+    k = qkv[..., nq * hd:].unflatten(-1, (nk, hd))
+    if which == "per_head":
+        out = torch.empty_like(qkv)
+        qo = out[..., : nq * hd].unflatten(-1, (nq, hd))
+        ko = out[..., nq * hd:].unflatten(-1, (nk, hd))
+        gq, gk = d["q_gamma"][:hd].contiguous(), d["k_gamma"][:hd].contiguous()
+        return Q.prepare_qk_norm_rope_per_head(q, k, gq, gk, d["cos"], d["sin"], eps=cfg.eps, q_out=qo, k_out=ko)
+    tp = 4
+    lq, lk = nq // tp, nk // tp
+    qs = torch.empty(1, cfg.seq, lq + lk, hd, dtype=cfg.dtype, device="cuda")   # one rank's Q|K slice
+    qs.copy_(torch.cat([q[:, :, :lq], k[:, :, :lk]], 2))
+    sq, sk = qs[:, :, :lq], qs[:, :, lq:]
+    sums = torch.empty(2, cfg.seq, dtype=torch.float32, device="cuda")
+    sum_step = Q.prepare_qk_sumsq_across_heads(sq, sk, sums)
+    if which == "split_sumsq":
+        return sum_step
+    sum_step()
+    sums.mul_(tp)                                    # stands in for the other ranks' sums
+    out = torch.empty_like(qs)
+    gq, gk = d["q_gamma"][: lq * hd].contiguous(), d["k_gamma"][: lk * hd].contiguous()
+    return Q.prepare_qk_apply_across_heads(sq, sk, gq, gk, d["cos"], d["sin"], sums, eps=cfg.eps,
+                                           q_norm_channels=nq * hd, k_norm_channels=nk * hd,
+                                           q_out=out[:, :, :lq], k_out=out[:, :, lq:])
 
-    step = Q.prepare_kv_rmsnorm_rope_cache(
-        d["kv"], d["gamma"], d["cos"], d["sin"], d["index"], d["k_cache"], d["ckv_cache"],
-        k_rope_scale=d["k_scale"], k_rope_offset=d["k_offset"], c_kv_scale=d["v_scale"],
-        c_kv_offset=d["v_offset"], v=d["v"], epsilon=cfg.eps, cache_mode=mode,
-        is_output_kv=cfg.is_output_kv, k_rope=d["k_rope"], c_kv=d["c_kv"])
+
+def forms_measure(torch, W, Q, d, flush, cold_iters):
+    cfg = W.WAN22_SELF_ATTN
+    sums_b, apply_b = W.algorithmic_bytes_qk_split(cfg, 4)
+    res = {}
+    for name, nbytes, kernel in (("per_head", W.algorithmic_bytes_per_head(cfg), "qk_per_head"),
+                                 ("split_sumsq", sums_b, "qk_split"), ("split_apply", apply_b, "qk_split")):
+        step = forms_setup(torch, W, Q, name, d)
+        for _ in range(5):
+            step()
+        hot = time_hot(torch, step, 50)
+        cold = time_cold(torch, step, cold_iters, flush)
+        res[name] = {"algorithmic_bytes": nbytes, "us_hot_mean": round(hot, 3), "us_cold_median": round(cold, 3),
+                     "gbs_hot": round(nbytes / hot / 1e3, 1), "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4),
+                     "frac_cold": round(nbytes / cold / 1e3 / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(kernel, "wan22_" + name)}
+        del step
+        torch.cuda.empty_cache()
+    res["per_head"]["workload"] = "Wan2.2 S=75600, 40+40 heads x 128 bf16, per-head RMS, [128] gammas, out of place"
+    res["split_sumsq"]["workload"] = ("Wan2.2 S=75600 split over tp=4 ranks: one rank's 10+10 heads, "
+                                      "per-token sums of squares -> fp32 [2, S]")
+    res["split_apply"]["workload"] = ("the same rank's apply pass: sums of all ranks, 5120-channel RMS, "
+                                      "gamma slices, RoPE, out of place")
+    res["split_two_pass_us_hot"] = round(res["split_sumsq"]["us_hot_mean"] + res["split_apply"]["us_hot_mean"], 3)
+    return res
+
+
+def kv_setup(torch, W, Q, cfg, **override):
+    d = W.make_kv_cache(cfg, device="cuda", prefill=False, **override)
+    cfg = d["cfg"]
+    mode = {W.NORM: "Norm", W.PA_BNSD: "PA_BNSD", W.PA_BLK_BNSD: "PA_BLK_BNSD"}[cfg.cache_mode]
+
+    def make(stream=None):
+        return Q.prepare_kv_rmsnorm_rope_cache(
+            d["kv"], d["gamma"], d["cos"], d["sin"], d["index"], d["k_cache"], d["ckv_cache"],
+            k_rope_scale=d["k_scale"], k_rope_offset=d["k_offset"], c_kv_scale=d["v_scale"],
+            c_kv_offset=d["v_offset"], v=d["v"], epsilon=cfg.eps, cache_mode=mode,
+            is_output_kv=cfg.is_output_kv, k_rope=d["k_rope"], c_kv=d["c_kv"], stream=stream)
+    step = make()
+    step.make = make                   # a launcher on another stream (graph capture)
     return d, step
 
 
@@ -163,21 +238,69 @@ def cpu_baseline(torch, W, d, cfg):
                                          values=False)
         return time.perf_counter() - t0
 
+    def run1(n):
+        args = sample(n)
+        t0 = time.perf_counter()
+        oracle.qk_norm_rope_across_heads(*args, cfg.eps, nq, nk, hd, oracle.BF16, nthreads=1, values=False)
+        return time.perf_counter() - t0
+
     probe = 2048
     t_probe = run(probe)
-    n = int(min(cfg.seq, max(probe, probe * 10.0 / max(t_probe, 1e-6))))   # about 10 s of oracle time
-    t = run(n)
+    # about 10 s of oracle CPU time (threads x wall), at most the whole workload
+    n = int(min(cfg.seq, max(probe, probe * 10.0 / max(t_probe * threads, 1e-6))))
+    t = sorted(run(n) for _ in range(3))[1]
+    n1 = 4096
+    t1 = run1(n1)
     per_token = W.algorithmic_bytes_across_heads(cfg) / cfg.seq
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(n * per_token / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "tokens_per_s": round(n / t, 1), "seconds": round(t, 3),
-            "sample": f"first {n} of {cfg.seq} tokens of the same workload, fp64 C oracle, "
-                      f"OpenMP over tokens, {threads} threads, bf16 outputs encoded"}
+            "tokens_per_s": round(n / t, 1), "seconds": round(t, 3), "cpu_model": model,
+            "one_thread": {"value": round(n1 * per_token / t1 / 1e9, 4), "unit": "GB/s", "tokens": n1,
+                           "seconds": round(t1, 3)},
+            "sample": f"first {n} of {cfg.seq} tokens of the same workload (median of 3 runs), fp64 C oracle, "
+                      f"OpenMP over tokens, {threads} threads, bf16 outputs encoded; one_thread: first {n1} "
+                      f"tokens on 1 thread"}
+
+
+def graph_replay_us(torch, step, calls=100, replays=20):
+    """Per-call time of `calls` launches captured in one HIP graph, replayed
+    back to back (launch overhead amortised)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    side = step.make(s)
+    for _ in range(3):
+        side()                         # warm up on a side stream, as capture requires
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = step.make(torch.cuda.current_stream())
+        for _ in range(calls):
+            captured()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * calls)
 
 
 def kv_measure(torch, W, Q, flush, cold_iters):
     out = {}
-    for cfg in (W.MLA_V1_PREFILL, W.MLA_V1_DECODE_QUANT, W.MLA_V2_SPLIT):
-        d, step = kv_setup(torch, W, Q, cfg)
+    for name, cfg, over in (("mla_v1_prefill", W.MLA_V1_PREFILL, {}),
+                            ("mla_v1_prefill_pa_blk_bnsd", W.MLA_V1_PREFILL, {"cache_mode": W.PA_BLK_BNSD}),
+                            ("mla_v1_decode_quant", W.MLA_V1_DECODE_QUANT, {}),
+                            ("mla_v2_split", W.MLA_V2_SPLIT, {})):
+        d, step = kv_setup(torch, W, Q, cfg, **over)
+        cfg = d["cfg"]
         for _ in range(5):
             step()
         hot = time_hot(torch, step, 200)
@@ -190,8 +313,10 @@ def kv_measure(torch, W, Q, flush, cold_iters):
                "frac_cold": round(nbytes / cold / 1e3 / PEAK_HBM_GBS, 4),
                "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4),
                "tokens_per_s_cold": round(tokens / cold * 1e6, 1),
-               "traffic": measured_traffic("kv_rmsnorm_rope_cache", cfg.name)}
-        out[cfg.name] = rec
+               "traffic": measured_traffic("kv_rmsnorm_rope_cache", name)}
+        if name == "mla_v1_decode_quant":
+            rec["us_graph_replay_per_call"] = round(graph_replay_us(torch, step), 3)
+        out[name] = rec
         del d
         torch.cuda.empty_cache()
     return out
@@ -210,6 +335,8 @@ def profile_run(torch, W, Q, which):
         return
     if which == "across":
         cfg, d, step = across_setup(torch, W, Q)
+    elif which in ("per_head", "split_sumsq", "split_apply"):
+        step = forms_setup(torch, W, Q, which)
     else:
         cfg = {"kv_v1_prefill": W.MLA_V1_PREFILL, "kv_v1_decode": W.MLA_V1_DECODE_QUANT,
                "kv_v2": W.MLA_V2_SPLIT}[which]
@@ -221,11 +348,16 @@ def profile_run(torch, W, Q, which):
     print(json.dumps({"profile": which, "launches": 5}))
 
 
+# profile target -> (kernel source group, workload, a substring naming the kernel
+# instantiation: the QK forms differ in the last template argument)
 PROFILE_WORKLOADS = {
-    "across": ("qk_across_heads", "wan22_self_attn"),
-    "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill"),
-    "kv_v1_decode": ("kv_rmsnorm_rope_cache", "mla_v1_decode_quant"),
-    "kv_v2": ("kv_rmsnorm_rope_cache", "mla_v2_split"),
+    "across": ("qk_across_heads", "wan22_self_attn", ", 0>(qknr::QkParams)"),
+    "per_head": ("qk_per_head", "wan22_per_head", ", 1>(qknr::QkParams)"),
+    "split_sumsq": ("qk_split", "wan22_split_sumsq", ", 2>(qknr::QkParams)"),
+    "split_apply": ("qk_split", "wan22_split_apply", ", 3>(qknr::QkParams)"),
+    "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill", "kv_rmsnorm_rope_cache_kernel"),
+    "kv_v1_decode": ("kv_rmsnorm_rope_cache", "mla_v1_decode_quant", "kv_rmsnorm_rope_cache_kernel"),
+    "kv_v2": ("kv_rmsnorm_rope_cache", "mla_v2_split", "kv_rmsnorm_rope_cache_kernel"),
 }
 
 
@@ -267,20 +399,25 @@ def summarize(prof_dir):
                               "fetch_scale": f_scale, "write_scale": w_scale},
               "kernels": {}}
     lines_by_kernel = {}
-    for prof, (kernel, wname) in PROFILE_WORKLOADS.items():
+    for prof, (kernel, wname, needle) in PROFILE_WORKLOADS.items():
         fv, wv = counters("fetch", prof), counters("write", prof)
-        f, w = pick(fv, "qknr::"), pick(wv, "qknr::")
+        f, w = pick(fv, needle), pick(wv, needle)
         if f is None or w is None:
             continue
-        cfg = cfgs[wname]
-        alg = (W.algorithmic_bytes_across_heads(cfg) if kernel == "qk_across_heads"
-               else W.algorithmic_bytes_kv_cache(cfg))
+        if wname == "wan22_per_head":
+            alg = W.algorithmic_bytes_per_head(W.WAN22_SELF_ATTN)
+        elif wname.startswith("wan22_split"):
+            alg = W.algorithmic_bytes_qk_split(W.WAN22_SELF_ATTN, 4)[0 if wname.endswith("sumsq") else 1]
+        elif kernel == "qk_across_heads":
+            alg = W.algorithmic_bytes_across_heads(cfgs[wname])
+        else:
+            alg = W.algorithmic_bytes_kv_cache(cfgs[wname])
         hbm = f * 1024 * f_scale + w * 1024 * w_scale
         record["kernels"][wname] = {"kernel": kernel, "source_hash": source_hash(kernel),
                                     "FETCH_SIZE_KiB": f, "WRITE_SIZE_KiB": w,
                                     "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes": alg,
                                     "traffic_over_algorithmic": round(hbm / alg, 4)}
-        kname = [k for k in fv if "qknr::" in k][0]
+        kname = [k for k in fv if needle in k][0]
         grids = set()
         for fpath in glob.glob(os.path.join(prof_dir, f"pmc_fetch_{prof}", "*counter_collection.csv")):
             grids |= {r["Grid_Size"] for r in csv.DictReader(open(fpath)) if r["Kernel_Name"] == kname}
@@ -302,11 +439,13 @@ def summarize(prof_dir):
             "python -u bench.py --profile <w>\n"
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write_<w> -o p -- "
             "python -u bench.py --profile <w>\n"
-            "  for <w> in across kv_v1_prefill kv_v1_decode kv_v2 copy; then "
+            "  for <w> in across per_head split_sumsq split_apply kv_v1_prefill kv_v1_decode kv_v2 copy; then "
             "python bench.py --summarize <dir>\n")
     calib = (f"calibration (copy of 1 GiB, __amd_rocclr_copyBuffer): FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE "
              f"{cw:.1f} KiB -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}\n")
     names = {"qk_across_heads": "qk_across_heads_wan22_s75600.txt",
+             "qk_per_head": "qk_per_head_wan22_s75600.txt",
+             "qk_split": "qk_split_passes_wan22_tp4_shard.txt",
              "kv_rmsnorm_rope_cache": "kv_rmsnorm_rope_cache_mla_workloads.txt"}
     for kernel, lines in lines_by_kernel.items():
         with open(os.path.join(ROOT, "profiles", names[kernel]), "w") as ftxt:
@@ -380,6 +519,8 @@ def main():
                            "gbs": round(2 * (1 << 30) / copy_us / 1e3, 1),
                            "frac": round(2 * (1 << 30) / copy_us / 1e3 / PEAK_HBM_GBS, 4)},
     }
+    if not args.no_forms:
+        result["qk_forms"] = forms_measure(torch, W, Q, d, flush, args.cold_iters)
     if not args.no_kv:
         result["kv_rmsnorm_rope_cache"] = kv_measure(torch, W, Q, flush, args.cold_iters)
     if not args.no_cpu:

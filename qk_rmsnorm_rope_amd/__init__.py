@@ -316,6 +316,53 @@ def qk_apply_across_heads(q, k, q_gamma, k_gamma, cos, sin, sumsq, *, eps, q_nor
     return q_out, k_out
 
 
+def _prepared(fn, a, extra, device, stream, keep):
+    """A zero-argument launcher of `fn(&a, *extra, stream)` with the arguments
+    marshalled once (the tensors in `keep` must stay alive and unmoved)."""
+    st = _stream(device, stream)
+    ref = ctypes.byref(a)
+
+    def launch():
+        _check(fn(ref, *extra, st))
+    launch.args, launch.tensors = a, keep
+    return launch
+
+
+def prepare_qk_norm_rope_per_head(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
+                                  apply_norm=True, apply_rope=True, stream=None):
+    """Prepared form of :func:`qk_norm_rope_per_head`."""
+    q_out = q if q_out is None else q_out
+    k_out = k if (k is not None and k_out is None) else k_out
+    a = qk_args(q, k, q_gamma, k_gamma, cos, sin, eps=eps, q_out=q_out, k_out=k_out,
+                apply_norm=apply_norm, apply_rope=apply_rope, per_head=True)
+    return _prepared(_lib.qknr_qk_norm_rope_per_head, a, (), q.device, stream,
+                     (q, k, q_out, k_out, q_gamma, k_gamma, cos, sin))
+
+
+def prepare_qk_sumsq_across_heads(q, k, sumsq, *, stream=None):
+    """Prepared form of :func:`qk_sumsq_across_heads` writing into `sumsq`."""
+    segs = 2 if k is not None else 1
+    if sumsq.dtype != torch.float32 or sumsq.numel() != segs * q.shape[0] * q.shape[1] or not sumsq.is_contiguous():
+        raise ValueError(f"sumsq must be a contiguous float32 tensor of {segs}*B*S elements")
+    a = qk_args(q, k, None, None, None, None, eps=0.0, apply_norm=False, apply_rope=False)
+    a.q_out = a.k_out = None
+    return _prepared(_lib.qknr_qk_sumsq_across_heads, a, (_ptr(sumsq),), q.device, stream, (q, k, sumsq))
+
+
+def prepare_qk_apply_across_heads(q, k, q_gamma, k_gamma, cos, sin, sumsq, *, eps, q_norm_channels,
+                                  k_norm_channels=0, q_out=None, k_out=None, apply_rope=True, stream=None):
+    """Prepared form of :func:`qk_apply_across_heads`."""
+    q_out = q if q_out is None else q_out
+    k_out = k if (k is not None and k_out is None) else k_out
+    segs = 2 if k is not None else 1
+    if sumsq.dtype != torch.float32 or sumsq.numel() != segs * q.shape[0] * q.shape[1] or not sumsq.is_contiguous():
+        raise ValueError("sumsq must be the contiguous float32 [segs, B*S] array of the sum pass")
+    a = qk_args(q, k, q_gamma, k_gamma, cos, sin, eps=eps, q_out=q_out, k_out=k_out, apply_norm=True,
+                apply_rope=apply_rope, q_norm_channels=q_norm_channels, k_norm_channels=k_norm_channels)
+    return _prepared(_lib.qknr_qk_apply_across_heads, a, (_ptr(sumsq),), q.device, stream,
+                     (q, k, q_out, k_out, q_gamma, k_gamma, cos, sin, sumsq))
+
+
 def permute_args(src, dst, head_dim, *, dim=-1, first=0, n_heads=None, inverse=False) -> PermuteArgs:
     """Fill ``qknr_permute_args`` for contiguous tensors src/dst of one shape."""
     if not (src.is_contiguous() and dst.is_contiguous()) or src.shape != dst.shape or src.dtype != dst.dtype:

@@ -322,6 +322,30 @@ ALL = {c.name: c for c in (TINY_ACROSS_HEADS, WAN22_SELF_ATTN, MLA_V1_PREFILL,
                            MLA_V1_DECODE_QUANT, MLA_V2_SPLIT)}
 
 
+def algorithmic_bytes_qk_split(cfg: AcrossHeadsConfig, tp: int):
+    """Bytes each pass of the split over `tp` ranks must move on one rank
+    (n_q/tp and n_k/tp heads): (sum pass, apply pass).
+
+    Sum pass: read the rank's Q and K once, write one fp32 sum per token and
+    segment. Apply pass: read Q, K, cos, sin and the sums once, write Q and K
+    once, read the rank's gamma slices once."""
+    e = torch.tensor([], dtype=cfg.dtype).element_size()
+    T = cfg.batch * cfg.seq
+    cq, ck = cfg.n_q_heads // tp * cfg.head_dim, cfg.n_k_heads // tp * cfg.head_dim
+    segs = 2 if ck else 1
+    sums = e * T * (cq + ck) + 4 * segs * T
+    apply = e * (T * (2 * (cq + ck) + 2 * cfg.head_dim) + cq + ck) + 4 * segs * T
+    return sums, apply
+
+
+def algorithmic_bytes_per_head(cfg: AcrossHeadsConfig) -> int:
+    """As the across-heads pass, with one [head_dim] gamma per segment."""
+    e = torch.tensor([], dtype=cfg.dtype).element_size()
+    T = cfg.batch * cfg.seq
+    cq, ck = cfg.n_q_heads * cfg.head_dim, cfg.n_k_heads * cfg.head_dim
+    return e * (T * (2 * (cq + ck) + 2 * cfg.head_dim) + cfg.head_dim * (2 if ck else 1))
+
+
 def algorithmic_bytes_across_heads(cfg: AcrossHeadsConfig) -> int:
     """Bytes the across-heads pass must move: Q and K read and written once,
     cos and sin read once per token, both gammas read once."""
