@@ -69,6 +69,8 @@ def _load():
         lib.oracle_qk_norm_rope.restype = i32
         lib.oracle_qk_sumsq.argtypes = [i64, i64, i64, i32, p, p]
         lib.oracle_qk_sumsq.restype = i32
+        lib.oracle_linear.argtypes = [i64, i64, i64, i32, p, i32, p, p, i32, p, p, i32, p, p, i32]
+        lib.oracle_linear.restype = i32
         lib.oracle_kv_rmsnorm_rope_cache.argtypes = (
             [i64] * 7 + [i32] + [p] * 5 + [i64, p, i32, i64, i64, i32, i32, p, p]
             + [p] * 4 + [f64, i32] + [p] * 6 + [i32])
@@ -193,6 +195,34 @@ def qk_norm_rope(q, k, q_gamma, k_gamma, cos, sin, eps, n_q_heads, n_k_heads, he
     if rc != 0:
         raise ValueError("oracle rejected the dimensions")
     return q_out, k_out, q_val, k_val
+
+
+def linear(a, w, a_dtype, w_dtype=None, bias=None, bias_dtype=None, a_scale=None, w_scale=None,
+           out_dtype=None, nthreads=None):
+    """The projection O = (A @ W^T) * a_scale[:, None] * w_scale[None, :] + bias.
+
+    a: [S, H] storage of ``a_dtype``; w: [I, H] storage of ``w_dtype`` (a linear
+    layer's [out, in] weight); bias [I] storage of ``bias_dtype``; scales fp64
+    or None. Returns (encoded output in ``out_dtype`` or None, exact fp64 [S, I]).
+    """
+    w_dtype = a_dtype if w_dtype is None else w_dtype
+    a = _c(a, STORAGE[a_dtype])
+    w = _c(w, STORAGE[w_dtype])
+    S, H = a.shape
+    I = w.shape[0]
+    assert w.shape == (I, H)
+    bias_dtype = a_dtype if bias_dtype is None else bias_dtype
+    b = _c(bias, STORAGE[bias_dtype]) if bias is not None else None
+    asc = _c(a_scale, np.float64) if a_scale is not None else None
+    wsc = _c(w_scale, np.float64) if w_scale is not None else None
+    out = np.empty((S, I), STORAGE[out_dtype]) if out_dtype is not None else None
+    val = np.empty((S, I), np.float64)
+    rc = _load().oracle_linear(S, H, I, a_dtype, _ptr(a), w_dtype, _ptr(w), _ptr(b), bias_dtype, _ptr(asc),
+                               _ptr(wsc), out_dtype if out_dtype is not None else F64, _ptr(out), _ptr(val),
+                               nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    return out, val
 
 
 def qk_sumsq(x, n_heads, head_dim, dtype):

@@ -347,6 +347,38 @@ int oracle_qk_sumsq(int64_t T, int64_t n, int64_t d, int dtype, const void *x,
     return 0;
 }
 
+/*
+ * [qkv_cte] "Upstream behavior" and "Interface": the projection that produces
+ * Q|K|V, O[S, I] = A[S, H] @ W[H, I] (+ bias), with the ROW_MX dequantisation
+ * of the same page (a per-row activation scale and a per-output-channel weight
+ * scale) when the operands are FP8 codes:
+ *   O[s, i] = (sum_h A[s, h] * W[i, h]) * a_scale[s] * w_scale[i] + bias[i].
+ * W is passed as [I, H] (one row per output channel, the layout of a linear
+ * layer's weight). A scale or the bias may be NULL (1 and 0). The sum is
+ * evaluated in fp64 over h in order; O is rounded once to out_dtype and, if
+ * o_val is given, also returned exactly. Returns 0, or -1 on bad sizes.
+ */
+int oracle_linear(int64_t S, int64_t H, int64_t I, int a_dtype, const void *A, int w_dtype,
+                  const void *W, const void *bias, int bias_dtype, const double *a_scale,
+                  const double *w_scale, int out_dtype, void *O, double *o_val, int nthreads) {
+    if (S < 0 || H < 1 || I < 1) return -1;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t s = 0; s < S; s++) {
+        for (int64_t i = 0; i < I; i++) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; h++)
+                acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, i * H + h);
+            if (a_scale) acc *= a_scale[s];
+            if (w_scale) acc *= w_scale[i];
+            if (bias) acc += load(bias_dtype, bias, i);
+            if (O) store(out_dtype, O, s * I + i, acc);
+            if (o_val) o_val[s * I + i] = acc;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* (b) KvRmsNormRopeCache                                                     */
 /* ------------------------------------------------------------------------ */

@@ -50,6 +50,10 @@ MUTANTS = {
                                      "ss / (double)C + eps"),
     "sumsq_not_squared": ("            double v = load(dtype, x, t * n * d + c);\n            ss += v * v;",
                           "            double v = load(dtype, x, t * n * d + c);\n            ss += fabs(v);"),
+    "linear_weight_transposed": ("acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, i * H + h);",
+                                 "acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, (h * I + i) % (I * H));"),
+    "linear_bias_dropped": ("            if (bias) acc += load(bias_dtype, bias, i);\n", ""),
+    "linear_weight_scale_dropped": ("            if (w_scale) acc *= w_scale[i];\n", ""),
     "c_kv_from_raw_in_v1": ("c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : y[i];",
                             "c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : load(in_dtype, kv, kv0 + i);"),
 }

@@ -254,6 +254,52 @@ def test_permutation_makes_rotate_half_equal_interleaved_rope_and_keeps_scores()
     np.testing.assert_allclose(s_rh, s_int, rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- the projection
+
+def test_linear_golden_hand_cases():
+    for c in _golden("linear_hand.json")["cases"]:
+        _, v = oracle.linear(np.array(c["A"], float), np.array(c["W"], float), oracle.F64,
+                             bias=None if c["bias"] is None else np.array(c["bias"], float),
+                             a_scale=c["a_scale"], w_scale=c["w_scale"], nthreads=1)
+        np.testing.assert_allclose(v, c["out"], rtol=1e-15, atol=1e-15)
+
+
+def test_linear_matches_numpy_matmul_and_brute_force():
+    rng = np.random.default_rng(30)
+    S, H, I = 9, 37, 13
+    a = torch.from_numpy(rng.standard_normal((S, H))).to(torch.bfloat16)
+    w = torch.from_numpy(rng.standard_normal((I, H)) / 6).to(torch.bfloat16)
+    b = torch.from_numpy(rng.standard_normal(I)).to(torch.bfloat16)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    out, v = oracle.linear(bits(a), bits(w), oracle.BF16, bias=bits(b), out_dtype=oracle.BF16, nthreads=2)
+    ref = a.double().numpy() @ w.double().numpy().T + b.double().numpy()      # library matmul
+    np.testing.assert_allclose(v, ref, rtol=1e-12, atol=1e-12)
+    ad, wd, bd = a.double().tolist(), w.double().tolist(), b.double().tolist()
+    for s_ in range(S):
+        for i in range(I):
+            brute_v = sum(ad[s_][h] * wd[i][h] for h in range(H)) + bd[i]
+            assert abs(v[s_, i] - brute_v) <= 1e-12 * (1 + abs(brute_v))
+            assert out[s_, i] == brute.encode_nearest("bf16", brute_v)
+
+
+def test_linear_fp8_row_scaled_and_identity_weight():
+    rng = np.random.default_rng(31)
+    S, H, I = 5, 16, 7
+    ac = rng.integers(0, 256, (S, H)).astype(np.uint8)
+    wc = rng.integers(0, 256, (I, H)).astype(np.uint8)
+    ac[(ac & 0x7F) == 0x7F] = 0                       # no NaN codes
+    wc[(wc & 0x7F) == 0x7F] = 0
+    asc, wsc = rng.uniform(0.01, 0.1, S), rng.uniform(0.01, 0.1, I)
+    _, v = oracle.linear(ac, wc, oracle.E4M3FN, a_scale=asc, w_scale=wsc, nthreads=1)
+    av, wv = oracle.decode(oracle.E4M3FN, ac), oracle.decode(oracle.E4M3FN, wc)
+    np.testing.assert_allclose(v, (av @ wv.T) * asc[:, None] * wsc[None, :], rtol=1e-12, atol=1e-12)
+    # identity weight plus bias returns the input plus bias exactly
+    x = rng.standard_normal((4, 6))
+    bias = rng.standard_normal(6)
+    _, v = oracle.linear(x, np.eye(6), oracle.F64, bias=bias, nthreads=1)
+    np.testing.assert_array_equal(v, x + bias)
+
+
 def test_across_heads_brute_force_tiny():
     rng = np.random.default_rng(5)
     for (T, nq, nk, d, norm, rope) in [(3, 2, 2, 4, 1, 1), (2, 3, 1, 6, 1, 1), (2, 1, 0, 2, 1, 1),
