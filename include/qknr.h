@@ -22,6 +22,8 @@
  *   qknr_interleaved_to_rotate_half  -- the offline lane permutation that turns
  *       an interleaved-pair checkpoint (weights, bias, gamma, cos/sin) into the
  *       rotate-half layout the kernels use (qkv_cte Design section 2).
+ *   qknr_qkv_projection  -- the QKV projection GEMM (matrix cores) with step a
+ *       of the across-heads norm in its epilogue (qkv_cte Design section 1).
  *
  *   qknr_kv_rmsnorm_rope_cache  -- the MLA operator of the CANN page
  *       "KvRmsNormRopeCache": RmsNorm (formula 1), interleaveRope (formula 2),
@@ -119,6 +121,8 @@ extern "C" {
  *   eps              added to the mean of squares inside the square root.
  *   q_norm_channels, k_norm_channels   0, except in qknr_qk_apply_across_heads
  *       (the channel count of the whole segment over every rank).
+ *   sumsq_parts      0, except in qknr_qk_apply_across_heads (partial sums per
+ *       token and segment, see there).
  */
 typedef struct qknr_qk_args {
     int32_t dtype;
@@ -146,7 +150,7 @@ typedef struct qknr_qk_args {
     float eps;
     int32_t apply_norm;
     int32_t apply_rope;
-    int32_t reserved;
+    int32_t sumsq_parts;
     int64_t q_norm_channels;
     int64_t k_norm_channels;
 } qknr_qk_args;
@@ -178,6 +182,10 @@ int32_t qknr_qk_sumsq_across_heads(const qknr_qk_args *args, float *sumsq, hipSt
  * norm_channels = args->q_norm_channels (Q) / k_norm_channels (K), the
  * channel count of the whole segment (n_heads*d_head*tp, below 2^24); 0 means
  * this call's own n*d_head. apply_norm must be 1.
+ * With args->sumsq_parts = P > 1 the sum of a token's segment is itself the
+ * sum, in order, of P partial sums laid out [seg][P][B*S]
+ *   sum = sumsq[(seg*P + 0)*B*S + t] + ... + sumsq[(seg*P + P-1)*B*S + t]
+ * (the per-tile sums qknr_qkv_projection writes); 0 or 1 means one sum.
  */
 int32_t qknr_qk_apply_across_heads(const qknr_qk_args *args, const float *sumsq, hipStream_t stream);
 
@@ -220,6 +228,54 @@ typedef struct qknr_permute_args {
 } qknr_permute_args;
 
 int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream_t stream);
+
+/*
+ * The QKV projection with step a of the across-heads norm fused into its
+ * epilogue ("Kernel reference: qkv_cte": "Upstream behavior" for
+ * O[S, I] = A[S, H] @ W + bias with I = (n_q + 2*n_kv)*d_head, Design
+ * section 1 step a for sum(x^2) accumulated as the output tiles are copied
+ * out). On matrix cores (bf16 in, fp32 accumulation):
+ *   out[m, n] = RNE_bf16( sum_k a[m, k] * w[n, k] + bias[n] )
+ * for m < rows, n < out_features, and, when q_cols > 0, for every 128-column
+ * tile of the Q columns [0, q_cols) and of the K columns [q_cols, q_cols +
+ * k_cols), the per-row sum of the squares of the stored (rounded) values:
+ *   sumsq[(seg*P + part)*rows + m],  P = q_cols / 128, seg 0 = Q, 1 = K.
+ * qknr_qk_apply_across_heads with sumsq_parts = P then finishes the norm and
+ * RoPE on the Q and K columns of `out` (steps b-c, with the sums of all
+ * ranks when the heads are split).
+ *
+ * Arguments:
+ *   dtype            QKNR_BF16 (a, w, bias, out).
+ *   rows, in_features, out_features   M = B*S >= 0, K = H (multiple of 64),
+ *       N = I (multiple of 128).
+ *   a [rows, in_features] with row stride a_row_stride; w [out_features,
+ *       in_features] (a linear layer's weight) with row stride w_row_stride;
+ *       bias [out_features] or NULL; out [rows, out_features] with row stride
+ *       out_row_stride. Strides are elements, multiples of 8; pointers 16-byte
+ *       aligned. out must not overlap a, w or bias.
+ *   q_cols, k_cols   multiples of 128 with q_cols + k_cols <= out_features;
+ *       k_cols is 0 or q_cols. q_cols = 0: no sums (sumsq ignored).
+ *   sumsq            fp32 [(k_cols ? 2 : 1) * P * rows], 4-byte aligned.
+ */
+typedef struct qknr_proj_args {
+    int32_t dtype;
+    int32_t reserved;
+    int64_t rows;
+    int64_t in_features;
+    int64_t out_features;
+    const void *a;
+    int64_t a_row_stride;
+    const void *w;
+    int64_t w_row_stride;
+    const void *bias;
+    void *out;
+    int64_t out_row_stride;
+    int64_t q_cols;
+    int64_t k_cols;
+    float *sumsq;
+} qknr_proj_args;
+
+int32_t qknr_qkv_projection(const qknr_proj_args *args, hipStream_t stream);
 
 /*
  * (b) KvRmsNormRopeCache.

@@ -5,7 +5,7 @@ This module only marshals torch tensors into the ABI's argument structs
 (pointers, element strides, dtype codes) and passes torch's current HIP stream.
 Every step of both operators runs in the HIP kernels of libqknr.so; there is
 no fallback: importing fails loudly if the library has not been built
-(``python -m qk_rmsnorm_rope_amd._build``).
+(``python qk_rmsnorm_rope_amd/_build.py``).
 
 Entry points (same names as the C ABI, without the ``qknr_`` prefix):
 
@@ -16,6 +16,8 @@ Entry points (same names as the C ABI, without the ``qknr_`` prefix):
 * :func:`qk_norm_rope_per_head` -- the upstream per-head qk-norm + RoPE.
 * :func:`interleaved_to_rotate_half` -- the offline lane permutation of an
   interleaved-pair checkpoint (qkv_cte Design section 2).
+* :func:`qkv_projection` -- the QKV projection GEMM on matrix cores with the
+  across-heads norm's sums of squares in its epilogue (qkv_cte Design section 1).
 * :func:`kv_rmsnorm_rope_cache` -- the KvRmsNormRopeCache operator (CANN page,
   formulas 1-5), argument names as on that page's parameter table.
 """
@@ -32,7 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libqknr.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m qk_rmsnorm_rope_amd._build, or __graft_entry__.build())")
+        "(python qk_rmsnorm_rope_amd/_build.py, or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -61,8 +63,17 @@ class QkArgs(ctypes.Structure):
         ("out_batch_stride", _i64), ("out_token_stride", _i64), ("out_head_stride", _i64),
         ("q_gamma", _p), ("k_gamma", _p), ("cos", _p), ("sin", _p),
         ("rope_batch_stride", _i64), ("rope_token_stride", _i64),
-        ("eps", ctypes.c_float), ("apply_norm", _i32), ("apply_rope", _i32), ("reserved", _i32),
+        ("eps", ctypes.c_float), ("apply_norm", _i32), ("apply_rope", _i32), ("sumsq_parts", _i32),
         ("q_norm_channels", _i64), ("k_norm_channels", _i64),
+    ]
+
+
+class ProjArgs(ctypes.Structure):
+    """Mirror of ``qknr_proj_args``."""
+    _fields_ = [
+        ("dtype", _i32), ("reserved", _i32), ("rows", _i64), ("in_features", _i64), ("out_features", _i64),
+        ("a", _p), ("a_row_stride", _i64), ("w", _p), ("w_row_stride", _i64), ("bias", _p),
+        ("out", _p), ("out_row_stride", _i64), ("q_cols", _i64), ("k_cols", _i64), ("sumsq", _p),
     ]
 
 
@@ -102,6 +113,8 @@ _lib.qknr_qk_norm_rope_per_head.argtypes = [ctypes.POINTER(QkArgs), _p]
 _lib.qknr_qk_norm_rope_per_head.restype = _i32
 _lib.qknr_interleaved_to_rotate_half.argtypes = [ctypes.POINTER(PermuteArgs), _p]
 _lib.qknr_interleaved_to_rotate_half.restype = _i32
+_lib.qknr_qkv_projection.argtypes = [ctypes.POINTER(ProjArgs), _p]
+_lib.qknr_qkv_projection.restype = _i32
 _lib.qknr_kv_rmsnorm_rope_cache.argtypes = [ctypes.POINTER(KvArgs), _p]
 _lib.qknr_kv_rmsnorm_rope_cache.restype = _i32
 _lib.qknr_kv_validate.argtypes = [ctypes.POINTER(KvArgs)]
@@ -113,6 +126,7 @@ _lib.qknr_version.restype = _i32
 
 EXPORTED = ("qknr_qk_norm_rope_across_heads", "qknr_qk_validate", "qknr_qk_sumsq_across_heads",
             "qknr_qk_apply_across_heads", "qknr_qk_norm_rope_per_head", "qknr_interleaved_to_rotate_half",
+            "qknr_qkv_projection",
             "qknr_kv_rmsnorm_rope_cache", "qknr_kv_validate", "qknr_last_error", "qknr_version")
 
 
@@ -163,7 +177,7 @@ def _last_dim_contiguous(name, t):
 
 def qk_args(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
             apply_norm=True, apply_rope=True, per_head=False, q_norm_channels=0,
-            k_norm_channels=0) -> QkArgs:
+            k_norm_channels=0, sumsq_parts=0) -> QkArgs:
     """Fill ``qknr_qk_args`` from tensors.
 
     q: [B, S, n_q_heads, d] (any strides, d contiguous) -- e.g. a BSD projection
@@ -218,6 +232,7 @@ def qk_args(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
     a.eps = float(eps)
     a.apply_norm, a.apply_rope = int(bool(apply_norm)), int(bool(apply_rope))
     a.q_norm_channels, a.k_norm_channels = int(q_norm_channels), int(k_norm_channels)
+    a.sumsq_parts = int(sumsq_parts)
     a._keep = (q_gamma, k_gamma)  # keep contiguous copies alive
     return a
 
@@ -296,21 +311,33 @@ def qk_sumsq_across_heads(q, k=None, *, sumsq=None, stream=None):
     return sumsq
 
 
+def _sum_parts(sumsq, q, segs):
+    T = q.shape[0] * q.shape[1]
+    if sumsq.dtype != torch.float32 or not sumsq.is_contiguous():
+        raise ValueError("sumsq must be a contiguous float32 [segs, parts, B*S] (or [segs, B*S]) array")
+    if T == 0:
+        return 1
+    if sumsq.numel() % (segs * T):
+        raise ValueError("sumsq must hold segs * parts * B*S floats")
+    return sumsq.numel() // (segs * T)
+
+
 def qk_apply_across_heads(q, k, q_gamma, k_gamma, cos, sin, sumsq, *, eps, q_norm_channels,
                           k_norm_channels=0, q_out=None, k_out=None, apply_rope=True, stream=None):
     """Step c of a split across-heads norm on this rank's heads: ``sumsq``
-    [segs, B*S] holds the sums added over every rank, ``*_norm_channels`` the
-    whole segment's channel count (n_heads*d*tp). Gammas are this rank's slice
-    of the segment-wide gamma. Returns (q_out, k_out)."""
+    [segs, B*S] holds the sums added over every rank (or [segs, P, B*S]
+    partial sums, added in order, e.g. the projection's per-tile sums),
+    ``*_norm_channels`` the whole segment's channel count (n_heads*d*tp; 0:
+    this call's own). Gammas are this rank's slice of the segment-wide gamma.
+    Returns (q_out, k_out)."""
     if q_out is None:
         q_out = q
     if k is not None and k_out is None:
         k_out = k
-    segs = 2 if k is not None else 1
-    if sumsq.dtype != torch.float32 or sumsq.numel() != segs * q.shape[0] * q.shape[1] or not sumsq.is_contiguous():
-        raise ValueError("sumsq must be the contiguous float32 [segs, B*S] array of the sum pass")
+    parts = _sum_parts(sumsq, q, 2 if k is not None else 1)
     a = qk_args(q, k, q_gamma, k_gamma, cos, sin, eps=eps, q_out=q_out, k_out=k_out, apply_norm=True,
-                apply_rope=apply_rope, q_norm_channels=q_norm_channels, k_norm_channels=k_norm_channels)
+                apply_rope=apply_rope, q_norm_channels=q_norm_channels, k_norm_channels=k_norm_channels,
+                sumsq_parts=parts)
     with torch.cuda.device(q.device):
         _check(_lib.qknr_qk_apply_across_heads(ctypes.byref(a), _ptr(sumsq), _stream(q.device, stream)))
     return q_out, k_out
@@ -354,13 +381,68 @@ def prepare_qk_apply_across_heads(q, k, q_gamma, k_gamma, cos, sin, sumsq, *, ep
     """Prepared form of :func:`qk_apply_across_heads`."""
     q_out = q if q_out is None else q_out
     k_out = k if (k is not None and k_out is None) else k_out
-    segs = 2 if k is not None else 1
-    if sumsq.dtype != torch.float32 or sumsq.numel() != segs * q.shape[0] * q.shape[1] or not sumsq.is_contiguous():
-        raise ValueError("sumsq must be the contiguous float32 [segs, B*S] array of the sum pass")
+    parts = _sum_parts(sumsq, q, 2 if k is not None else 1)
     a = qk_args(q, k, q_gamma, k_gamma, cos, sin, eps=eps, q_out=q_out, k_out=k_out, apply_norm=True,
-                apply_rope=apply_rope, q_norm_channels=q_norm_channels, k_norm_channels=k_norm_channels)
+                apply_rope=apply_rope, q_norm_channels=q_norm_channels, k_norm_channels=k_norm_channels,
+                sumsq_parts=parts)
     return _prepared(_lib.qknr_qk_apply_across_heads, a, (_ptr(sumsq),), q.device, stream,
                      (q, k, q_out, k_out, q_gamma, k_gamma, cos, sin, sumsq))
+
+
+def proj_args(a, w, bias, out, *, q_cols=0, k_cols=0, sumsq=None) -> ProjArgs:
+    """Fill ``qknr_proj_args``: a [M, K], w [N, K] (a linear layer's weight),
+    bias [N] or None, out [M, N]; last dimensions contiguous."""
+    if a.dim() != 2 or w.dim() != 2 or out.dim() != 2:
+        raise ValueError("a, w and out must be 2-D ([M, K], [N, K], [M, N])")
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(out.shape) != (M, N) or (bias is not None and bias.numel() != N):
+        raise ValueError("shapes must be a [M, K], w [N, K], bias [N], out [M, N]")
+    for name, t in (("a", a), ("w", w), ("out", out)):
+        _last_dim_contiguous(name, t)
+    for t in (w, bias, out):
+        if t is not None and t.dtype != a.dtype:
+            raise TypeError("a, w, bias and out share one dtype")
+    r = ProjArgs()
+    r.dtype = _dtype(a)
+    r.rows, r.in_features, r.out_features = M, K, N
+    r.a, r.a_row_stride = _ptr(a), a.stride(0)
+    r.w, r.w_row_stride = _ptr(w), w.stride(0)
+    bias = bias.contiguous() if bias is not None else None
+    r.bias = _ptr(bias)
+    r.out, r.out_row_stride = _ptr(out), out.stride(0)
+    r.q_cols, r.k_cols = q_cols, k_cols
+    if q_cols:
+        segs = 2 if k_cols else 1
+        need = segs * (q_cols // 128) * M
+        if sumsq is None or sumsq.dtype != torch.float32 or not sumsq.is_contiguous() or sumsq.numel() != need:
+            raise ValueError(f"sumsq must be a contiguous float32 tensor of {need} elements")
+    r.sumsq = _ptr(sumsq) if q_cols else None
+    r._keep = (bias,)
+    return r
+
+
+def qkv_projection(a, w, bias=None, *, out=None, q_cols=0, k_cols=0, sumsq=None, stream=None):
+    """out = a @ w.T + bias on matrix cores (bf16), plus, for q_cols > 0, the
+    per-row sums of squares of each 128-column tile of the Q columns
+    [0, q_cols) and K columns [q_cols, q_cols + k_cols): fp32
+    [segs, q_cols // 128, M], ready for :func:`qk_apply_across_heads`.
+    Returns (out, sumsq)."""
+    M, N = a.shape[0], w.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=a.dtype, device=a.device)
+    if q_cols and sumsq is None:
+        sumsq = torch.empty(2 if k_cols else 1, q_cols // 128, M, dtype=torch.float32, device=a.device)
+    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq)
+    with torch.cuda.device(a.device):
+        _check(_lib.qknr_qkv_projection(ctypes.byref(r), _stream(a.device, stream)))
+    return out, sumsq
+
+
+def prepare_qkv_projection(a, w, bias=None, *, out, q_cols=0, k_cols=0, sumsq=None, stream=None):
+    """Prepared form of :func:`qkv_projection` (arguments marshalled once)."""
+    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq)
+    return _prepared(_lib.qknr_qkv_projection, r, (), a.device, stream, (a, w, bias, out, sumsq))
 
 
 def permute_args(src, dst, head_dim, *, dim=-1, first=0, n_heads=None, inverse=False) -> PermuteArgs:

@@ -11,6 +11,7 @@
 #include <climits>
 #include <cstdio>
 #include <string>
+#include <utility>
 
 #include "qknr.h"
 #include "launch.h"
@@ -91,6 +92,8 @@ int32_t qk_check(const qknr_qk_args *a, int mode, const float *sumsq, QkPlan *ou
     const int64_t k_total = a->k_norm_channels ? a->k_norm_channels : own_k;
     if (mode != qknr::QK_APPLY && (q_total != own_q || (has_k && k_total != own_k)))
         return fail(QKNR_INVALID_ARGUMENT, "q_norm_channels/k_norm_channels are for the apply pass only (else 0)");
+    if (a->sumsq_parts < 0 || (mode != qknr::QK_APPLY && a->sumsq_parts > 1) || a->sumsq_parts > 65536)
+        return fail(QKNR_INVALID_ARGUMENT, "sumsq_parts is 0 or 1 except in the apply pass (at most 65536)");
     if (q_total < own_q || (has_k && k_total < own_k) || q_total >= (1LL << 24) || k_total >= (1LL << 24))
         return fail(QKNR_INVALID_ARGUMENT,
                     "norm channel counts must cover this call's heads and stay below 2^24");
@@ -134,6 +137,9 @@ int32_t qk_check(const qknr_qk_args *a, int mode, const float *sumsq, QkPlan *ou
     const int64_t max_heads = a->n_q_heads > a->n_k_heads ? a->n_q_heads : a->n_k_heads;
     const int64_t span_in = ((max_heads - 1) * a->in_head_stride + a->head_dim) * es;
     const int64_t span_out = sums_only ? 0 : ((max_heads - 1) * a->out_head_stride + a->head_dim) * es;
+    if (mode == qknr::QK_APPLY && a->sumsq_parts > 1 &&
+        (int64_t)a->sumsq_parts * (has_k ? 2 : 1) * (tokens > 0 ? tokens : 1) >= (1LL << 40))
+        return fail(QKNR_INVALID_ARGUMENT, "sumsq array too large");
     if (tokens >= (1LL << 31) || span_in >= (1LL << 32) || span_out >= (1LL << 32))
         return fail(QKNR_UNSUPPORTED, "more than 2^31 tokens, or one token's heads span 4 GiB or more");
 
@@ -157,6 +163,7 @@ int32_t qk_check(const qknr_qk_args *a, int mode, const float *sumsq, QkPlan *ou
     p.k_channels = (float)(has_k ? k_total : a->head_dim);
     p.eps = a->eps;
     p.sumsq = const_cast<float *>(sumsq);
+    p.sum_parts = a->sumsq_parts > 1 ? a->sumsq_parts : 1;
     int J = qknr::qk_plan(p, vec);
     if (J < 0 && vec == wide && fits(narrow)) {
         vec = narrow;
@@ -407,6 +414,54 @@ int32_t qknr_qk_apply_across_heads(const qknr_qk_args *args, const float *sumsq,
 
 int32_t qknr_qk_norm_rope_per_head(const qknr_qk_args *args, hipStream_t stream) {
     return qk_run(args, qknr::QK_PER_HEAD, nullptr, stream);
+}
+
+int32_t qknr_qkv_projection(const qknr_proj_args *a, hipStream_t stream) {
+    if (!a) return fail(QKNR_INVALID_ARGUMENT, "args is NULL");
+    if (a->dtype != QKNR_BF16) return fail(QKNR_UNSUPPORTED, "the projection is built for QKNR_BF16 only");
+    if (a->rows < 0 || a->in_features < 1 || a->out_features < 1)
+        return fail(QKNR_INVALID_ARGUMENT, "rows >= 0, in_features >= 1, out_features >= 1");
+    if (a->in_features % 64 || a->out_features % 128)
+        return fail(QKNR_UNSUPPORTED, "in_features must be a multiple of 64 and out_features of 128");
+    if (a->q_cols < 0 || a->k_cols < 0 || a->q_cols % 128 || a->k_cols % 128 ||
+        a->q_cols + a->k_cols > a->out_features || (a->k_cols && a->k_cols != a->q_cols) ||
+        (a->k_cols && !a->q_cols))
+        return fail(QKNR_INVALID_ARGUMENT,
+                    "q_cols, k_cols: multiples of 128, k_cols 0 or q_cols, q_cols + k_cols <= out_features");
+    if (a->a_row_stride < a->in_features || a->w_row_stride < a->in_features ||
+        a->out_row_stride < a->out_features)
+        return fail(QKNR_INVALID_ARGUMENT, "row strides must cover a row");
+    if (a->a_row_stride % 8 || a->w_row_stride % 8 || a->out_row_stride % 8)
+        return fail(QKNR_UNSUPPORTED, "row strides must be multiples of 8 elements");
+    if (a->rows == 0) return ok();
+    if (!a->a || !a->w || !a->out) return fail(QKNR_INVALID_ARGUMENT, "a, w and out are required");
+    if (!aligned(a->a, 16) || !aligned(a->w, 16) || !aligned(a->out, 16) || !aligned(a->bias, 2))
+        return fail(QKNR_UNSUPPORTED, "a, w and out must be 16-byte aligned");
+    if (a->q_cols && (!a->sumsq || !aligned(a->sumsq, 4)))
+        return fail(QKNR_INVALID_ARGUMENT, "sumsq (4-byte aligned) is required when q_cols > 0");
+    if (a->rows >= (1LL << 31) || a->out_features >= (1LL << 31) || a->in_features >= (1LL << 31))
+        return fail(QKNR_UNSUPPORTED, "sizes of 2^31 or more");
+    const int64_t tiles = ((a->rows + 255) / 256) * (a->out_features / 128);
+    if (tiles >= (1LL << 31)) return fail(QKNR_UNSUPPORTED, "more than 2^31 tiles");
+    auto span = [](const void *p, int64_t rows, int64_t stride, int64_t cols) {
+        const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+        return std::pair<uintptr_t, uintptr_t>(b, b + (uintptr_t)(((rows - 1) * stride + cols) * 2));
+    };
+    const auto o = span(a->out, a->rows, a->out_row_stride, a->out_features);
+    const std::pair<uintptr_t, uintptr_t> ins[] = {span(a->a, a->rows, a->a_row_stride, a->in_features),
+                                                   span(a->w, a->out_features, a->w_row_stride, a->in_features),
+                                                   a->bias ? span(a->bias, 1, 0, a->out_features)
+                                                           : std::pair<uintptr_t, uintptr_t>(0, 0)};
+    for (const auto &r : ins)
+        if (r.first < o.second && o.first < r.second) return fail(QKNR_INVALID_ARGUMENT, "out overlaps an input");
+    qknr::ProjParams p{};
+    p.a = a->a; p.w = a->w; p.bias = a->bias; p.o = a->out; p.sumsq = a->sumsq;
+    p.m = a->rows; p.n = a->out_features; p.k = a->in_features;
+    p.lda = a->a_row_stride; p.ldw = a->w_row_stride; p.ldo = a->out_row_stride;
+    p.q_cols = a->q_cols; p.k_cols = a->k_cols; p.parts = a->q_cols / 128;
+    hipError_t e = qknr::proj_launch(p, stream);
+    if (e != hipSuccess) return fail(QKNR_DEVICE_ERROR, "launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *a, hipStream_t stream) {

@@ -69,7 +69,8 @@ struct QkParams {
     int32_t segs;              // 2 with a K segment, 1 for Q only
     int32_t apply_norm, apply_rope;
     float q_channels, k_channels, eps;   // RMS denominators (QK_PER_HEAD: head_dim)
-    float *sumsq;              // QK_SUMSQ output / QK_APPLY input, fp32 [segs, tokens]
+    float *sumsq;              // QK_SUMSQ output [segs, tokens] / QK_APPLY input [segs, sum_parts, tokens]
+    int32_t sum_parts;         // QK_APPLY: partial sums per token and segment, added in order
 };
 
 // Fills the lane geometry of p for chunk width `vec`; returns J > 0 or -1.
@@ -93,6 +94,23 @@ struct PermuteParams {
 };
 // unit: bytes moved per access (1, 2, 4, 8 or 16), dividing the bytes per index.
 hipError_t permute_launch(const PermuteParams &p, int unit, hipStream_t stream);
+
+// QKV projection O[m, n] = sum_k A[m, k] W[n, k] + bias[n] (bf16 in and out,
+// fp32 accumulation) with per-row partial sums of squares of the Q columns
+// [0, q_cols) and the K columns [q_cols, q_cols + k_cols) of each 128-column
+// tile: sumsq[(seg*parts + part)*m + row], parts = q_cols / 128.
+struct ProjParams {
+    const void *a;             // [m, k], row stride lda
+    const void *w;             // [n, k], row stride ldw
+    const void *bias;          // [n] or nullptr
+    void *o;                   // [m, n], row stride ldo
+    float *sumsq;
+    int64_t m, n, k, lda, ldw, ldo;
+    int64_t q_cols, k_cols, parts;
+    uint32_t tiles_m, tiles_n; // set by the launcher
+};
+// n a multiple of 128, k of 64; leading dimensions multiples of 8 elements.
+hipError_t proj_launch(ProjParams &p, hipStream_t stream);
 
 // (b) KvRmsNormRopeCache
 enum CacheCode : int32_t { CODE_SAME = 0, CODE_INT8 = 1, CODE_E4M3FN = 2, CODE_E5M2 = 3 };

@@ -204,7 +204,10 @@ __global__ __launch_bounds__(256) void qk_kernel(QkParams p) {
         }
     } else if constexpr (MODE == QK_APPLY) {
         if (norm && unit_ok) {
-            const float ss = p.sumsq[(uint32_t)seg * p.tokens + t];
+            // the segment's partial sums (one per rank, or per projection tile), in order
+            const float *sp = p.sumsq + (uint64_t)seg * (uint32_t)p.sum_parts * p.tokens + t;
+            float ss = 0.0f;
+            for (int i = 0; i < p.sum_parts; i++) ss += sp[(uint64_t)i * p.tokens];
             r = rsqrtf(ss / (seg ? p.k_channels : p.q_channels) + p.eps);
         }
     } else {   // QK_PER_HEAD

@@ -51,7 +51,8 @@ def test_header_constants_match_binding():
 
 def test_struct_layouts_match_c(tmp_path):
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "qknr.h"', "int main(void) {"]
-    structs = (("qknr_qk_args", Q.QkArgs), ("qknr_kv_args", Q.KvArgs), ("qknr_permute_args", Q.PermuteArgs))
+    structs = (("qknr_qk_args", Q.QkArgs), ("qknr_kv_args", Q.KvArgs), ("qknr_permute_args", Q.PermuteArgs),
+               ("qknr_proj_args", Q.ProjArgs))
     for cname, py in structs:
         lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
         for f, _ in py._fields_:
@@ -181,6 +182,49 @@ def test_permute_rejects_invalid_arguments(kw):
 def test_permute_empty_tensor_is_a_noop():
     assert int(Q._lib.qknr_interleaved_to_rotate_half(ctypes.byref(_perm(outer=0, src=None, dst=None)),
                                                        None)) == Q.OK
+
+
+def _proj(**kw):
+    a = Q.ProjArgs()
+    a.dtype, a.rows, a.in_features, a.out_features = Q.BF16, 300, 128, 384
+    a.a, a.a_row_stride = 0x100000, 128
+    a.w, a.w_row_stride = 0x200000, 128
+    a.bias = None
+    a.out, a.out_row_stride = 0x400000, 384
+    a.q_cols, a.k_cols, a.sumsq = 128, 128, 0x800000
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(dtype=Q.F32), Q.UNSUPPORTED),
+    (dict(in_features=100, a_row_stride=104, w_row_stride=104), Q.UNSUPPORTED),    # K not a multiple of 64
+    (dict(out_features=300, out_row_stride=304), Q.UNSUPPORTED),                   # N not a multiple of 128
+    (dict(q_cols=64, k_cols=64), Q.INVALID_ARGUMENT),
+    (dict(q_cols=128, k_cols=256), Q.INVALID_ARGUMENT),                              # k_cols must be 0 or q_cols
+    (dict(q_cols=256, k_cols=256), Q.INVALID_ARGUMENT),                              # beyond out_features
+    (dict(sumsq=None), Q.INVALID_ARGUMENT),
+    (dict(sumsq=0x800002), Q.INVALID_ARGUMENT),
+    (dict(a_row_stride=120), Q.INVALID_ARGUMENT),                                    # shorter than a row
+    (dict(out=0x100000 + 64), Q.INVALID_ARGUMENT),                                   # out overlaps a
+    (dict(a=0x100008), Q.UNSUPPORTED),                                               # not 16-byte aligned
+    (dict(rows=-1), Q.INVALID_ARGUMENT),
+])
+def test_projection_rejects_invalid_arguments(kw, code):
+    assert int(Q._lib.qknr_qkv_projection(ctypes.byref(_proj(**kw)), None)) == code
+    assert Q.last_error() != ""
+
+
+def test_projection_zero_rows_is_a_noop():
+    assert int(Q._lib.qknr_qkv_projection(ctypes.byref(_proj(rows=0, a=None, w=None, out=None)), None)) == Q.OK
+
+
+def test_apply_partial_sums_only_in_the_apply_pass():
+    a = _qk()
+    a.sumsq_parts = 4
+    assert Q.qk_validate(a) == Q.INVALID_ARGUMENT
+    assert _call("qknr_qk_norm_rope_per_head", a) == Q.INVALID_ARGUMENT
 
 
 def test_qk_too_many_heads_is_unsupported():

@@ -1,0 +1,148 @@
+"""GPU parity of qknr_qkv_projection (the QKV GEMM with step a of the
+across-heads norm in its epilogue) and of the projection -> apply path.
+
+Cases: a small ragged case (300 rows: two row-tiles, the second partial;
+3 column tiles: Q, K and V) with bias; no bias and no sums; the Wan2.2 width
+(hidden 5120 -> 15360 columns, 40 + 40 + 40 heads) at 1000 rows with sampled
+rows against the oracle, the per-tile sums against fp64 sums of the stored
+outputs, and the projection -> apply path against the oracle's across-heads
+operator on the stored Q|K; the full S = 75600 case on sampled rows; two runs
+bit-identical.
+
+The projection's outputs are checked against the oracle's exact fp64 values
+at the bf16 bar; the sums against fp64 sums of the kernel's own stored bf16
+outputs (the values the apply pass reads), so each check has one rounding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import check_float, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import qk_rmsnorm_rope_amd as lib
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return lib
+
+
+def _oracle_rows(d, rows, with_bias=True):
+    a = host(d["a"][rows])
+    _, v = oracle.linear(a, host(d["w"]), oracle.BF16, bias=host(d["bias"]) if with_bias else None)
+    return v
+
+
+def _check_sums(out, sumsq, q_cols, k_cols, what):
+    o = out.float().double().cpu().numpy()
+    parts = q_cols // 128
+    got = sumsq.cpu().double().numpy().reshape(-1, parts, out.shape[0])
+    for seg, c0 in ((0, 0), (1, q_cols)):
+        if seg == 1 and not k_cols:
+            continue
+        for p in range(parts):
+            ref = (o[:, c0 + p * 128: c0 + (p + 1) * 128] ** 2).sum(1)
+            np.testing.assert_allclose(got[seg, p], ref, rtol=1e-5, atol=1e-6, err_msg=f"{what} seg {seg} part {p}")
+
+
+def _small(seq=300, hidden=256, heads=1, seed=5):
+    return W.make_qkv_projection(W.WAN22_QKV_PROJ, device="cuda", seq=seq, hidden=hidden, n_q_heads=heads,
+                                 n_k_heads=heads, seed=seed)
+
+
+def test_small_ragged_with_bias_and_sums(Q):
+    d = _small()
+    out, s = Q.qkv_projection(d["a"], d["w"], d["bias"], q_cols=128, k_cols=128)
+    torch.cuda.synchronize()
+    rows = np.arange(300)
+    check_float(out, _oracle_rows(d, rows), "small/out")
+    _check_sums(out, s, 128, 128, "small")
+
+
+def test_no_bias_no_sums_and_q_only_sums(Q):
+    d = _small(seq=77, hidden=192, heads=2, seed=6)
+    out, s = Q.qkv_projection(d["a"], d["w"], None)
+    torch.cuda.synchronize()
+    assert s is None
+    check_float(out, _oracle_rows(d, np.arange(77), with_bias=False), "nobias/out")
+    out2, s2 = Q.qkv_projection(d["a"], d["w"], d["bias"], q_cols=256)
+    torch.cuda.synchronize()
+    assert tuple(s2.shape) == (1, 2, 77)
+    _check_sums(out2, s2, 256, 0, "q-only")
+
+
+def test_strided_operands_and_output(Q):
+    """Row strides larger than the rows: a slice of a wider activation buffer
+    and an output written into a wider buffer."""
+    d = _small(seq=130, hidden=128, heads=1, seed=7)
+    wide = torch.zeros(130, 128 + 64, dtype=torch.bfloat16, device="cuda")
+    wide[:, 32:160] = d["a"]
+    a = wide[:, 32:160]
+    big = torch.full((130, 384 + 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = big[:, 64:448]
+    Q.qkv_projection(a, d["w"], d["bias"], out=o)
+    torch.cuda.synchronize()
+    check_float(o, _oracle_rows(d, np.arange(130)), "strided/out")
+    assert bool((big[:, :64] == 7.0).all()) and bool((big[:, 448:] == 7.0).all())
+
+
+def _wan(seq):
+    return W.make_qkv_projection(W.WAN22_QKV_PROJ, device="cuda", seq=seq)
+
+
+def _apply(Q, d, out, s):
+    nq, nk, hd = 40, 40, 128
+    q = out[:, : nq * hd].unflatten(-1, (nq, hd)).unsqueeze(0)
+    k = out[:, nq * hd: (nq + nk) * hd].unflatten(-1, (nk, hd)).unsqueeze(0)
+    qi, ki = q.clone(), k.clone()
+    Q.qk_apply_across_heads(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"], s, eps=d["eps"],
+                            q_norm_channels=0)
+    torch.cuda.synchronize()
+    return qi, ki, q, k
+
+
+def test_wan_width_projection_sums_and_apply(Q):
+    S = 1000
+    d = _wan(S)
+    out, s = Q.qkv_projection(d["a"], d["w"], d["bias"], q_cols=5120, k_cols=5120)
+    torch.cuda.synchronize()
+    assert tuple(s.shape) == (2, 40, S)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(S - 8, S),
+                                     np.random.default_rng(3).choice(S, 48, replace=False)]))
+    check_float(out[torch.as_tensor(rows, device="cuda")], _oracle_rows(d, rows), "wan1000/out")
+    _check_sums(out, s, 5120, 5120, "wan1000")
+    qi, ki, q, k = _apply(Q, d, out, s)
+    T = S
+    _, _, rq, rk = oracle.qk_norm_rope_across_heads(
+        host(qi.reshape(T, -1)), host(ki.reshape(T, -1)), host(d["q_gamma"]), host(d["k_gamma"]),
+        host(d["cos"][0]), host(d["sin"][0]), d["eps"], 40, 40, 128, oracle.BF16)
+    check_float(q, rq.reshape(q.shape), "wan1000/apply-q")
+    check_float(k, rk.reshape(k.shape), "wan1000/apply-k")
+    # V columns are the projection's, untouched by the apply pass
+    check_float(out[torch.as_tensor(rows, device="cuda"), 10240:],
+                _oracle_rows(d, rows)[:, 10240:], "wan1000/v")
+
+
+def test_wan_full_size_sampled_and_deterministic(Q):
+    S = 75600
+    d = _wan(S)
+    out, s = Q.qkv_projection(d["a"], d["w"], d["bias"], q_cols=5120, k_cols=5120)
+    out2 = torch.empty_like(out)
+    s2 = torch.empty_like(s)
+    Q.qkv_projection(d["a"], d["w"], d["bias"], out=out2, q_cols=5120, k_cols=5120, sumsq=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(s, s2)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(S - 4, S),
+                                     np.random.default_rng(4).choice(S, 24, replace=False)]))
+    idx = torch.as_tensor(rows, device="cuda")
+    check_float(out[idx], _oracle_rows(d, rows), "full/out")
+    o = out[idx].float().double().cpu().numpy()
+    got = s[:, :, idx].cpu().double().numpy()
+    for seg, c0 in ((0, 0), (1, 5120)):
+        ref = (o[:, c0: c0 + 5120] ** 2).reshape(len(rows), 40, 128).sum(-1).T
+        np.testing.assert_allclose(got[seg], ref, rtol=1e-5, atol=1e-6)

@@ -159,6 +159,57 @@ def make_across_heads(cfg: AcrossHeadsConfig, device="cpu", **override):
                 n_k_heads=cfg.n_k_heads, head_dim=d)
 
 
+@dataclasses.dataclass(frozen=True)
+class QkvProjectionConfig:
+    """The projection that produces Q|K|V ahead of the across-heads norm:
+    A [S, hidden] @ W^T with W [(n_q + 2 n_k) * d, hidden], plus bias."""
+    name: str
+    seq: int
+    hidden: int
+    n_q_heads: int
+    n_k_heads: int
+    head_dim: int
+    dtype: torch.dtype
+    eps: float
+    seed: int
+
+
+# Wan2.2-A14B self-attention: hidden 5120, 40 heads of 128 for Q, K and V.
+WAN22_QKV_PROJ = QkvProjectionConfig(
+    name="wan22_qkv_projection", seq=75600, hidden=5120, n_q_heads=40, n_k_heads=40,
+    head_dim=128, dtype=torch.bfloat16, eps=1e-6, seed=1006)
+
+
+def make_qkv_projection(cfg: QkvProjectionConfig, device="cpu", **override):
+    """Draw the projection's operands: activations A [S, hidden] ~ N(0, 1)
+    (post-modulation hidden states), weight W [I, hidden] ~ N(0, 1/hidden) so
+    that outputs are ~N(0, 1), bias [I] ~ N(0, 0.1^2); plus the norm's gammas
+    ~U(0.5, 1.5) and the Wan 3D rotate-half tables for the sequence (1D tables
+    when the sequence does not fill the 21x45x80 grid). Draw order: A, W,
+    bias, q_gamma, k_gamma."""
+    cfg = dataclasses.replace(cfg, **override) if override else cfg
+    g = _gen(cfg.seed, device)
+    d = cfg.head_dim
+    I = (cfg.n_q_heads + 2 * cfg.n_k_heads) * d
+    a = _normal((cfg.seq, cfg.hidden), g, device, cfg.dtype)
+    w = (torch.randn((I, cfg.hidden), generator=g, device=device) / math.sqrt(cfg.hidden)).to(cfg.dtype)
+    bias = (torch.randn((I,), generator=g, device=device) * 0.1).to(cfg.dtype)
+    q_gamma = _uniform((cfg.n_q_heads * d,), 0.5, 1.5, g, device, cfg.dtype)
+    k_gamma = _uniform((cfg.n_k_heads * d,), 0.5, 1.5, g, device, cfg.dtype)
+    if cfg.seq == 21 * 45 * 80:
+        cos, sin = wan_3d_table(21, 45, 80, d, device=device)
+    else:
+        cos, sin = rotate_half_table_1d(torch.arange(cfg.seq, device=device), d)
+    return dict(cfg=cfg, a=a, w=w, bias=bias, q_gamma=q_gamma, k_gamma=k_gamma,
+                cos=cos.to(cfg.dtype)[None].contiguous(), sin=sin.to(cfg.dtype)[None].contiguous(),
+                eps=cfg.eps, out_features=I)
+
+
+def flops_qkv_projection(cfg: QkvProjectionConfig) -> int:
+    """Multiply-adds of the projection counted as 2 flops each."""
+    return 2 * cfg.seq * cfg.hidden * (cfg.n_q_heads + 2 * cfg.n_k_heads) * cfg.head_dim
+
+
 # ---------------------------------------------------------------------------
 # KV RMSNorm + RoPE + cache workloads
 # ---------------------------------------------------------------------------
