@@ -14,10 +14,13 @@ PA_BLK_BNSD indexing, V1 decode quantised, also as a HIP-graph replay, V2
 split) timed the same way, cold (L2 and MALL evicted by reading 1 GiB before
 every launch) and hot, and the other forms of the QK operator on the Wan2.2
 shape: per-head norm, and the two passes of the across-heads norm split over
-tp = 4 ranks at one rank's share (10 + 10 heads).
+tp = 4 ranks at one rank's share (10 + 10 heads); and the QKV projection
+(75600 x 5120 -> 15360, bf16 matrix cores) with the norm's sums in its
+epilogue followed by the apply pass, next to the unfused pipeline of a
+library GEMM (torch.addmm, hipBLASLt) and the single-pass epilogue kernel.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv] [--no-forms]
-       python bench.py --profile {across,per_head,split_sumsq,split_apply,kv_v1_prefill,
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv] [--no-forms] [--no-proj]
+       python bench.py --profile {across,per_head,split_sumsq,split_apply,proj,kv_v1_prefill,
                                   kv_v1_decode,kv_v2,copy}
        (a short fixed run of one kernel, for rocprofv3 counter collection)
        python bench.py --summarize DIR
@@ -37,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 matrix-core peak
 METRIC = "achieved HBM GB/s (% of MI355X peak) + tokens/s for fused norm+RoPE(+cache)"
 KERNEL_SOURCES = {
     "qk_across_heads": ["qk_rmsnorm_rope_amd/csrc/qk_across_heads.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
@@ -45,6 +49,7 @@ KERNEL_SOURCES = {
                     "qk_rmsnorm_rope_amd/csrc/device_common.h"],
     "qk_split": ["qk_rmsnorm_rope_amd/csrc/qk_split.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
                  "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+    "qkv_proj": ["qk_rmsnorm_rope_amd/csrc/qkv_proj.hip", "qk_rmsnorm_rope_amd/csrc/device_common.h"],
     "kv_rmsnorm_rope_cache": ["qk_rmsnorm_rope_amd/csrc/kv_rmsnorm_rope_cache.hip",
                               "qk_rmsnorm_rope_amd/csrc/device_common.h"],
 }
@@ -80,9 +85,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-kv", action="store_true", help="skip the KvRmsNormRopeCache workloads")
     ap.add_argument("--no-forms", action="store_true", help="skip the per-head and split forms of (a)")
+    ap.add_argument("--no-proj", action="store_true", help="skip the QKV projection")
     ap.add_argument("--cold-iters", type=int, default=30)
     ap.add_argument("--profile", default=None,
-                    choices=["across", "per_head", "split_sumsq", "split_apply", "kv_v1_prefill",
+                    choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "kv_v1_prefill",
                              "kv_v1_decode", "kv_v2", "copy"])
     ap.add_argument("--summarize", default=None, metavar="DIR")
     return ap.parse_args()
@@ -162,6 +168,59 @@ def forms_measure(torch, W, Q, d, flush, cold_iters):
     res["split_apply"]["workload"] = ("the same rank's apply pass: sums of all ranks, 5120-channel RMS, "
                                       "gamma slices, RoPE, out of place")
     res["split_two_pass_us_hot"] = round(res["split_sumsq"]["us_hot_mean"] + res["split_apply"]["us_hot_mean"], 3)
+    return res
+
+
+def proj_setup(torch, W, Q):
+    """The Wan2.2 QKV projection with the norm's sums (fused path), its apply
+    pass, and the pieces of the unfused reference pipeline."""
+    cfg = W.WAN22_QKV_PROJ
+    d = W.make_qkv_projection(cfg, device="cuda")
+    S, I, hd = cfg.seq, d["out_features"], cfg.head_dim
+    nq, nk = cfg.n_q_heads, cfg.n_k_heads
+    out = torch.empty(S, I, dtype=cfg.dtype, device="cuda")
+    sums = torch.empty(2, S, nq * hd // 128, dtype=torch.float32, device="cuda")
+    proj = Q.prepare_qkv_projection(d["a"], d["w"], d["bias"], out=out, q_cols=nq * hd, k_cols=nk * hd,
+                                    sumsq=sums)
+    q = out[:, : nq * hd].unflatten(-1, (nq, hd)).unsqueeze(0)
+    k = out[:, nq * hd: (nq + nk) * hd].unflatten(-1, (nk, hd)).unsqueeze(0)
+    qkv_n = torch.empty(1, S, (nq + nk) * hd, dtype=cfg.dtype, device="cuda")   # normalised Q|K
+    qo = qkv_n[..., : nq * hd].unflatten(-1, (nq, hd))
+    ko = qkv_n[..., nq * hd:].unflatten(-1, (nk, hd))
+    apply = Q.prepare_qk_apply_across_heads(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"], sums,
+                                            eps=cfg.eps, q_norm_channels=0, q_out=qo, k_out=ko)
+    fused_epilogue = Q.prepare_qk_norm_rope_across_heads(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"],
+                                                         eps=cfg.eps, q_out=qo, k_out=ko)
+    out_lib = torch.empty_like(out)
+    lib_gemm = lambda: torch.addmm(d["bias"], d["a"], d["w"].t(), out=out_lib)
+    return cfg, d, proj, apply, fused_epilogue, lib_gemm
+
+
+def proj_measure(torch, W, Q):
+    cfg, d, proj, apply, epilogue, lib_gemm = proj_setup(torch, W, Q)
+    flops = W.flops_qkv_projection(cfg)
+    S, hd = cfg.seq, cfg.head_dim
+    e = 2
+    apply_bytes = S * (2 * (cfg.n_q_heads + cfg.n_k_heads) * hd * e + 2 * hd * e + 2 * 40 * 4) \
+        + (cfg.n_q_heads + cfg.n_k_heads) * hd * e
+    res = {"workload": "Wan2.2 self-attention QKV projection: A [75600, 5120] @ W^T, W [15360, 5120], "
+                       "+ bias, bf16 in/out, fp32 accumulation; then the across-heads norm + RoPE of Q|K",
+           "flops": flops}
+    for name, fn, it in (("projection_with_sums", proj, 10), ("apply_pass", apply, 30),
+                         ("library_gemm_torch_addmm", lib_gemm, 10), ("single_pass_epilogue", epilogue, 30)):
+        for _ in range(3):
+            fn()
+        res[name + "_us"] = round(time_hot(torch, fn, it), 1)
+    p_us, lib_us = res["projection_with_sums_us"], res["library_gemm_torch_addmm_us"]
+    res["projection_tflops"] = round(flops / p_us / 1e6, 1)
+    res["projection_frac_bf16_peak"] = round(flops / p_us / 1e6 / PEAK_BF16_TFLOPS, 4)
+    res["library_gemm_tflops"] = round(flops / lib_us / 1e6, 1)
+    res["apply_pass_gbs"] = round(apply_bytes / res["apply_pass_us"] / 1e3, 1)
+    res["fused_pipeline_us"] = round(p_us + res["apply_pass_us"], 1)
+    res["unfused_library_pipeline_us"] = round(lib_us + res["single_pass_epilogue_us"], 1)
+    res["roofline"] = {"bound": "mfma", "achieved": res["projection_tflops"], "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": res["projection_frac_bf16_peak"],
+                       "traffic": measured_traffic("qkv_proj", "wan22_qkv_projection")}
     return res
 
 
@@ -337,6 +396,8 @@ def profile_run(torch, W, Q, which):
         cfg, d, step = across_setup(torch, W, Q)
     elif which in ("per_head", "split_sumsq", "split_apply"):
         step = forms_setup(torch, W, Q, which)
+    elif which == "proj":
+        step = proj_setup(torch, W, Q)[2]
     else:
         cfg = {"kv_v1_prefill": W.MLA_V1_PREFILL, "kv_v1_decode": W.MLA_V1_DECODE_QUANT,
                "kv_v2": W.MLA_V2_SPLIT}[which]
@@ -355,6 +416,7 @@ PROFILE_WORKLOADS = {
     "per_head": ("qk_per_head", "wan22_per_head", ", 1>(qknr::QkParams)"),
     "split_sumsq": ("qk_split", "wan22_split_sumsq", ", 2>(qknr::QkParams)"),
     "split_apply": ("qk_split", "wan22_split_apply", ", 3>(qknr::QkParams)"),
+    "proj": ("qkv_proj", "wan22_qkv_projection", "qkv_proj_bf16_kernel"),
     "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v1_decode": ("kv_rmsnorm_rope_cache", "mla_v1_decode_quant", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v2": ("kv_rmsnorm_rope_cache", "mla_v2_split", "kv_rmsnorm_rope_cache_kernel"),
@@ -404,7 +466,10 @@ def summarize(prof_dir):
         f, w = pick(fv, needle), pick(wv, needle)
         if f is None or w is None:
             continue
-        if wname == "wan22_per_head":
+        if wname == "wan22_qkv_projection":
+            c = W.WAN22_QKV_PROJ      # compulsory bytes: A, W, bias read once; out, sums written once
+            alg = 2 * (c.seq * c.hidden + 15360 * c.hidden + 15360 + c.seq * 15360) + 4 * 2 * 40 * c.seq
+        elif wname == "wan22_per_head":
             alg = W.algorithmic_bytes_per_head(W.WAN22_SELF_ATTN)
         elif wname.startswith("wan22_split"):
             alg = W.algorithmic_bytes_qk_split(W.WAN22_SELF_ATTN, 4)[0 if wname.endswith("sumsq") else 1]
@@ -439,13 +504,14 @@ def summarize(prof_dir):
             "python -u bench.py --profile <w>\n"
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write_<w> -o p -- "
             "python -u bench.py --profile <w>\n"
-            "  for <w> in across per_head split_sumsq split_apply kv_v1_prefill kv_v1_decode kv_v2 copy; then "
+            "  for <w> in across per_head split_sumsq split_apply proj kv_v1_prefill kv_v1_decode kv_v2 copy; then "
             "python bench.py --summarize <dir>\n")
     calib = (f"calibration (copy of 1 GiB, __amd_rocclr_copyBuffer): FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE "
              f"{cw:.1f} KiB -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}\n")
     names = {"qk_across_heads": "qk_across_heads_wan22_s75600.txt",
              "qk_per_head": "qk_per_head_wan22_s75600.txt",
              "qk_split": "qk_split_passes_wan22_tp4_shard.txt",
+             "qkv_proj": "qkv_projection_wan22_s75600.txt",
              "kv_rmsnorm_rope_cache": "kv_rmsnorm_rope_cache_mla_workloads.txt"}
     for kernel, lines in lines_by_kernel.items():
         with open(os.path.join(ROOT, "profiles", names[kernel]), "w") as ftxt:
@@ -523,6 +589,8 @@ def main():
         result["qk_forms"] = forms_measure(torch, W, Q, d, flush, args.cold_iters)
     if not args.no_kv:
         result["kv_rmsnorm_rope_cache"] = kv_measure(torch, W, Q, flush, args.cold_iters)
+    if not args.no_proj:
+        result["qkv_projection"] = proj_measure(torch, W, Q)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, W, d, cfg)
     print(json.dumps(result))

@@ -183,9 +183,11 @@ int32_t qknr_qk_sumsq_across_heads(const qknr_qk_args *args, float *sumsq, hipSt
  * channel count of the whole segment (n_heads*d_head*tp, below 2^24); 0 means
  * this call's own n*d_head. apply_norm must be 1.
  * With args->sumsq_parts = P > 1 the sum of a token's segment is itself the
- * sum, in order, of P partial sums laid out [seg][P][B*S]
- *   sum = sumsq[(seg*P + 0)*B*S + t] + ... + sumsq[(seg*P + P-1)*B*S + t]
- * (the per-tile sums qknr_qkv_projection writes); 0 or 1 means one sum.
+ * sum of P partial sums laid out [seg][B*S][P]
+ *   sum = sumsq[(seg*B*S + t)*P + 0] + ... + sumsq[(seg*B*S + t)*P + P-1]
+ * added in a fixed order (a pairwise tree; the same bits on every run), e.g.
+ * the per-tile sums qknr_qkv_projection writes; 0 or 1 means one sum (the
+ * layout of step a).
  */
 int32_t qknr_qk_apply_across_heads(const qknr_qk_args *args, const float *sumsq, hipStream_t stream);
 
@@ -239,7 +241,7 @@ int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream
  * for m < rows, n < out_features, and, when q_cols > 0, for every 128-column
  * tile of the Q columns [0, q_cols) and of the K columns [q_cols, q_cols +
  * k_cols), the per-row sum of the squares of the stored (rounded) values:
- *   sumsq[(seg*P + part)*rows + m],  P = q_cols / 128, seg 0 = Q, 1 = K.
+ *   sumsq[(seg*rows + m)*P + part],  P = q_cols / 128, seg 0 = Q, 1 = K.
  * qknr_qk_apply_across_heads with sumsq_parts = P then finishes the norm and
  * RoPE on the Q and K columns of `out` (steps b-c, with the sums of all
  * ranks when the heads are split).

@@ -314,7 +314,7 @@ def qk_sumsq_across_heads(q, k=None, *, sumsq=None, stream=None):
 def _sum_parts(sumsq, q, segs):
     T = q.shape[0] * q.shape[1]
     if sumsq.dtype != torch.float32 or not sumsq.is_contiguous():
-        raise ValueError("sumsq must be a contiguous float32 [segs, parts, B*S] (or [segs, B*S]) array")
+        raise ValueError("sumsq must be a contiguous float32 [segs, B*S, parts] (or [segs, B*S]) array")
     if T == 0:
         return 1
     if sumsq.numel() % (segs * T):
@@ -325,8 +325,8 @@ def _sum_parts(sumsq, q, segs):
 def qk_apply_across_heads(q, k, q_gamma, k_gamma, cos, sin, sumsq, *, eps, q_norm_channels,
                           k_norm_channels=0, q_out=None, k_out=None, apply_rope=True, stream=None):
     """Step c of a split across-heads norm on this rank's heads: ``sumsq``
-    [segs, B*S] holds the sums added over every rank (or [segs, P, B*S]
-    partial sums, added in order, e.g. the projection's per-tile sums),
+    [segs, B*S] holds the sums added over every rank (or [segs, B*S, P]
+    partial sums, added in a fixed order, e.g. the projection's per-tile sums),
     ``*_norm_channels`` the whole segment's channel count (n_heads*d*tp; 0:
     this call's own). Gammas are this rank's slice of the segment-wide gamma.
     Returns (q_out, k_out)."""
@@ -426,13 +426,13 @@ def qkv_projection(a, w, bias=None, *, out=None, q_cols=0, k_cols=0, sumsq=None,
     """out = a @ w.T + bias on matrix cores (bf16), plus, for q_cols > 0, the
     per-row sums of squares of each 128-column tile of the Q columns
     [0, q_cols) and K columns [q_cols, q_cols + k_cols): fp32
-    [segs, q_cols // 128, M], ready for :func:`qk_apply_across_heads`.
+    [segs, M, q_cols // 128], ready for :func:`qk_apply_across_heads`.
     Returns (out, sumsq)."""
     M, N = a.shape[0], w.shape[0]
     if out is None:
         out = torch.empty(M, N, dtype=a.dtype, device=a.device)
     if q_cols and sumsq is None:
-        sumsq = torch.empty(2 if k_cols else 1, q_cols // 128, M, dtype=torch.float32, device=a.device)
+        sumsq = torch.empty(2 if k_cols else 1, M, q_cols // 128, dtype=torch.float32, device=a.device)
     r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq)
     with torch.cuda.device(a.device):
         _check(_lib.qknr_qkv_projection(ctypes.byref(r), _stream(a.device, stream)))

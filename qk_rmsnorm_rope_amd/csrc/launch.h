@@ -69,7 +69,7 @@ struct QkParams {
     int32_t segs;              // 2 with a K segment, 1 for Q only
     int32_t apply_norm, apply_rope;
     float q_channels, k_channels, eps;   // RMS denominators (QK_PER_HEAD: head_dim)
-    float *sumsq;              // QK_SUMSQ output [segs, tokens] / QK_APPLY input [segs, sum_parts, tokens]
+    float *sumsq;              // QK_SUMSQ output [segs, tokens] / QK_APPLY input [segs, tokens, sum_parts]
     int32_t sum_parts;         // QK_APPLY: partial sums per token and segment, added in order
 };
 
@@ -98,7 +98,7 @@ hipError_t permute_launch(const PermuteParams &p, int unit, hipStream_t stream);
 // QKV projection O[m, n] = sum_k A[m, k] W[n, k] + bias[n] (bf16 in and out,
 // fp32 accumulation) with per-row partial sums of squares of the Q columns
 // [0, q_cols) and the K columns [q_cols, q_cols + k_cols) of each 128-column
-// tile: sumsq[(seg*parts + part)*m + row], parts = q_cols / 128.
+// tile: sumsq[(seg*m + row)*parts + part], parts = q_cols / 128.
 struct ProjParams {
     const void *a;             // [m, k], row stride lda
     const void *w;             // [n, k], row stride ldw

@@ -204,10 +204,15 @@ __global__ __launch_bounds__(256) void qk_kernel(QkParams p) {
         }
     } else if constexpr (MODE == QK_APPLY) {
         if (norm && unit_ok) {
-            // the segment's partial sums (one per rank, or per projection tile), in order
-            const float *sp = p.sumsq + (uint64_t)seg * (uint32_t)p.sum_parts * p.tokens + t;
+            // the token's partial sums (one per projection tile; one in all when
+            // the ranks' sums were already added) are contiguous: lane i loads
+            // part i, and a fixed DPP tree adds them (the whole wave is active)
+            const float *sp = p.sumsq + ((uint64_t)seg * p.tokens + t) * (uint32_t)p.sum_parts;
             float ss = 0.0f;
-            for (int i = 0; i < p.sum_parts; i++) ss += sp[(uint64_t)i * p.tokens];
+            for (int i0 = 0; i0 < p.sum_parts; i0 += 64) {
+                const float v = i0 + lane < p.sum_parts ? sp[i0 + lane] : 0.0f;
+                ss += wave_sum(v);
+            }
             r = rsqrtf(ss / (seg ? p.k_channels : p.q_channels) + p.eps);
         }
     } else {   // QK_PER_HEAD

@@ -22,10 +22,10 @@
 //     consecutive rows hit 16 disjoint bank groups; two k-step buffers (128 KB)
 //     let the next step's loads run under the current step's MFMAs, with one
 //     barrier per k step;
-//   * tiles are ordered in groups of 8 row-tiles and each XCD (workgroups go
-//     round-robin over the 8 XCDs) takes a contiguous range of them, so the
-//     workgroups running together on one XCD share A rows and W columns in
-//     its L2; the whole weight (157 MB for Wan2.2) stays in the 256 MB MALL;
+//   * tiles are ordered in groups of 8 row-tiles, row-tile fastest; since
+//     workgroups go round-robin over the 8 XCDs, each XCD then works through
+//     one row-tile (2.6 MB of A for Wan2.2, held in its 4 MB L2) across all
+//     column tiles, while the weight (157 MB) streams from the 256 MB MALL;
 //   * epilogue: bias, RNE to bf16, the tile staged through LDS and written
 //     with 16-byte stores, the sums of squares taken from the rounded values
 //     (the values the apply pass reads back) with 16-lane DPP reductions, one
@@ -41,7 +41,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int THREADS = 512;
+constexpr int WAVES_M = 2, WAVES_N = 4;             // wave grid of a workgroup (two per SIMD)
+constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+constexpr int NWAVES = WAVES_M * WAVES_N;
+constexpr int MT = BM / WAVES_M / 32, NT = BN / WAVES_N / 32;   // 32x32 MFMA tiles per wave
+constexpr int LOADS = (BM / 8) / NWAVES;            // LDS-DMA instructions per wave per operand and k step
 constexpr int STAGE_ELEMS = (BM + BN) * BK;         // one k step of A and W tiles (64 KB)
 constexpr int LDC_S = BN + 8;                       // LDS row stride of the staged output tile
 constexpr int GROUP_M = 8;
@@ -76,10 +80,8 @@ __device__ __forceinline__ float sumsq8(const U4 &v) {
 __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_BYTES / 2];
 
-    // tile order: a contiguous range of logical tiles per XCD, grouped by GROUP_M row-tiles
-    const uint32_t per_xcd = gridDim.x / 8;
-    const uint32_t lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (lid >= p.tiles_m * p.tiles_n) return;
+    // tile order: groups of GROUP_M row-tiles, row-tile fastest (workgroup i runs on XCD i % 8)
+    const uint32_t lid = blockIdx.x;
     const uint32_t in_group = GROUP_M * p.tiles_n;
     const uint32_t first_m = (lid / in_group) * GROUP_M;
     const uint32_t gm = min((uint32_t)GROUP_M, p.tiles_m - first_m);
@@ -90,17 +92,17 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     // LDS-DMA sources: wave `wave`, instruction j fills tile rows 8*(4*wave + j) .. +7
     // (A rows for j < 4 of the A pass, W rows in the W pass); lane l -> row + l/8,
     // slot l%8, holding logical chunk swz(row, l%8).
-    const uint16_t *a_src[4], *w_src[4];
+    const uint16_t *a_src[LOADS], *w_src[LOADS];
     {
         const int slot = lane & 7;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int row = 8 * (4 * wave + j) + (lane >> 3);
+        for (int j = 0; j < LOADS; j++) {
+            const int row = 8 * (LOADS * wave + j) + (lane >> 3);
             const int c = swz(row, slot);
             int64_t ra = m0 + row;
             if (ra >= p.m) ra = p.m - 1;             // rows past M: any valid data, never stored
@@ -115,18 +117,18 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
         uint16_t *bs = as + BM * BK;
         const int64_t k0 = (int64_t)ks * BK;
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            __builtin_amdgcn_global_load_lds(a_src[j] + k0, as + (4 * wave + j) * 8 * BK, 16, 0, 0);
+        for (int j = 0; j < LOADS; j++)
+            __builtin_amdgcn_global_load_lds(a_src[j] + k0, as + (LOADS * wave + j) * 8 * BK, 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            __builtin_amdgcn_global_load_lds(w_src[j] + k0, bs + (4 * wave + j) * 8 * BK, 16, 0, 0);
+        for (int j = 0; j < LOADS; j++)
+            __builtin_amdgcn_global_load_lds(w_src[j] + k0, bs + (LOADS * wave + j) * 8 * BK, 16, 0, 0);
     };
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[MT][NT];
 #pragma unroll
-    for (int mi = 0; mi < 4; mi++)
+    for (int mi = 0; mi < MT; mi++)
 #pragma unroll
-        for (int ni = 0; ni < 2; ni++)
+        for (int ni = 0; ni < NT; ni++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[mi][ni][r] = 0.0f;
 
@@ -144,21 +146,21 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; kk++) {
             const int c = kk * 2 + fc;                // logical 16-byte chunk of this substep
-            bf16x8_t af[4], bfr[2];
+            bf16x8_t af[MT], bfr[NT];
 #pragma unroll
-            for (int mi = 0; mi < 4; mi++) {
-                const int row = wm * 128 + mi * 32 + fr;
+            for (int mi = 0; mi < MT; mi++) {
+                const int row = wm * (MT * 32) + mi * 32 + fr;
                 af[mi] = as_bf16x8(ld_lds16(as + row * BK + swz(row, c) * 8));
             }
 #pragma unroll
-            for (int ni = 0; ni < 2; ni++) {
-                const int row = wn * 64 + ni * 32 + fr;
+            for (int ni = 0; ni < NT; ni++) {
+                const int row = wn * (NT * 32) + ni * 32 + fr;
                 bfr[ni] = as_bf16x8(ld_lds16(bs + row * BK + swz(row, c) * 8));
             }
 #pragma unroll
-            for (int mi = 0; mi < 4; mi++)
+            for (int mi = 0; mi < MT; mi++)
 #pragma unroll
-                for (int ni = 0; ni < 2; ni++)
+                for (int ni = 0; ni < NT; ni++)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0);            // this wave's loads of the next step have landed
@@ -169,15 +171,15 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
     uint16_t *Cs = lds;                           // [BM][LDC_S]
     const uint16_t *bias = reinterpret_cast<const uint16_t *>(p.bias);
 #pragma unroll
-    for (int ni = 0; ni < 2; ni++) {
-        const int col = wn * 64 + ni * 32 + fr;
+    for (int ni = 0; ni < NT; ni++) {
+        const int col = wn * (NT * 32) + ni * 32 + fr;
         float bv = 0.0f;
         if (bias && n0 + col < p.n) bv = __uint_as_float((uint32_t)bias[n0 + col] << 16);
 #pragma unroll
-        for (int mi = 0; mi < 4; mi++) {
+        for (int mi = 0; mi < MT; mi++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int row = wm * 128 + mi * 32 + fc * 4 + (r >> 2) * 8 + (r & 3);
+                const int row = wm * (MT * 32) + mi * 32 + fc * 4 + (r >> 2) * 8 + (r & 3);
                 const uint32_t packed = pack_bf16(acc[mi][ni][r] + bv, 0.0f);
                 Cs[row * LDC_S + col] = (uint16_t)(packed & 0xFFFFu);
             }
@@ -201,14 +203,15 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
     const bool col_ok = hc0 < p.n;
     uint16_t *o_base = reinterpret_cast<uint16_t *>(p.o);
     const int cr = t >> 5, cc = t & 31;
+    constexpr int ROWS_PER_PASS = THREADS / 32;
 #pragma unroll 4
-    for (int j = 0; j < BM / 16; j++) {
-        const int row = cr + 16 * j;
+    for (int j = 0; j < BM / ROWS_PER_PASS; j++) {
+        const int row = cr + ROWS_PER_PASS * j;
         const U4 v = ld_lds16(Cs + row * LDC_S + cc * 8);
         const bool ok = m0 + row < p.m;
         if (ok && col_ok) st_global16(o_base + (m0 + row) * p.ldo + n0 + cc * 8, v);
         const float ss = group_sum<16>(sumsq8(v));
-        if (seg >= 0 && ok && (cc & 15) == 0) p.sumsq[((int64_t)seg * p.parts + part) * p.m + m0 + row] = ss;
+        if (seg >= 0 && ok && (cc & 15) == 0) p.sumsq[((int64_t)seg * p.m + m0 + row) * p.parts + part] = ss;
     }
 }
 
@@ -219,8 +222,7 @@ hipError_t proj_launch(ProjParams &p, hipStream_t stream) {
     p.tiles_n = (uint32_t)((p.n + BN - 1) / BN);
     const uint64_t tiles = (uint64_t)p.tiles_m * p.tiles_n;
     if (tiles == 0) return hipSuccess;
-    const uint64_t grid = (tiles + 7) / 8 * 8;          // a whole number of tiles per XCD
-    hipLaunchKernelGGL(qkv_proj_bf16_kernel, dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
+    hipLaunchKernelGGL(qkv_proj_bf16_kernel, dim3((uint32_t)tiles), dim3(THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ def _oracle_rows(d, rows, with_bias=True):
 def _check_sums(out, sumsq, q_cols, k_cols, what):
     o = out.float().double().cpu().numpy()
     parts = q_cols // 128
-    got = sumsq.cpu().double().numpy().reshape(-1, parts, out.shape[0])
+    got = sumsq.cpu().double().numpy().reshape(-1, out.shape[0], parts).transpose(0, 2, 1)
     for seg, c0 in ((0, 0), (1, q_cols)):
         if seg == 1 and not k_cols:
             continue
@@ -72,7 +72,7 @@ def test_no_bias_no_sums_and_q_only_sums(Q):
     check_float(out, _oracle_rows(d, np.arange(77), with_bias=False), "nobias/out")
     out2, s2 = Q.qkv_projection(d["a"], d["w"], d["bias"], q_cols=256)
     torch.cuda.synchronize()
-    assert tuple(s2.shape) == (1, 2, 77)
+    assert tuple(s2.shape) == (1, 77, 2)
     _check_sums(out2, s2, 256, 0, "q-only")
 
 
@@ -111,7 +111,7 @@ def test_wan_width_projection_sums_and_apply(Q):
     d = _wan(S)
     out, s = Q.qkv_projection(d["a"], d["w"], d["bias"], q_cols=5120, k_cols=5120)
     torch.cuda.synchronize()
-    assert tuple(s.shape) == (2, 40, S)
+    assert tuple(s.shape) == (2, S, 40)
     rows = np.unique(np.concatenate([np.arange(8), np.arange(S - 8, S),
                                      np.random.default_rng(3).choice(S, 48, replace=False)]))
     check_float(out[torch.as_tensor(rows, device="cuda")], _oracle_rows(d, rows), "wan1000/out")
@@ -142,7 +142,7 @@ def test_wan_full_size_sampled_and_deterministic(Q):
     idx = torch.as_tensor(rows, device="cuda")
     check_float(out[idx], _oracle_rows(d, rows), "full/out")
     o = out[idx].float().double().cpu().numpy()
-    got = s[:, :, idx].cpu().double().numpy()
+    got = s[:, idx, :].cpu().double().numpy()
     for seg, c0 in ((0, 0), (1, 5120)):
-        ref = (o[:, c0: c0 + 5120] ** 2).reshape(len(rows), 40, 128).sum(-1).T
+        ref = (o[:, c0: c0 + 5120] ** 2).reshape(len(rows), 40, 128).sum(-1)
         np.testing.assert_allclose(got[seg], ref, rtol=1e-5, atol=1e-6)
