@@ -22,10 +22,12 @@
 //     consecutive rows hit 16 disjoint bank groups; two k-step buffers (128 KB)
 //     let the next step's loads run under the current step's MFMAs, with one
 //     barrier per k step;
-//   * tiles are ordered in groups of 8 row-tiles, row-tile fastest; since
-//     workgroups go round-robin over the 8 XCDs, each XCD then works through
-//     one row-tile (2.6 MB of A for Wan2.2, held in its 4 MB L2) across all
-//     column tiles, while the weight (157 MB) streams from the 256 MB MALL;
+//   * workgroups go round-robin over the 8 XCDs; each XCD takes a contiguous
+//     range of tiles ordered in groups of 8 row-tiles, row-tile fastest, so
+//     the ~32 workgroups running together on one XCD cover 8 row-tiles x 4
+//     column-tiles and read each k step of 12 tiles through its L2 instead
+//     of 32 (measured: L2 misses 6.5x the compulsory bytes, against 16x when
+//     the XCDs share one row-tile each); the weight (157 MB) fits the MALL;
 //   * epilogue: bias, RNE to bf16, the tile staged through LDS and written
 //     with 16-byte stores, the sums of squares taken from the rounded values
 //     (the values the apply pass reads back) with 16-lane DPP reductions, one
@@ -80,8 +82,11 @@ __device__ __forceinline__ float sumsq8(const U4 &v) {
 __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_BYTES / 2];
 
-    // tile order: groups of GROUP_M row-tiles, row-tile fastest (workgroup i runs on XCD i % 8)
-    const uint32_t lid = blockIdx.x;
+    // tile order: a contiguous range of logical tiles per XCD (workgroup i runs on
+    // XCD i % 8), grouped by GROUP_M row-tiles
+    const uint32_t per_xcd = gridDim.x / 8;
+    const uint32_t lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (lid >= p.tiles_m * p.tiles_n) return;
     const uint32_t in_group = GROUP_M * p.tiles_n;
     const uint32_t first_m = (lid / in_group) * GROUP_M;
     const uint32_t gm = min((uint32_t)GROUP_M, p.tiles_m - first_m);
@@ -222,7 +227,8 @@ hipError_t proj_launch(ProjParams &p, hipStream_t stream) {
     p.tiles_n = (uint32_t)((p.n + BN - 1) / BN);
     const uint64_t tiles = (uint64_t)p.tiles_m * p.tiles_n;
     if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(qkv_proj_bf16_kernel, dim3((uint32_t)tiles), dim3(THREADS), 0, stream, p);
+    const uint64_t grid = (tiles + 7) / 8 * 8;          // a whole number of tiles per XCD
+    hipLaunchKernelGGL(qkv_proj_bf16_kernel, dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
