@@ -236,8 +236,11 @@ int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream
  * epilogue ("Kernel reference: qkv_cte": "Upstream behavior" for
  * O[S, I] = A[S, H] @ W + bias with I = (n_q + 2*n_kv)*d_head, Design
  * section 1 step a for sum(x^2) accumulated as the output tiles are copied
- * out). On matrix cores (bf16 in, fp32 accumulation):
- *   out[m, n] = RNE_bf16( sum_k a[m, k] * w[n, k] + bias[n] )
+ * out). On matrix cores (bf16 or FP8 E4M3 operands, fp32 accumulation):
+ *   out[m, n] = RNE_bf16( sum_k a[m, k] * w[n, k] * a_scale[m] * w_scale[n] + bias[n] )
+ * (a NULL scale is 1: bf16 operands normally have none; FP8 operands with a
+ * per-row activation scale and a per-output-channel weight scale are the
+ * page's ROW_MX mode).
  * for m < rows, n < out_features, and, when q_cols > 0, for every 128-column
  * tile of the Q columns [0, q_cols) and of the K columns [q_cols, q_cols +
  * k_cols), the per-row sum of the squares of the stored (rounded) values:
@@ -247,14 +250,16 @@ int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream
  * ranks when the heads are split).
  *
  * Arguments:
- *   dtype            QKNR_BF16 (a, w, bias, out).
- *   rows, in_features, out_features   M = B*S >= 0, K = H (multiple of 64),
- *       N = I (multiple of 128).
+ *   dtype            QKNR_BF16 or QKNR_FP8_E4M3FN: the type of a and w; bias
+ *       and out are bf16 in both cases.
+ *   rows, in_features, out_features   M = B*S >= 0, K = H (a multiple of 128
+ *       bytes: 64 bf16 or 128 FP8 values), N = I (multiple of 128).
  *   a [rows, in_features] with row stride a_row_stride; w [out_features,
  *       in_features] (a linear layer's weight) with row stride w_row_stride;
  *       bias [out_features] or NULL; out [rows, out_features] with row stride
- *       out_row_stride. Strides are elements, multiples of 8; pointers 16-byte
- *       aligned. out must not overlap a, w or bias.
+ *       out_row_stride. Strides are elements and multiples of 16 bytes;
+ *       pointers 16-byte aligned. out must not overlap a, w or bias.
+ *   a_scale [rows], w_scale [out_features]   fp32 or NULL.
  *   q_cols, k_cols   multiples of 128 with q_cols + k_cols <= out_features;
  *       k_cols is 0 or q_cols. q_cols = 0: no sums (sumsq ignored).
  *   sumsq            fp32 [(k_cols ? 2 : 1) * P * rows], 4-byte aligned.
@@ -275,6 +280,8 @@ typedef struct qknr_proj_args {
     int64_t q_cols;
     int64_t k_cols;
     float *sumsq;
+    const float *a_scale;
+    const float *w_scale;
 } qknr_proj_args;
 
 int32_t qknr_qkv_projection(const qknr_proj_args *args, hipStream_t stream);

@@ -213,8 +213,11 @@ def linear(a, w, a_dtype, w_dtype=None, bias=None, bias_dtype=None, a_scale=None
     assert w.shape == (I, H)
     bias_dtype = a_dtype if bias_dtype is None else bias_dtype
     b = _c(bias, STORAGE[bias_dtype]) if bias is not None else None
-    asc = _c(a_scale, np.float64) if a_scale is not None else None
-    wsc = _c(w_scale, np.float64) if w_scale is not None else None
+    asc = np.ascontiguousarray(a_scale, dtype=np.float64) if a_scale is not None else None
+    wsc = np.ascontiguousarray(w_scale, dtype=np.float64) if w_scale is not None else None
+    for name, sc, n in (("a_scale", asc, S), ("w_scale", wsc, I)):
+        if sc is not None and sc.shape != (n,):
+            raise ValueError(f"{name} must have {n} entries")
     out = np.empty((S, I), STORAGE[out_dtype]) if out_dtype is not None else None
     val = np.empty((S, I), np.float64)
     rc = _load().oracle_linear(S, H, I, a_dtype, _ptr(a), w_dtype, _ptr(w), _ptr(b), bias_dtype, _ptr(asc),

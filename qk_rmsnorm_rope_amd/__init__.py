@@ -74,6 +74,7 @@ class ProjArgs(ctypes.Structure):
         ("dtype", _i32), ("reserved", _i32), ("rows", _i64), ("in_features", _i64), ("out_features", _i64),
         ("a", _p), ("a_row_stride", _i64), ("w", _p), ("w_row_stride", _i64), ("bias", _p),
         ("out", _p), ("out_row_stride", _i64), ("q_cols", _i64), ("k_cols", _i64), ("sumsq", _p),
+        ("a_scale", _p), ("w_scale", _p),
     ]
 
 
@@ -389,9 +390,10 @@ def prepare_qk_apply_across_heads(q, k, q_gamma, k_gamma, cos, sin, sumsq, *, ep
                      (q, k, q_out, k_out, q_gamma, k_gamma, cos, sin, sumsq))
 
 
-def proj_args(a, w, bias, out, *, q_cols=0, k_cols=0, sumsq=None) -> ProjArgs:
+def proj_args(a, w, bias, out, *, q_cols=0, k_cols=0, sumsq=None, a_scale=None, w_scale=None) -> ProjArgs:
     """Fill ``qknr_proj_args``: a [M, K], w [N, K] (a linear layer's weight),
-    bias [N] or None, out [M, N]; last dimensions contiguous."""
+    both bf16 or both float8_e4m3fn; bias [N] and out [M, N] bf16; a_scale [M]
+    and w_scale [N] float32 or None; last dimensions contiguous."""
     if a.dim() != 2 or w.dim() != 2 or out.dim() != 2:
         raise ValueError("a, w and out must be 2-D ([M, K], [N, K], [M, N])")
     M, K = a.shape
@@ -400,9 +402,14 @@ def proj_args(a, w, bias, out, *, q_cols=0, k_cols=0, sumsq=None) -> ProjArgs:
         raise ValueError("shapes must be a [M, K], w [N, K], bias [N], out [M, N]")
     for name, t in (("a", a), ("w", w), ("out", out)):
         _last_dim_contiguous(name, t)
-    for t in (w, bias, out):
-        if t is not None and t.dtype != a.dtype:
-            raise TypeError("a, w, bias and out share one dtype")
+    if w.dtype != a.dtype or a.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise TypeError("a and w are both bfloat16 or both float8_e4m3fn")
+    for t in (bias, out):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise TypeError("bias and out are bfloat16")
+    for name, t, n in (("a_scale", a_scale, M), ("w_scale", w_scale, N)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
     r = ProjArgs()
     r.dtype = _dtype(a)
     r.rows, r.in_features, r.out_features = M, K, N
@@ -418,31 +425,36 @@ def proj_args(a, w, bias, out, *, q_cols=0, k_cols=0, sumsq=None) -> ProjArgs:
         if sumsq is None or sumsq.dtype != torch.float32 or not sumsq.is_contiguous() or sumsq.numel() != need:
             raise ValueError(f"sumsq must be a contiguous float32 tensor of {need} elements")
     r.sumsq = _ptr(sumsq) if q_cols else None
+    r.a_scale, r.w_scale = _ptr(a_scale), _ptr(w_scale)
     r._keep = (bias,)
     return r
 
 
-def qkv_projection(a, w, bias=None, *, out=None, q_cols=0, k_cols=0, sumsq=None, stream=None):
-    """out = a @ w.T + bias on matrix cores (bf16), plus, for q_cols > 0, the
+def qkv_projection(a, w, bias=None, *, out=None, q_cols=0, k_cols=0, sumsq=None, a_scale=None, w_scale=None,
+                   stream=None):
+    """out = (a @ w.T) * a_scale[:, None] * w_scale[None, :] + bias on matrix
+    cores (bf16 operands, or float8_e4m3fn operands with ROW_MX scales; the
+    output is bf16), plus, for q_cols > 0, the
     per-row sums of squares of each 128-column tile of the Q columns
     [0, q_cols) and K columns [q_cols, q_cols + k_cols): fp32
     [segs, M, q_cols // 128], ready for :func:`qk_apply_across_heads`.
     Returns (out, sumsq)."""
     M, N = a.shape[0], w.shape[0]
     if out is None:
-        out = torch.empty(M, N, dtype=a.dtype, device=a.device)
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=a.device)
     if q_cols and sumsq is None:
         sumsq = torch.empty(2 if k_cols else 1, M, q_cols // 128, dtype=torch.float32, device=a.device)
-    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq)
+    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq, a_scale=a_scale, w_scale=w_scale)
     with torch.cuda.device(a.device):
         _check(_lib.qknr_qkv_projection(ctypes.byref(r), _stream(a.device, stream)))
     return out, sumsq
 
 
-def prepare_qkv_projection(a, w, bias=None, *, out, q_cols=0, k_cols=0, sumsq=None, stream=None):
+def prepare_qkv_projection(a, w, bias=None, *, out, q_cols=0, k_cols=0, sumsq=None, a_scale=None,
+                           w_scale=None, stream=None):
     """Prepared form of :func:`qkv_projection` (arguments marshalled once)."""
-    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq)
-    return _prepared(_lib.qknr_qkv_projection, r, (), a.device, stream, (a, w, bias, out, sumsq))
+    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq, a_scale=a_scale, w_scale=w_scale)
+    return _prepared(_lib.qknr_qkv_projection, r, (), a.device, stream, (a, w, bias, out, sumsq, a_scale, w_scale))
 
 
 def permute_args(src, dst, head_dim, *, dim=-1, first=0, n_heads=None, inverse=False) -> PermuteArgs:

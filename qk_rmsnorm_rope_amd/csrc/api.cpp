@@ -418,11 +418,14 @@ int32_t qknr_qk_norm_rope_per_head(const qknr_qk_args *args, hipStream_t stream)
 
 int32_t qknr_qkv_projection(const qknr_proj_args *a, hipStream_t stream) {
     if (!a) return fail(QKNR_INVALID_ARGUMENT, "args is NULL");
-    if (a->dtype != QKNR_BF16) return fail(QKNR_UNSUPPORTED, "the projection is built for QKNR_BF16 only");
+    if (a->dtype != QKNR_BF16 && a->dtype != QKNR_FP8_E4M3FN)
+        return fail(QKNR_UNSUPPORTED, "the projection is built for QKNR_BF16 and QKNR_FP8_E4M3FN operands");
+    const bool fp8 = a->dtype == QKNR_FP8_E4M3FN;
+    const int eb = fp8 ? 1 : 2;
     if (a->rows < 0 || a->in_features < 1 || a->out_features < 1)
         return fail(QKNR_INVALID_ARGUMENT, "rows >= 0, in_features >= 1, out_features >= 1");
-    if (a->in_features % 64 || a->out_features % 128)
-        return fail(QKNR_UNSUPPORTED, "in_features must be a multiple of 64 and out_features of 128");
+    if ((a->in_features * eb) % 128 || a->out_features % 128)
+        return fail(QKNR_UNSUPPORTED, "in_features must be a multiple of 128 bytes and out_features of 128");
     if (a->q_cols < 0 || a->k_cols < 0 || a->q_cols % 128 || a->k_cols % 128 ||
         a->q_cols + a->k_cols > a->out_features || (a->k_cols && a->k_cols != a->q_cols) ||
         (a->k_cols && !a->q_cols))
@@ -431,35 +434,40 @@ int32_t qknr_qkv_projection(const qknr_proj_args *a, hipStream_t stream) {
     if (a->a_row_stride < a->in_features || a->w_row_stride < a->in_features ||
         a->out_row_stride < a->out_features)
         return fail(QKNR_INVALID_ARGUMENT, "row strides must cover a row");
-    if (a->a_row_stride % 8 || a->w_row_stride % 8 || a->out_row_stride % 8)
-        return fail(QKNR_UNSUPPORTED, "row strides must be multiples of 8 elements");
+    if ((a->a_row_stride * eb) % 16 || (a->w_row_stride * eb) % 16 || a->out_row_stride % 8)
+        return fail(QKNR_UNSUPPORTED, "row strides must be multiples of 16 bytes");
     if (a->rows == 0) return ok();
     if (!a->a || !a->w || !a->out) return fail(QKNR_INVALID_ARGUMENT, "a, w and out are required");
-    if (!aligned(a->a, 16) || !aligned(a->w, 16) || !aligned(a->out, 16) || !aligned(a->bias, 2))
-        return fail(QKNR_UNSUPPORTED, "a, w and out must be 16-byte aligned");
+    if (!aligned(a->a, 16) || !aligned(a->w, 16) || !aligned(a->out, 16) || !aligned(a->bias, 2) ||
+        !aligned(a->a_scale, 4) || !aligned(a->w_scale, 4))
+        return fail(QKNR_UNSUPPORTED, "a, w and out must be 16-byte aligned (bias 2, scales 4)");
     if (a->q_cols && (!a->sumsq || !aligned(a->sumsq, 4)))
         return fail(QKNR_INVALID_ARGUMENT, "sumsq (4-byte aligned) is required when q_cols > 0");
     if (a->rows >= (1LL << 31) || a->out_features >= (1LL << 31) || a->in_features >= (1LL << 31))
         return fail(QKNR_UNSUPPORTED, "sizes of 2^31 or more");
     const int64_t tiles = ((a->rows + 255) / 256) * (a->out_features / 128);
     if (tiles >= (1LL << 31)) return fail(QKNR_UNSUPPORTED, "more than 2^31 tiles");
-    auto span = [](const void *p, int64_t rows, int64_t stride, int64_t cols) {
+    auto span = [](const void *p, int64_t rows, int64_t stride, int64_t cols, int bytes) {
         const uintptr_t b = reinterpret_cast<uintptr_t>(p);
-        return std::pair<uintptr_t, uintptr_t>(b, b + (uintptr_t)(((rows - 1) * stride + cols) * 2));
+        return std::pair<uintptr_t, uintptr_t>(b, b + (uintptr_t)(((rows - 1) * stride + cols) * bytes));
     };
-    const auto o = span(a->out, a->rows, a->out_row_stride, a->out_features);
-    const std::pair<uintptr_t, uintptr_t> ins[] = {span(a->a, a->rows, a->a_row_stride, a->in_features),
-                                                   span(a->w, a->out_features, a->w_row_stride, a->in_features),
-                                                   a->bias ? span(a->bias, 1, 0, a->out_features)
-                                                           : std::pair<uintptr_t, uintptr_t>(0, 0)};
+    const auto o = span(a->out, a->rows, a->out_row_stride, a->out_features, 2);
+    const std::pair<uintptr_t, uintptr_t> none(0, 0);
+    const std::pair<uintptr_t, uintptr_t> ins[] = {
+        span(a->a, a->rows, a->a_row_stride, a->in_features, eb),
+        span(a->w, a->out_features, a->w_row_stride, a->in_features, eb),
+        a->bias ? span(a->bias, 1, 0, a->out_features, 2) : none,
+        a->a_scale ? span(a->a_scale, 1, 0, a->rows, 4) : none,
+        a->w_scale ? span(a->w_scale, 1, 0, a->out_features, 4) : none};
     for (const auto &r : ins)
         if (r.first < o.second && o.first < r.second) return fail(QKNR_INVALID_ARGUMENT, "out overlaps an input");
     qknr::ProjParams p{};
     p.a = a->a; p.w = a->w; p.bias = a->bias; p.o = a->out; p.sumsq = a->sumsq;
+    p.a_scale = a->a_scale; p.w_scale = a->w_scale;
     p.m = a->rows; p.n = a->out_features; p.k = a->in_features;
     p.lda = a->a_row_stride; p.ldw = a->w_row_stride; p.ldo = a->out_row_stride;
     p.q_cols = a->q_cols; p.k_cols = a->k_cols; p.parts = a->q_cols / 128;
-    hipError_t e = qknr::proj_launch(p, stream);
+    hipError_t e = qknr::proj_launch(p, fp8, stream);
     if (e != hipSuccess) return fail(QKNR_DEVICE_ERROR, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }

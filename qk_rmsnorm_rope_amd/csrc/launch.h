@@ -95,22 +95,25 @@ struct PermuteParams {
 // unit: bytes moved per access (1, 2, 4, 8 or 16), dividing the bytes per index.
 hipError_t permute_launch(const PermuteParams &p, int unit, hipStream_t stream);
 
-// QKV projection O[m, n] = sum_k A[m, k] W[n, k] + bias[n] (bf16 in and out,
-// fp32 accumulation) with per-row partial sums of squares of the Q columns
+// QKV projection O[m, n] = sum_k A[m, k] W[n, k] (* a_scale[m] * w_scale[n])
+// + bias[n] (bf16 or FP8 E4M3 operands, fp32 accumulation, bf16 bias and
+// output) with per-row partial sums of squares of the Q columns
 // [0, q_cols) and the K columns [q_cols, q_cols + k_cols) of each 128-column
 // tile: sumsq[(seg*m + row)*parts + part], parts = q_cols / 128.
 struct ProjParams {
     const void *a;             // [m, k], row stride lda
     const void *w;             // [n, k], row stride ldw
-    const void *bias;          // [n] or nullptr
+    const void *bias;          // [n] bf16 or nullptr
+    const float *a_scale;      // [m] or nullptr (per-row dequantisation)
+    const float *w_scale;      // [n] or nullptr (per-channel dequantisation)
     void *o;                   // [m, n], row stride ldo
     float *sumsq;
     int64_t m, n, k, lda, ldw, ldo;
     int64_t q_cols, k_cols, parts;
     uint32_t tiles_m, tiles_n; // set by the launcher
 };
-// n a multiple of 128, k of 64; leading dimensions multiples of 8 elements.
-hipError_t proj_launch(ProjParams &p, hipStream_t stream);
+// n a multiple of 128, k of 128 bytes; leading dimensions multiples of 16 bytes.
+hipError_t proj_launch(ProjParams &p, bool fp8, hipStream_t stream);
 
 // (b) KvRmsNormRopeCache
 enum CacheCode : int32_t { CODE_SAME = 0, CODE_INT8 = 1, CODE_E4M3FN = 2, CODE_E5M2 = 3 };

@@ -1,5 +1,6 @@
 // qkv_proj.hip -- the QKV projection with step a of the across-heads norm in
-// its epilogue, for gfx950 matrix cores.
+// its epilogue, for gfx950 matrix cores, with bf16 operands or FP8 E4M3
+// operands with per-row / per-channel dequantisation scales (ROW_MX).
 //
 // "Kernel reference: qkv_cte" describes the projection O[S, I] = A[S, H] @ W +
 // bias that produces Q|K|V ("Upstream behavior") and, for the across-heads
@@ -11,9 +12,11 @@
 //
 // MI355X design:
 //   * 256 x 256 output tile per workgroup of 8 waves (2 x 4), each wave
-//     128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16 (fp32 accumulators):
-//     128 flops per byte staged, so the L2 -> LDS stream stays well below the
-//     L2 bandwidth at the matrix cores' rate;
+//     128 x 64 = 4 x 2 tiles of 32 x 32 MFMAs with fp32 accumulators:
+//     v_mfma_f32_32x32x16_bf16, or for FP8 v_mfma_scale_f32_32x32x64_f8f6f4
+//     (unit block scales; the ROW_MX scales are applied in the epilogue);
+//     a k step is one 128-byte row per operand row (64 bf16 or 128 FP8
+//     values), so both types share the LDS tiling below;
 //   * both operands are K-contiguous (W is [I, H], a linear layer's weight), so
 //     every MFMA operand is one 16-byte LDS read;
 //   * tiles move global -> LDS with global_load_lds_dwordx4 (no registers):
@@ -40,19 +43,21 @@ namespace qknr {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256;
+constexpr int ROW_BYTES = 128;                      // one k step of one tile row, in bytes
 constexpr int WAVES_M = 2, WAVES_N = 4;             // wave grid of a workgroup (two per SIMD)
 constexpr int THREADS = 64 * WAVES_M * WAVES_N;
 constexpr int NWAVES = WAVES_M * WAVES_N;
 constexpr int MT = BM / WAVES_M / 32, NT = BN / WAVES_N / 32;   // 32x32 MFMA tiles per wave
 constexpr int LOADS = (BM / 8) / NWAVES;            // LDS-DMA instructions per wave per operand and k step
-constexpr int STAGE_ELEMS = (BM + BN) * BK;         // one k step of A and W tiles (64 KB)
-constexpr int LDC_S = BN + 8;                       // LDS row stride of the staged output tile
+constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;  // one k step of A and W tiles (64 KB)
+constexpr int LDC_S = BN + 8;                       // LDS row stride of the staged output tile (elements)
 constexpr int GROUP_M = 8;
-constexpr int LDS_BYTES_AB = 2 * STAGE_ELEMS * 2;   // two k-step buffers: 128 KB
-constexpr int LDS_BYTES_C = BM * LDC_S * 2;         // 132 KB
+constexpr int LDS_BYTES_AB = 2 * STAGE_BYTES;       // two k-step buffers: 128 KB
+constexpr int LDS_BYTES_C = BM * LDC_S * 2 + BM * 4;   // 132 KB output tile + the row scales
 constexpr int LDS_BYTES = LDS_BYTES_AB > LDS_BYTES_C ? LDS_BYTES_AB : LDS_BYTES_C;
 
 struct alignas(16) U4 {
@@ -60,10 +65,10 @@ struct alignas(16) U4 {
 };
 
 __device__ __forceinline__ void st_global16(void *p, const U4 &v) { *reinterpret_cast<U4 *>(p) = v; }
-__device__ __forceinline__ U4 ld_lds16(const uint16_t *p) { return *reinterpret_cast<const U4 *>(p); }
-__device__ __forceinline__ bf16x8_t as_bf16x8(const U4 &v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ U4 ld_lds16(const void *p) { return *reinterpret_cast<const U4 *>(p); }
 
-// LDS slot of logical 16-byte chunk c (0..7) of tile row r (rows of 128 bytes).
+// LDS slot of logical 16-byte chunk c (0..7) of tile row r (rows of 128 bytes):
+// 16 consecutive rows of one chunk land in 16 distinct 4-bank groups.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Sum of squares of the 8 bf16 values of a 16-byte chunk (fp32).
@@ -79,8 +84,44 @@ __device__ __forceinline__ float sumsq8(const U4 &v) {
     return s;
 }
 
-__global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_BYTES / 2];
+// One MFMA operand of substep kk of a k step: the lane's 16 (bf16) or 32
+// (FP8) bytes of tile row `row`; lanes l and l + 32 hold the two halves of the
+// substep's k range (any split works as long as A and W use the same one).
+template <bool FP8>
+struct Frag;
+
+template <>
+struct Frag<false> {
+    bf16x8_t v;
+    __device__ __forceinline__ void read(const uint8_t *tile, int row, int kk, int half) {
+        v = __builtin_bit_cast(bf16x8_t, ld_lds16(tile + row * ROW_BYTES + swz(row, kk * 2 + half) * 16));
+    }
+};
+
+template <>
+struct Frag<true> {
+    i32x8_t v;
+    __device__ __forceinline__ void read(const uint8_t *tile, int row, int kk, int half) {
+        const int c = kk * 4 + half * 2;
+        const U4 lo = ld_lds16(tile + row * ROW_BYTES + swz(row, c) * 16);
+        const U4 hi = ld_lds16(tile + row * ROW_BYTES + swz(row, c + 1) * 16);
+        v = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+};
+
+__device__ __forceinline__ f32x16_t mfma(const Frag<false> &a, const Frag<false> &b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma(const Frag<true> &a, const Frag<true> &b, f32x16_t c) {
+    // both operands FP8 E4M3 (format 0), block scales 2^(127 - 127) = 1
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
+    constexpr int EB = FP8 ? 1 : 2;                 // operand bytes per element
+    constexpr int KSUB = FP8 ? 2 : 4;               // MFMA substeps per 128-byte k step
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
     // tile order: a contiguous range of logical tiles per XCD (workgroup i runs on
     // XCD i % 8), grouped by GROUP_M row-tiles
@@ -99,10 +140,10 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    // LDS-DMA sources: wave `wave`, instruction j fills tile rows 8*(4*wave + j) .. +7
-    // (A rows for j < 4 of the A pass, W rows in the W pass); lane l -> row + l/8,
-    // slot l%8, holding logical chunk swz(row, l%8).
-    const uint16_t *a_src[LOADS], *w_src[LOADS];
+    // LDS-DMA sources: wave `wave`, instruction j fills tile rows 8*(LOADS*wave + j) .. +7
+    // of A, then the same rows of W; lane l -> row + l/8, slot l%8, holding logical
+    // chunk swz(row, l%8).
+    const uint8_t *a_src[LOADS], *w_src[LOADS];
     {
         const int slot = lane & 7;
 #pragma unroll
@@ -113,20 +154,20 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
             if (ra >= p.m) ra = p.m - 1;             // rows past M: any valid data, never stored
             int64_t rw = n0 + row;
             if (rw >= p.n) rw = p.n - 1;             // columns past N (a final half tile)
-            a_src[j] = reinterpret_cast<const uint16_t *>(p.a) + ra * p.lda + c * 8;
-            w_src[j] = reinterpret_cast<const uint16_t *>(p.w) + rw * p.ldw + c * 8;
+            a_src[j] = reinterpret_cast<const uint8_t *>(p.a) + (ra * p.lda) * EB + c * 16;
+            w_src[j] = reinterpret_cast<const uint8_t *>(p.w) + (rw * p.ldw) * EB + c * 16;
         }
     }
     auto issue_loads = [&](int ks, int buf) {
-        uint16_t *as = lds + buf * STAGE_ELEMS;
-        uint16_t *bs = as + BM * BK;
-        const int64_t k0 = (int64_t)ks * BK;
+        uint8_t *as = lds + buf * STAGE_BYTES;
+        uint8_t *bs = as + BM * ROW_BYTES;
+        const int64_t k0 = (int64_t)ks * ROW_BYTES;
 #pragma unroll
         for (int j = 0; j < LOADS; j++)
-            __builtin_amdgcn_global_load_lds(a_src[j] + k0, as + (LOADS * wave + j) * 8 * BK, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(a_src[j] + k0, as + (LOADS * wave + j) * 8 * ROW_BYTES, 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < LOADS; j++)
-            __builtin_amdgcn_global_load_lds(w_src[j] + k0, bs + (LOADS * wave + j) * 8 * BK, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(w_src[j] + k0, bs + (LOADS * wave + j) * 8 * ROW_BYTES, 16, 0, 0);
     };
 
     f32x16_t acc[MT][NT];
@@ -137,55 +178,59 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[mi][ni][r] = 0.0f;
 
-    // fragment rows: lane holds row (l % 32) of a 32-row tile and k chunk (l / 32) of a 16-k substep
+    // fragment rows: lane holds row (l % 32) of a 32-row tile and half (l / 32) of a substep's k
     const int fr = lane & 31, fc = lane >> 5;
-    const int ksteps = (int)(p.k / BK);
+    const int ksteps = (int)(p.k * EB / ROW_BYTES);
     issue_loads(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int ks = 0; ks < ksteps; ks++) {
         const int buf = ks & 1;
         if (ks + 1 < ksteps) issue_loads(ks + 1, buf ^ 1);
-        const uint16_t *as = lds + buf * STAGE_ELEMS;
-        const uint16_t *bs = as + BM * BK;
+        const uint8_t *as = lds + buf * STAGE_BYTES;
+        const uint8_t *bs = as + BM * ROW_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; kk++) {
-            const int c = kk * 2 + fc;                // logical 16-byte chunk of this substep
-            bf16x8_t af[MT], bfr[NT];
+        for (int kk = 0; kk < KSUB; kk++) {
+            Frag<FP8> af[MT], bfr[NT];
 #pragma unroll
-            for (int mi = 0; mi < MT; mi++) {
-                const int row = wm * (MT * 32) + mi * 32 + fr;
-                af[mi] = as_bf16x8(ld_lds16(as + row * BK + swz(row, c) * 8));
-            }
+            for (int mi = 0; mi < MT; mi++) af[mi].read(as, wm * (MT * 32) + mi * 32 + fr, kk, fc);
 #pragma unroll
-            for (int ni = 0; ni < NT; ni++) {
-                const int row = wn * (NT * 32) + ni * 32 + fr;
-                bfr[ni] = as_bf16x8(ld_lds16(bs + row * BK + swz(row, c) * 8));
-            }
+            for (int ni = 0; ni < NT; ni++) bfr[ni].read(bs, wn * (NT * 32) + ni * 32 + fr, kk, fc);
 #pragma unroll
             for (int mi = 0; mi < MT; mi++)
 #pragma unroll
-                for (int ni = 0; ni < NT; ni++)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+                for (int ni = 0; ni < NT; ni++) acc[mi][ni] = mfma(af[mi], bfr[ni], acc[mi][ni]);
         }
         __builtin_amdgcn_s_waitcnt(0);            // this wave's loads of the next step have landed
         __syncthreads();                          // ... everyone's, and no wave still reads `buf`
     }
 
-    // epilogue 1: bias, round to bf16, stage the 256 x 256 tile in LDS
-    uint16_t *Cs = lds;                           // [BM][LDC_S]
+    // epilogue 1: scales, bias, round to bf16, stage the 256 x 256 tile in LDS
+    uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);           // [BM][LDC_S]
+    float *row_scale = reinterpret_cast<float *>(lds + BM * LDC_S * 2);
+    if (p.a_scale && t < BM) {
+        int64_t r = m0 + t;
+        if (r >= p.m) r = p.m - 1;
+        row_scale[t] = p.a_scale[r];
+    }
+    __syncthreads();
     const uint16_t *bias = reinterpret_cast<const uint16_t *>(p.bias);
 #pragma unroll
     for (int ni = 0; ni < NT; ni++) {
         const int col = wn * (NT * 32) + ni * 32 + fr;
-        float bv = 0.0f;
-        if (bias && n0 + col < p.n) bv = __uint_as_float((uint32_t)bias[n0 + col] << 16);
+        const bool col_in = n0 + col < p.n;
+        float bv = 0.0f, cs = 1.0f;
+        if (bias && col_in) bv = __uint_as_float((uint32_t)bias[n0 + col] << 16);
+        if (p.w_scale && col_in) cs = p.w_scale[n0 + col];
 #pragma unroll
         for (int mi = 0; mi < MT; mi++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int row = wm * (MT * 32) + mi * 32 + fc * 4 + (r >> 2) * 8 + (r & 3);
-                const uint32_t packed = pack_bf16(acc[mi][ni][r] + bv, 0.0f);
+                float v = acc[mi][ni][r];
+                if (p.a_scale) v *= row_scale[row];
+                if (p.w_scale) v *= cs;
+                const uint32_t packed = pack_bf16(v + bv, 0.0f);
                 Cs[row * LDC_S + col] = (uint16_t)(packed & 0xFFFFu);
             }
         }
@@ -222,13 +267,14 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_bf16_kernel(ProjParams p) {
 
 }  // namespace
 
-hipError_t proj_launch(ProjParams &p, hipStream_t stream) {
+hipError_t proj_launch(ProjParams &p, bool fp8, hipStream_t stream) {
     p.tiles_m = (uint32_t)((p.m + BM - 1) / BM);
     p.tiles_n = (uint32_t)((p.n + BN - 1) / BN);
     const uint64_t tiles = (uint64_t)p.tiles_m * p.tiles_n;
     if (tiles == 0) return hipSuccess;
     const uint64_t grid = (tiles + 7) / 8 * 8;          // a whole number of tiles per XCD
-    hipLaunchKernelGGL(qkv_proj_bf16_kernel, dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
+    if (fp8) hipLaunchKernelGGL(qkv_proj_kernel<true>, dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
+    else hipLaunchKernelGGL(qkv_proj_kernel<false>, dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

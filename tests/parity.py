@@ -59,6 +59,24 @@ def check_float(gpu, ref, what, fp32=False):
     return rel
 
 
+def check_dot(gpu, ref, mag, k, what):
+    """Outputs of a k-term dot product rounded to bf16: the bf16 bar plus the
+    classical worst-case bound for recursive fp32 summation, k * 2^-24 times
+    the sum of the magnitudes of the terms (`mag` = sum_k |a_k w_k|, scaled as
+    the output is). The matrix cores' FP8 dot product adds its 64-term blocks
+    in an order of its own, so the exact fp64 value is off by up to that much
+    before the output rounding."""
+    g = values(gpu).reshape(ref.shape)
+    err = np.abs(g - ref)
+    bound = 8e-3 * np.abs(ref) + 1e-3 + k * 2.0 ** -24 * mag
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.argmax(np.where(bad, err - bound, -np.inf))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside the dot-product bound; worst at "
+                             f"flat {i}: gpu {g.flat[i]!r} ref {ref.flat[i]!r} term magnitude {mag.flat[i]!r}")
+    return float((err / np.maximum(mag, 1e-30)).max()) if err.size else 0.0
+
+
 def check_int8(gpu_codes, ref_codes, t, what):
     g = np.asarray(gpu_codes, np.int64).reshape(ref_codes.shape)
     r = np.asarray(ref_codes, np.int64)

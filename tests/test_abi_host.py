@@ -199,6 +199,8 @@ def _proj(**kw):
 
 @pytest.mark.parametrize("kw, code", [
     (dict(dtype=Q.F32), Q.UNSUPPORTED),
+    (dict(dtype=Q.FP8_E4M3FN, in_features=64), Q.UNSUPPORTED),                     # FP8 K: 128-byte multiples
+    (dict(a_scale=0x900002), Q.UNSUPPORTED),                                         # scale misaligned
     (dict(in_features=100, a_row_stride=104, w_row_stride=104), Q.UNSUPPORTED),    # K not a multiple of 64
     (dict(out_features=300, out_row_stride=304), Q.UNSUPPORTED),                   # N not a multiple of 128
     (dict(q_cols=64, k_cols=64), Q.INVALID_ARGUMENT),

@@ -2,12 +2,13 @@
 across-heads norm in its epilogue) and of the projection -> apply path.
 
 Cases: a small ragged case (300 rows: two row-tiles, the second partial;
-3 column tiles: Q, K and V) with bias; no bias and no sums; the Wan2.2 width
+3 column tiles: Q, K and V) with bias; no bias and no sums; FP8 E4M3 operands
+with ROW_MX scales (and without scales); the Wan2.2 width
 (hidden 5120 -> 15360 columns, 40 + 40 + 40 heads) at 1000 rows with sampled
 rows against the oracle, the per-tile sums against fp64 sums of the stored
 outputs, and the projection -> apply path against the oracle's across-heads
 operator on the stored Q|K; the full S = 75600 case on sampled rows; two runs
-bit-identical.
+bit-identical -- the last two with bf16 and with FP8 ROW_MX operands.
 
 The projection's outputs are checked against the oracle's exact fp64 values
 at the bf16 bar; the sums against fp64 sums of the kernel's own stored bf16
@@ -19,7 +20,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import check_float, host
+from tests.parity import check_dot, check_float, host
 
 pytestmark = pytest.mark.gpu
 
@@ -33,9 +34,39 @@ def Q():
 
 
 def _oracle_rows(d, rows, with_bias=True):
-    a = host(d["a"][rows])
-    _, v = oracle.linear(a, host(d["w"]), oracle.BF16, bias=host(d["bias"]) if with_bias else None)
+    bias = host(d["bias"]) if with_bias else None
+    if d["cfg"].operands == "fp8":
+        a8 = d["a8"][torch.as_tensor(rows, device=d["a8"].device)].view(torch.uint8).cpu().numpy()
+        _, v = oracle.linear(a8, d["w8"].view(torch.uint8).cpu().numpy(), oracle.E4M3FN, bias=bias,
+                             bias_dtype=oracle.BF16, a_scale=d["a_scale"].cpu().numpy()[rows],
+                             w_scale=d["w_scale"].cpu().numpy())
+        return v
+    _, v = oracle.linear(host(d["a"][rows]), host(d["w"]), oracle.BF16, bias=bias)
     return v
+
+
+def _fp8_magnitude(d, rows, scaled=True):
+    """sum_k |a_k w_k| of the FP8 operands (times the scales), per output."""
+    a = np.abs(oracle.decode(oracle.E4M3FN, d["a8"].view(torch.uint8).cpu().numpy()[rows]))
+    w = np.abs(oracle.decode(oracle.E4M3FN, d["w8"].view(torch.uint8).cpu().numpy()))
+    mag = a @ w.T
+    if scaled:
+        mag *= d["a_scale"].cpu().double().numpy()[rows][:, None] * d["w_scale"].cpu().double().numpy()[None, :]
+    return mag
+
+
+def _check_out(d, got, rows, what):
+    ref = _oracle_rows(d, rows)
+    if d["cfg"].operands == "fp8":
+        check_dot(got, ref, _fp8_magnitude(d, rows), d["cfg"].hidden, what)
+    else:
+        check_float(got, ref, what)
+
+
+def _project(Q, d, **kw):
+    if d["cfg"].operands == "fp8":
+        return Q.qkv_projection(d["a8"], d["w8"], d["bias"], a_scale=d["a_scale"], w_scale=d["w_scale"], **kw)
+    return Q.qkv_projection(d["a"], d["w"], d["bias"], **kw)
 
 
 def _check_sums(out, sumsq, q_cols, k_cols, what):
@@ -76,6 +107,23 @@ def test_no_bias_no_sums_and_q_only_sums(Q):
     _check_sums(out2, s2, 256, 0, "q-only")
 
 
+def test_fp8_small_ragged_with_scales(Q):
+    """FP8 E4M3 operands (K = 256 values = 2 k steps of 128 bytes), per-row and
+    per-channel scales, bias, 300 rows."""
+    d = W.make_qkv_projection(W.WAN22_QKV_PROJ_FP8, device="cuda", seq=300, hidden=256, n_q_heads=1,
+                              n_k_heads=1, seed=8)
+    out, s = _project(Q, d, q_cols=128, k_cols=128)
+    torch.cuda.synchronize()
+    _check_out(d, out, np.arange(300), "fp8-small/out")
+    _check_sums(out, s, 128, 128, "fp8-small")
+    # without scales the codes are multiplied as they are (sums of up to 256 products of +-448)
+    o2, _ = Q.qkv_projection(d["a8"], d["w8"], None)
+    torch.cuda.synchronize()
+    _, v = oracle.linear(d["a8"].view(torch.uint8).cpu().numpy(), d["w8"].view(torch.uint8).cpu().numpy(),
+                         oracle.E4M3FN)
+    check_dot(o2, v, _fp8_magnitude(d, np.arange(300), scaled=False), 256, "fp8-small/unscaled")
+
+
 def test_strided_operands_and_output(Q):
     """Row strides larger than the rows: a slice of a wider activation buffer
     and an output written into a wider buffer."""
@@ -91,8 +139,8 @@ def test_strided_operands_and_output(Q):
     assert bool((big[:, :64] == 7.0).all()) and bool((big[:, 448:] == 7.0).all())
 
 
-def _wan(seq):
-    return W.make_qkv_projection(W.WAN22_QKV_PROJ, device="cuda", seq=seq)
+def _wan(seq, fp8=False):
+    return W.make_qkv_projection(W.WAN22_QKV_PROJ_FP8 if fp8 else W.WAN22_QKV_PROJ, device="cuda", seq=seq)
 
 
 def _apply(Q, d, out, s):
@@ -106,15 +154,16 @@ def _apply(Q, d, out, s):
     return qi, ki, q, k
 
 
-def test_wan_width_projection_sums_and_apply(Q):
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8_row_mx"])
+def test_wan_width_projection_sums_and_apply(Q, fp8):
     S = 1000
-    d = _wan(S)
-    out, s = Q.qkv_projection(d["a"], d["w"], d["bias"], q_cols=5120, k_cols=5120)
+    d = _wan(S, fp8)
+    out, s = _project(Q, d, q_cols=5120, k_cols=5120)
     torch.cuda.synchronize()
     assert tuple(s.shape) == (2, S, 40)
     rows = np.unique(np.concatenate([np.arange(8), np.arange(S - 8, S),
                                      np.random.default_rng(3).choice(S, 48, replace=False)]))
-    check_float(out[torch.as_tensor(rows, device="cuda")], _oracle_rows(d, rows), "wan1000/out")
+    _check_out(d, out[torch.as_tensor(rows, device="cuda")], rows, "wan1000/out")
     _check_sums(out, s, 5120, 5120, "wan1000")
     qi, ki, q, k = _apply(Q, d, out, s)
     T = S
@@ -124,23 +173,28 @@ def test_wan_width_projection_sums_and_apply(Q):
     check_float(q, rq.reshape(q.shape), "wan1000/apply-q")
     check_float(k, rk.reshape(k.shape), "wan1000/apply-k")
     # V columns are the projection's, untouched by the apply pass
-    check_float(out[torch.as_tensor(rows, device="cuda"), 10240:],
-                _oracle_rows(d, rows)[:, 10240:], "wan1000/v")
+    ref = _oracle_rows(d, rows)[:, 10240:]
+    got = out[torch.as_tensor(rows, device="cuda"), 10240:]
+    if fp8:
+        check_dot(got, ref, _fp8_magnitude(d, rows)[:, 10240:], 5120, "wan1000/v")
+    else:
+        check_float(got, ref, "wan1000/v")
 
 
-def test_wan_full_size_sampled_and_deterministic(Q):
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8_row_mx"])
+def test_wan_full_size_sampled_and_deterministic(Q, fp8):
     S = 75600
-    d = _wan(S)
-    out, s = Q.qkv_projection(d["a"], d["w"], d["bias"], q_cols=5120, k_cols=5120)
+    d = _wan(S, fp8)
+    out, s = _project(Q, d, q_cols=5120, k_cols=5120)
     out2 = torch.empty_like(out)
     s2 = torch.empty_like(s)
-    Q.qkv_projection(d["a"], d["w"], d["bias"], out=out2, q_cols=5120, k_cols=5120, sumsq=s2)
+    _project(Q, d, out=out2, q_cols=5120, k_cols=5120, sumsq=s2)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(s, s2)
     rows = np.unique(np.concatenate([np.arange(4), np.arange(S - 4, S),
                                      np.random.default_rng(4).choice(S, 24, replace=False)]))
     idx = torch.as_tensor(rows, device="cuda")
-    check_float(out[idx], _oracle_rows(d, rows), "full/out")
+    _check_out(d, out[idx], rows, "full/out")
     o = out[idx].float().double().cpu().numpy()
     got = s[:, idx, :].cpu().double().numpy()
     for seg, c0 in ((0, 0), (1, 5120)):

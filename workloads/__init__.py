@@ -172,12 +172,25 @@ class QkvProjectionConfig:
     dtype: torch.dtype
     eps: float
     seed: int
+    operands: str = "bf16"   # "bf16", or "fp8": E4M3 codes with per-row / per-channel scales (ROW_MX)
 
 
 # Wan2.2-A14B self-attention: hidden 5120, 40 heads of 128 for Q, K and V.
 WAN22_QKV_PROJ = QkvProjectionConfig(
     name="wan22_qkv_projection", seq=75600, hidden=5120, n_q_heads=40, n_k_heads=40,
     head_dim=128, dtype=torch.bfloat16, eps=1e-6, seed=1006)
+WAN22_QKV_PROJ_FP8 = dataclasses.replace(WAN22_QKV_PROJ, name="wan22_qkv_projection_fp8", seed=1007,
+                                         operands="fp8")
+
+
+def quantize_rows_e4m3(x: torch.Tensor):
+    """Row-wise FP8 E4M3 quantisation of the operands (what the producer of a
+    ROW_MX operand hands over): scale = max|row| / 448, codes = RNE(x / scale).
+    Returns (codes as float8_e4m3fn, fp32 scales)."""
+    amax = x.float().abs().amax(dim=1).clamp_min(1e-12)
+    scale = amax / 448.0
+    codes = (x.float() / scale[:, None]).to(torch.float8_e4m3fn)
+    return codes, scale.contiguous()
 
 
 def make_qkv_projection(cfg: QkvProjectionConfig, device="cpu", **override):
@@ -200,9 +213,14 @@ def make_qkv_projection(cfg: QkvProjectionConfig, device="cpu", **override):
         cos, sin = wan_3d_table(21, 45, 80, d, device=device)
     else:
         cos, sin = rotate_half_table_1d(torch.arange(cfg.seq, device=device), d)
-    return dict(cfg=cfg, a=a, w=w, bias=bias, q_gamma=q_gamma, k_gamma=k_gamma,
-                cos=cos.to(cfg.dtype)[None].contiguous(), sin=sin.to(cfg.dtype)[None].contiguous(),
-                eps=cfg.eps, out_features=I)
+    d = dict(cfg=cfg, a=a, w=w, bias=bias, q_gamma=q_gamma, k_gamma=k_gamma,
+             cos=cos.to(cfg.dtype)[None].contiguous(), sin=sin.to(cfg.dtype)[None].contiguous(),
+             eps=cfg.eps, out_features=I)
+    if cfg.operands == "fp8":
+        # FP8 operands from the same draws, quantised per activation row and per output channel
+        d["a8"], d["a_scale"] = quantize_rows_e4m3(a)
+        d["w8"], d["w_scale"] = quantize_rows_e4m3(w)
+    return d
 
 
 def flops_qkv_projection(cfg: QkvProjectionConfig) -> int:
