@@ -15,13 +15,14 @@ split) timed the same way, cold (L2 and MALL evicted by reading 1 GiB before
 every launch) and hot, and the other forms of the QK operator on the Wan2.2
 shape: per-head norm, and the two passes of the across-heads norm split over
 tp = 4 ranks at one rank's share (10 + 10 heads); and the QKV projection
-(75600 x 5120 -> 15360, bf16 matrix cores) with the norm's sums in its
-epilogue followed by the apply pass, next to the unfused pipeline of a
-library GEMM (torch.addmm, hipBLASLt) and the single-pass epilogue kernel.
+(75600 x 5120 -> 15360 on the matrix cores, bf16 operands and FP8 ROW_MX
+operands) with the norm's sums in its epilogue followed by the apply pass,
+next to the unfused pipeline of a library GEMM (torch.addmm /
+torch._scaled_mm, hipBLASLt) and the single-pass epilogue kernel.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv] [--no-forms] [--no-proj]
-       python bench.py --profile {across,per_head,split_sumsq,split_apply,proj,kv_v1_prefill,
-                                  kv_v1_decode,kv_v2,copy}
+       python bench.py --profile {across,per_head,split_sumsq,split_apply,proj,proj_fp8,
+                                  kv_v1_prefill,kv_v1_decode,kv_v2,copy}
        (a short fixed run of one kernel, for rocprofv3 counter collection)
        python bench.py --summarize DIR
        (turn the rocprofv3 CSVs under DIR into the text summaries and the
@@ -41,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 matrix-core peak
+PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 matrix-core peak
 METRIC = "achieved HBM GB/s (% of MI355X peak) + tokens/s for fused norm+RoPE(+cache)"
 KERNEL_SOURCES = {
     "qk_across_heads": ["qk_rmsnorm_rope_amd/csrc/qk_across_heads.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
@@ -88,7 +90,7 @@ def parse():
     ap.add_argument("--no-proj", action="store_true", help="skip the QKV projection")
     ap.add_argument("--cold-iters", type=int, default=30)
     ap.add_argument("--profile", default=None,
-                    choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "kv_v1_prefill",
+                    choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "proj_fp8", "kv_v1_prefill",
                              "kv_v1_decode", "kv_v2", "copy"])
     ap.add_argument("--summarize", default=None, metavar="DIR")
     return ap.parse_args()
@@ -196,6 +198,37 @@ def proj_setup(torch, W, Q):
     return cfg, d, proj, apply, fused_epilogue, lib_gemm
 
 
+def proj_fp8_measure(torch, W, Q, apply, epilogue):
+    """The same projection with FP8 E4M3 operands and ROW_MX scales, next to
+    torch._scaled_mm with row-wise scales (hipBLASLt)."""
+    cfg = W.WAN22_QKV_PROJ_FP8
+    d = W.make_qkv_projection(cfg, device="cuda")
+    S, I = cfg.seq, d["out_features"]
+    flops = W.flops_qkv_projection(cfg)
+    out = torch.empty(S, I, dtype=torch.bfloat16, device="cuda")
+    sums = torch.empty(2, S, 40, dtype=torch.float32, device="cuda")
+    proj = Q.prepare_qkv_projection(d["a8"], d["w8"], d["bias"], out=out, q_cols=5120, k_cols=5120, sumsq=sums,
+                                    a_scale=d["a_scale"], w_scale=d["w_scale"])
+    res = {"workload": "the same projection with FP8 E4M3 operands, per-row and per-channel fp32 scales (ROW_MX)"}
+    for _ in range(3):
+        proj()
+    us = time_hot(torch, proj, 10)
+    res["projection_with_sums_us"] = round(us, 1)
+    res["projection_tflops"] = round(flops / us / 1e6, 1)
+    res["projection_frac_fp8_peak"] = round(flops / us / 1e6 / PEAK_FP8_TFLOPS, 4)
+    try:
+        wt, sa, sb = d["w8"].t(), d["a_scale"][:, None].contiguous(), d["w_scale"][None, :].contiguous()
+        lib = lambda: torch._scaled_mm(d["a8"], wt, scale_a=sa, scale_b=sb, bias=d["bias"], out_dtype=torch.bfloat16)
+        for _ in range(3):
+            lib()
+        lus = time_hot(torch, lib, 10)
+        res["library_gemm_torch_scaled_mm_us"] = round(lus, 1)
+        res["library_gemm_tflops"] = round(flops / lus / 1e6, 1)
+    except Exception as e:                      # the library path is a reference only
+        res["library_gemm_error"] = str(e)[:200]
+    return res
+
+
 def proj_measure(torch, W, Q):
     cfg, d, proj, apply, epilogue, lib_gemm = proj_setup(torch, W, Q)
     flops = W.flops_qkv_projection(cfg)
@@ -221,6 +254,14 @@ def proj_measure(torch, W, Q):
     res["roofline"] = {"bound": "mfma", "achieved": res["projection_tflops"], "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": res["projection_frac_bf16_peak"],
                        "traffic": measured_traffic("qkv_proj", "wan22_qkv_projection")}
+    del d, proj, lib_gemm
+    torch.cuda.empty_cache()
+    f8 = proj_fp8_measure(torch, W, Q, apply, epilogue)
+    f8["fused_pipeline_us"] = round(f8["projection_with_sums_us"] + res["apply_pass_us"], 1)
+    if "library_gemm_torch_scaled_mm_us" in f8:
+        f8["unfused_library_pipeline_us"] = round(f8["library_gemm_torch_scaled_mm_us"] +
+                                                  res["single_pass_epilogue_us"], 1)
+    res["fp8_row_mx"] = f8
     return res
 
 
@@ -398,6 +439,12 @@ def profile_run(torch, W, Q, which):
         step = forms_setup(torch, W, Q, which)
     elif which == "proj":
         step = proj_setup(torch, W, Q)[2]
+    elif which == "proj_fp8":
+        d = W.make_qkv_projection(W.WAN22_QKV_PROJ_FP8, device="cuda")
+        out = torch.empty(d["cfg"].seq, d["out_features"], dtype=torch.bfloat16, device="cuda")
+        sums = torch.empty(2, d["cfg"].seq, 40, dtype=torch.float32, device="cuda")
+        step = Q.prepare_qkv_projection(d["a8"], d["w8"], d["bias"], out=out, q_cols=5120, k_cols=5120,
+                                        sumsq=sums, a_scale=d["a_scale"], w_scale=d["w_scale"])
     else:
         cfg = {"kv_v1_prefill": W.MLA_V1_PREFILL, "kv_v1_decode": W.MLA_V1_DECODE_QUANT,
                "kv_v2": W.MLA_V2_SPLIT}[which]
@@ -416,7 +463,8 @@ PROFILE_WORKLOADS = {
     "per_head": ("qk_per_head", "wan22_per_head", ", 1>(qknr::QkParams)"),
     "split_sumsq": ("qk_split", "wan22_split_sumsq", ", 2>(qknr::QkParams)"),
     "split_apply": ("qk_split", "wan22_split_apply", ", 3>(qknr::QkParams)"),
-    "proj": ("qkv_proj", "wan22_qkv_projection", "qkv_proj_bf16_kernel"),
+    "proj": ("qkv_proj", "wan22_qkv_projection", "qkv_proj_kernel<false>"),
+    "proj_fp8": ("qkv_proj", "wan22_qkv_projection_fp8", "qkv_proj_kernel<true>"),
     "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v1_decode": ("kv_rmsnorm_rope_cache", "mla_v1_decode_quant", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v2": ("kv_rmsnorm_rope_cache", "mla_v2_split", "kv_rmsnorm_rope_cache_kernel"),
@@ -466,9 +514,12 @@ def summarize(prof_dir):
         f, w = pick(fv, needle), pick(wv, needle)
         if f is None or w is None:
             continue
-        if wname == "wan22_qkv_projection":
-            c = W.WAN22_QKV_PROJ      # compulsory bytes: A, W, bias read once; out, sums written once
-            alg = 2 * (c.seq * c.hidden + 15360 * c.hidden + 15360 + c.seq * 15360) + 4 * 2 * 40 * c.seq
+        if wname.startswith("wan22_qkv_projection"):
+            c = W.WAN22_QKV_PROJ      # compulsory bytes: A, W (and scales), bias read once; out, sums written once
+            eb = 1 if wname.endswith("fp8") else 2
+            alg = eb * (c.seq * c.hidden + 15360 * c.hidden) + 2 * (15360 + c.seq * 15360) + 4 * 2 * 40 * c.seq
+            if eb == 1:
+                alg += 4 * (c.seq + 15360)
         elif wname == "wan22_per_head":
             alg = W.algorithmic_bytes_per_head(W.WAN22_SELF_ATTN)
         elif wname.startswith("wan22_split"):
@@ -504,7 +555,8 @@ def summarize(prof_dir):
             "python -u bench.py --profile <w>\n"
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write_<w> -o p -- "
             "python -u bench.py --profile <w>\n"
-            "  for <w> in across per_head split_sumsq split_apply proj kv_v1_prefill kv_v1_decode kv_v2 copy; then "
+            "  for <w> in across per_head split_sumsq split_apply proj proj_fp8 kv_v1_prefill kv_v1_decode kv_v2 copy;\n"
+            "  then "
             "python bench.py --summarize <dir>\n")
     calib = (f"calibration (copy of 1 GiB, __amd_rocclr_copyBuffer): FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE "
              f"{cw:.1f} KiB -> scale fetch x{f_scale:.4f}, write x{w_scale:.4f}\n")
