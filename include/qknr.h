@@ -332,6 +332,7 @@ int32_t qknr_qkv_projection(const qknr_proj_args *args, hipStream_t stream);
  *   kv_strides[3], v_strides[3], rope_strides[3], k_rope_strides[3],
  *   c_kv_strides[3]: element strides of the (b, n, s) axes; the channel axis is
  *       contiguous. rope_strides[2] == 0 is the S-axis broadcast (Srope = 1).
+ *       Every stride is below 2^32 elements (QKNR_UNSUPPORTED otherwise).
  *   index            int64 device array (see Scatter): Bkv*Skv entries (NORM,
  *       PA_BNSD) or Bkv*ceil(Skv/block_size) (PA_BLK_BNSD).
  *   cache_mode       QKNR_CACHE_NORM, QKNR_CACHE_PA_BNSD or QKNR_CACHE_PA_BLK_BNSD.
@@ -340,7 +341,7 @@ int32_t qknr_qkv_projection(const qknr_proj_args *args, hipStream_t stream);
  *   k_cache_dtype, ckv_cache_dtype   dtype, QKNR_INT8, QKNR_FP8_E4M3FN or QKNR_FP8_E5M2.
  *   k_cache_strides[3], ckv_cache_strides[3]: element strides of the cache's
  *       leading axes: NORM (batch, row, head); paged (block, slot in block,
- *       head). The channel axis is contiguous.
+ *       head). The channel axis is contiguous. Below 2^32 elements.
  *   k_scale, k_offset, v_scale, v_offset   fp32 device arrays or NULL; the
  *       *_qshape fields give their shapes (QKNR_QSHAPE_*). A scale is required
  *       exactly when the cache dtype differs from dtype; an offset needs its

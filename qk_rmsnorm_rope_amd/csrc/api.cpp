@@ -287,11 +287,16 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
     if (out_kv && (!a->k_rope || !a->c_kv))
         return fail(QKNR_INVALID_ARGUMENT, "is_output_kv needs k_rope and c_kv");
 
+    const int64_t kStride32 = 1LL << 32;
     for (int i = 0; i < 3; i++) {
         if (a->kv_strides[i] < 0 || a->rope_strides[i] < 0 || (v2 && a->v_strides[i] < 0) ||
             a->k_cache_strides[i] < 0 || a->ckv_cache_strides[i] < 0 ||
             (out_kv && (a->k_rope_strides[i] < 0 || a->c_kv_strides[i] < 0)))
             return fail(QKNR_INVALID_ARGUMENT, "strides must be >= 0");
+        if (a->kv_strides[i] >= kStride32 || a->rope_strides[i] >= kStride32 || (v2 && a->v_strides[i] >= kStride32) ||
+            a->k_cache_strides[i] >= kStride32 || a->ckv_cache_strides[i] >= kStride32 ||
+            (out_kv && (a->k_rope_strides[i] >= kStride32 || a->c_kv_strides[i] >= kStride32)))
+            return fail(QKNR_UNSUPPORTED, "strides must be < 2^32 elements");
     }
 
     // vector width: 8 elements (16-byte accesses) or 4 (8-byte)
@@ -354,13 +359,17 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
         p.k_rows_whole_lines = whole(a->k_cache, (int64_t)k_dim * kb, a->k_cache_strides, kb) ? 1 : 0;
         p.c_rows_whole_lines = whole(a->ckv_cache, (int64_t)c_dim * cb, a->ckv_cache_strides, cb) ? 1 : 0;
     }
-    p.kv_b = a->kv_strides[0]; p.kv_n = a->kv_strides[1]; p.kv_s = a->kv_strides[2];
-    p.v_b = a->v_strides[0]; p.v_n = a->v_strides[1]; p.v_s = a->v_strides[2];
-    p.rope_b = a->rope_strides[0]; p.rope_n = a->rope_strides[1]; p.rope_s = a->rope_strides[2];
-    p.kr_b = a->k_rope_strides[0]; p.kr_n = a->k_rope_strides[1]; p.kr_s = a->k_rope_strides[2];
-    p.ck_b = a->c_kv_strides[0]; p.ck_n = a->c_kv_strides[1]; p.ck_s = a->c_kv_strides[2];
-    p.kc0 = a->k_cache_strides[0]; p.kc1 = a->k_cache_strides[1]; p.kc2 = a->k_cache_strides[2];
-    p.cc0 = a->ckv_cache_strides[0]; p.cc1 = a->ckv_cache_strides[1]; p.cc2 = a->ckv_cache_strides[2];
+    // strides checked above to be in [0, 2^32) where they are used; unused ones are 0
+    auto u32 = [](int64_t v) { return (uint32_t)(v >= 0 && v < (1LL << 32) ? v : 0); };
+    p.kv_b = u32(a->kv_strides[0]); p.kv_n = u32(a->kv_strides[1]); p.kv_s = u32(a->kv_strides[2]);
+    if (v2) { p.v_b = u32(a->v_strides[0]); p.v_n = u32(a->v_strides[1]); p.v_s = u32(a->v_strides[2]); }
+    p.rope_b = u32(a->rope_strides[0]); p.rope_n = u32(a->rope_strides[1]); p.rope_s = u32(a->rope_strides[2]);
+    if (out_kv) {
+        p.kr_b = u32(a->k_rope_strides[0]); p.kr_n = u32(a->k_rope_strides[1]); p.kr_s = u32(a->k_rope_strides[2]);
+        p.ck_b = u32(a->c_kv_strides[0]); p.ck_n = u32(a->c_kv_strides[1]); p.ck_s = u32(a->c_kv_strides[2]);
+    }
+    p.kc0 = u32(a->k_cache_strides[0]); p.kc1 = u32(a->k_cache_strides[1]); p.kc2 = u32(a->k_cache_strides[2]);
+    p.cc0 = u32(a->ckv_cache_strides[0]); p.cc1 = u32(a->ckv_cache_strides[1]); p.cc2 = u32(a->ckv_cache_strides[2]);
     p.capacity = capacity;
     p.heads = a->heads;
     p.mode = a->cache_mode;     // 0 Norm, 1 PA_BNSD, 2 PA_BLK_BNSD

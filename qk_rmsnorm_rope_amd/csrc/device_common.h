@@ -236,11 +236,26 @@ __device__ __forceinline__ void store_vec_nt(T *p, const float *in) {
 // cache encoders
 // ---------------------------------------------------------------------------
 
-// INT8: round half to even (v_rndne_f32), clamp to [-128, 127].
+// Every encoder returns the code in bits 0..7 of its result; the higher bits
+// are unspecified (the packers take byte 0 only). All three are branch-free.
+
+// INT8: clamp to [-128, 127], then round half to even by adding 1.5 * 2^23:
+// the sum lies in [2^23, 2^24), where fp32 spacing is 1, so the add rounds
+// the value to an integer (ties to even, as 1.5 * 2^23 is even) and the low
+// mantissa bits hold that integer in two's complement. Clamping first gives
+// the same code as rounding first because both bounds are integers. NaN
+// clamps to -128.
 __device__ __forceinline__ uint32_t enc_int8(float t) {
-    float r = __builtin_rintf(t);
-    r = fminf(fmaxf(r, -128.0f), 127.0f);
-    return (uint32_t)(int32_t)r & 0xFFu;
+    const float c = fminf(fmaxf(t, -128.0f), 127.0f);
+    return __float_as_uint(c + 12582912.0f);
+}
+
+// The subnormal field of an FP8 code: rint(|t| * 2^k) for |t| below the
+// smallest normal 2^-m (k = m + mantissa bits), computed as the low bits of
+// fma(min(|t|, 2^-m), 2^k, 2^23): the product is exact (a power-of-two
+// scaling), and the one rounding of the fma to spacing 1 is round half to even.
+__device__ __forceinline__ uint32_t fp8_subnormal_field(float af, float smallest_normal, float scale) {
+    return __float_as_uint(fmaf(fminf(af, smallest_normal), scale, 8388608.0f)) - 0x4B000000u;
 }
 
 // FP8 E4M3FN (OCP): bias 7, 3 mantissa bits, largest finite 448, no
@@ -249,24 +264,16 @@ __device__ __forceinline__ uint32_t enc_int8(float t) {
 //   below 2^-6 the format is subnormal with spacing 2^-9, so the code is the
 //   integer rint(|t| * 2^9) (0..8; 8 is the smallest normal, code 0x08);
 //   otherwise drop 20 mantissa bits with round-to-nearest-even and rebias the
-//   exponent from 127 to 7.
+//   exponent from 127 to 7. Every case is computed and the right one selected.
 __device__ __forceinline__ uint32_t enc_e4m3fn(float t) {
-    uint32_t u = __float_as_uint(t);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    float af = __uint_as_float(a);
-    uint32_t code;
-    if (a > 0x7F800000u) {
-        code = 0x7Fu;                                    // NaN
-    } else if (af >= 448.0f) {
-        code = 0x7Eu;                                    // saturate
-    } else if (af < 0.015625f) {                         // 2^-6
-        code = (uint32_t)__builtin_rintf(af * 512.0f);   // subnormal field (exact scaling)
-    } else {
-        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);    // RNE at mantissa bit 20
-        code = (r >> 20) - (120u << 3);                  // exponent 127 -> 7
-    }
-    return sign | code;
+    const uint32_t u = __float_as_uint(t);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const float af = __uint_as_float(a);
+    const uint32_t nrm = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);   // RNE at bit 20, rebias
+    uint32_t code = af < 0.015625f ? fp8_subnormal_field(af, 0.015625f, 512.0f) : nrm;
+    code = af >= 448.0f ? 0x7Eu : code;                  // saturate (inf included)
+    code = a > 0x7F800000u ? 0x7Fu : code;               // NaN
+    return ((u >> 24) & 0x80u) | code;
 }
 
 // OCP FP8 E5M2 (bias 15, 2 mantissa bits, largest finite 57344 = 0x7B, inf and
@@ -277,22 +284,24 @@ __device__ __forceinline__ uint32_t enc_e4m3fn(float t) {
 //   otherwise drop 21 mantissa bits with round-to-nearest-even and rebias the
 //   exponent from 127 to 15.
 __device__ __forceinline__ uint32_t enc_e5m2(float t) {
-    uint32_t u = __float_as_uint(t);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    float af = __uint_as_float(a);
-    uint32_t code;
-    if (a > 0x7F800000u) {
-        code = 0x7Fu;                                    // NaN
-    } else if (af >= 57344.0f) {
-        code = 0x7Bu;                                    // saturate
-    } else if (af < 6.103515625e-05f) {                  // 2^-14
-        code = (uint32_t)__builtin_rintf(af * 65536.0f); // subnormal field (exact scaling)
-    } else {
-        uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);    // RNE at mantissa bit 21
-        code = (r >> 21) - (112u << 2);                  // exponent 127 -> 15
-    }
-    return sign | code;
+    const uint32_t u = __float_as_uint(t);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const float af = __uint_as_float(a);
+    const uint32_t nrm = ((a + 0xFFFFFu + ((a >> 21) & 1u)) >> 21) - (112u << 2);   // RNE at bit 21, rebias
+    uint32_t code = af < 6.103515625e-05f ? fp8_subnormal_field(af, 6.103515625e-05f, 65536.0f) : nrm;
+    code = af >= 57344.0f ? 0x7Bu : code;
+    code = a > 0x7F800000u ? 0x7Fu : code;
+    return ((u >> 24) & 0x80u) | code;
+}
+
+// Byte 0 of each of four words -> one word (b0 lowest), with v_perm_b32.
+__device__ __forceinline__ uint32_t pack_bytes4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);   // [b0, b1, 0, 0]
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0C0C0400u);   // [b2, b3, 0, 0]
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);               // [b0, b1, b2, b3]
+}
+__device__ __forceinline__ uint32_t pack_bytes2(uint32_t b0, uint32_t b1) {
+    return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);
 }
 
 // ---------------------------------------------------------------------------

@@ -46,7 +46,7 @@
 
 namespace qknr {
 
-// Store N codes (one byte each) at p (naturally aligned).
+// Store N codes (byte 0 of each word) at p (naturally aligned).
 template <int N>
 __device__ __forceinline__ void store_codes(void *p, const uint32_t *code, bool nt) {
     if constexpr (N >= 4) {
@@ -54,12 +54,11 @@ __device__ __forceinline__ void store_codes(void *p, const uint32_t *code, bool 
         Words<W> r;
 #pragma unroll
         for (int i = 0; i < W; i++)
-            r.w[i] = code[4 * i] | (code[4 * i + 1] << 8) | (code[4 * i + 2] << 16) | (code[4 * i + 3] << 24);
+            r.w[i] = pack_bytes4(code[4 * i], code[4 * i + 1], code[4 * i + 2], code[4 * i + 3]);
         if (nt) store_words_nt<W>(p, r); else store_words<W>(p, r);
-    } else if constexpr (N == 2) {
-        *reinterpret_cast<uint16_t *>(p) = (uint16_t)(code[0] | (code[1] << 8));
     } else {
-        *reinterpret_cast<uint8_t *>(p) = (uint8_t)code[0];
+        static_assert(N == 2, "2, 4 or 8 codes");
+        *reinterpret_cast<uint16_t *>(p) = (uint16_t)pack_bytes2(code[0], code[1]);
     }
 }
 
@@ -72,29 +71,27 @@ __device__ __forceinline__ void load_qparam(const float *p, int shape, int n, in
         for (int i = 0; i < N; i++) out[i] = v;
         return;
     }
-    const float *q = p + (shape == QS_HEAD_CHANNEL ? (int64_t)n * width : 0) + c;
+    const float *q = p + (shape == QS_HEAD_CHANNEL ? n * width : 0) + c;
     if constexpr (N % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < N / 4; i++) {
             float4 v = reinterpret_cast<const float4 *>(q)[i];
             out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
         }
-    } else if constexpr (N % 2 == 0) {
+    } else {
+        static_assert(N % 2 == 0, "even parameter counts");
 #pragma unroll
         for (int i = 0; i < N / 2; i++) {
             float2 v = reinterpret_cast<const float2 *>(q)[i];
             out[2 * i] = v.x; out[2 * i + 1] = v.y;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; i++) out[i] = q[i];
     }
 }
 
-// One destination row (a cache row, with its encoding and parameters).
+// One destination row (a cache row and its quantisation parameters); the
+// encoding is a template parameter of the code that writes it.
 struct CacheRow {
     uint8_t *row;            // nullptr: no cache write for this token
-    int code;                // CacheCode
     const float *scale, *offset;
     int qshape, n, width;
     bool nt;                 // the row covers whole 128-byte lines: streaming stores
@@ -116,36 +113,34 @@ struct QuantParams {
     }
 };
 
-// Write N quantised values starting at channel c (int8 / E4M3FN, t =
-// x*scale (+offset) in fp32 with one rounding), parameters already loaded.
-template <int N>
+template <int CODE>
+__device__ __forceinline__ uint32_t encode(float t) {
+    if constexpr (CODE == CODE_INT8) return enc_int8(t);
+    else if constexpr (CODE == CODE_E4M3FN) return enc_e4m3fn(t);
+    else return enc_e5m2(t);
+}
+
+// Write N quantised values starting at channel c (t = x*scale (+offset) in
+// fp32 with one rounding), parameters already loaded.
+template <int CODE, int N>
 __device__ __forceinline__ void put_codes(const CacheRow &d, int c, const float *x, const QuantParams<N> &qp) {
-    const float *sc = qp.sc, *of = qp.of;
     uint32_t q[N];
-    if (d.code == CODE_INT8) {
 #pragma unroll
-        for (int i = 0; i < N; i++) q[i] = enc_int8(fmaf(x[i], sc[i], of[i]));
-    } else if (d.code == CODE_E4M3FN) {
-#pragma unroll
-        for (int i = 0; i < N; i++) q[i] = enc_e4m3fn(fmaf(x[i], sc[i], of[i]));
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; i++) q[i] = enc_e5m2(fmaf(x[i], sc[i], of[i]));
-    }
+    for (int i = 0; i < N; i++) q[i] = encode<CODE>(fmaf(x[i], qp.sc[i], qp.of[i]));
     store_codes<N>(d.row + c, q, d.nt);
 }
 
 // Write N values starting at channel c: quantised, or rounded to T.
-template <typename T, int N>
+template <typename T, int CODE, int N>
 __device__ __forceinline__ void put_cache(const CacheRow &d, int c, const float *x) {
-    if (d.code == CODE_SAME) {
+    if constexpr (CODE == CODE_SAME) {
         if (d.nt) store_vec_nt<T, N>(reinterpret_cast<T *>(d.row) + c, x);
         else store_vec<T, N>(reinterpret_cast<T *>(d.row) + c, x);
-        return;
+    } else {
+        QuantParams<N> qp;
+        qp.load(d.scale, d.offset, d.qshape, d.n, d.width, c);
+        put_codes<CODE, N>(d, c, x, qp);
     }
-    QuantParams<N> qp;
-    qp.load(d.scale, d.offset, d.qshape, d.n, d.width, c);
-    put_codes<N>(d, c, x, qp);
 }
 
 __device__ __forceinline__ float row_sum(float v, int G) {
@@ -187,7 +182,9 @@ struct RowPos {
     bool ok;
 };
 
-__device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t row) {
+// Row `blk * 256/G + tid/G` of the part whose lane groups are G = 2^shift wide.
+__device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t blk, int shift) {
+    const uint32_t row = (blk << (8 - shift)) + (threadIdx.x >> shift);
     RowPos r{0, 0, 0, row < p.rows};
     if (r.ok) {
         const uint32_t bn = fastdiv(row, p.seq_div);
@@ -196,6 +193,11 @@ __device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t row) {
         r.n = bn - r.b * (uint32_t)p.heads;
     }
     return r;
+}
+
+// Element offset b*sb + n*sn + s*ss (32-bit strides, 64-bit sum).
+__device__ __forceinline__ uint64_t row_off(const RowPos &r, uint32_t sb, uint32_t sn, uint32_t ss) {
+    return (uint64_t)r.b * sb + (uint64_t)r.n * sn + (uint64_t)r.s * ss;
 }
 
 // The cache slot of token (b, s), or -1. Norm and PA_BNSD: index[b*S + s].
@@ -209,11 +211,10 @@ __device__ __forceinline__ int64_t token_slot(const KvParams &p, const RowPos &r
     return start < 0 ? -1 : start + (int64_t)(r.s - run * (uint32_t)p.block_size);
 }
 
-// The cache row of token (b, s), head n, for the k cache (is_k) or the ckv cache.
-template <typename T>
-__device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int64_t slot, const RowPos &r) {
+// The cache row of token (b, s), head n, for the k cache (is_k) or the ckv
+// cache; `eb` is the cache's element size in bytes.
+__device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int eb, int64_t slot, const RowPos &r) {
     CacheRow d;
-    d.code = is_k ? p.k_code : p.c_code;
     d.scale = is_k ? p.k_scale : p.v_scale;
     d.offset = is_k ? p.k_offset : p.v_offset;
     d.qshape = is_k ? p.k_qshape : p.v_qshape;
@@ -222,31 +223,31 @@ __device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int6
     d.nt = (is_k ? p.k_rows_whole_lines : p.c_rows_whole_lines) != 0;
     d.row = nullptr;
     if (slot >= 0 && slot < p.capacity) {
-        const int64_t s0 = is_k ? p.kc0 : p.cc0, s1 = is_k ? p.kc1 : p.cc1, s2 = is_k ? p.kc2 : p.cc2;
-        int64_t off;
+        const uint32_t s0 = is_k ? p.kc0 : p.cc0, s1 = is_k ? p.kc1 : p.cc1, s2 = is_k ? p.kc2 : p.cc2;
+        uint64_t off;
         if (p.mode == 0) {
-            off = r.b * s0 + slot * s1 + r.n * s2;
+            off = (uint64_t)r.b * s0 + (uint64_t)(uint32_t)slot * s1 + (uint64_t)r.n * s2;
         } else {
             const uint32_t blk = fastdiv((uint32_t)slot, p.block_div);     // slot < capacity < 2^31
             const uint32_t in_blk = (uint32_t)slot - blk * (uint32_t)p.block_size;
-            off = blk * s0 + in_blk * s1 + r.n * s2;
+            off = (uint64_t)blk * s0 + (uint64_t)in_blk * s1 + (uint64_t)r.n * s2;
         }
-        const int eb = d.code == CODE_SAME ? (int)sizeof(T) : 1;
-        d.row = reinterpret_cast<uint8_t *>(is_k ? p.k_cache : p.ckv_cache) + off * eb;
+        d.row = reinterpret_cast<uint8_t *>(is_k ? p.k_cache : p.ckv_cache) + off * (uint32_t)eb;
     }
     return d;
 }
 
 // Part A: the normed part of a row. V1: y = RmsNorm(kv[:Dv]) -> ckv cache,
 // c_kv. V2: y = RmsNorm(kv); the first rope_size values rotated -> k cache,
-// k_rope (the planner keeps every rotated chunk in slot 0).
-template <typename T, int VEC, bool V2, int CA>
+// k_rope (the planner keeps every rotated chunk in slot 0). CODE: the
+// encoding of that cache.
+template <typename T, int VEC, bool V2, int CA, int CODE>
 __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
     constexpr int H = VEC / 2;
-    const int G = p.ga;
+    const int G = 1 << p.ga_shift;
     const int gl = threadIdx.x & (G - 1);
-    const RowPos r = row_pos(p, blk * (uint32_t)(256 / G) + threadIdx.x / (uint32_t)G);
-    const T *kv = reinterpret_cast<const T *>(p.kv) + r.b * p.kv_b + r.n * p.kv_n + r.s * p.kv_s;
+    const RowPos r = row_pos(p, blk, p.ga_shift);
+    const T *kv = reinterpret_cast<const T *>(p.kv) + row_off(r, p.kv_b, p.kv_n, p.kv_s);
     const T *gamma = reinterpret_cast<const T *>(p.gamma);
 
     Chunk<T, VEC> x[CA], gm[CA];
@@ -262,7 +263,7 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
         }
     }
     if (V2 && r.ok && gl < p.n_rope_chunks) {
-        const int64_t ro = r.b * p.rope_b + r.n * p.rope_n + r.s * p.rope_s;
+        const uint64_t ro = row_off(r, p.rope_b, p.rope_n, p.rope_s);
         rc.load(reinterpret_cast<const T *>(p.cos) + ro, reinterpret_cast<const T *>(p.sin) + ro, gl * H,
                 p.half_rope, p.stream_rope != 0);
     }
@@ -276,12 +277,12 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
     const float inv_rms = rsqrtf(ss / (float)p.rms_size + p.eps);
     if (!r.ok) return;
 
-    const CacheRow d = cache_row<T>(p, V2, slot, r);
+    const CacheRow d = cache_row(p, V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
     const bool out_kv = p.out_kv != 0;
     T *raw = nullptr;   // c_kv (V1) or k_rope (V2)
     if (out_kv)
-        raw = V2 ? reinterpret_cast<T *>(p.k_rope) + r.b * p.kr_b + r.n * p.kr_n + r.s * p.kr_s
-                 : reinterpret_cast<T *>(p.c_kv) + r.b * p.ck_b + r.n * p.ck_n + r.s * p.ck_s;
+        raw = V2 ? reinterpret_cast<T *>(p.k_rope) + row_off(r, p.kr_b, p.kr_n, p.kr_s)
+                 : reinterpret_cast<T *>(p.c_kv) + row_off(r, p.ck_b, p.ck_n, p.ck_s);
 #pragma unroll
     for (int i = 0; i < CA; i++) {
         const int c = gl + i * G;
@@ -297,15 +298,15 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
             const int j0 = c * H;
             rc.apply(y, o1, o2);
             if (d.row) {
-                put_cache<T, H>(d, j0, o1);
-                put_cache<T, H>(d, p.half_rope + j0, o2);
+                put_cache<T, CODE, H>(d, j0, o1);
+                put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
             }
             if (out_kv) {
                 store_vec_nt<T, H>(raw + j0, o1);
                 store_vec_nt<T, H>(raw + p.half_rope + j0, o2);
             }
         } else {
-            if (d.row) put_cache<T, VEC>(d, c * VEC, y);
+            if (d.row) put_cache<T, CODE, VEC>(d, c * VEC, y);
             if (out_kv) store_vec_nt<T, VEC>(raw + c * VEC, y);
         }
     }
@@ -313,29 +314,30 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
 
 // Part B: V1: interleaveRope of the raw kv[Dv:] -> k cache, k_rope.
 //         V2: v_optional -> ckv cache (quantised or copied), c_kv (copied).
-template <typename T, int VEC, bool V2, int CB>
+// CODE: the encoding of that cache.
+template <typename T, int VEC, bool V2, int CB, int CODE>
 __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
     constexpr int H = VEC / 2;
-    const int G = p.gb;
+    constexpr bool kQuantV = V2 && CODE != CODE_SAME;   // V2 quantised ckv: parameters requested with the data
+    const int G = 1 << p.gb_shift;
     const int gl = threadIdx.x & (G - 1);
-    const RowPos r = row_pos(p, blk * (uint32_t)(256 / G) + threadIdx.x / (uint32_t)G);
-    const T *src = V2 ? reinterpret_cast<const T *>(p.v) + r.b * p.v_b + r.n * p.v_n + r.s * p.v_s
-                      : reinterpret_cast<const T *>(p.kv) + r.b * p.kv_b + r.n * p.kv_n + r.s * p.kv_s + p.rms_size;
-    const int64_t ro = r.b * p.rope_b + r.n * p.rope_n + r.s * p.rope_s;
+    const RowPos r = row_pos(p, blk, p.gb_shift);
+    const T *src = V2 ? reinterpret_cast<const T *>(p.v) + row_off(r, p.v_b, p.v_n, p.v_s)
+                      : reinterpret_cast<const T *>(p.kv) + row_off(r, p.kv_b, p.kv_n, p.kv_s) + p.rms_size;
+    const uint64_t ro = row_off(r, p.rope_b, p.rope_n, p.rope_s);
     const T *cs = reinterpret_cast<const T *>(p.cos) + ro;
     const T *sn = reinterpret_cast<const T *>(p.sin) + ro;
 
     Chunk<T, VEC> z[CB];
     RopeCoef<T, H> rc[V2 ? 1 : CB];
-    QuantParams<VEC> qp[V2 ? CB : 1];     // V2 quantised ckv: requested with the data
-    const bool quant = V2 && p.c_code != CODE_SAME;
+    QuantParams<VEC> qp[kQuantV ? CB : 1];
 #pragma unroll
     for (int i = 0; i < CB; i++) {
         const int c = gl + i * G;
         if (r.ok && c < p.nx) {
             z[i].load_nt(src + c * VEC);
-            if (!V2) rc[i].load(cs, sn, c * H, p.half_rope, p.stream_rope != 0);
-            if (quant) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r.n, p.c_dim, c * VEC);
+            if constexpr (!V2) rc[i].load(cs, sn, c * H, p.half_rope, p.stream_rope != 0);
+            if constexpr (kQuantV) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r.n, p.c_dim, c * VEC);
         } else {
             z[i].zero();
         }
@@ -343,12 +345,12 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
     const int64_t slot = token_slot(p, r);
     if (!r.ok) return;
 
-    const CacheRow d = cache_row<T>(p, !V2, slot, r);
+    const CacheRow d = cache_row(p, !V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
     const bool out_kv = p.out_kv != 0;
     T *raw = nullptr;   // k_rope (V1) or c_kv (V2)
     if (out_kv)
-        raw = V2 ? reinterpret_cast<T *>(p.c_kv) + r.b * p.ck_b + r.n * p.ck_n + r.s * p.ck_s
-                 : reinterpret_cast<T *>(p.k_rope) + r.b * p.kr_b + r.n * p.kr_n + r.s * p.kr_s;
+        raw = V2 ? reinterpret_cast<T *>(p.c_kv) + row_off(r, p.ck_b, p.ck_n, p.ck_s)
+                 : reinterpret_cast<T *>(p.k_rope) + row_off(r, p.kr_b, p.kr_n, p.kr_s);
 #pragma unroll
     for (int i = 0; i < CB; i++) {
         const int c = gl + i * G;
@@ -359,8 +361,8 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
             const int j0 = c * H;
             rc[i].apply(zv, o1, o2);
             if (d.row) {
-                put_cache<T, H>(d, j0, o1);
-                put_cache<T, H>(d, p.half_rope + j0, o2);
+                put_cache<T, CODE, H>(d, j0, o1);
+                put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
             }
             if (out_kv) {
                 store_vec_nt<T, H>(raw + j0, o1);
@@ -368,7 +370,7 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
             }
         } else {
             if (d.row) {
-                if (d.code == CODE_SAME) {
+                if constexpr (CODE == CODE_SAME) {
                     T *dst = reinterpret_cast<T *>(d.row) + c * VEC;
                     if (d.nt) {
                         z[i].store_nt(dst);
@@ -381,7 +383,7 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
                 } else {
                     float zv[VEC];
                     z[i].decode(zv);
-                    put_codes<VEC>(d, c * VEC, zv, qp[i]);
+                    put_codes<CODE, VEC>(d, c * VEC, zv, qp[i]);
                 }
             }
             if (out_kv) z[i].store_nt(raw + c * VEC);
@@ -389,15 +391,36 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
     }
 }
 
-// Blocks [0, blocks_a) run part A, the rest part B. The occupancy hint keeps
-// register use low enough for many rows in flight (lower for the widest rows
-// and for two V2 value chunks with their parameters, so that no instantiation
-// spills).
+// Blocks [0, blocks_a) run part A, the rest part B; each part dispatches once
+// on the encoding of the cache it writes, so the per-chunk code is
+// specialised. The occupancy hint keeps register use low enough for many
+// rows in flight (lower for the widest rows and for two V2 value chunks with
+// their parameters, so that no instantiation spills).
 template <typename T, int VEC, bool V2, int CA, int CB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CA >= 4 ? 6 : ((CA == 3 || (V2 && CB == 2)) ? 7 : 8), 8))) void kv_rmsnorm_rope_cache_kernel(
-    KvParams p) {
-    if (blockIdx.x < p.blocks_a) part_a<T, VEC, V2, CA>(p, blockIdx.x);
-    else part_b<T, VEC, V2, CB>(p, blockIdx.x - p.blocks_a);
+    KvParams params) {
+    // Read the fields where they are used, from the kernel-argument segment
+    // (scalar loads), rather than all at entry: the entry loads of a struct
+    // this wide stay live across both parts and spill.
+    (void)params;
+    const KvParams &p = *(const KvParams *)__builtin_amdgcn_kernarg_segment_ptr();
+    if (blockIdx.x < p.blocks_a) {
+        const uint32_t blk = blockIdx.x;
+        switch (V2 ? p.k_code : p.c_code) {
+        case CODE_INT8: part_a<T, VEC, V2, CA, CODE_INT8>(p, blk); break;
+        case CODE_E4M3FN: part_a<T, VEC, V2, CA, CODE_E4M3FN>(p, blk); break;
+        case CODE_E5M2: part_a<T, VEC, V2, CA, CODE_E5M2>(p, blk); break;
+        default: part_a<T, VEC, V2, CA, CODE_SAME>(p, blk); break;
+        }
+    } else {
+        const uint32_t blk = blockIdx.x - p.blocks_a;
+        switch (V2 ? p.c_code : p.k_code) {
+        case CODE_INT8: part_b<T, VEC, V2, CB, CODE_INT8>(p, blk); break;
+        case CODE_E4M3FN: part_b<T, VEC, V2, CB, CODE_E4M3FN>(p, blk); break;
+        case CODE_E5M2: part_b<T, VEC, V2, CB, CODE_E5M2>(p, blk); break;
+        default: part_b<T, VEC, V2, CB, CODE_SAME>(p, blk); break;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -441,6 +464,8 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
     if (ga < 0 || gb < 0) return -1;
     p.ga = ga;
     p.gb = gb;
+    p.ga_shift = __builtin_ctz((unsigned)ga);
+    p.gb_shift = __builtin_ctz((unsigned)gb);
     p.blocks_a = (p.rows + (256 / ga) - 1) / (256 / ga);
     p.blocks_b = (p.rows + (256 / gb) - 1) / (256 / gb);
     if ((uint64_t)p.blocks_a + p.blocks_b >= (1ull << 31)) return -1;

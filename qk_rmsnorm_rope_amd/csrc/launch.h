@@ -134,13 +134,14 @@ struct KvParams {
     uint32_t rows;             // B*N*S (< 2^31)
     uint32_t seq;
     FastDiv seq_div, heads_div, block_div;   // row -> (b, n, s); slot -> (block, offset)
-    int64_t kv_b, kv_n, kv_s;
-    int64_t v_b, v_n, v_s;
-    int64_t rope_b, rope_n, rope_s;
-    int64_t kr_b, kr_n, kr_s;  // k_rope strides
-    int64_t ck_b, ck_n, ck_s;  // c_kv strides
-    int64_t kc0, kc1, kc2;     // k_cache strides (NORM: batch,row,head; PA: block,slot,head)
-    int64_t cc0, cc1, cc2;     // ckv_cache strides
+    // strides in elements, each < 2^32 (offsets are summed in 64 bits)
+    uint32_t kv_b, kv_n, kv_s;
+    uint32_t v_b, v_n, v_s;
+    uint32_t rope_b, rope_n, rope_s;
+    uint32_t kr_b, kr_n, kr_s; // k_rope strides
+    uint32_t ck_b, ck_n, ck_s; // c_kv strides
+    uint32_t kc0, kc1, kc2;    // k_cache strides (NORM: batch,row,head; PA: block,slot,head)
+    uint32_t cc0, cc1, cc2;    // ckv_cache strides
     int64_t capacity;          // NORM: Scache; PA: block_num*block_size
     int32_t heads;
     int32_t mode;              // 0 NORM, 1 PA_BNSD, 2 PA_BLK_BNSD
@@ -152,6 +153,7 @@ struct KvParams {
     int32_t nx;                // part B chunks per row (V1: raw rope tail; V2: v row)
     int32_t n_rope_chunks;     // V2: rope_size / VEC (normed chunks that are rotated)
     int32_t ga, gb;            // lanes per row in part A / part B: 8, 16, 32 or 64
+    int32_t ga_shift, gb_shift; // log2 of ga, gb
     uint32_t blocks_a, blocks_b;   // blocks of part A, then of part B
     int32_t k_code, c_code;    // CacheCode
     int32_t k_qshape, v_qshape;
