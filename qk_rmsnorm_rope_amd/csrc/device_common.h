@@ -270,7 +270,8 @@ __device__ __forceinline__ uint32_t enc_e4m3fn(float t) {
     const uint32_t a = u & 0x7FFFFFFFu;
     const float af = __uint_as_float(a);
     const uint32_t nrm = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);   // RNE at bit 20, rebias
-    uint32_t code = af < 0.015625f ? fp8_subnormal_field(af, 0.015625f, 512.0f) : nrm;
+    const uint32_t sub = fp8_subnormal_field(af, 0.015625f, 512.0f);
+    uint32_t code = af < 0.015625f ? sub : nrm;
     code = af >= 448.0f ? 0x7Eu : code;                  // saturate (inf included)
     code = a > 0x7F800000u ? 0x7Fu : code;               // NaN
     return ((u >> 24) & 0x80u) | code;
@@ -288,7 +289,8 @@ __device__ __forceinline__ uint32_t enc_e5m2(float t) {
     const uint32_t a = u & 0x7FFFFFFFu;
     const float af = __uint_as_float(a);
     const uint32_t nrm = ((a + 0xFFFFFu + ((a >> 21) & 1u)) >> 21) - (112u << 2);   // RNE at bit 21, rebias
-    uint32_t code = af < 6.103515625e-05f ? fp8_subnormal_field(af, 6.103515625e-05f, 65536.0f) : nrm;
+    const uint32_t sub = fp8_subnormal_field(af, 6.103515625e-05f, 65536.0f);
+    uint32_t code = af < 6.103515625e-05f ? sub : nrm;
     code = af >= 57344.0f ? 0x7Bu : code;
     code = a > 0x7F800000u ? 0x7Fu : code;
     return ((u >> 24) & 0x80u) | code;

@@ -101,6 +101,25 @@ struct CacheRow {
 template <int N>
 struct QuantParams {
     float sc[N], of[N];
+    // from a wave's staged copy [scale[width] | offset[width]] (see WaveParams)
+    // (c and width are multiples of 4 for N >= 4, of 2 for N == 2)
+    __device__ __forceinline__ void load_lds(const float *wp, int width, int c) {
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < N; i += 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(wp + c + i);
+                const float4 b = *reinterpret_cast<const float4 *>(wp + width + c + i);
+                sc[i] = a.x; sc[i + 1] = a.y; sc[i + 2] = a.z; sc[i + 3] = a.w;
+                of[i] = b.x; of[i + 1] = b.y; of[i + 2] = b.z; of[i + 3] = b.w;
+            }
+        } else {
+            static_assert(N == 2, "2, 4 or 8 parameters");
+            const float2 a = *reinterpret_cast<const float2 *>(wp + c);
+            const float2 b = *reinterpret_cast<const float2 *>(wp + width + c);
+            sc[0] = a.x; sc[1] = a.y;
+            of[0] = b.x; of[1] = b.y;
+        }
+    }
     __device__ __forceinline__ void load(const float *scale, const float *offset, int qshape, int n, int width,
                                          int c) {
         load_qparam<N>(scale, qshape, n, width, c, sc);
@@ -195,6 +214,66 @@ __device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t blk, int s
     return r;
 }
 
+// Per-channel quantisation parameters shared by every row of a wavefront,
+// staged once per wave in its own LDS region as [scale[width] | offset[width]]
+// (offset 0 if absent): one 16-byte load per lane instead of the parameters
+// of every chunk of every row through the vector cache, where they would
+// compete with the row data. Used when a wave holds several rows (G < 64),
+// the parameters are per channel or per head and channel, 2*width <=
+// lds_wave_floats (<= 512), and every row of the wave has the same head
+// (checked from its first and last row). Only the
+// wave writes and reads its region, and LDS accesses of one wave complete in
+// order, so no barrier is needed.
+extern __shared__ float4 kv_lds[];
+
+constexpr int kWaveParamFloats = 512;   // at most 2 KB per wave: two 16-byte pieces per lane
+
+struct WaveParams {
+    float4 v[2];      // staged 16-byte pieces of this lane (lane, lane + 64)
+    float *wp;        // the wave's LDS region
+    bool on;
+
+    // The head of the wave's rows, the decision, and the loads (issued first,
+    // so that the data loads behind them do not wait for them).
+    __device__ __forceinline__ void load(const KvParams &p, uint32_t blk, int shift, const float *scale,
+                                         const float *offset, int qshape, int width) {
+        const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        wp = reinterpret_cast<float *>(kv_lds) + wave * (uint32_t)p.lds_wave_floats;
+        const uint32_t first = (blk << (8 - shift)) + (wave << (6 - shift));
+        // (a wave of one row, G = 64, reads each parameter once anyway)
+        on = shift < 6 && qshape != QS_SCALAR && 2 * width <= p.lds_wave_floats && first < p.rows;
+        if (!on) return;
+        const uint32_t last = min(first + (64u >> shift) - 1u, p.rows - 1u);
+        const uint32_t bn = fastdiv(first, p.seq_div);
+        if (p.heads > 1 && qshape == QS_HEAD_CHANNEL && fastdiv(last, p.seq_div) != bn) {
+            on = false;
+            return;
+        }
+        const uint32_t n = bn - fastdiv(bn, p.heads_div) * (uint32_t)p.heads;
+        const uint64_t base = qshape == QS_HEAD_CHANNEL ? (uint64_t)n * (uint32_t)width : 0;
+        const int q4 = width >> 2;
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int q = lane + 64 * j;
+            if (q < q4) v[j] = reinterpret_cast<const float4 *>(scale + base)[q];
+            else if (q < 2 * q4) v[j] = offset ? reinterpret_cast<const float4 *>(offset + base)[q - q4]
+                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+    __device__ __forceinline__ void store(int width) const {
+        if (!on) return;
+        const int q4 = width >> 2;
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int q = lane + 64 * j;
+            if (q < 2 * q4) reinterpret_cast<float4 *>(wp)[q] = v[j];
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+};
+
 // Element offset b*sb + n*sn + s*ss (32-bit strides, 64-bit sum).
 __device__ __forceinline__ uint64_t row_off(const RowPos &r, uint32_t sb, uint32_t sn, uint32_t ss) {
     return (uint64_t)r.b * sb + (uint64_t)r.n * sn + (uint64_t)r.s * ss;
@@ -250,14 +329,29 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
     const T *kv = reinterpret_cast<const T *>(p.kv) + row_off(r, p.kv_b, p.kv_n, p.kv_s);
     const T *gamma = reinterpret_cast<const T *>(p.gamma);
 
+    // Quantisation parameters of the cache this part writes (V1: ckv, V2: k):
+    // staged per wave in LDS where possible; else V1's ([1] or [Dc], the same
+    // for every row) are requested with the data when they fit in registers
+    // and V2's are loaded at the store.
+    constexpr bool kQuant = CODE != CODE_SAME;
+    const int qwidth = V2 ? p.k_dim : p.c_dim;
+    WaveParams wpar;
+    wpar.on = false;
+    if constexpr (kQuant)
+        wpar.load(p, blk, p.ga_shift, V2 ? p.k_scale : p.v_scale, V2 ? p.k_offset : p.v_offset,
+                  V2 ? p.k_qshape : p.v_qshape, qwidth);
+    const bool kPre = !V2 && kQuant && CA == 1 && !wpar.on;
     Chunk<T, VEC> x[CA], gm[CA];
     RopeCoef<T, H> rc;
+    QuantParams<VEC> qp[(!V2 && kQuant && CA == 1) ? CA : 1];
 #pragma unroll
     for (int i = 0; i < CA; i++) {
         const int c = gl + i * G;
         if (r.ok && c < p.nr) {
             x[i].load_nt(kv + c * VEC);
             gm[i].load(gamma + c * VEC);
+            if constexpr (!V2 && kQuant && CA == 1)
+                if (kPre) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r.n, p.c_dim, c * VEC);
         } else {
             x[i].zero();
         }
@@ -268,6 +362,7 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
                 p.half_rope, p.stream_rope != 0);
     }
     const int64_t slot = token_slot(p, r);
+    if constexpr (kQuant) wpar.store(qwidth);
 
     // (1) RmsNorm statistic over rms_size values, reduced over the group
     float ss = 0.0f;
@@ -298,15 +393,33 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
             const int j0 = c * H;
             rc.apply(y, o1, o2);
             if (d.row) {
-                put_cache<T, CODE, H>(d, j0, o1);
-                put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
+                if (kQuant && wpar.on) {
+                    QuantParams<H> q1, q2;
+                    q1.load_lds(wpar.wp, qwidth, j0);
+                    q2.load_lds(wpar.wp, qwidth, p.half_rope + j0);
+                    put_codes<CODE, H>(d, j0, o1, q1);
+                    put_codes<CODE, H>(d, p.half_rope + j0, o2, q2);
+                } else {
+                    put_cache<T, CODE, H>(d, j0, o1);
+                    put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
+                }
             }
             if (out_kv) {
                 store_vec_nt<T, H>(raw + j0, o1);
                 store_vec_nt<T, H>(raw + p.half_rope + j0, o2);
             }
         } else {
-            if (d.row) put_cache<T, CODE, VEC>(d, c * VEC, y);
+            if (d.row) {
+                if (kQuant && wpar.on) {
+                    QuantParams<VEC> ql;
+                    ql.load_lds(wpar.wp, qwidth, c * VEC);
+                    put_codes<CODE, VEC>(d, c * VEC, y, ql);
+                } else if (kPre) {
+                    put_codes<CODE, VEC>(d, c * VEC, y, qp[i]);
+                } else {
+                    put_cache<T, CODE, VEC>(d, c * VEC, y);
+                }
+            }
             if (out_kv) store_vec_nt<T, VEC>(raw + c * VEC, y);
         }
     }
@@ -328,21 +441,43 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
     const T *cs = reinterpret_cast<const T *>(p.cos) + ro;
     const T *sn = reinterpret_cast<const T *>(p.sin) + ro;
 
+    // Quantisation parameters of the cache this part writes (V1: k, V2: ckv):
+    // staged per wave in LDS where possible; else requested with the data
+    // (V1's k-cache parameters, [1] or [Dk], only for one chunk per lane).
+    constexpr bool kQuant = CODE != CODE_SAME;
+    constexpr bool kPreKT = !V2 && kQuant && CB == 1;
+    const int qwidth = V2 ? p.c_dim : p.k_dim;
+    WaveParams wpar;
+    wpar.on = false;
+    if constexpr (kQuant)
+        wpar.load(p, blk, p.gb_shift, V2 ? p.v_scale : p.k_scale, V2 ? p.v_offset : p.k_offset,
+                  V2 ? p.v_qshape : p.k_qshape, qwidth);
+    const bool kPreV = kQuantV && !wpar.on;
+    const bool kPreK = kPreKT && !wpar.on;
     Chunk<T, VEC> z[CB];
     RopeCoef<T, H> rc[V2 ? 1 : CB];
     QuantParams<VEC> qp[kQuantV ? CB : 1];
+    QuantParams<H> qk1[kPreKT ? CB : 1], qk2[kPreKT ? CB : 1];
 #pragma unroll
     for (int i = 0; i < CB; i++) {
         const int c = gl + i * G;
         if (r.ok && c < p.nx) {
             z[i].load_nt(src + c * VEC);
             if constexpr (!V2) rc[i].load(cs, sn, c * H, p.half_rope, p.stream_rope != 0);
-            if constexpr (kQuantV) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r.n, p.c_dim, c * VEC);
+            if constexpr (kQuantV)
+                if (kPreV) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r.n, p.c_dim, c * VEC);
+            if constexpr (kPreKT) {
+                if (kPreK) {
+                    qk1[i].load(p.k_scale, p.k_offset, p.k_qshape, (int)r.n, p.k_dim, c * H);
+                    qk2[i].load(p.k_scale, p.k_offset, p.k_qshape, (int)r.n, p.k_dim, p.half_rope + c * H);
+                }
+            }
         } else {
             z[i].zero();
         }
     }
     const int64_t slot = token_slot(p, r);
+    if constexpr (kQuant) wpar.store(qwidth);
     if (!r.ok) return;
 
     const CacheRow d = cache_row(p, !V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
@@ -361,8 +496,19 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
             const int j0 = c * H;
             rc[i].apply(zv, o1, o2);
             if (d.row) {
-                put_cache<T, CODE, H>(d, j0, o1);
-                put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
+                if (kQuant && wpar.on) {
+                    QuantParams<H> q1, q2;
+                    q1.load_lds(wpar.wp, qwidth, j0);
+                    q2.load_lds(wpar.wp, qwidth, p.half_rope + j0);
+                    put_codes<CODE, H>(d, j0, o1, q1);
+                    put_codes<CODE, H>(d, p.half_rope + j0, o2, q2);
+                } else if (kPreK) {
+                    put_codes<CODE, H>(d, j0, o1, qk1[i]);
+                    put_codes<CODE, H>(d, p.half_rope + j0, o2, qk2[i]);
+                } else {
+                    put_cache<T, CODE, H>(d, j0, o1);
+                    put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
+                }
             }
             if (out_kv) {
                 store_vec_nt<T, H>(raw + j0, o1);
@@ -383,7 +529,13 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
                 } else {
                     float zv[VEC];
                     z[i].decode(zv);
-                    put_codes<CODE, VEC>(d, c * VEC, zv, qp[i]);
+                    if (wpar.on) {
+                        QuantParams<VEC> ql;
+                        ql.load_lds(wpar.wp, qwidth, c * VEC);
+                        put_codes<CODE, VEC>(d, c * VEC, zv, ql);
+                    } else {
+                        put_codes<CODE, VEC>(d, c * VEC, zv, qp[i]);
+                    }
                 }
             }
             if (out_kv) z[i].store_nt(raw + c * VEC);
@@ -397,7 +549,12 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
 // rows in flight (lower for the widest rows and for two V2 value chunks with
 // their parameters, so that no instantiation spills).
 template <typename T, int VEC, bool V2, int CA, int CB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CA >= 4 ? 6 : ((CA == 3 || (V2 && CB == 2)) ? 7 : 8), 8))) void kv_rmsnorm_rope_cache_kernel(
+#ifdef KV_W
+#define KV_WAVES(CA, CB, V2) KV_W
+#else
+#define KV_WAVES(CA, CB, V2) (CA >= 4 ? 6 : ((CA == 3 || (V2 && CB == 2)) ? 7 : 8))
+#endif
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV_WAVES(CA, CB, V2), 8))) void kv_rmsnorm_rope_cache_kernel(
     KvParams params) {
     // Read the fields where they are used, from the kernel-argument segment
     // (scalar loads), rather than all at entry: the entry loads of a struct
@@ -465,6 +622,15 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
     p.ga = ga;
     p.gb = gb;
     p.ga_shift = __builtin_ctz((unsigned)ga);
+    // per-wave LDS for staged quantisation parameters: 2*width floats of the
+    // widest quantised cache with per-channel parameters that fits 2 KB
+    {
+        int w = 0;
+        if (p.k_code != CODE_SAME && p.k_qshape != QS_SCALAR && 2 * p.k_dim <= kWaveParamFloats) w = p.k_dim;
+        if (p.c_code != CODE_SAME && p.v_qshape != QS_SCALAR && 2 * p.c_dim <= kWaveParamFloats && p.c_dim > w)
+            w = p.c_dim;
+        p.lds_wave_floats = 2 * w;
+    }
     p.gb_shift = __builtin_ctz((unsigned)gb);
     p.blocks_a = (p.rows + (256 / ga) - 1) / (256 / ga);
     p.blocks_b = (p.rows + (256 / gb) - 1) / (256 / gb);
@@ -477,7 +643,8 @@ static hipError_t launch_t(const KvParams &p, int ca, int cb, hipStream_t stream
     dim3 grid(p.blocks_a + p.blocks_b), block(256);
 #define QKNR_KV(CAV, CBV)                                                                                 \
     if (ca == CAV && cb == CBV) {                                                                         \
-        hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CAV, CBV>), grid, block, 0, stream, p); \
+        hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CAV, CBV>), grid, block,              \
+                           4u * (uint32_t)p.lds_wave_floats * 4u, stream, p);                             \
         return hipGetLastError();                                                                         \
     }
     QKNR_KV(1, 1) QKNR_KV(2, 1) QKNR_KV(3, 1) QKNR_KV(4, 1)

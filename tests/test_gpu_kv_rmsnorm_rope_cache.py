@@ -9,8 +9,9 @@ tokens per batch in a Norm cache, fp16 inputs, fp8 ckv in V2, scalar and
 [1, D] scale shapes, S-axis broadcast of cos/sin, the 8-byte access path, and
 determinism; FP8 E5M2 caches (with and without saturation) and PA_BLK_BNSD
 block-start indexing (full V1 prefill size; ragged runs; starts off block
-boundaries; runs marked -1). Untouched cache rows must keep their pre-filled
-bytes exactly.
+boundaries; runs marked -1); quantised rows where a wavefront's rows share one
+head (parameters staged per wave) and where they straddle two heads. Untouched
+cache rows must keep their pre-filled bytes exactly.
 """
 import numpy as np
 import pytest
@@ -119,6 +120,13 @@ VARIANTS = {
                                                      index_kind="blocks_unaligned",
                                                      ckv_cache_dtype=torch.float8_e5m2, v_offset=None,
                                                      v_scale=(1.0, 8.0, "ND"), is_output_kv=True)),
+    # 8 rows per wavefront (16496 rows) with S = 1031: waves that straddle two
+    # heads load their per-head parameters per lane, the others share them
+    "v2_waves_straddle_heads": (W.MLA_V2_SPLIT, dict(batch=2, heads=8, seq=1031, block_num=20, is_output_kv=True)),
+    # V1 with per-channel int8 parameters at 16800 rows: several rows per wave
+    "v1_channel_int8_many_rows": (W.MLA_V1_PREFILL, dict(batch=8, seq=2100, block_num=140, k_cache_dtype=torch.int8,
+                                                         ckv_cache_dtype=torch.int8, k_scale=(20.0, 40.0, "D"),
+                                                         v_scale=(20.0, 40.0, "1D"))),
     "v2_pablk_bf16_n2": (W.MLA_V2_SPLIT, dict(cache_mode=W.PA_BLK_BNSD, batch=3, heads=2, seq=129, block_num=12,
                                               k_cache_dtype=torch.bfloat16, ckv_cache_dtype=torch.bfloat16,
                                               k_scale=None, k_offset=None, v_scale=None, v_offset=None,
