@@ -46,6 +46,10 @@
 
 namespace qknr {
 
+// Per-wave LDS regions (launch-time size: 4 waves x lds_wave_bytes): staged
+// quantisation parameters, then staged codes (WaveParams, WaveCodes).
+extern __shared__ float4 kv_lds[];
+
 // Store N codes (byte 0 of each word) at p (naturally aligned).
 template <int N>
 __device__ __forceinline__ void store_codes(void *p, const uint32_t *code, bool nt) {
@@ -92,6 +96,8 @@ __device__ __forceinline__ void load_qparam(const float *p, int shape, int n, in
 // encoding is a template parameter of the code that writes it.
 struct CacheRow {
     uint8_t *row;            // nullptr: no cache write for this token
+    int32_t stage;           // >= 0: quantised codes go to kv_lds at this byte offset (the wave's copy of the row)
+    int64_t off;             // byte offset of row in its cache (-1: none)
     const float *scale, *offset;
     int qshape, n, width;
     bool nt;                 // the row covers whole 128-byte lines: streaming stores
@@ -146,7 +152,8 @@ __device__ __forceinline__ void put_codes(const CacheRow &d, int c, const float 
     uint32_t q[N];
 #pragma unroll
     for (int i = 0; i < N; i++) q[i] = encode<CODE>(fmaf(x[i], qp.sc[i], qp.of[i]));
-    store_codes<N>(d.row + c, q, d.nt);
+    if (d.stage >= 0) store_codes<N>(reinterpret_cast<uint8_t *>(kv_lds) + d.stage + c, q, false);
+    else store_codes<N>(d.row + c, q, d.nt);
 }
 
 // Write N values starting at channel c: quantised, or rounded to T.
@@ -219,12 +226,11 @@ __device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t blk, int s
 // (offset 0 if absent): one 16-byte load per lane instead of the parameters
 // of every chunk of every row through the vector cache, where they would
 // compete with the row data. Used when a wave holds several rows (G < 64),
-// the parameters are per channel or per head and channel, 2*width <=
-// lds_wave_floats (<= 512), and every row of the wave has the same head
+// the parameters are per channel or per head and channel, 8*width <=
+// lds_param_bytes (<= 2 KB), and every row of the wave has the same head
 // (checked from its first and last row). Only the
 // wave writes and reads its region, and LDS accesses of one wave complete in
 // order, so no barrier is needed.
-extern __shared__ float4 kv_lds[];
 
 constexpr int kWaveParamFloats = 512;   // at most 2 KB per wave: two 16-byte pieces per lane
 
@@ -238,10 +244,10 @@ struct WaveParams {
     __device__ __forceinline__ void load(const KvParams &p, uint32_t blk, int shift, const float *scale,
                                          const float *offset, int qshape, int width) {
         const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        wp = reinterpret_cast<float *>(kv_lds) + wave * (uint32_t)p.lds_wave_floats;
+        wp = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(kv_lds) + wave * (uint32_t)p.lds_wave_bytes);
         const uint32_t first = (blk << (8 - shift)) + (wave << (6 - shift));
         // (a wave of one row, G = 64, reads each parameter once anyway)
-        on = shift < 6 && qshape != QS_SCALAR && 2 * width <= p.lds_wave_floats && first < p.rows;
+        on = shift < 6 && qshape != QS_SCALAR && 8 * width <= p.lds_param_bytes && first < p.rows;
         if (!on) return;
         const uint32_t last = min(first + (64u >> shift) - 1u, p.rows - 1u);
         const uint32_t bn = fastdiv(first, p.seq_div);
@@ -274,6 +280,56 @@ struct WaveParams {
     }
 };
 
+// Quantised codes of the wave's rows staged in LDS (after the parameters,
+// rows of `width` bytes packed back to back) and written out in 16-byte
+// pieces: lane q takes pieces q and q + 64, so the 8..64 lanes of a row store
+// it contiguously, and whole 128-byte lines leave in one request instead of
+// the 4- and 8-byte pieces of the lanes' own chunks. The destination row of a
+// piece comes from the lane that computed the row (ds_bpermute), so every
+// lane of the wave takes part in the flush. Used when a wave holds several
+// rows and the row width is a multiple of 16 bytes.
+struct WaveCodes {
+    uint32_t buf;     // byte offset of the wave's staged rows in kv_lds
+    int width;        // bytes per row
+    bool on;
+
+    __device__ __forceinline__ void init(const KvParams &p, int shift, int width_bytes) {
+        const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        buf = wave * (uint32_t)p.lds_wave_bytes + (uint32_t)p.lds_param_bytes;
+        width = width_bytes;
+        on = shift < 6 && (width_bytes & 15) == 0 && (64 >> shift) * width_bytes <= p.lds_code_bytes;
+    }
+    // byte offset in kv_lds of this lane's row in the staging buffer
+    __device__ __forceinline__ int32_t row_buf(int shift) const {
+        return (int32_t)(buf + ((threadIdx.x & 63) >> shift) * (uint32_t)width);
+    }
+    // cache: the cache's base; off: this lane's row offset in it (-1: none).
+    // Executed by every lane.
+    __device__ __forceinline__ void flush(int shift, uint8_t *cache, int64_t off, bool nt) const {
+        __builtin_amdgcn_wave_barrier();
+        const int ppr = width >> 4;                    // pieces per row
+        const int pieces = (64 >> shift) * ppr;        // <= 128
+        const float inv_ppr = 1.0f / (float)ppr;
+        const int lane = threadIdx.x & 63;
+        const uint8_t *staged = reinterpret_cast<const uint8_t *>(kv_lds) + buf;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int q = lane + 64 * j;
+            // q / ppr for q < 128: (q + 0.5) / ppr is at least 0.5 / ppr from an integer
+            const int rw = q < pieces ? (int)(((float)q + 0.5f) * inv_ppr) : 0;
+            const int src = (rw << shift) << 2;
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(uint64_t)off);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)((uint64_t)off >> 32));
+            const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
+            if (q < pieces && o >= 0) {
+                const Words<4> v = load_words<4>(staged + q * 16);
+                uint8_t *at = cache + o + (q - rw * ppr) * 16;
+                if (nt) store_words_nt<4>(at, v); else store_words<4>(at, v);
+            }
+        }
+    }
+};
+
 // Element offset b*sb + n*sn + s*ss (32-bit strides, 64-bit sum).
 __device__ __forceinline__ uint64_t row_off(const RowPos &r, uint32_t sb, uint32_t sn, uint32_t ss) {
     return (uint64_t)r.b * sb + (uint64_t)r.n * sn + (uint64_t)r.s * ss;
@@ -301,6 +357,8 @@ __device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int 
     d.width = is_k ? p.k_dim : p.c_dim;
     d.nt = (is_k ? p.k_rows_whole_lines : p.c_rows_whole_lines) != 0;
     d.row = nullptr;
+    d.stage = -1;
+    d.off = -1;
     if (slot >= 0 && slot < p.capacity) {
         const uint32_t s0 = is_k ? p.kc0 : p.cc0, s1 = is_k ? p.kc1 : p.cc1, s2 = is_k ? p.kc2 : p.cc2;
         uint64_t off;
@@ -311,7 +369,8 @@ __device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int 
             const uint32_t in_blk = (uint32_t)slot - blk * (uint32_t)p.block_size;
             off = (uint64_t)blk * s0 + (uint64_t)in_blk * s1 + (uint64_t)r.n * s2;
         }
-        d.row = reinterpret_cast<uint8_t *>(is_k ? p.k_cache : p.ckv_cache) + off * (uint32_t)eb;
+        d.off = (int64_t)(off * (uint32_t)eb);
+        d.row = reinterpret_cast<uint8_t *>(is_k ? p.k_cache : p.ckv_cache) + d.off;
     }
     return d;
 }
@@ -370,18 +429,23 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
     for (int i = 0; i < CA; i++) ss = x[i].sumsq(ss);
     ss = row_sum(ss, G);
     const float inv_rms = rsqrtf(ss / (float)p.rms_size + p.eps);
-    if (!r.ok) return;
 
-    const CacheRow d = cache_row(p, V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
+    CacheRow d = cache_row(p, V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
+    WaveCodes wc;
+    wc.on = false;
+    if constexpr (kQuant) {
+        wc.init(p, p.ga_shift, qwidth);
+        if (wc.on) d.stage = wc.row_buf(p.ga_shift);
+    }
     const bool out_kv = p.out_kv != 0;
     T *raw = nullptr;   // c_kv (V1) or k_rope (V2)
-    if (out_kv)
+    if (out_kv && r.ok)
         raw = V2 ? reinterpret_cast<T *>(p.k_rope) + row_off(r, p.kr_b, p.kr_n, p.kr_s)
                  : reinterpret_cast<T *>(p.c_kv) + row_off(r, p.ck_b, p.ck_n, p.ck_s);
 #pragma unroll
     for (int i = 0; i < CA; i++) {
         const int c = gl + i * G;
-        if (c >= p.nr) continue;
+        if (!r.ok || c >= p.nr) continue;
         float xv[VEC], g[VEC], y[VEC];
         x[i].decode(xv);
         gm[i].decode(g);
@@ -423,6 +487,8 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
             if (out_kv) store_vec_nt<T, VEC>(raw + c * VEC, y);
         }
     }
+    if constexpr (kQuant)
+        if (wc.on) wc.flush(p.ga_shift, reinterpret_cast<uint8_t *>(V2 ? p.k_cache : p.ckv_cache), d.off, d.nt);
 }
 
 // Part B: V1: interleaveRope of the raw kv[Dv:] -> k cache, k_rope.
@@ -478,18 +544,23 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
     }
     const int64_t slot = token_slot(p, r);
     if constexpr (kQuant) wpar.store(qwidth);
-    if (!r.ok) return;
 
-    const CacheRow d = cache_row(p, !V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
+    CacheRow d = cache_row(p, !V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
+    WaveCodes wc;
+    wc.on = false;
+    if constexpr (kQuant) {
+        wc.init(p, p.gb_shift, qwidth);
+        if (wc.on) d.stage = wc.row_buf(p.gb_shift);
+    }
     const bool out_kv = p.out_kv != 0;
     T *raw = nullptr;   // k_rope (V1) or c_kv (V2)
-    if (out_kv)
+    if (out_kv && r.ok)
         raw = V2 ? reinterpret_cast<T *>(p.c_kv) + row_off(r, p.ck_b, p.ck_n, p.ck_s)
                  : reinterpret_cast<T *>(p.k_rope) + row_off(r, p.kr_b, p.kr_n, p.kr_s);
 #pragma unroll
     for (int i = 0; i < CB; i++) {
         const int c = gl + i * G;
-        if (c >= p.nx) continue;
+        if (!r.ok || c >= p.nx) continue;
         if constexpr (!V2) {
             float zv[VEC], o1[H], o2[H];
             z[i].decode(zv);
@@ -541,6 +612,8 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
             if (out_kv) z[i].store_nt(raw + c * VEC);
         }
     }
+    if constexpr (kQuant)
+        if (wc.on) wc.flush(p.gb_shift, reinterpret_cast<uint8_t *>(V2 ? p.ckv_cache : p.k_cache), d.off, d.nt);
 }
 
 // Blocks [0, blocks_a) run part A, the rest part B; each part dispatches once
@@ -622,16 +695,26 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
     p.ga = ga;
     p.gb = gb;
     p.ga_shift = __builtin_ctz((unsigned)ga);
-    // per-wave LDS for staged quantisation parameters: 2*width floats of the
-    // widest quantised cache with per-channel parameters that fits 2 KB
+    p.gb_shift = __builtin_ctz((unsigned)gb);
+    // per-wave LDS: staged quantisation parameters (2*width floats of the
+    // widest quantised cache with per-channel parameters that fits 2 KB), then
+    // staged codes (the rows of a wave, for rows whose width in bytes is a
+    // multiple of 16)
     {
         int w = 0;
         if (p.k_code != CODE_SAME && p.k_qshape != QS_SCALAR && 2 * p.k_dim <= kWaveParamFloats) w = p.k_dim;
         if (p.c_code != CODE_SAME && p.v_qshape != QS_SCALAR && 2 * p.c_dim <= kWaveParamFloats && p.c_dim > w)
             w = p.c_dim;
-        p.lds_wave_floats = 2 * w;
+        p.lds_param_bytes = 8 * w;
+        // part A writes the k cache (V2) or the ckv cache (V1); part B the other
+        const int wa = v2 ? p.k_dim : p.c_dim, ca_code = v2 ? p.k_code : p.c_code;
+        const int wb = v2 ? p.c_dim : p.k_dim, cb_code = v2 ? p.c_code : p.k_code;
+        int cbytes = 0;
+        if (ca_code != CODE_SAME && ga < 64 && wa % 16 == 0) cbytes = (64 / ga) * wa;
+        if (cb_code != CODE_SAME && gb < 64 && wb % 16 == 0 && (64 / gb) * wb > cbytes) cbytes = (64 / gb) * wb;
+        p.lds_code_bytes = cbytes;
+        p.lds_wave_bytes = p.lds_param_bytes + p.lds_code_bytes;
     }
-    p.gb_shift = __builtin_ctz((unsigned)gb);
     p.blocks_a = (p.rows + (256 / ga) - 1) / (256 / ga);
     p.blocks_b = (p.rows + (256 / gb) - 1) / (256 / gb);
     if ((uint64_t)p.blocks_a + p.blocks_b >= (1ull << 31)) return -1;
@@ -644,7 +727,7 @@ static hipError_t launch_t(const KvParams &p, int ca, int cb, hipStream_t stream
 #define QKNR_KV(CAV, CBV)                                                                                 \
     if (ca == CAV && cb == CBV) {                                                                         \
         hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CAV, CBV>), grid, block,              \
-                           4u * (uint32_t)p.lds_wave_floats * 4u, stream, p);                             \
+                           4u * (uint32_t)p.lds_wave_bytes, stream, p);                                   \
         return hipGetLastError();                                                                         \
     }
     QKNR_KV(1, 1) QKNR_KV(2, 1) QKNR_KV(3, 1) QKNR_KV(4, 1)
