@@ -616,7 +616,8 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
         if (wc.on) wc.flush(p.gb_shift, reinterpret_cast<uint8_t *>(V2 ? p.ckv_cache : p.k_cache), d.off, d.nt);
 }
 
-// Blocks [0, blocks_a) run part A, the rest part B; each part dispatches once
+// V2: blocks [0, blocks_a) run part A, the rest part B; V1 the other way
+// round. Each part dispatches once
 // on the encoding of the cache it writes, so the per-chunk code is
 // specialised. The occupancy hint keeps register use low enough for many
 // rows in flight (lower for the widest rows and for two V2 value chunks with
@@ -634,8 +635,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV_WAVES(CA
     // this wide stay live across both parts and spill.
     (void)params;
     const KvParams &p = *(const KvParams *)__builtin_amdgcn_kernarg_segment_ptr();
-    if (blockIdx.x < p.blocks_a) {
-        const uint32_t blk = blockIdx.x;
+    // V1: part B's blocks first (its rows are short and latency-bound; started
+    // early they overlap part A's stream instead of forming the tail);
+    // V2: part A's first (measured: V1 prefill -2.6 %, V2 split +9 % the other way)
+    constexpr bool kBFirst = !V2;
+    const uint32_t first_blocks = kBFirst ? p.blocks_b : p.blocks_a;
+    if (kBFirst ? blockIdx.x >= first_blocks : blockIdx.x < first_blocks) {
+        const uint32_t blk = kBFirst ? blockIdx.x - first_blocks : blockIdx.x;
         switch (V2 ? p.k_code : p.c_code) {
         case CODE_INT8: part_a<T, VEC, V2, CA, CODE_INT8>(p, blk); break;
         case CODE_E4M3FN: part_a<T, VEC, V2, CA, CODE_E4M3FN>(p, blk); break;
@@ -643,7 +649,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV_WAVES(CA
         default: part_a<T, VEC, V2, CA, CODE_SAME>(p, blk); break;
         }
     } else {
-        const uint32_t blk = blockIdx.x - p.blocks_a;
+        const uint32_t blk = kBFirst ? blockIdx.x : blockIdx.x - first_blocks;
         switch (V2 ? p.c_code : p.k_code) {
         case CODE_INT8: part_b<T, VEC, V2, CB, CODE_INT8>(p, blk); break;
         case CODE_E4M3FN: part_b<T, VEC, V2, CB, CODE_E4M3FN>(p, blk); break;
