@@ -7,8 +7,7 @@
  * the benchmark do. It shares no code, header, table or helper with the HIP
  * kernels.
  *
- * Sources (cited by page title and section; the pages are described in
- * the design doc):
+ * Sources (cited by page title and section):
  *   [qkv_cte]  "Kernel reference: qkv_cte -- Wan2.2 additions to the NKI Library
  *              QKV CTE MXFP8 projection", Design section 1 (across-heads QK
  *              RMSNorm, steps a-c) and section 2 (bundled rotate-half RoPE,
@@ -22,8 +21,8 @@
  *              table; the constraint tables for cache_mode / index.
  *
  * Everything is evaluated in IEEE double on the exactly decoded inputs and
- * rounded once at the end. Readings of points the pages leave open are listed
- * in DESIGN.md ("Readings of the pages").
+ * rounded once at the end. Where the pages leave a point open, the reading
+ * taken is stated at the function that depends on it.
  *
  * Every function here is pinned by tests/test_oracle_pins.py against closed
  * forms, hand cases, library special cases and an independent pure-Python
@@ -433,7 +432,8 @@ static double quantise(int cdtype, void *cache, int64_t pos, double x,
  *   k_scale/k_offset [N, Dk_out], v_scale/v_offset [N, Dc] fp64 or NULL (the
  *   wrapper broadcasts [1], [D], [1, D] to [N, D]).
  *   index == -1, or a slot outside the cache: the token writes no cache row
- *   (reading in the design doc).
+ *   (the pages allow -1 without saying what it does; skipping the token's
+ *   cache rows is the plainest reading, and the raw outputs are still written).
  * Outputs: caches updated in place; k_rope/c_kv (if out_kv) in in_dtype;
  * optional exact values: k_x/c_x (the values fed to Quant) and k_t/c_t (the
  * values right before rounding, = x*scale+offset, or x without quantisation).
