@@ -26,21 +26,26 @@
 //     (positions j + R/2), so the rotation needs no data exchange between
 //     lanes: each lane writes two half-chunks;
 //   * quantisation (int8 RNE + clamp, or FP8 E4M3FN / E5M2 RNE saturating) is fused
-//     into the stores; each cache row is written by whole-chunk vector stores
-//     to its slot, so there are no atomics and each output byte has one writer;
+//     into the stores; there are no atomics and each output byte has one writer;
+//     each part is specialised (one dispatch per block) on the encoding of the
+//     cache it writes;
+//   * when a wave holds several rows, quantised caches use two per-wave LDS
+//     regions: the wave's per-head (or per-channel) scale/offset rows, loaded
+//     once per wave instead of per lane and chunk, and the wave's rows of
+//     codes, written out in 16-byte pieces so that whole lines leave in one
+//     request (WaveParams, WaveCodes below);
 //   * an index of -1 (or, defensively, outside the cache) writes no cache row;
 //   * data read once (kv, v, per-row cos/sin) moves with non-temporal loads;
 //     k_rope / c_kv and cache rows made of whole 128-byte lines with
 //     non-temporal stores; cache rows that cover lines only in part (e.g. 192-
 //     or 64-byte int8 rows) with ordinary stores, so that neighbouring rows
-//     written by other waves merge in L2 before they reach HBM; gamma and the
-//     quantisation parameters, reused by every row, stay cached;
+//     written by other waves merge in L2 before they reach HBM; gamma, reused
+//     by every row, stays cached;
 //   * row -> (b, n, s) and slot -> (block, offset) use multiply-high division
-//     by the invariant sizes instead of 64-bit divides;
-//   * gamma, the cos/sin of rotated chunks and (in part B) the quantisation
-//     parameters are requested together with the row data, so their latency
-//     overlaps the HBM latency (part A loads its quantisation parameters at
-//     the store: holding them from the start would cost occupancy).
+//     by the invariant sizes instead of 64-bit divides; kernel fields are read
+//     from the kernel-argument segment where they are used;
+//   * gamma and the cos/sin of rotated chunks are requested together with the
+//     row data, so their latency overlaps the HBM latency.
 #include "device_common.h"
 #include "launch.h"
 
