@@ -36,11 +36,13 @@
 //     request (WaveParams, WaveCodes below);
 //   * an index of -1 (or, defensively, outside the cache) writes no cache row;
 //   * data read once (kv, v, per-row cos/sin) moves with non-temporal loads;
-//     k_rope / c_kv and cache rows made of whole 128-byte lines with
-//     non-temporal stores; cache rows that cover lines only in part (e.g. 192-
-//     or 64-byte int8 rows) with ordinary stores, so that neighbouring rows
-//     written by other waves merge in L2 before they reach HBM; gamma, reused
-//     by every row, stays cached;
+//     k_rope / c_kv (contiguous) and quantised cache rows made of whole
+//     128-byte lines with non-temporal stores; quantised rows that cover lines
+//     only in part (e.g. 192- or 64-byte int8 rows) with ordinary stores, so
+//     that neighbouring rows written by other waves merge in L2 before they
+//     reach HBM, and cache rows of the kv dtype with ordinary stores too
+//     (measured faster at random slots); gamma, reused by every row, stays
+//     cached;
 //   * row -> (b, n, s) and slot -> (block, offset) use multiply-high division
 //     by the invariant sizes instead of 64-bit divides; kernel fields are read
 //     from the kernel-argument segment where they are used;
@@ -360,7 +362,9 @@ __device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int 
     d.qshape = is_k ? p.k_qshape : p.v_qshape;
     d.n = (int)r.n;
     d.width = is_k ? p.k_dim : p.c_dim;
-    d.nt = (is_k ? p.k_rows_whole_lines : p.c_rows_whole_lines) != 0;
+    // streaming stores only for quantised rows made of whole lines: rows of the
+    // kv dtype at random slots do better as ordinary stores (MLA V1 prefill -5 %)
+    d.nt = eb == 1 && (is_k ? p.k_rows_whole_lines : p.c_rows_whole_lines) != 0;
     d.row = nullptr;
     d.stage = -1;
     d.off = -1;
