@@ -346,19 +346,6 @@ int32_t kv_check(const qknr_kv_args *a, KvPlan *out) {
     p.heads_div = qknr::make_fastdiv((uint32_t)a->heads);
     p.block_div = qknr::make_fastdiv((uint32_t)(a->cache_mode == QKNR_CACHE_NORM ? 1 : a->block_size));
     p.stream_rope = s_bcast ? 0 : 1;
-    {
-        // a cache row covers whole 128-byte lines when its size and every row
-        // start (base pointer and leading strides) are multiples of 128 bytes
-        const int kb = k_quant ? 1 : es, cb = c_quant ? 1 : es;
-        auto whole = [](const void *base, int64_t row_bytes, const int64_t *strides, int eb) {
-            if (row_bytes % 128 || !aligned(base, 128)) return false;
-            for (int i = 0; i < 3; i++)
-                if ((strides[i] * eb) % 128) return false;
-            return true;
-        };
-        p.k_rows_whole_lines = whole(a->k_cache, (int64_t)k_dim * kb, a->k_cache_strides, kb) ? 1 : 0;
-        p.c_rows_whole_lines = whole(a->ckv_cache, (int64_t)c_dim * cb, a->ckv_cache_strides, cb) ? 1 : 0;
-    }
     // strides checked above to be in [0, 2^32) where they are used; unused ones are 0
     auto u32 = [](int64_t v) { return (uint32_t)(v >= 0 && v < (1LL << 32) ? v : 0); };
     p.kv_b = u32(a->kv_strides[0]); p.kv_n = u32(a->kv_strides[1]); p.kv_s = u32(a->kv_strides[2]);

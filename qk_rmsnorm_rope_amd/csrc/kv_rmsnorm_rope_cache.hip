@@ -36,13 +36,11 @@
 //     request (WaveParams, WaveCodes below);
 //   * an index of -1 (or, defensively, outside the cache) writes no cache row;
 //   * data read once (kv, v, per-row cos/sin) moves with non-temporal loads;
-//     k_rope / c_kv (contiguous) and quantised cache rows made of whole
-//     128-byte lines with non-temporal stores; quantised rows that cover lines
-//     only in part (e.g. 192- or 64-byte int8 rows) with ordinary stores, so
-//     that neighbouring rows written by other waves merge in L2 before they
-//     reach HBM, and cache rows of the kv dtype with ordinary stores too
-//     (measured faster at random slots); gamma, reused by every row, stays
-//     cached;
+//     k_rope / c_kv (contiguous) with non-temporal stores; cache rows (at
+//     random slots) with ordinary stores, which measured faster for every
+//     row width here: rows that cover lines only in part (the 192-byte int8
+//     rows) merge with their neighbours in L2 before they reach HBM; gamma,
+//     reused by every row, stays cached;
 //   * row -> (b, n, s) and slot -> (block, offset) use multiply-high division
 //     by the invariant sizes instead of 64-bit divides; kernel fields are read
 //     from the kernel-argument segment where they are used;
@@ -59,14 +57,14 @@ extern __shared__ float4 kv_lds[];
 
 // Store N codes (byte 0 of each word) at p (naturally aligned).
 template <int N>
-__device__ __forceinline__ void store_codes(void *p, const uint32_t *code, bool nt) {
+__device__ __forceinline__ void store_codes(void *p, const uint32_t *code) {
     if constexpr (N >= 4) {
         constexpr int W = N / 4;
         Words<W> r;
 #pragma unroll
         for (int i = 0; i < W; i++)
             r.w[i] = pack_bytes4(code[4 * i], code[4 * i + 1], code[4 * i + 2], code[4 * i + 3]);
-        if (nt) store_words_nt<W>(p, r); else store_words<W>(p, r);
+        store_words<W>(p, r);
     } else {
         static_assert(N == 2, "2, 4 or 8 codes");
         *reinterpret_cast<uint16_t *>(p) = (uint16_t)pack_bytes2(code[0], code[1]);
@@ -107,7 +105,6 @@ struct CacheRow {
     int64_t off;             // byte offset of row in its cache (-1: none)
     const float *scale, *offset;
     int qshape, n, width;
-    bool nt;                 // the row covers whole 128-byte lines: streaming stores
 };
 
 // The scale and offset (0 if absent) of N consecutive channels from c.
@@ -159,16 +156,15 @@ __device__ __forceinline__ void put_codes(const CacheRow &d, int c, const float 
     uint32_t q[N];
 #pragma unroll
     for (int i = 0; i < N; i++) q[i] = encode<CODE>(fmaf(x[i], qp.sc[i], qp.of[i]));
-    if (d.stage >= 0) store_codes<N>(reinterpret_cast<uint8_t *>(kv_lds) + d.stage + c, q, false);
-    else store_codes<N>(d.row + c, q, d.nt);
+    if (d.stage >= 0) store_codes<N>(reinterpret_cast<uint8_t *>(kv_lds) + d.stage + c, q);
+    else store_codes<N>(d.row + c, q);
 }
 
 // Write N values starting at channel c: quantised, or rounded to T.
 template <typename T, int CODE, int N>
 __device__ __forceinline__ void put_cache(const CacheRow &d, int c, const float *x) {
     if constexpr (CODE == CODE_SAME) {
-        if (d.nt) store_vec_nt<T, N>(reinterpret_cast<T *>(d.row) + c, x);
-        else store_vec<T, N>(reinterpret_cast<T *>(d.row) + c, x);
+        store_vec<T, N>(reinterpret_cast<T *>(d.row) + c, x);
     } else {
         QuantParams<N> qp;
         qp.load(d.scale, d.offset, d.qshape, d.n, d.width, c);
@@ -312,7 +308,7 @@ struct WaveCodes {
     }
     // cache: the cache's base; off: this lane's row offset in it (-1: none).
     // Executed by every lane.
-    __device__ __forceinline__ void flush(int shift, uint8_t *cache, int64_t off, bool nt) const {
+    __device__ __forceinline__ void flush(int shift, uint8_t *cache, int64_t off) const {
         __builtin_amdgcn_wave_barrier();
         const int ppr = width >> 4;                    // pieces per row
         const int pieces = (64 >> shift) * ppr;        // <= 128
@@ -331,7 +327,7 @@ struct WaveCodes {
             if (q < pieces && o >= 0) {
                 const Words<4> v = load_words<4>(staged + q * 16);
                 uint8_t *at = cache + o + (q - rw * ppr) * 16;
-                if (nt) store_words_nt<4>(at, v); else store_words<4>(at, v);
+                store_words<4>(at, v);
             }
         }
     }
@@ -362,9 +358,6 @@ __device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int 
     d.qshape = is_k ? p.k_qshape : p.v_qshape;
     d.n = (int)r.n;
     d.width = is_k ? p.k_dim : p.c_dim;
-    // streaming stores only for quantised rows made of whole lines: rows of the
-    // kv dtype at random slots do better as ordinary stores (MLA V1 prefill -5 %)
-    d.nt = eb == 1 && (is_k ? p.k_rows_whole_lines : p.c_rows_whole_lines) != 0;
     d.row = nullptr;
     d.stage = -1;
     d.off = -1;
@@ -497,7 +490,7 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
         }
     }
     if constexpr (kQuant)
-        if (wc.on) wc.flush(p.ga_shift, reinterpret_cast<uint8_t *>(V2 ? p.k_cache : p.ckv_cache), d.off, d.nt);
+        if (wc.on) wc.flush(p.ga_shift, reinterpret_cast<uint8_t *>(V2 ? p.k_cache : p.ckv_cache), d.off);
 }
 
 // Part B: V1: interleaveRope of the raw kv[Dv:] -> k cache, k_rope.
@@ -598,14 +591,10 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
             if (d.row) {
                 if constexpr (CODE == CODE_SAME) {
                     T *dst = reinterpret_cast<T *>(d.row) + c * VEC;
-                    if (d.nt) {
-                        z[i].store_nt(dst);
-                    } else {
-                        Words<Chunk<T, VEC>::kWords> rw;
+                    Words<Chunk<T, VEC>::kWords> rw;
 #pragma unroll
-                        for (int q = 0; q < Chunk<T, VEC>::kWords; q++) rw.w[q] = z[i].w[q];
-                        store_words<Chunk<T, VEC>::kWords>(dst, rw);
-                    }
+                    for (int q = 0; q < Chunk<T, VEC>::kWords; q++) rw.w[q] = z[i].w[q];
+                    store_words<Chunk<T, VEC>::kWords>(dst, rw);
                 } else {
                     float zv[VEC];
                     z[i].decode(zv);
@@ -622,7 +611,7 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
         }
     }
     if constexpr (kQuant)
-        if (wc.on) wc.flush(p.gb_shift, reinterpret_cast<uint8_t *>(V2 ? p.ckv_cache : p.k_cache), d.off, d.nt);
+        if (wc.on) wc.flush(p.gb_shift, reinterpret_cast<uint8_t *>(V2 ? p.ckv_cache : p.k_cache), d.off);
 }
 
 // V2: blocks [0, blocks_a) run part A, the rest part B; V1 the other way

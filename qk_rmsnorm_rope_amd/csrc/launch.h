@@ -160,7 +160,6 @@ struct KvParams {
     int32_t k_qshape, v_qshape;
     int32_t out_kv;
     int32_t stream_rope;       // cos/sin read once (no S-axis broadcast): streaming loads
-    int32_t k_rows_whole_lines, c_rows_whole_lines;   // cache rows are whole 128-byte lines
     float eps;
 };
 
