@@ -127,6 +127,15 @@ VARIANTS = {
     "v1_channel_int8_many_rows": (W.MLA_V1_PREFILL, dict(batch=8, seq=2100, block_num=140, k_cache_dtype=torch.int8,
                                                          ckv_cache_dtype=torch.int8, k_scale=(20.0, 40.0, "D"),
                                                          v_scale=(20.0, 40.0, "1D"))),
+    # FP8 codes staged per wave (16384 rows, 8 per wavefront): E5M2 in V2, E4M3FN in V1
+    "v2_e5m2_both_staged": (W.MLA_V2_SPLIT, dict(batch=2, heads=8, seq=1024, block_num=16,
+                                                 k_cache_dtype=torch.float8_e5m2, ckv_cache_dtype=torch.float8_e5m2,
+                                                 k_scale=(1.0, 8.0, "ND"), v_scale=(1.0, 8.0, "ND"),
+                                                 v_offset=None)),
+    "v1_e4m3_both_many_rows": (W.MLA_V1_PREFILL, dict(batch=8, seq=2048, block_num=128,
+                                                      k_cache_dtype=torch.float8_e4m3fn,
+                                                      ckv_cache_dtype=torch.float8_e4m3fn, k_scale=(1.0, 8.0, "D"),
+                                                      v_scale=(1.0, 8.0, "1D"))),
     "v2_pablk_bf16_n2": (W.MLA_V2_SPLIT, dict(cache_mode=W.PA_BLK_BNSD, batch=3, heads=2, seq=129, block_num=12,
                                               k_cache_dtype=torch.bfloat16, ckv_cache_dtype=torch.bfloat16,
                                               k_scale=None, k_offset=None, v_scale=None, v_offset=None,
