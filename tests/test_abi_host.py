@@ -333,3 +333,16 @@ def test_kv_unbuilt_modes_and_types_are_unsupported():
     b = _kv(kdt=torch.int8, ks=f32(64), bs=32)
     b.k_cache_dtype = 9                      # a cache encoding that is not built
     assert Q.kv_validate(b) == Q.UNSUPPORTED
+
+
+def test_kv_strides_of_2_pow_32_elements_are_unsupported():
+    """Strides are carried as 32-bit element counts (offsets are summed in 64 bits)."""
+    a = _kv()
+    a.kv_strides[0] = 1 << 32
+    assert Q.kv_validate(a) == Q.UNSUPPORTED
+    b = _kv()
+    b.k_cache_strides[0] = (1 << 32) + 64
+    assert Q.kv_validate(b) == Q.UNSUPPORTED
+    c = _kv()
+    c.kv_strides[0] = (1 << 32) - 576            # just below the limit: accepted
+    assert Q.kv_validate(c) == Q.OK
