@@ -211,6 +211,18 @@ struct RowPos {
     bool ok;
 };
 
+// Position of row index `row`; ok is false past the last row.
+__device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t row) {
+    RowPos r{0, 0, 0, row < p.rows};
+    if (r.ok) {
+        const uint32_t bn = fastdiv(row, p.seq_div);
+        r.s = row - bn * p.seq;
+        r.b = fastdiv(bn, p.heads_div);
+        r.n = bn - r.b * (uint32_t)p.heads;
+    }
+    return r;
+}
+
 // Row `blk * 256/G + tid/G` of the part whose lane groups are G = 2^shift wide.
 __device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t blk, int shift) {
     const uint32_t row = (blk << (8 - shift)) + (threadIdx.x >> shift);
@@ -245,14 +257,15 @@ struct WaveParams {
     // The head of the wave's rows, the decision, and the loads (issued first,
     // so that the data loads behind them do not wait for them).
     __device__ __forceinline__ void load(const KvParams &p, uint32_t blk, int shift, const float *scale,
-                                         const float *offset, int qshape, int width) {
+                                         const float *offset, int qshape, int width, int rsteps = 1) {
         const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         wp = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(kv_lds) + wave * (uint32_t)p.lds_wave_bytes);
-        const uint32_t first = (blk << (8 - shift)) + (wave << (6 - shift));
+        // the wave's rows: (64 / G) consecutive rows in each of rsteps steps 256 / G apart
+        const uint32_t first = blk * ((uint32_t)rsteps << (8 - shift)) + (wave << (6 - shift));
         // (a wave of one row, G = 64, reads each parameter once anyway)
         on = shift < 6 && qshape != QS_SCALAR && 8 * width <= p.lds_param_bytes && first < p.rows;
         if (!on) return;
-        const uint32_t last = min(first + (64u >> shift) - 1u, p.rows - 1u);
+        const uint32_t last = min(first + ((uint32_t)(rsteps - 1) << (8 - shift)) + (64u >> shift) - 1u, p.rows - 1u);
         const uint32_t bn = fastdiv(first, p.seq_div);
         if (p.heads > 1 && qshape == QS_HEAD_CHANNEL && fastdiv(last, p.seq_div) != bn) {
             on = false;
@@ -296,22 +309,24 @@ struct WaveCodes {
     int width;        // bytes per row
     bool on;
 
-    __device__ __forceinline__ void init(const KvParams &p, int shift, int width_bytes) {
+    __device__ __forceinline__ void init(const KvParams &p, int shift, int width_bytes, int rsteps = 1) {
         const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         buf = wave * (uint32_t)p.lds_wave_bytes + (uint32_t)p.lds_param_bytes;
         width = width_bytes;
-        on = shift < 6 && (width_bytes & 15) == 0 && (64 >> shift) * width_bytes <= p.lds_code_bytes;
+        on = shift < 6 && (width_bytes & 15) == 0 && rsteps * (64 >> shift) * width_bytes <= p.lds_code_bytes;
     }
-    // byte offset in kv_lds of this lane's row in the staging buffer
-    __device__ __forceinline__ int32_t row_buf(int shift) const {
-        return (int32_t)(buf + ((threadIdx.x & 63) >> shift) * (uint32_t)width);
+    // byte offset in kv_lds of this lane's row of step k in the staging buffer
+    __device__ __forceinline__ int32_t row_buf(int shift, int k = 0) const {
+        return (int32_t)(buf + (uint32_t)(k * (64 >> shift) + ((threadIdx.x & 63) >> shift)) * (uint32_t)width);
     }
-    // cache: the cache's base; off: this lane's row offset in it (-1: none).
-    // Executed by every lane.
-    __device__ __forceinline__ void flush(int shift, uint8_t *cache, int64_t off) const {
+    // cache: the cache's base; off[k]: this lane's row offset in it for step k
+    // (-1: none). Executed by every lane.
+    template <int R>
+    __device__ __forceinline__ void flush(int shift, uint8_t *cache, const int64_t *off) const {
         __builtin_amdgcn_wave_barrier();
         const int ppr = width >> 4;                    // pieces per row
-        const int pieces = (64 >> shift) * ppr;        // <= 128
+        const int rpw = 64 >> shift;                   // rows per wave and step
+        const int pieces = R * rpw * ppr;              // <= 128
         const float inv_ppr = 1.0f / (float)ppr;
         const int lane = threadIdx.x & 63;
         const uint8_t *staged = reinterpret_cast<const uint8_t *>(kv_lds) + buf;
@@ -319,15 +334,19 @@ struct WaveCodes {
         for (int j = 0; j < 2; j++) {
             const int q = lane + 64 * j;
             // q / ppr for q < 128: (q + 0.5) / ppr is at least 0.5 / ppr from an integer
-            const int rw = q < pieces ? (int)(((float)q + 0.5f) * inv_ppr) : 0;
+            const int rs = q < pieces ? (int)(((float)q + 0.5f) * inv_ppr) : 0;
+            const int kstep = rs / rpw, rw = rs - kstep * rpw;
             const int src = (rw << shift) << 2;
-            const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(uint64_t)off);
-            const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)((uint64_t)off >> 32));
-            const int64_t o = (int64_t)(((uint64_t)hi << 32) | lo);
+            int64_t o = -1;
+#pragma unroll
+            for (int k = 0; k < R; k++) {
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(uint64_t)off[k]);
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)((uint64_t)off[k] >> 32));
+                if (k == kstep) o = (int64_t)(((uint64_t)hi << 32) | lo);
+            }
             if (q < pieces && o >= 0) {
                 const Words<4> v = load_words<4>(staged + q * 16);
-                uint8_t *at = cache + o + (q - rw * ppr) * 16;
-                store_words<4>(at, v);
+                store_words<4>(cache + o + (q - rs * ppr) * 16, v);
             }
         }
     }
@@ -490,143 +509,158 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
         }
     }
     if constexpr (kQuant)
-        if (wc.on) wc.flush(p.ga_shift, reinterpret_cast<uint8_t *>(V2 ? p.k_cache : p.ckv_cache), d.off);
+        if (wc.on) wc.flush<1>(p.ga_shift, reinterpret_cast<uint8_t *>(V2 ? p.k_cache : p.ckv_cache), &d.off);
 }
 
 // Part B: V1: interleaveRope of the raw kv[Dv:] -> k cache, k_rope.
 //         V2: v_optional -> ckv cache (quantised or copied), c_kv (copied).
-// CODE: the encoding of that cache.
-template <typename T, int VEC, bool V2, int CB, int CODE>
+// CODE: the encoding of that cache. Each lane takes R rows, 256/G apart, whose
+// loads are all issued before any is used.
+template <typename T, int VEC, bool V2, int CB, int CODE, int R>
 __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
     constexpr int H = VEC / 2;
-    constexpr bool kQuantV = V2 && CODE != CODE_SAME;   // V2 quantised ckv: parameters requested with the data
-    const int G = 1 << p.gb_shift;
+    constexpr bool kQuant = CODE != CODE_SAME;
+    constexpr bool kQuantV = V2 && kQuant;              // V2 quantised ckv
+    constexpr bool kPreKT = !V2 && kQuant && CB == 1 && R == 1;
+    const int shift = p.gb_shift;
+    const int G = 1 << shift;
     const int gl = threadIdx.x & (G - 1);
-    const RowPos r = row_pos(p, blk, p.gb_shift);
-    const T *src = V2 ? reinterpret_cast<const T *>(p.v) + row_off(r, p.v_b, p.v_n, p.v_s)
-                      : reinterpret_cast<const T *>(p.kv) + row_off(r, p.kv_b, p.kv_n, p.kv_s) + p.rms_size;
-    const uint64_t ro = row_off(r, p.rope_b, p.rope_n, p.rope_s);
-    const T *cs = reinterpret_cast<const T *>(p.cos) + ro;
-    const T *sn = reinterpret_cast<const T *>(p.sin) + ro;
+    const uint32_t row0 = blk * ((uint32_t)R << (8 - shift)) + (threadIdx.x >> shift);
 
     // Quantisation parameters of the cache this part writes (V1: k, V2: ckv):
     // staged per wave in LDS where possible; else requested with the data
-    // (V1's k-cache parameters, [1] or [Dk], only for one chunk per lane).
-    constexpr bool kQuant = CODE != CODE_SAME;
-    constexpr bool kPreKT = !V2 && kQuant && CB == 1;
+    // (one row per lane) or loaded at the store.
     const int qwidth = V2 ? p.c_dim : p.k_dim;
     WaveParams wpar;
     wpar.on = false;
     if constexpr (kQuant)
-        wpar.load(p, blk, p.gb_shift, V2 ? p.v_scale : p.k_scale, V2 ? p.v_offset : p.k_offset,
-                  V2 ? p.v_qshape : p.k_qshape, qwidth);
-    const bool kPreV = kQuantV && !wpar.on;
+        wpar.load(p, blk, shift, V2 ? p.v_scale : p.k_scale, V2 ? p.v_offset : p.k_offset,
+                  V2 ? p.v_qshape : p.k_qshape, qwidth, R);
+    const bool kPreV = kQuantV && R == 1 && !wpar.on;
     const bool kPreK = kPreKT && !wpar.on;
-    Chunk<T, VEC> z[CB];
-    RopeCoef<T, H> rc[V2 ? 1 : CB];
-    QuantParams<VEC> qp[kQuantV ? CB : 1];
+
+    RowPos r[R];
+    Chunk<T, VEC> z[R][CB];
+    RopeCoef<T, H> rc[V2 ? 1 : R][V2 ? 1 : CB];
+    QuantParams<VEC> qp[(kQuantV && R == 1) ? CB : 1];
     QuantParams<H> qk1[kPreKT ? CB : 1], qk2[kPreKT ? CB : 1];
 #pragma unroll
-    for (int i = 0; i < CB; i++) {
-        const int c = gl + i * G;
-        if (r.ok && c < p.nx) {
-            z[i].load_nt(src + c * VEC);
-            if constexpr (!V2) rc[i].load(cs, sn, c * H, p.half_rope, p.stream_rope != 0);
-            if constexpr (kQuantV)
-                if (kPreV) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r.n, p.c_dim, c * VEC);
-            if constexpr (kPreKT) {
-                if (kPreK) {
-                    qk1[i].load(p.k_scale, p.k_offset, p.k_qshape, (int)r.n, p.k_dim, c * H);
-                    qk2[i].load(p.k_scale, p.k_offset, p.k_qshape, (int)r.n, p.k_dim, p.half_rope + c * H);
-                }
-            }
-        } else {
-            z[i].zero();
-        }
-    }
-    const int64_t slot = token_slot(p, r);
-    if constexpr (kQuant) wpar.store(qwidth);
-
-    CacheRow d = cache_row(p, !V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
-    WaveCodes wc;
-    wc.on = false;
-    if constexpr (kQuant) {
-        wc.init(p, p.gb_shift, qwidth);
-        if (wc.on) d.stage = wc.row_buf(p.gb_shift);
-    }
-    const bool out_kv = p.out_kv != 0;
-    T *raw = nullptr;   // k_rope (V1) or c_kv (V2)
-    if (out_kv && r.ok)
-        raw = V2 ? reinterpret_cast<T *>(p.c_kv) + row_off(r, p.ck_b, p.ck_n, p.ck_s)
-                 : reinterpret_cast<T *>(p.k_rope) + row_off(r, p.kr_b, p.kr_n, p.kr_s);
+    for (int k = 0; k < R; k++) {
+        r[k] = row_pos(p, row0 + ((uint32_t)k << (8 - shift)));
+        const T *src = V2 ? reinterpret_cast<const T *>(p.v) + row_off(r[k], p.v_b, p.v_n, p.v_s)
+                          : reinterpret_cast<const T *>(p.kv) + row_off(r[k], p.kv_b, p.kv_n, p.kv_s) + p.rms_size;
+        const uint64_t ro = row_off(r[k], p.rope_b, p.rope_n, p.rope_s);
+        const T *cs = reinterpret_cast<const T *>(p.cos) + ro;
+        const T *sn = reinterpret_cast<const T *>(p.sin) + ro;
 #pragma unroll
-    for (int i = 0; i < CB; i++) {
-        const int c = gl + i * G;
-        if (!r.ok || c >= p.nx) continue;
-        if constexpr (!V2) {
-            float zv[VEC], o1[H], o2[H];
-            z[i].decode(zv);
-            const int j0 = c * H;
-            rc[i].apply(zv, o1, o2);
-            if (d.row) {
-                if (kQuant && wpar.on) {
-                    QuantParams<H> q1, q2;
-                    q1.load_lds(wpar.wp, qwidth, j0);
-                    q2.load_lds(wpar.wp, qwidth, p.half_rope + j0);
-                    put_codes<CODE, H>(d, j0, o1, q1);
-                    put_codes<CODE, H>(d, p.half_rope + j0, o2, q2);
-                } else if (kPreK) {
-                    put_codes<CODE, H>(d, j0, o1, qk1[i]);
-                    put_codes<CODE, H>(d, p.half_rope + j0, o2, qk2[i]);
-                } else {
-                    put_cache<T, CODE, H>(d, j0, o1);
-                    put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
-                }
-            }
-            if (out_kv) {
-                store_vec_nt<T, H>(raw + j0, o1);
-                store_vec_nt<T, H>(raw + p.half_rope + j0, o2);
-            }
-        } else {
-            if (d.row) {
-                if constexpr (CODE == CODE_SAME) {
-                    T *dst = reinterpret_cast<T *>(d.row) + c * VEC;
-                    Words<Chunk<T, VEC>::kWords> rw;
-#pragma unroll
-                    for (int q = 0; q < Chunk<T, VEC>::kWords; q++) rw.w[q] = z[i].w[q];
-                    store_words<Chunk<T, VEC>::kWords>(dst, rw);
-                } else {
-                    float zv[VEC];
-                    z[i].decode(zv);
-                    if (wpar.on) {
-                        QuantParams<VEC> ql;
-                        ql.load_lds(wpar.wp, qwidth, c * VEC);
-                        put_codes<CODE, VEC>(d, c * VEC, zv, ql);
-                    } else {
-                        put_codes<CODE, VEC>(d, c * VEC, zv, qp[i]);
+        for (int i = 0; i < CB; i++) {
+            const int c = gl + i * G;
+            if (r[k].ok && c < p.nx) {
+                z[k][i].load_nt(src + c * VEC);
+                if constexpr (!V2) rc[k][i].load(cs, sn, c * H, p.half_rope, p.stream_rope != 0);
+                if constexpr (kQuantV && R == 1)
+                    if (kPreV) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r[k].n, p.c_dim, c * VEC);
+                if constexpr (kPreKT) {
+                    if (kPreK) {
+                        qk1[i].load(p.k_scale, p.k_offset, p.k_qshape, (int)r[k].n, p.k_dim, c * H);
+                        qk2[i].load(p.k_scale, p.k_offset, p.k_qshape, (int)r[k].n, p.k_dim, p.half_rope + c * H);
                     }
                 }
+            } else {
+                z[k][i].zero();
             }
-            if (out_kv) z[i].store_nt(raw + c * VEC);
+        }
+    }
+    int64_t slot[R];
+#pragma unroll
+    for (int k = 0; k < R; k++) slot[k] = token_slot(p, r[k]);
+    if constexpr (kQuant) wpar.store(qwidth);
+
+    WaveCodes wc;
+    wc.on = false;
+    if constexpr (kQuant) wc.init(p, shift, qwidth, R);
+    const bool out_kv = p.out_kv != 0;
+    int64_t offs[R];
+#pragma unroll
+    for (int k = 0; k < R; k++) {
+        CacheRow d = cache_row(p, !V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot[k], r[k]);
+        offs[k] = d.off;
+        if (kQuant && wc.on) d.stage = wc.row_buf(shift, k);
+        T *raw = nullptr;   // k_rope (V1) or c_kv (V2)
+        if (out_kv && r[k].ok)
+            raw = V2 ? reinterpret_cast<T *>(p.c_kv) + row_off(r[k], p.ck_b, p.ck_n, p.ck_s)
+                     : reinterpret_cast<T *>(p.k_rope) + row_off(r[k], p.kr_b, p.kr_n, p.kr_s);
+#pragma unroll
+        for (int i = 0; i < CB; i++) {
+            const int c = gl + i * G;
+            if (!r[k].ok || c >= p.nx) continue;
+            if constexpr (!V2) {
+                float zv[VEC], o1[H], o2[H];
+                z[k][i].decode(zv);
+                const int j0 = c * H;
+                rc[k][i].apply(zv, o1, o2);
+                if (d.row) {
+                    if (kQuant && wpar.on) {
+                        QuantParams<H> q1, q2;
+                        q1.load_lds(wpar.wp, qwidth, j0);
+                        q2.load_lds(wpar.wp, qwidth, p.half_rope + j0);
+                        put_codes<CODE, H>(d, j0, o1, q1);
+                        put_codes<CODE, H>(d, p.half_rope + j0, o2, q2);
+                    } else if (kPreK) {
+                        put_codes<CODE, H>(d, j0, o1, qk1[i]);
+                        put_codes<CODE, H>(d, p.half_rope + j0, o2, qk2[i]);
+                    } else {
+                        put_cache<T, CODE, H>(d, j0, o1);
+                        put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
+                    }
+                }
+                if (out_kv) {
+                    store_vec_nt<T, H>(raw + j0, o1);
+                    store_vec_nt<T, H>(raw + p.half_rope + j0, o2);
+                }
+            } else {
+                if (d.row) {
+                    if constexpr (CODE == CODE_SAME) {
+                        T *dst = reinterpret_cast<T *>(d.row) + c * VEC;
+                        Words<Chunk<T, VEC>::kWords> rw;
+#pragma unroll
+                        for (int q = 0; q < Chunk<T, VEC>::kWords; q++) rw.w[q] = z[k][i].w[q];
+                        store_words<Chunk<T, VEC>::kWords>(dst, rw);
+                    } else {
+                        float zv[VEC];
+                        z[k][i].decode(zv);
+                        if (wpar.on) {
+                            QuantParams<VEC> ql;
+                            ql.load_lds(wpar.wp, qwidth, c * VEC);
+                            put_codes<CODE, VEC>(d, c * VEC, zv, ql);
+                        } else if (kPreV) {
+                            put_codes<CODE, VEC>(d, c * VEC, zv, qp[i]);
+                        } else {
+                            put_cache<T, CODE, VEC>(d, c * VEC, zv);
+                        }
+                    }
+                }
+                if (out_kv) z[k][i].store_nt(raw + c * VEC);
+            }
         }
     }
     if constexpr (kQuant)
-        if (wc.on) wc.flush(p.gb_shift, reinterpret_cast<uint8_t *>(V2 ? p.ckv_cache : p.k_cache), d.off);
+        if (wc.on) wc.flush<R>(shift, reinterpret_cast<uint8_t *>(V2 ? p.ckv_cache : p.k_cache), offs);
 }
 
 // V2: blocks [0, blocks_a) run part A, the rest part B; V1 the other way
 // round. Each part dispatches once
 // on the encoding of the cache it writes, so the per-chunk code is
-// specialised. The occupancy hint keeps register use low enough for many
-// rows in flight (lower for the widest rows and for two V2 value chunks with
-// their parameters, so that no instantiation spills).
-template <typename T, int VEC, bool V2, int CA, int CB>
+// specialised. RB: part B's rows per lane. The occupancy hint keeps register
+// use low enough for many rows in flight (lower for the widest rows, for two
+// V2 value chunks and for two rows per lane, so that no instantiation spills).
+template <typename T, int VEC, bool V2, int CA, int CB, int RB>
 #ifdef KV_W
 #define KV_WAVES(CA, CB, V2) KV_W
 #else
 #define KV_WAVES(CA, CB, V2) (CA >= 4 ? 6 : ((CA == 3 || (V2 && CB == 2)) ? 7 : 8))
 #endif
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV_WAVES(CA, CB, V2), 8))) void kv_rmsnorm_rope_cache_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 2 && KV_WAVES(CA, CB, V2) > 7 ? 7 : KV_WAVES(CA, CB, V2), 8))) void kv_rmsnorm_rope_cache_kernel(
     KvParams params) {
     // Read the fields where they are used, from the kernel-argument segment
     // (scalar loads), rather than all at entry: the entry loads of a struct
@@ -649,10 +683,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KV_WAVES(CA
     } else {
         const uint32_t blk = kBFirst ? blockIdx.x : blockIdx.x - first_blocks;
         switch (V2 ? p.c_code : p.k_code) {
-        case CODE_INT8: part_b<T, VEC, V2, CB, CODE_INT8>(p, blk); break;
-        case CODE_E4M3FN: part_b<T, VEC, V2, CB, CODE_E4M3FN>(p, blk); break;
-        case CODE_E5M2: part_b<T, VEC, V2, CB, CODE_E5M2>(p, blk); break;
-        default: part_b<T, VEC, V2, CB, CODE_SAME>(p, blk); break;
+        case CODE_INT8: part_b<T, VEC, V2, CB, CODE_INT8, RB>(p, blk); break;
+        case CODE_E4M3FN: part_b<T, VEC, V2, CB, CODE_E4M3FN, RB>(p, blk); break;
+        case CODE_E5M2: part_b<T, VEC, V2, CB, CODE_E5M2, RB>(p, blk); break;
+        default: part_b<T, VEC, V2, CB, CODE_SAME, RB>(p, blk); break;
         }
     }
 }
@@ -700,6 +734,11 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
     p.gb = gb;
     p.ga_shift = __builtin_ctz((unsigned)ga);
     p.gb_shift = __builtin_ctz((unsigned)gb);
+    // part B: two rows per lane (both rows' loads issued before either is
+    // used) when the part keeps at least 2048 waves that way; its short rows
+    // are latency-bound with one (16-byte chunks only; not for V1's two-chunk
+    // rope tails, whose coefficients would not fit)
+    p.rb = (vec == 8 && (v2 || cb == 1) && (uint64_t)p.rows * (uint64_t)gb >= 2ull * 2048ull * 64ull) ? 2 : 1;
     // per-wave LDS: staged quantisation parameters (2*width floats of the
     // widest quantised cache with per-channel parameters that fits 2 KB), then
     // staged codes (the rows of a wave, for rows whose width in bytes is a
@@ -715,12 +754,12 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
         const int wb = v2 ? p.c_dim : p.k_dim, cb_code = v2 ? p.c_code : p.k_code;
         int cbytes = 0;
         if (ca_code != CODE_SAME && ga < 64 && wa % 16 == 0) cbytes = (64 / ga) * wa;
-        if (cb_code != CODE_SAME && gb < 64 && wb % 16 == 0 && (64 / gb) * wb > cbytes) cbytes = (64 / gb) * wb;
+        if (cb_code != CODE_SAME && gb < 64 && wb % 16 == 0 && p.rb * (64 / gb) * wb > cbytes) cbytes = p.rb * (64 / gb) * wb;
         p.lds_code_bytes = cbytes;
         p.lds_wave_bytes = p.lds_param_bytes + p.lds_code_bytes;
     }
     p.blocks_a = (p.rows + (256 / ga) - 1) / (256 / ga);
-    p.blocks_b = (p.rows + (256 / gb) - 1) / (256 / gb);
+    p.blocks_b = (p.rows + (p.rb * 256 / gb) - 1) / (p.rb * 256 / gb);
     if ((uint64_t)p.blocks_a + p.blocks_b >= (1ull << 31)) return -1;
     return 0;
 }
@@ -728,14 +767,18 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
 template <typename T, int VEC, bool V2>
 static hipError_t launch_t(const KvParams &p, int ca, int cb, hipStream_t stream) {
     dim3 grid(p.blocks_a + p.blocks_b), block(256);
-#define QKNR_KV(CAV, CBV)                                                                                 \
-    if (ca == CAV && cb == CBV) {                                                                         \
-        hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CAV, CBV>), grid, block,              \
+#define QKNR_KV(CAV, CBV, RBV)                                                                            \
+    if (ca == CAV && cb == CBV && p.rb == RBV) {                                                         \
+        hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CAV, CBV, RBV>), grid, block,         \
                            4u * (uint32_t)p.lds_wave_bytes, stream, p);                                   \
         return hipGetLastError();                                                                         \
     }
-    QKNR_KV(1, 1) QKNR_KV(2, 1) QKNR_KV(3, 1) QKNR_KV(4, 1)
-    QKNR_KV(1, 2) QKNR_KV(2, 2) QKNR_KV(3, 2) QKNR_KV(4, 2)
+    QKNR_KV(1, 1, 1) QKNR_KV(2, 1, 1) QKNR_KV(3, 1, 1) QKNR_KV(4, 1, 1)
+    QKNR_KV(1, 2, 1) QKNR_KV(2, 2, 1) QKNR_KV(3, 2, 1) QKNR_KV(4, 2, 1)
+    if constexpr (VEC == 8) {
+        QKNR_KV(1, 1, 2) QKNR_KV(2, 1, 2) QKNR_KV(3, 1, 2) QKNR_KV(4, 1, 2)
+        if constexpr (V2) { QKNR_KV(1, 2, 2) QKNR_KV(2, 2, 2) QKNR_KV(3, 2, 2) QKNR_KV(4, 2, 2) }
+    }
 #undef QKNR_KV
     return hipErrorInvalidValue;
 }

@@ -127,6 +127,14 @@ VARIANTS = {
     "v1_channel_int8_many_rows": (W.MLA_V1_PREFILL, dict(batch=8, seq=2100, block_num=140, k_cache_dtype=torch.int8,
                                                          ckv_cache_dtype=torch.int8, k_scale=(20.0, 40.0, "D"),
                                                          v_scale=(20.0, 40.0, "1D"))),
+    # two rows per lane in part B (>= 32768 rows at 8 lanes per row): V2 with waves that
+    # straddle two heads (S = 2061), V1 with int8 / FP8 caches
+    "v2_two_rows_per_lane_straddle": (W.MLA_V2_SPLIT, dict(batch=2, heads=8, seq=2061, block_num=40,
+                                                           is_output_kv=True)),
+    "v1_quant_two_rows_per_lane": (W.MLA_V1_PREFILL, dict(batch=8, seq=4100, block_num=260,
+                                                          k_cache_dtype=torch.int8,
+                                                          ckv_cache_dtype=torch.float8_e4m3fn,
+                                                          k_scale=(20.0, 40.0, "D"), v_scale=(1.0, 8.0, "1D"))),
     # FP8 codes staged per wave (16384 rows, 8 per wavefront): E5M2 in V2, E4M3FN in V1
     "v2_e5m2_both_staged": (W.MLA_V2_SPLIT, dict(batch=2, heads=8, seq=1024, block_num=16,
                                                  k_cache_dtype=torch.float8_e5m2, ckv_cache_dtype=torch.float8_e5m2,
