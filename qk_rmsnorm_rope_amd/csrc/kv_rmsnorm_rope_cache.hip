@@ -313,7 +313,8 @@ struct WaveCodes {
         const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         buf = wave * (uint32_t)p.lds_wave_bytes + (uint32_t)p.lds_param_bytes;
         width = width_bytes;
-        on = shift < 6 && (width_bytes & 15) == 0 && rsteps * (64 >> shift) * width_bytes <= p.lds_code_bytes;
+        on = shift < 6 && (width_bytes & 15) == 0 && rsteps * (64 >> shift) * width_bytes <= p.lds_code_bytes &&
+             rsteps * (64 >> shift) * (width_bytes >> 4) <= 128;   // flush() moves at most two pieces per lane
     }
     // byte offset in kv_lds of this lane's row of step k in the staging buffer
     __device__ __forceinline__ int32_t row_buf(int shift, int k = 0) const {
@@ -399,117 +400,136 @@ __device__ __forceinline__ CacheRow cache_row(const KvParams &p, bool is_k, int 
 // Part A: the normed part of a row. V1: y = RmsNorm(kv[:Dv]) -> ckv cache,
 // c_kv. V2: y = RmsNorm(kv); the first rope_size values rotated -> k cache,
 // k_rope (the planner keeps every rotated chunk in slot 0). CODE: the
-// encoding of that cache.
-template <typename T, int VEC, bool V2, int CA, int CODE>
+// encoding of that cache. Each lane takes R rows, 256/G apart, whose loads
+// are all issued before any is used; gamma serves all of them.
+template <typename T, int VEC, bool V2, int CA, int CODE, int R>
 __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
     constexpr int H = VEC / 2;
-    const int G = 1 << p.ga_shift;
+    constexpr bool kQuant = CODE != CODE_SAME;
+    const int shift = p.ga_shift;
+    const int G = 1 << shift;
     const int gl = threadIdx.x & (G - 1);
-    const RowPos r = row_pos(p, blk, p.ga_shift);
-    const T *kv = reinterpret_cast<const T *>(p.kv) + row_off(r, p.kv_b, p.kv_n, p.kv_s);
+    const uint32_t row0 = blk * ((uint32_t)R << (8 - shift)) + (threadIdx.x >> shift);
     const T *gamma = reinterpret_cast<const T *>(p.gamma);
 
     // Quantisation parameters of the cache this part writes (V1: ckv, V2: k):
     // staged per wave in LDS where possible; else V1's ([1] or [Dc], the same
     // for every row) are requested with the data when they fit in registers
     // and V2's are loaded at the store.
-    constexpr bool kQuant = CODE != CODE_SAME;
     const int qwidth = V2 ? p.k_dim : p.c_dim;
     WaveParams wpar;
     wpar.on = false;
     if constexpr (kQuant)
-        wpar.load(p, blk, p.ga_shift, V2 ? p.k_scale : p.v_scale, V2 ? p.k_offset : p.v_offset,
-                  V2 ? p.k_qshape : p.v_qshape, qwidth);
-    const bool kPre = !V2 && kQuant && CA == 1 && !wpar.on;
-    Chunk<T, VEC> x[CA], gm[CA];
-    RopeCoef<T, H> rc;
-    QuantParams<VEC> qp[(!V2 && kQuant && CA == 1) ? CA : 1];
+        wpar.load(p, blk, shift, V2 ? p.k_scale : p.v_scale, V2 ? p.k_offset : p.v_offset,
+                  V2 ? p.k_qshape : p.v_qshape, qwidth, R);
+    constexpr bool kPreT = !V2 && kQuant && CA == 1 && R == 1;
+    const bool kPre = kPreT && !wpar.on;
+    RowPos r[R];
+    Chunk<T, VEC> x[R][CA], gm[CA];
+    RopeCoef<T, H> rc[V2 ? R : 1];
+    QuantParams<VEC> qp[kPreT ? CA : 1];
 #pragma unroll
-    for (int i = 0; i < CA; i++) {
-        const int c = gl + i * G;
-        if (r.ok && c < p.nr) {
-            x[i].load_nt(kv + c * VEC);
-            gm[i].load(gamma + c * VEC);
-            if constexpr (!V2 && kQuant && CA == 1)
-                if (kPre) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r.n, p.c_dim, c * VEC);
-        } else {
-            x[i].zero();
+    for (int k = 0; k < R; k++) {
+        r[k] = row_pos(p, row0 + ((uint32_t)k << (8 - shift)));
+        const T *kv = reinterpret_cast<const T *>(p.kv) + row_off(r[k], p.kv_b, p.kv_n, p.kv_s);
+#pragma unroll
+        for (int i = 0; i < CA; i++) {
+            const int c = gl + i * G;
+            if (r[k].ok && c < p.nr) {
+                x[k][i].load_nt(kv + c * VEC);
+                if (k == 0) gm[i].load(gamma + c * VEC);
+                if constexpr (kPreT)
+                    if (k == 0 && kPre) qp[i].load(p.v_scale, p.v_offset, p.v_qshape, (int)r[k].n, p.c_dim, c * VEC);
+            } else {
+                x[k][i].zero();
+            }
+        }
+        if constexpr (V2) {
+            if (r[k].ok && gl < p.n_rope_chunks) {
+                const uint64_t ro = row_off(r[k], p.rope_b, p.rope_n, p.rope_s);
+                rc[k].load(reinterpret_cast<const T *>(p.cos) + ro, reinterpret_cast<const T *>(p.sin) + ro, gl * H,
+                           p.half_rope, p.stream_rope != 0);
+            }
         }
     }
-    if (V2 && r.ok && gl < p.n_rope_chunks) {
-        const uint64_t ro = row_off(r, p.rope_b, p.rope_n, p.rope_s);
-        rc.load(reinterpret_cast<const T *>(p.cos) + ro, reinterpret_cast<const T *>(p.sin) + ro, gl * H,
-                p.half_rope, p.stream_rope != 0);
-    }
-    const int64_t slot = token_slot(p, r);
+    int64_t slot[R];
+#pragma unroll
+    for (int k = 0; k < R; k++) slot[k] = token_slot(p, r[k]);
     if constexpr (kQuant) wpar.store(qwidth);
 
     // (1) RmsNorm statistic over rms_size values, reduced over the group
-    float ss = 0.0f;
+    float inv_rms[R];
 #pragma unroll
-    for (int i = 0; i < CA; i++) ss = x[i].sumsq(ss);
-    ss = row_sum(ss, G);
-    const float inv_rms = rsqrtf(ss / (float)p.rms_size + p.eps);
+    for (int k = 0; k < R; k++) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CA; i++) ss = x[k][i].sumsq(ss);
+        ss = row_sum(ss, G);
+        inv_rms[k] = rsqrtf(ss / (float)p.rms_size + p.eps);
+    }
 
-    CacheRow d = cache_row(p, V2, CODE == CODE_SAME ? (int)sizeof(T) : 1, slot, r);
     WaveCodes wc;
     wc.on = false;
-    if constexpr (kQuant) {
-        wc.init(p, p.ga_shift, qwidth);
-        if (wc.on) d.stage = wc.row_buf(p.ga_shift);
-    }
+    if constexpr (kQuant) wc.init(p, shift, qwidth, R);
     const bool out_kv = p.out_kv != 0;
-    T *raw = nullptr;   // c_kv (V1) or k_rope (V2)
-    if (out_kv && r.ok)
-        raw = V2 ? reinterpret_cast<T *>(p.k_rope) + row_off(r, p.kr_b, p.kr_n, p.kr_s)
-                 : reinterpret_cast<T *>(p.c_kv) + row_off(r, p.ck_b, p.ck_n, p.ck_s);
+    int64_t offs[R];
 #pragma unroll
-    for (int i = 0; i < CA; i++) {
-        const int c = gl + i * G;
-        if (!r.ok || c >= p.nr) continue;
-        float xv[VEC], g[VEC], y[VEC];
-        x[i].decode(xv);
-        gm[i].decode(g);
+    for (int k = 0; k < R; k++) {
+        CacheRow d = cache_row(p, V2, kQuant ? 1 : (int)sizeof(T), slot[k], r[k]);
+        offs[k] = d.off;
+        if (kQuant && wc.on) d.stage = wc.row_buf(shift, k);
+        T *raw = nullptr;   // c_kv (V1) or k_rope (V2)
+        if (out_kv && r[k].ok)
+            raw = V2 ? reinterpret_cast<T *>(p.k_rope) + row_off(r[k], p.kr_b, p.kr_n, p.kr_s)
+                     : reinterpret_cast<T *>(p.c_kv) + row_off(r[k], p.ck_b, p.ck_n, p.ck_s);
 #pragma unroll
-        for (int e = 0; e < VEC; e++) y[e] = xv[e] * inv_rms * g[e];
-        if (V2 && i == 0 && c < p.n_rope_chunks) {
-            // (2) interleaveRope on the normed head: rope_out replaces y there
-            float o1[H], o2[H];
-            const int j0 = c * H;
-            rc.apply(y, o1, o2);
-            if (d.row) {
-                if (kQuant && wpar.on) {
-                    QuantParams<H> q1, q2;
-                    q1.load_lds(wpar.wp, qwidth, j0);
-                    q2.load_lds(wpar.wp, qwidth, p.half_rope + j0);
-                    put_codes<CODE, H>(d, j0, o1, q1);
-                    put_codes<CODE, H>(d, p.half_rope + j0, o2, q2);
-                } else {
-                    put_cache<T, CODE, H>(d, j0, o1);
-                    put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
+        for (int i = 0; i < CA; i++) {
+            const int c = gl + i * G;
+            if (!r[k].ok || c >= p.nr) continue;
+            float xv[VEC], g[VEC], y[VEC];
+            x[k][i].decode(xv);
+            gm[i].decode(g);
+#pragma unroll
+            for (int e = 0; e < VEC; e++) y[e] = xv[e] * inv_rms[k] * g[e];
+            if (V2 && i == 0 && c < p.n_rope_chunks) {
+                // (2) interleaveRope on the normed head: rope_out replaces y there
+                float o1[H], o2[H];
+                const int j0 = c * H;
+                rc[V2 ? k : 0].apply(y, o1, o2);
+                if (d.row) {
+                    if (kQuant && wpar.on) {
+                        QuantParams<H> q1, q2;
+                        q1.load_lds(wpar.wp, qwidth, j0);
+                        q2.load_lds(wpar.wp, qwidth, p.half_rope + j0);
+                        put_codes<CODE, H>(d, j0, o1, q1);
+                        put_codes<CODE, H>(d, p.half_rope + j0, o2, q2);
+                    } else {
+                        put_cache<T, CODE, H>(d, j0, o1);
+                        put_cache<T, CODE, H>(d, p.half_rope + j0, o2);
+                    }
                 }
-            }
-            if (out_kv) {
-                store_vec_nt<T, H>(raw + j0, o1);
-                store_vec_nt<T, H>(raw + p.half_rope + j0, o2);
-            }
-        } else {
-            if (d.row) {
-                if (kQuant && wpar.on) {
-                    QuantParams<VEC> ql;
-                    ql.load_lds(wpar.wp, qwidth, c * VEC);
-                    put_codes<CODE, VEC>(d, c * VEC, y, ql);
-                } else if (kPre) {
-                    put_codes<CODE, VEC>(d, c * VEC, y, qp[i]);
-                } else {
-                    put_cache<T, CODE, VEC>(d, c * VEC, y);
+                if (out_kv) {
+                    store_vec_nt<T, H>(raw + j0, o1);
+                    store_vec_nt<T, H>(raw + p.half_rope + j0, o2);
                 }
+            } else {
+                if (d.row) {
+                    if (kQuant && wpar.on) {
+                        QuantParams<VEC> ql;
+                        ql.load_lds(wpar.wp, qwidth, c * VEC);
+                        put_codes<CODE, VEC>(d, c * VEC, y, ql);
+                    } else if (kPre) {
+                        put_codes<CODE, VEC>(d, c * VEC, y, qp[i]);
+                    } else {
+                        put_cache<T, CODE, VEC>(d, c * VEC, y);
+                    }
+                }
+                if (out_kv) store_vec_nt<T, VEC>(raw + c * VEC, y);
             }
-            if (out_kv) store_vec_nt<T, VEC>(raw + c * VEC, y);
         }
     }
     if constexpr (kQuant)
-        if (wc.on) wc.flush<1>(p.ga_shift, reinterpret_cast<uint8_t *>(V2 ? p.k_cache : p.ckv_cache), &d.off);
+        if (wc.on) wc.flush<R>(shift, reinterpret_cast<uint8_t *>(V2 ? p.k_cache : p.ckv_cache), offs);
 }
 
 // Part B: V1: interleaveRope of the raw kv[Dv:] -> k cache, k_rope.
@@ -651,16 +671,17 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
 // V2: blocks [0, blocks_a) run part A, the rest part B; V1 the other way
 // round. Each part dispatches once
 // on the encoding of the cache it writes, so the per-chunk code is
-// specialised. RB: part B's rows per lane. The occupancy hint keeps register
-// use low enough for many rows in flight (lower for the widest rows, for two
-// V2 value chunks and for two rows per lane, so that no instantiation spills).
-template <typename T, int VEC, bool V2, int CA, int CB, int RB>
+// specialised. RA, RB: rows per lane in part A and part B. The occupancy hint
+// keeps register use low enough for many rows in flight (lower for the widest
+// rows, for two V2 value chunks and for two rows per lane, so that no
+// instantiation spills).
+template <typename T, int VEC, bool V2, int CA, int CB, int RA, int RB>
 #ifdef KV_W
 #define KV_WAVES(CA, CB, V2) KV_W
 #else
 #define KV_WAVES(CA, CB, V2) (CA >= 4 ? 6 : ((CA == 3 || (V2 && CB == 2)) ? 7 : 8))
 #endif
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 2 && KV_WAVES(CA, CB, V2) > 7 ? 7 : KV_WAVES(CA, CB, V2), 8))) void kv_rmsnorm_rope_cache_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RA == 2 ? 4 : (RB == 2 && KV_WAVES(CA, CB, V2) > 7 ? 7 : KV_WAVES(CA, CB, V2)), 8))) void kv_rmsnorm_rope_cache_kernel(
     KvParams params) {
     // Read the fields where they are used, from the kernel-argument segment
     // (scalar loads), rather than all at entry: the entry loads of a struct
@@ -675,10 +696,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 2 && 
     if (kBFirst ? blockIdx.x >= first_blocks : blockIdx.x < first_blocks) {
         const uint32_t blk = kBFirst ? blockIdx.x - first_blocks : blockIdx.x;
         switch (V2 ? p.k_code : p.c_code) {
-        case CODE_INT8: part_a<T, VEC, V2, CA, CODE_INT8>(p, blk); break;
-        case CODE_E4M3FN: part_a<T, VEC, V2, CA, CODE_E4M3FN>(p, blk); break;
-        case CODE_E5M2: part_a<T, VEC, V2, CA, CODE_E5M2>(p, blk); break;
-        default: part_a<T, VEC, V2, CA, CODE_SAME>(p, blk); break;
+        case CODE_INT8: part_a<T, VEC, V2, CA, CODE_INT8, RA>(p, blk); break;
+        case CODE_E4M3FN: part_a<T, VEC, V2, CA, CODE_E4M3FN, RA>(p, blk); break;
+        case CODE_E5M2: part_a<T, VEC, V2, CA, CODE_E5M2, RA>(p, blk); break;
+        default: part_a<T, VEC, V2, CA, CODE_SAME, RA>(p, blk); break;
         }
     } else {
         const uint32_t blk = kBFirst ? blockIdx.x : blockIdx.x - first_blocks;
@@ -739,6 +760,9 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
     // are latency-bound with one (16-byte chunks only; not for V1's two-chunk
     // rope tails, whose coefficients would not fit)
     p.rb = (vec == 8 && (v2 || cb == 1) && (uint64_t)p.rows * (uint64_t)gb >= 2ull * 2048ull * 64ull) ? 2 : 1;
+    // part A: two rows per lane as well in V1 (at four waves per SIMD: its rows
+    // of 512 normed values hold more registers); V2's part A measured no faster
+    p.ra = (!v2 && p.rb == 2 && (uint64_t)p.rows * (uint64_t)ga >= 2ull * 2048ull * 64ull) ? 2 : 1;
     // per-wave LDS: staged quantisation parameters (2*width floats of the
     // widest quantised cache with per-channel parameters that fits 2 KB), then
     // staged codes (the rows of a wave, for rows whose width in bytes is a
@@ -753,12 +777,13 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
         const int wa = v2 ? p.k_dim : p.c_dim, ca_code = v2 ? p.k_code : p.c_code;
         const int wb = v2 ? p.c_dim : p.k_dim, cb_code = v2 ? p.c_code : p.k_code;
         int cbytes = 0;
-        if (ca_code != CODE_SAME && ga < 64 && wa % 16 == 0) cbytes = (64 / ga) * wa;
+        if (ca_code != CODE_SAME && ga < 64 && wa % 16 == 0) cbytes = p.ra * (64 / ga) * wa;
         if (cb_code != CODE_SAME && gb < 64 && wb % 16 == 0 && p.rb * (64 / gb) * wb > cbytes) cbytes = p.rb * (64 / gb) * wb;
+        if (cbytes > 2048) cbytes = 2048;   // wider staged rows fall back to direct stores
         p.lds_code_bytes = cbytes;
         p.lds_wave_bytes = p.lds_param_bytes + p.lds_code_bytes;
     }
-    p.blocks_a = (p.rows + (256 / ga) - 1) / (256 / ga);
+    p.blocks_a = (p.rows + (p.ra * 256 / ga) - 1) / (p.ra * 256 / ga);
     p.blocks_b = (p.rows + (p.rb * 256 / gb) - 1) / (p.rb * 256 / gb);
     if ((uint64_t)p.blocks_a + p.blocks_b >= (1ull << 31)) return -1;
     return 0;
@@ -767,17 +792,21 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
 template <typename T, int VEC, bool V2>
 static hipError_t launch_t(const KvParams &p, int ca, int cb, hipStream_t stream) {
     dim3 grid(p.blocks_a + p.blocks_b), block(256);
-#define QKNR_KV(CAV, CBV, RBV)                                                                            \
-    if (ca == CAV && cb == CBV && p.rb == RBV) {                                                         \
-        hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CAV, CBV, RBV>), grid, block,         \
+#define QKNR_KV(CAV, CBV, RAV, RBV)                                                                       \
+    if (ca == CAV && cb == CBV && p.ra == RAV && p.rb == RBV) {                                           \
+        hipLaunchKernelGGL((kv_rmsnorm_rope_cache_kernel<T, VEC, V2, CAV, CBV, RAV, RBV>), grid, block,    \
                            4u * (uint32_t)p.lds_wave_bytes, stream, p);                                   \
         return hipGetLastError();                                                                         \
     }
-    QKNR_KV(1, 1, 1) QKNR_KV(2, 1, 1) QKNR_KV(3, 1, 1) QKNR_KV(4, 1, 1)
-    QKNR_KV(1, 2, 1) QKNR_KV(2, 2, 1) QKNR_KV(3, 2, 1) QKNR_KV(4, 2, 1)
+    QKNR_KV(1, 1, 1, 1) QKNR_KV(2, 1, 1, 1) QKNR_KV(3, 1, 1, 1) QKNR_KV(4, 1, 1, 1)
+    QKNR_KV(1, 2, 1, 1) QKNR_KV(2, 2, 1, 1) QKNR_KV(3, 2, 1, 1) QKNR_KV(4, 2, 1, 1)
     if constexpr (VEC == 8) {
-        QKNR_KV(1, 1, 2) QKNR_KV(2, 1, 2) QKNR_KV(3, 1, 2) QKNR_KV(4, 1, 2)
-        if constexpr (V2) { QKNR_KV(1, 2, 2) QKNR_KV(2, 2, 2) QKNR_KV(3, 2, 2) QKNR_KV(4, 2, 2) }
+        QKNR_KV(1, 1, 1, 2) QKNR_KV(2, 1, 1, 2) QKNR_KV(3, 1, 1, 2) QKNR_KV(4, 1, 1, 2)
+        if constexpr (V2) {
+            QKNR_KV(1, 2, 1, 2) QKNR_KV(2, 2, 1, 2) QKNR_KV(3, 2, 1, 2) QKNR_KV(4, 2, 1, 2)
+        } else {
+            QKNR_KV(1, 1, 2, 2) QKNR_KV(2, 1, 2, 2) QKNR_KV(3, 1, 2, 2) QKNR_KV(4, 1, 2, 2)
+        }
     }
 #undef QKNR_KV
     return hipErrorInvalidValue;

@@ -154,7 +154,7 @@ struct KvParams {
     int32_t n_rope_chunks;     // V2: rope_size / VEC (normed chunks that are rotated)
     int32_t ga, gb;            // lanes per row in part A / part B: 8, 16, 32 or 64
     int32_t ga_shift, gb_shift; // log2 of ga, gb
-    int32_t rb;                // part B: rows per lane (1 or 2)
+    int32_t ra, rb;            // rows per lane in part A / part B (1 or 2)
     int32_t lds_param_bytes, lds_code_bytes, lds_wave_bytes;   // per-wave LDS: staged parameters, staged codes
     uint32_t blocks_a, blocks_b;   // blocks of part A, then of part B
     int32_t k_code, c_code;    // CacheCode
