@@ -675,13 +675,12 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
 // keeps register use low enough for many rows in flight (lower for the widest
 // rows, for two V2 value chunks and for two rows per lane, so that no
 // instantiation spills).
+constexpr int kv_waves(int ca, int cb, bool v2, int ra, int rb) {
+    return ra == 2 ? 4 : (ca >= 4 ? 6 : ((ca == 3 || (v2 && cb == 2) || rb == 2) ? 7 : 8));
+}
+
 template <typename T, int VEC, bool V2, int CA, int CB, int RA, int RB>
-#ifdef KV_W
-#define KV_WAVES(CA, CB, V2) KV_W
-#else
-#define KV_WAVES(CA, CB, V2) (CA >= 4 ? 6 : ((CA == 3 || (V2 && CB == 2)) ? 7 : 8))
-#endif
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RA == 2 ? 4 : (RB == 2 && KV_WAVES(CA, CB, V2) > 7 ? 7 : KV_WAVES(CA, CB, V2)), 8))) void kv_rmsnorm_rope_cache_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kv_waves(CA, CB, V2, RA, RB), 8))) void kv_rmsnorm_rope_cache_kernel(
     KvParams params) {
     // Read the fields where they are used, from the kernel-argument segment
     // (scalar loads), rather than all at entry: the entry loads of a struct
