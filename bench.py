@@ -403,7 +403,9 @@ def kv_measure(torch, W, Q, flush, cold_iters):
         cfg = d["cfg"]
         for _ in range(5):
             step()
-        hot = time_hot(torch, step, 200)
+        # back-to-back launches: the median of three runs of 200 (a single run is
+        # sensitive to what ran just before: clocks, dirty lines left in the MALL)
+        hot = sorted(time_hot(torch, step, 200) for _ in range(3))[1]
         cold = time_cold(torch, step, cold_iters, flush)
         nbytes = W.algorithmic_bytes_kv_cache(cfg)
         tokens = cfg.batch * cfg.seq
