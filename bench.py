@@ -53,6 +53,8 @@ KERNEL_SOURCES = {
                  "qk_rmsnorm_rope_amd/csrc/device_common.h"],
     "qkv_proj": ["qk_rmsnorm_rope_amd/csrc/qkv_proj.hip", "qk_rmsnorm_rope_amd/csrc/device_common.h"],
     "kv_rmsnorm_rope_cache": ["qk_rmsnorm_rope_amd/csrc/kv_rmsnorm_rope_cache.hip",
+                              "qk_rmsnorm_rope_amd/csrc/kv_rmsnorm_rope_cache_f16.hip",
+                              "qk_rmsnorm_rope_amd/csrc/kv_kernel.h",
                               "qk_rmsnorm_rope_amd/csrc/device_common.h"],
 }
 

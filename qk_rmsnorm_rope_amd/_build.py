@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqknr.so")
 SOURCES = ["api.cpp", "qk_across_heads.hip", "qk_per_head.hip", "qk_split.hip", "permute.hip",
-           "qkv_proj.hip", "kv_rmsnorm_rope_cache.hip"]
+           "qkv_proj.hip", "kv_rmsnorm_rope_cache.hip",
+           "kv_rmsnorm_rope_cache_f16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
