@@ -405,8 +405,10 @@ def kv_measure(torch, W, Q, flush, cold_iters):
         cfg = d["cfg"]
         for _ in range(5):
             step()
-        # back-to-back launches: the median of three runs of 200 (a single run is
-        # sensitive to what ran just before: clocks, dirty lines left in the MALL)
+        # back-to-back launches: one untimed run of 200 first (the first
+        # milliseconds of a new workload run 2-4 % slower while the clocks
+        # settle), then the median of three runs of 200
+        time_hot(torch, step, 200)
         hot = sorted(time_hot(torch, step, 200) for _ in range(3))[1]
         cold = time_cold(torch, step, cold_iters, flush)
         nbytes = W.algorithmic_bytes_kv_cache(cfg)
