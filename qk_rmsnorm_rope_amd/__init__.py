@@ -222,7 +222,9 @@ def qk_args(q, k, q_gamma, k_gamma, cos, sin, *, eps, q_out=None, k_out=None,
         if q_gamma is None or q_gamma.numel() != gq or (nk and (k_gamma is None or k_gamma.numel() != gk)):
             raise ValueError("gammas must be [head_dim] (per head)" if per_head else
                              "gammas must be [n_heads * head_dim] (segment-wide)")
-        a.q_gamma, a.k_gamma = _ptr(q_gamma.contiguous()), _ptr(k_gamma.contiguous() if nk else None)
+        q_gamma = q_gamma.contiguous()
+        k_gamma = k_gamma.contiguous() if nk else None
+        a.q_gamma, a.k_gamma = _ptr(q_gamma), _ptr(k_gamma)
     if apply_rope:
         if (cos.dim() != 3 or cos.shape[0] not in (1, B) or cos.shape[1] != S or cos.shape[2] != d
                 or sin.shape != cos.shape or cos.stride() != sin.stride()):
