@@ -8,7 +8,10 @@ with ROW_MX scales (and without scales); the Wan2.2 width
 rows against the oracle, the per-tile sums against fp64 sums of the stored
 outputs, and the projection -> apply path against the oracle's across-heads
 operator on the stored Q|K; the full S = 75600 case on sampled rows; two runs
-bit-identical -- the last two with bf16 and with FP8 ROW_MX operands.
+bit-identical -- the last two with bf16 and with FP8 ROW_MX operands; and 16
+seeded random shapes (1-1500 rows, hidden up to 1024 bf16 / 2048 FP8 values,
+1-4 Q heads with as many or fewer K heads, with or without bias, sums over
+Q and K, Q only, or none).
 
 The projection's outputs are checked against the oracle's exact fp64 values
 at the bf16 bar; the sums against fp64 sums of the kernel's own stored bf16
@@ -200,3 +203,43 @@ def test_wan_full_size_sampled_and_deterministic(Q, fp8):
     for seg, c0 in ((0, 0), (1, 5120)):
         ref = (o[:, c0: c0 + 5120] ** 2).reshape(len(rows), 40, 128).sum(-1)
         np.testing.assert_allclose(got[seg], ref, rtol=1e-5, atol=1e-6)
+
+
+def _draw_proj(i):
+    """Seeded random projection shapes: rows 1-1500 (ragged 256-row tiles),
+    hidden 128-1024 bf16 values (or 128-2048 FP8), 1-4 Q heads and as many or
+    fewer K heads of 128, bias or not, sums over Q and K, Q only, or none."""
+    rng = np.random.default_rng(9100 + i)
+    fp8 = bool(rng.random() < 0.4)
+    step = 128 if fp8 else 64                     # one 128-byte k step
+    hidden = step * int(rng.integers(2, 17))
+    nq = int(rng.integers(1, 5))
+    nk = int(rng.choice([nq, max(1, nq - 1), 1]))
+    sums = str(rng.choice(["qk", "q", "none"])) if nk == nq else str(rng.choice(["q", "none"]))
+    return dict(fp8=fp8, seq=int(rng.integers(1, 1501)), hidden=hidden, n_q=nq, n_k=nk,
+                bias=bool(rng.random() < 0.7), sums=sums, seed=9100 + i)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_projection_shapes(Q, i):
+    c = _draw_proj(i)
+    print(f"case {i}: {c}", flush=True)
+    cfg = W.WAN22_QKV_PROJ_FP8 if c["fp8"] else W.WAN22_QKV_PROJ
+    d = W.make_qkv_projection(cfg, device="cuda", seq=c["seq"], hidden=c["hidden"], n_q_heads=c["n_q"],
+                              n_k_heads=c["n_k"], seed=c["seed"])
+    q_cols = 128 * c["n_q"] if c["sums"] != "none" else 0
+    k_cols = 128 * c["n_k"] if c["sums"] == "qk" else 0
+    if not c["bias"]:
+        d["bias"] = None
+    out, s = _project(Q, d, q_cols=q_cols, k_cols=k_cols)
+    torch.cuda.synchronize()
+    rows = np.arange(c["seq"])
+    ref = _oracle_rows(d, rows, with_bias=c["bias"])
+    if c["fp8"]:
+        check_dot(out, ref, _fp8_magnitude(d, rows), c["hidden"], f"random-{i}/out")
+    else:
+        check_float(out, ref, f"random-{i}/out")
+    if q_cols:
+        _check_sums(out, s, q_cols, k_cols, f"random-{i}")
+    else:
+        assert s is None
