@@ -7,7 +7,8 @@ that combinations nobody picked also meet the parity bar: V1 or V2 (N in
 bf16 or fp16, each cache unquantised, int8 (with or without offsets), FP8
 E4M3FN or E5M2 (some with scales that saturate), every parameter shape the
 version allows, Norm / PA_BNSD / PA_BLK_BNSD caches with block sizes 32-128,
-skipped tokens (index -1), k_rope / c_kv where they take effect, and from one
+skipped tokens (index -1), k_rope / c_kv where they take effect, row-padded
+inputs and outputs (16- and 8-byte access paths), cos/sin shared over S, and from one
 row to 40,000 rows (so the launch planner's choices -- lanes per row, rows per
 lane, staged parameters and codes, waves that straddle heads -- vary too).
 
@@ -89,13 +90,41 @@ def _draw(i):
     # k_rope / c_kv take effect for paged caches, and for Norm only in V2 with a quantised cache
     over["is_output_kv"] = bool(rng.random() < 0.5) and (mode != W.NORM or (v2 and quant))
     base = W.MLA_V2_SPLIT if v2 else W.MLA_V1_PREFILL
-    return base, over
+    # layout of the inputs and raw outputs: rows padded by 8 elements (16-byte accesses
+    # stay legal) or by 4 (the 8-byte access path), and one cos/sin row shared by every
+    # position (allowed for Norm caches and unquantised paged caches)
+    lay = dict(pad=pick([0, 0, 8, 4]), out_pad=pick([0, 0, 8]),
+               s_bcast=bool(rng.random() < 0.2) and (mode == W.NORM or not quant) and seq > 1,
+               s_pos=int(rng.integers(0, seq)))
+    return base, over, lay
 
 
-def _describe(base, over):
+def _relayout(d, lay):
+    """The same values in the drawn layout: kv and v as views into row-padded
+    buffers, cos/sin of one position broadcast over S, k_rope / c_kv as views
+    into row-padded outputs."""
+    def padded(t, pad):
+        if t is None or not pad:
+            return t
+        full = torch.zeros(*t.shape[:-1], t.shape[-1] + pad, dtype=t.dtype, device=t.device)
+        view = full[..., : t.shape[-1]]
+        view.copy_(t)
+        return view
+    d["kv"] = padded(d["kv"], lay["pad"])
+    d["v"] = padded(d["v"], lay["pad"])
+    if lay["s_bcast"]:
+        s0 = lay["s_pos"]
+        d["cos"] = d["cos"][:, :, s0:s0 + 1].contiguous()
+        d["sin"] = d["sin"][:, :, s0:s0 + 1].contiguous()
+    d["k_rope"] = padded(d["k_rope"], lay["out_pad"])
+    d["c_kv"] = padded(d["c_kv"], lay["out_pad"])
+    return d
+
+
+def _describe(base, over, lay):
     keys = ("batch", "heads", "seq", "kv_dim", "rope_size", "v_dim", "cache_mode", "block_size", "k_cache_dtype",
             "ckv_cache_dtype", "invalid_every", "is_output_kv")
-    return base.name + " " + " ".join(f"{k}={over[k]}" for k in keys)
+    return base.name + " " + " ".join(f"{k}={over[k]}" for k in keys) + f" layout={lay}"
 
 
 def _args(Q, d):
@@ -110,10 +139,10 @@ def test_random_cases_are_legal_calls():
     """Host validation accepts every drawn case (CPU tensors; nothing runs on a GPU)."""
     import qk_rmsnorm_rope_amd as Q
     for i in range(N_CASES):
-        base, over = _draw(i)
-        d = W.make_kv_cache(base, device="cpu", **over)
+        base, over, lay = _draw(i)
+        d = _relayout(W.make_kv_cache(base, device="cpu", **over), lay)
         code = Q.kv_validate(_args(Q, d))
-        assert code == 0, f"case {i} ({_describe(base, over)}): {Q.last_error()}"
+        assert code == 0, f"case {i} ({_describe(base, over, lay)}): {Q.last_error()}"
 
 
 @pytest.mark.gpu
@@ -122,9 +151,9 @@ def test_random_case(i):
     import qk_rmsnorm_rope_amd as Q
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    base, over = _draw(i)
-    print(f"case {i}: {_describe(base, over)}", flush=True)
-    d = W.make_kv_cache(base, device="cuda", **over)
+    base, over, lay = _draw(i)
+    print(f"case {i}: {_describe(base, over, lay)}", flush=True)
+    d = _relayout(W.make_kv_cache(base, device="cuda", **over), lay)
     assert Q.kv_validate(_args(Q, d)) == 0, Q.last_error()
     rep, _ = check_kv(Q, d, f"random-{i}")
     print(rep)

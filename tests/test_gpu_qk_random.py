@@ -4,8 +4,10 @@
 2-4 head shards composed back), the element type (bf16, fp16, fp32), the head
 size (64, 96, 128, 256), the head counts (1-64 Q heads, 0 to as many K heads,
 so Q-only and grouped K), batch and sequence (1-700 tokens per batch), in or out
-of place, a cos/sin table shared by the batch or one per batch, and (for the
-single-pass forms) norm-only or rope-only calls. The launch choices that follow
+of place, a cos/sin table shared by the batch or one per batch, the layout of Q
+and K (the BSD projection buffer, separate NBSd tensors, or heads padded by 8 or
+4 elements: the 16- and 8-byte access paths), and (for the single-pass forms)
+norm-only or rope-only calls. The launch choices that follow
 from them -- chunks per half head, heads per lane, 1/2/4 waves per unit -- vary
 with the draw. A CPU test checks that host validation accepts every drawn
 case, so the GPU test never skips.
@@ -39,9 +41,43 @@ def _draw(i):
     norm, rope = True, True
     if form != "split" and rng.random() < 0.2:
         norm, rope = pick([(True, False), (False, True)])
-    return dict(form=form, dtype=dtype, head_dim=hd, n_q=nq, n_k=nk, tp=tp, batch=batch, seq=seq,
-                in_place=bool(rng.random() < 0.5), shared_table=bool(rng.random() < 0.3), norm=norm, rope=rope,
-                eps=pick([1e-6, 1e-5]), seed=8000 + i)
+    c = dict(form=form, dtype=dtype, head_dim=hd, n_q=nq, n_k=nk, tp=tp, batch=batch, seq=seq,
+             in_place=bool(rng.random() < 0.5), shared_table=bool(rng.random() < 0.3), norm=norm, rope=rope,
+             eps=pick([1e-6, 1e-5]), seed=8000 + i)
+    # memory layout of Q and K (and of the outputs): the BSD projection buffer, separate
+    # NBSd tensors viewed as [B, S, N, d], or heads padded by 8 or 4 elements
+    c["layout"] = pick(["bsd", "bsd", "nbsd", "pad8", "pad4"])
+    if c["layout"] == "pad4" and nq * hd > 4096:
+        c["layout"] = "pad8"      # 8-byte accesses hold fewer heads per block: wide segments are unsupported
+    return c
+
+
+def _views(d, c, buf_like=None):
+    """Q and K views [B, S, N, d] in the case's layout holding the values of
+    the workload's BSD buffer (or, with buf_like, fresh storage of that layout
+    filled with 5.0, for outputs)."""
+    q0, k0 = qk_views(d)
+    lay = c["layout"]
+    B, S, nq, hd = q0.shape
+    nk = k0.shape[2] if k0 is not None else 0
+    dev, dt = q0.device, q0.dtype
+    if lay == "bsd":
+        if buf_like is None:
+            return q0, k0
+        return qk_views(dict(d, qkv=torch.full_like(d["qkv"], 5.0)))
+    if lay == "nbsd":
+        q = torch.full((nq, B, S, hd), 5.0, dtype=dt, device=dev).permute(1, 2, 0, 3)
+        k = torch.full((nk, B, S, hd), 5.0, dtype=dt, device=dev).permute(1, 2, 0, 3) if nk else None
+    else:
+        pad = 8 if lay == "pad8" else 4
+        buf = torch.full((B, S, nq + nk, hd + pad), 5.0, dtype=dt, device=dev)
+        q = buf[:, :, :nq, :hd]
+        k = buf[:, :, nq:, :hd] if nk else None
+    if buf_like is None:
+        q.copy_(q0)
+        if nk:
+            k.copy_(k0)
+    return q, k
 
 
 def _split(Q, q, k, oq, ok_, qg, kg, cos, sin, eps, tp):
@@ -80,7 +116,7 @@ def test_random_qk_cases_are_legal_calls():
     for i in range(N_CASES):
         c = _draw(i)
         d = _inputs(c, "cpu")
-        q, k = qk_views(d)
+        q, k = _views(d, c)
         if c["form"] == "split":
             lq, lk = c["n_q"] // c["tp"], c["n_k"] // c["tp"]
             q, k = q[:, :, :lq], k[:, :, :lk]
@@ -99,21 +135,19 @@ def test_random_qk_case(i):
     c = _draw(i)
     print(f"case {i}: {c}", flush=True)
     d = _inputs(c, "cuda")
-    q, k = qk_views(d)
+    q, k = _views(d, c)
     qi = q.clone()
     ki = k.clone() if k is not None else None
     fp32 = c["dtype"] == torch.float32
     if c["form"] == "split":
-        out = torch.full_like(d["qkv"], 5.0)
-        oq, ok_ = qk_views(dict(d, qkv=out))
+        oq, ok_ = _views(d, c, buf_like=True)
         _split(Q, q, k, oq, ok_, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"], c["eps"], c["tp"])
         rq, rk = _oracle(qi, ki, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"], c["eps"])
     else:
         if c["in_place"]:
             oq, ok_ = q, k
         else:
-            out = torch.full_like(d["qkv"], 5.0)
-            oq, ok_ = qk_views(dict(d, qkv=out))
+            oq, ok_ = _views(d, c, buf_like=True)
         call = Q.qk_norm_rope_per_head if c["form"] == "per_head" else Q.qk_norm_rope_across_heads
         cos, sin = (d["cos"], d["sin"]) if c["rope"] else (None, None)
         call(q, k, d["q_gamma"], d["k_gamma"], cos, sin, eps=c["eps"], q_out=oq,
