@@ -90,7 +90,7 @@ def parse():
     ap.add_argument("--no-kv", action="store_true", help="skip the KvRmsNormRopeCache workloads")
     ap.add_argument("--no-forms", action="store_true", help="skip the per-head and split forms of (a)")
     ap.add_argument("--no-proj", action="store_true", help="skip the QKV projection")
-    ap.add_argument("--cold-iters", type=int, default=30)
+    ap.add_argument("--cold-iters", type=int, default=50)
     ap.add_argument("--profile", default=None,
                     choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "proj_fp8", "kv_v1_prefill",
                              "kv_v1_decode", "kv_v2", "copy"])
@@ -397,6 +397,7 @@ def graph_replay_us(torch, step, calls=100, replays=20):
 
 def kv_measure(torch, W, Q, flush, cold_iters):
     out = {}
+    torch.cuda.empty_cache()          # each workload's tensors come from fresh allocations
     for name, cfg, over in (("mla_v1_prefill", W.MLA_V1_PREFILL, {}),
                             ("mla_v1_prefill_pa_blk_bnsd", W.MLA_V1_PREFILL, {"cache_mode": W.PA_BLK_BNSD}),
                             ("mla_v1_decode_quant", W.MLA_V1_DECODE_QUANT, {}),
@@ -423,7 +424,7 @@ def kv_measure(torch, W, Q, flush, cold_iters):
         if name == "mla_v1_decode_quant":
             rec["us_graph_replay_per_call"] = round(graph_replay_us(torch, step), 3)
         out[name] = rec
-        del d
+        del d, step
         torch.cuda.empty_cache()
     return out
 
