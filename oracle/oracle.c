@@ -388,8 +388,8 @@ int oracle_linear(int64_t S, int64_t H, int64_t I, int a_dtype, const void *A, i
  * as torch.round does) and clamped to [-128, 127] for INT8. For FLOAT8E4M3FN
  * and FLOAT8E5M2 the pages give no separate formula; the value is cast to the
  * format with round to nearest even, saturating at its largest finite value
- * (+-448, +-57344). The rounding decision is taken on the fp32 value of t,
- * the precision the GPU kernel computes t in.
+ * (+-448, +-57344). Every decision is taken on the exact t, with no
+ * intermediate rounding: formula (3) has none.
  * Returns t (the exact pre-rounding value) and writes the code.
  */
 static double quantise(int cdtype, void *cache, int64_t pos, double x,
@@ -398,14 +398,14 @@ static double quantise(int cdtype, void *cache, int64_t pos, double x,
     if (scale) t = t * scale[qi];
     if (offset) t = t + offset[qi];
     if (cdtype == ORC_INT8) {
-        double r = nearbyint((double)(float)t);
+        double r = nearbyint(t);
         if (r < -128.0) r = -128.0;
         if (r > 127.0) r = 127.0;
         ((int8_t *)cache)[pos] = (int8_t)r;
     } else if (cdtype == ORC_E4M3FN) {
-        ((uint8_t *)cache)[pos] = enc_e4m3fn((double)(float)t);
+        ((uint8_t *)cache)[pos] = enc_e4m3fn(t);
     } else if (cdtype == ORC_E5M2) {
-        ((uint8_t *)cache)[pos] = enc_e5m2((double)(float)t);
+        ((uint8_t *)cache)[pos] = enc_e5m2(t);
     } else {
         store(cdtype, cache, pos, t);
     }
@@ -527,7 +527,10 @@ int oracle_kv_rmsnorm_rope_cache(
             int kq = k_scale != NULL, cq = v_scale != NULL;
             for (int64_t j = 0; j < Dk_out; j++) {
                 double t = rope_out[j];
-                if (kq) t = t * k_scale[n * Dk_out + j] + (k_offset ? k_offset[n * Dk_out + j] : 0.0);
+                if (kq) {
+                    t = t * k_scale[n * Dk_out + j];
+                    if (k_offset) t = t + k_offset[n * Dk_out + j];
+                }
                 if (krow >= 0)
                     quantise(k_dtype, k_cache, krow + j, rope_out[j], kq ? k_scale : NULL,
                              kq ? k_offset : NULL, n * Dk_out + j);
@@ -538,7 +541,10 @@ int oracle_kv_rmsnorm_rope_cache(
             }
             for (int64_t i = 0; i < Dc; i++) {
                 double t = c_src[i];
-                if (cq) t = t * v_scale[n * Dc + i] + (v_offset ? v_offset[n * Dc + i] : 0.0);
+                if (cq) {
+                    t = t * v_scale[n * Dc + i];
+                    if (v_offset) t = t + v_offset[n * Dc + i];
+                }
                 if (crow >= 0)
                     quantise(ckv_dtype, ckv_cache, crow + i, c_src[i], cq ? v_scale : NULL,
                              cq ? v_offset : NULL, n * Dc + i);

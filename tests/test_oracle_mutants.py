@@ -30,7 +30,7 @@ MUTANTS = {
     "pa_head_major_layout": ("int64_t r = (blk * block_size + off) * N + n;",
                              "int64_t r = (blk * N + n) * block_size + off;"),
     "norm_ignores_batch": ("int64_t r = (b * N + n) * cache_dim0 + slot;", "int64_t r = n * cache_dim0 + slot;"),
-    "round_half_up": ("double r = nearbyint((double)(float)t);", "double r = floor((double)(float)t + 0.5);"),
+    "round_half_up": ("double r = nearbyint(t);", "double r = floor(t + 0.5);"),
     "offset_before_scale": ("    if (scale) t = t * scale[qi];\n    if (offset) t = t + offset[qi];",
                             "    if (offset) t = t + offset[qi];\n    if (scale) t = t * scale[qi];"),
     "e4m3_no_saturation": ("if (a >= 448.0) return s | 0x7E;", "if (a >= 464.0) return s | 0x7F;"),
