@@ -132,6 +132,46 @@ __device__ __forceinline__ void store_words(void *p, const Words<WORDS> &r) {
     }
 }
 
+// LDS accesses through pointers typed for the LDS address space, so that
+// they always compile to ds_read / ds_write: whatever form the global
+// accesses above take (cache-policy bits, inline assembly), an LDS address
+// can never reach a global store.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+template <int WORDS>
+__device__ __forceinline__ void lds_store_words(lds_u8 *p, const Words<WORDS> &r) {
+    if constexpr (WORDS == 4) {
+        u32x4_t v = {r.w[0], r.w[1], r.w[2], r.w[3]};
+        *reinterpret_cast<lds_u32x4 *>(p) = v;
+    } else if constexpr (WORDS == 2) {
+        u32x2_t v = {r.w[0], r.w[1]};
+        *reinterpret_cast<lds_u32x2 *>(p) = v;
+    } else {
+        static_assert(WORDS == 1, "1, 2 or 4 words");
+        *reinterpret_cast<lds_u32 *>(p) = r.w[0];
+    }
+}
+
+template <int WORDS>
+__device__ __forceinline__ Words<WORDS> lds_load_words(const lds_u8 *p) {
+    Words<WORDS> r;
+    if constexpr (WORDS == 4) {
+        const u32x4_t v = *reinterpret_cast<const lds_u32x4 *>(p);
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else if constexpr (WORDS == 2) {
+        const u32x2_t v = *reinterpret_cast<const lds_u32x2 *>(p);
+        r.w[0] = v.x; r.w[1] = v.y;
+    } else {
+        static_assert(WORDS == 1, "1, 2 or 4 words");
+        r.w[0] = *reinterpret_cast<const lds_u32 *>(p);
+    }
+    return r;
+}
+
 // VEC elements of T held as raw 32-bit words (VEC * sizeof(T) in {4, 8, 16}
 // bytes): loaded and stored with one naturally aligned vector access and
 // decoded to fp32 only where an element is used, which keeps registers

@@ -57,22 +57,42 @@
 namespace qknr {
 
 // Per-wave LDS regions (launch-time size: 4 waves x lds_wave_bytes): staged
-// quantisation parameters, then staged codes (WaveParams, WaveCodes).
+// quantisation parameters, then staged codes (WaveParams, WaveCodes). Every
+// access to them goes through LDS-typed pointers (kv_lds_at).
 extern __shared__ float4 kv_lds[];
 
-// Store N codes (byte 0 of each word) at p (naturally aligned).
+__device__ __forceinline__ lds_u8 *kv_lds_at(uint32_t byte_off) {
+    return (lds_u8 *)kv_lds + byte_off;
+}
+
+// N codes (byte 0 of each word) packed into N/4 words.
+template <int W>
+__device__ __forceinline__ Words<W> pack_codes(const uint32_t *code) {
+    Words<W> r;
+#pragma unroll
+    for (int i = 0; i < W; i++) r.w[i] = pack_bytes4(code[4 * i], code[4 * i + 1], code[4 * i + 2], code[4 * i + 3]);
+    return r;
+}
+
+// Store N codes at p in global memory (naturally aligned).
 template <int N>
 __device__ __forceinline__ void store_codes(void *p, const uint32_t *code) {
     if constexpr (N >= 4) {
-        constexpr int W = N / 4;
-        Words<W> r;
-#pragma unroll
-        for (int i = 0; i < W; i++)
-            r.w[i] = pack_bytes4(code[4 * i], code[4 * i + 1], code[4 * i + 2], code[4 * i + 3]);
-        store_words<W>(p, r);
+        store_words<N / 4>(p, pack_codes<N / 4>(code));
     } else {
         static_assert(N == 2, "2, 4 or 8 codes");
         *reinterpret_cast<uint16_t *>(p) = (uint16_t)pack_bytes2(code[0], code[1]);
+    }
+}
+
+// Store N codes into the wave's LDS staging at byte offset `off` of kv_lds.
+template <int N>
+__device__ __forceinline__ void stage_codes(uint32_t off, const uint32_t *code) {
+    if constexpr (N >= 4) {
+        lds_store_words<N / 4>(kv_lds_at(off), pack_codes<N / 4>(code));
+    } else {
+        static_assert(N == 2, "2, 4 or 8 codes");
+        *reinterpret_cast<lds_u16 *>(kv_lds_at(off)) = (uint16_t)pack_bytes2(code[0], code[1]);
     }
 }
 
@@ -112,27 +132,32 @@ struct CacheRow {
     int qshape, n, width;
 };
 
-// The scale and offset (0 if absent) of N consecutive channels from c.
+// The scale and offset of N consecutive channels from c. An absent offset is
+// -0, so that fmaf(x, scale, offset) is exactly x*scale, signed zeros included.
 template <int N>
 struct QuantParams {
     float sc[N], of[N];
-    // from a wave's staged copy [scale[width] | offset[width]] (see WaveParams)
-    // (c and width are multiples of 4 for N >= 4, of 2 for N == 2)
-    __device__ __forceinline__ void load_lds(const float *wp, int width, int c) {
+    // from a wave's staged copy [scale[width] | offset[width]] at byte offset
+    // wp of kv_lds (see WaveParams); c and width are multiples of 4 for N >= 4,
+    // of 2 for N == 2
+    __device__ __forceinline__ void load_lds(uint32_t wp, int width, int c) {
+        const lds_u8 *s = kv_lds_at(wp + 4u * (uint32_t)c);
+        const lds_u8 *o = kv_lds_at(wp + 4u * (uint32_t)(width + c));
         if constexpr (N % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < N; i += 4) {
-                const float4 a = *reinterpret_cast<const float4 *>(wp + c + i);
-                const float4 b = *reinterpret_cast<const float4 *>(wp + width + c + i);
-                sc[i] = a.x; sc[i + 1] = a.y; sc[i + 2] = a.z; sc[i + 3] = a.w;
-                of[i] = b.x; of[i + 1] = b.y; of[i + 2] = b.z; of[i + 3] = b.w;
+                const Words<4> a = lds_load_words<4>(s + 4 * i), b = lds_load_words<4>(o + 4 * i);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    sc[i + e] = __uint_as_float(a.w[e]);
+                    of[i + e] = __uint_as_float(b.w[e]);
+                }
             }
         } else {
             static_assert(N == 2, "2, 4 or 8 parameters");
-            const float2 a = *reinterpret_cast<const float2 *>(wp + c);
-            const float2 b = *reinterpret_cast<const float2 *>(wp + width + c);
-            sc[0] = a.x; sc[1] = a.y;
-            of[0] = b.x; of[1] = b.y;
+            const Words<2> a = lds_load_words<2>(s), b = lds_load_words<2>(o);
+            sc[0] = __uint_as_float(a.w[0]); sc[1] = __uint_as_float(a.w[1]);
+            of[0] = __uint_as_float(b.w[0]); of[1] = __uint_as_float(b.w[1]);
         }
     }
     __device__ __forceinline__ void load(const float *scale, const float *offset, int qshape, int n, int width,
@@ -142,7 +167,7 @@ struct QuantParams {
             load_qparam<N>(offset, qshape, n, width, c, of);
         } else {
 #pragma unroll
-            for (int i = 0; i < N; i++) of[i] = 0.0f;
+            for (int i = 0; i < N; i++) of[i] = -0.0f;   // fmaf(x, s, -0) == x*s, signed zeros included
         }
     }
 };
@@ -161,7 +186,7 @@ __device__ __forceinline__ void put_codes(const CacheRow &d, int c, const float 
     uint32_t q[N];
 #pragma unroll
     for (int i = 0; i < N; i++) q[i] = encode<CODE>(fmaf(x[i], qp.sc[i], qp.of[i]));
-    if (d.stage >= 0) store_codes<N>(reinterpret_cast<uint8_t *>(kv_lds) + d.stage + c, q);
+    if (d.stage >= 0) stage_codes<N>((uint32_t)(d.stage + c), q);
     else store_codes<N>(d.row + c, q);
 }
 
@@ -243,7 +268,7 @@ __device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t blk, int s
 
 // Per-channel quantisation parameters shared by every row of a wavefront,
 // staged once per wave in its own LDS region as [scale[width] | offset[width]]
-// (offset 0 if absent): one 16-byte load per lane instead of the parameters
+// (offset -0 if absent): one 16-byte load per lane instead of the parameters
 // of every chunk of every row through the vector cache, where they would
 // compete with the row data. Used when a wave holds several rows (G < 64),
 // the parameters are per channel or per head and channel, 8*width <=
@@ -256,7 +281,7 @@ constexpr int kWaveParamFloats = 512;   // at most 2 KB per wave: two 16-byte pi
 
 struct WaveParams {
     float4 v[2];      // staged 16-byte pieces of this lane (lane, lane + 64)
-    float *wp;        // the wave's LDS region
+    uint32_t wp;      // byte offset of the wave's region in kv_lds
     bool on;
 
     // The head of the wave's rows, the decision, and the loads (issued first,
@@ -264,7 +289,7 @@ struct WaveParams {
     __device__ __forceinline__ void load(const KvParams &p, uint32_t blk, int shift, const float *scale,
                                          const float *offset, int qshape, int width, int rsteps = 1) {
         const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        wp = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(kv_lds) + wave * (uint32_t)p.lds_wave_bytes);
+        wp = wave * (uint32_t)p.lds_wave_bytes;
         // the wave's rows: (64 / G) consecutive rows in each of rsteps steps 256 / G apart
         const uint32_t first = blk * ((uint32_t)rsteps << (8 - shift)) + (wave << (6 - shift));
         // (a wave of one row, G = 64, reads each parameter once anyway)
@@ -285,7 +310,7 @@ struct WaveParams {
             const int q = lane + 64 * j;
             if (q < q4) v[j] = reinterpret_cast<const float4 *>(scale + base)[q];
             else if (q < 2 * q4) v[j] = offset ? reinterpret_cast<const float4 *>(offset + base)[q - q4]
-                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                                               : make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
         }
     }
     __device__ __forceinline__ void store(int width) const {
@@ -295,7 +320,12 @@ struct WaveParams {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int q = lane + 64 * j;
-            if (q < 2 * q4) reinterpret_cast<float4 *>(wp)[q] = v[j];
+            if (q < 2 * q4) {
+                Words<4> w;
+                w.w[0] = __float_as_uint(v[j].x); w.w[1] = __float_as_uint(v[j].y);
+                w.w[2] = __float_as_uint(v[j].z); w.w[3] = __float_as_uint(v[j].w);
+                lds_store_words<4>(kv_lds_at(wp + 16u * (uint32_t)q), w);
+            }
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -308,17 +338,19 @@ struct WaveParams {
 // the 4- and 8-byte pieces of the lanes' own chunks. The destination row of a
 // piece comes from the lane that computed the row (ds_bpermute), so every
 // lane of the wave takes part in the flush. Used when a wave holds several
-// rows and the row width is a multiple of 16 bytes.
+// rows, the row width is a multiple of 16 bytes and the planner allowed it for
+// the part (a cache whose base and strides are 16-byte multiples).
 struct WaveCodes {
     uint32_t buf;     // byte offset of the wave's staged rows in kv_lds
     int width;        // bytes per row
     bool on;
 
-    __device__ __forceinline__ void init(const KvParams &p, int shift, int width_bytes, int rsteps = 1) {
+    __device__ __forceinline__ void init(const KvParams &p, bool allowed, int shift, int width_bytes,
+                                         int rsteps = 1) {
         const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         buf = wave * (uint32_t)p.lds_wave_bytes + (uint32_t)p.lds_param_bytes;
         width = width_bytes;
-        on = shift < 6 && (width_bytes & 15) == 0 && rsteps * (64 >> shift) * width_bytes <= p.lds_code_bytes &&
+        on = allowed && shift < 6 && (width_bytes & 15) == 0 && rsteps * (64 >> shift) * width_bytes <= p.lds_code_bytes &&
              rsteps * (64 >> shift) * (width_bytes >> 4) <= 128;   // flush() moves at most two pieces per lane
     }
     // byte offset in kv_lds of this lane's row of step k in the staging buffer
@@ -335,7 +367,7 @@ struct WaveCodes {
         const int pieces = R * rpw * ppr;              // <= 128
         const float inv_ppr = 1.0f / (float)ppr;
         const int lane = threadIdx.x & 63;
-        const uint8_t *staged = reinterpret_cast<const uint8_t *>(kv_lds) + buf;
+        const lds_u8 *staged = kv_lds_at(buf);
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int q = lane + 64 * j;
@@ -351,7 +383,7 @@ struct WaveCodes {
                 if (k == kstep) o = (int64_t)(((uint64_t)hi << 32) | lo);
             }
             if (q < pieces && o >= 0) {
-                const Words<4> v = load_words<4>(staged + q * 16);
+                const Words<4> v = lds_load_words<4>(staged + q * 16);
                 store_words<4>(cache + o + (q - rs * ppr) * 16, v);
             }
         }
@@ -475,7 +507,7 @@ __device__ __forceinline__ void part_a(const KvParams &p, uint32_t blk) {
 
     WaveCodes wc;
     wc.on = false;
-    if constexpr (kQuant) wc.init(p, shift, qwidth, R);
+    if constexpr (kQuant) wc.init(p, p.stage_a != 0, shift, qwidth, R);
     const bool out_kv = p.out_kv != 0;
     int64_t offs[R];
 #pragma unroll
@@ -603,7 +635,7 @@ __device__ __forceinline__ void part_b(const KvParams &p, uint32_t blk) {
 
     WaveCodes wc;
     wc.on = false;
-    if constexpr (kQuant) wc.init(p, shift, qwidth, R);
+    if constexpr (kQuant) wc.init(p, p.stage_b != 0, shift, qwidth, R);
     const bool out_kv = p.out_kv != 0;
     int64_t offs[R];
 #pragma unroll

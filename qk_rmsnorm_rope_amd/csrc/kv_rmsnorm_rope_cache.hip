@@ -71,12 +71,24 @@ int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb) {
             w = p.c_dim;
         p.lds_param_bytes = 8 * w;
         // part A writes the k cache (V2) or the ckv cache (V1); part B the other
+        // Staged rows leave as 16-byte stores at the row's own address, so the
+        // cache base and its strides (bytes; quantised elements are one byte)
+        // must be multiples of 16; other layouts keep the lanes' own stores.
+        const auto lines16 = [](const void *base, uint32_t s0, uint32_t s1, uint32_t s2) {
+            return (reinterpret_cast<uintptr_t>(base) & 15u) == 0 && (s0 & 15u) == 0 && (s1 & 15u) == 0 &&
+                   (s2 & 15u) == 0;
+        };
+        const bool k16 = lines16(p.k_cache, p.kc0, p.kc1, p.kc2), c16 = lines16(p.ckv_cache, p.cc0, p.cc1, p.cc2);
         const int wa = v2 ? p.k_dim : p.c_dim, ca_code = v2 ? p.k_code : p.c_code;
         const int wb = v2 ? p.c_dim : p.k_dim, cb_code = v2 ? p.c_code : p.k_code;
+        const bool a16 = v2 ? k16 : c16, b16 = v2 ? c16 : k16;
+        const int need_a = p.ra * (64 / ga) * wa, need_b = p.rb * (64 / gb) * wb;
+        // wider staged rows than 2 KB per wave fall back to direct stores
+        p.stage_a = ca_code != CODE_SAME && ga < 64 && wa % 16 == 0 && a16 && need_a <= 2048;
+        p.stage_b = cb_code != CODE_SAME && gb < 64 && wb % 16 == 0 && b16 && need_b <= 2048;
         int cbytes = 0;
-        if (ca_code != CODE_SAME && ga < 64 && wa % 16 == 0) cbytes = p.ra * (64 / ga) * wa;
-        if (cb_code != CODE_SAME && gb < 64 && wb % 16 == 0 && p.rb * (64 / gb) * wb > cbytes) cbytes = p.rb * (64 / gb) * wb;
-        if (cbytes > 2048) cbytes = 2048;   // wider staged rows fall back to direct stores
+        if (p.stage_a) cbytes = need_a;
+        if (p.stage_b && need_b > cbytes) cbytes = need_b;
         p.lds_code_bytes = cbytes;
         p.lds_wave_bytes = p.lds_param_bytes + p.lds_code_bytes;
     }

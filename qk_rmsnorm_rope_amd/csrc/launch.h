@@ -156,6 +156,7 @@ struct KvParams {
     int32_t ga_shift, gb_shift; // log2 of ga, gb
     int32_t ra, rb;            // rows per lane in part A / part B (1 or 2)
     int32_t lds_param_bytes, lds_code_bytes, lds_wave_bytes;   // per-wave LDS: staged parameters, staged codes
+    int32_t stage_a, stage_b;  // the part's cache rows may leave as staged 16-byte pieces (see kv_plan)
     uint32_t blocks_a, blocks_b;   // blocks of part A, then of part B
     int32_t k_code, c_code;    // CacheCode
     int32_t k_qshape, v_qshape;

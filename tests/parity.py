@@ -214,14 +214,36 @@ def run_gpu_kv(Q, d):
         is_output_kv=cfg.is_output_kv, k_rope=d["k_rope"], c_kv=d["c_kv"])
 
 
+def padded_cache(cache, pad_bytes, seed):
+    """The cache's values in a buffer whose rows are pad_bytes longer (the
+    padding filled with seeded random bytes); returns (view, full buffer)."""
+    pad = pad_bytes // cache.element_size()
+    g = torch.Generator(device=cache.device).manual_seed(seed + 31)
+    full_shape = tuple(cache.shape[:-1]) + (cache.shape[-1] + pad,)
+    raw = torch.randint(0, 256, full_shape[:-1] + (full_shape[-1] * cache.element_size(),), generator=g,
+                        device=cache.device, dtype=torch.uint8)
+    full = raw.view(cache.dtype)
+    view = full[..., : cache.shape[-1]]
+    view.copy_(cache)
+    return view, full
+
+
 def check_kv(Q, d, what, big_cache=False):
     """Run the HIP operator and the oracle on workload d and compare:
     untouched cache rows bit-exact, written rows within the code/float rules,
-    k_rope / c_kv within the float rule. Returns a small report dict."""
+    k_rope / c_kv within the float rule, and the padding of row-padded caches
+    (d["k_cache_full"], d["ckv_cache_full"]) untouched. Returns a small report
+    dict."""
     cfg = d["cfg"]
     k_pre, c_pre = d["k_cache"].clone(), d["ckv_cache"].clone()
+    pads = {n: d[n + "_full"][..., d[n].shape[-1]:].clone() for n in ("k_cache", "ckv_cache") if n + "_full" in d}
     run_gpu_kv(Q, d)
     torch.cuda.synchronize()
+    for n, before in pads.items():
+        after = d[n + "_full"][..., d[n].shape[-1]:]
+        assert torch.equal(after.view(torch.uint8) if after.element_size() == 1 else after.view(torch.int16),
+                           before.view(torch.uint8) if before.element_size() == 1 else before.view(torch.int16)), \
+            f"{what}/{n}: the row padding was written"
     r = run_oracle_kv(d, inplace_zero_caches=big_cache)
     rows = cache_rows(d)                          # [B, N, S]
     valid = rows >= 0
@@ -232,8 +254,8 @@ def check_kv(Q, d, what, big_cache=False):
             ("k_cache", d["k_cache"], k_pre, r["k_t"], r["k_x"], r["k_cache"]),
             ("ckv_cache", d["ckv_cache"], c_pre, r["c_t"], r["c_x"], r["ckv_cache"])):
         width = cache.shape[-1]
-        g2 = cache.view(-1, width)
-        p2 = pre.view(-1, width)
+        g2 = cache.reshape(-1, width)
+        p2 = pre.reshape(-1, width)
         bytes_now = g2.view(torch.uint8) if cache.element_size() == 1 else g2.view(torch.int16)
         bytes_pre = p2.view(torch.uint8) if cache.element_size() == 1 else p2.view(torch.int16)
         changed = (bytes_now != bytes_pre).any(-1)
@@ -254,4 +276,21 @@ def check_kv(Q, d, what, big_cache=False):
     if cfg.is_output_kv and d["k_rope"] is not None:
         report["k_rope_rel"] = check_float(d["k_rope"], r["k_x"], f"{what}/k_rope")
         report["c_kv_rel"] = check_float(d["c_kv"], r["c_x"], f"{what}/c_kv")
+        # An unquantised cache row is the same rounding of the same value as
+        # the raw output row: the two must agree bit for bit.
+        vmask = torch.as_tensor(valid, device=d["kv"].device)
+        for name, cache, out in (("k_cache", d["k_cache"], d["k_rope"]), ("ckv_cache", d["ckv_cache"], d["c_kv"])):
+            if cache.dtype != out.dtype:
+                continue
+            width = cache.shape[-1]
+            got = cache.reshape(-1, width)[torch.as_tensor(flat, device=cache.device)]
+            raw = out.reshape(B_N_S(cfg) + (width,))[vmask]
+            same = got.view(torch.int16) == raw.view(torch.int16)
+            assert bool(same.all()), (f"{what}/{name}: {int((~same).sum())} cache elements differ from "
+                                      f"the raw output row's bits")
+        report["cache_equals_raw_rows"] = True
     return report, r
+
+
+def B_N_S(cfg):
+    return (cfg.batch, cfg.heads, cfg.seq)

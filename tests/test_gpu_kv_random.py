@@ -8,7 +8,8 @@ bf16 or fp16, each cache unquantised, int8 (with or without offsets), FP8
 E4M3FN or E5M2 (some with scales that saturate), every parameter shape the
 version allows, Norm / PA_BNSD / PA_BLK_BNSD caches with block sizes 32-128,
 skipped tokens (index -1), k_rope / c_kv where they take effect, row-padded
-inputs and outputs (16- and 8-byte access paths), cos/sin shared over S, and from one
+inputs and outputs (16- and 8-byte access paths), cache rows padded by 8 or 16
+bytes (the padding must stay untouched), cos/sin shared over S, and from one
 row to 40,000 rows (so the launch planner's choices -- lanes per row, rows per
 lane, staged parameters and codes, waves that straddle heads -- vary too).
 
@@ -20,7 +21,7 @@ import pytest
 import torch
 
 import workloads as W
-from tests.parity import LIB_MODE, check_kv
+from tests.parity import LIB_MODE, check_kv, padded_cache
 
 N_CASES = 40
 
@@ -96,6 +97,9 @@ def _draw(i):
     lay = dict(pad=pick([0, 0, 8, 4]), out_pad=pick([0, 0, 8]),
                s_bcast=bool(rng.random() < 0.2) and (mode == W.NORM or not quant) and seq > 1,
                s_pos=int(rng.integers(0, seq)))
+    # cache rows padded by 8 bytes (quantised rows then leave by the lanes' own
+    # stores: staged 16-byte pieces need 16-byte rows) or by 16 (staging stays on)
+    lay["cache_pad"] = pick([0, 0, 0, 8, 16])
     return base, over, lay
 
 
@@ -118,6 +122,9 @@ def _relayout(d, lay):
         d["sin"] = d["sin"][:, :, s0:s0 + 1].contiguous()
     d["k_rope"] = padded(d["k_rope"], lay["out_pad"])
     d["c_kv"] = padded(d["c_kv"], lay["out_pad"])
+    if lay.get("cache_pad"):
+        for name in ("k_cache", "ckv_cache"):
+            d[name], d[name + "_full"] = padded_cache(d[name], lay["cache_pad"], d["cfg"].seed)
     return d
 
 
