@@ -9,10 +9,12 @@ Printed: ONE JSON line with the headline throughput (algorithmic HBM GB/s over
 the timed steps), tokens/s, the roofline of the kernel (bytes it must move /
 its average launch time, measured with HIP events on the launch stream, vs
 MI355X's 8 TB/s), the fp64 CPU oracle timed on a bounded sample of the same
-workload, the KvRmsNormRopeCache workloads (MLA V1 prefill, also with
-PA_BLK_BNSD indexing, V1 decode quantised, also as a HIP-graph replay, V2
-split) timed the same way, cold (L2 and MALL evicted by reading 1 GiB before
-every launch) and hot, and the other forms of the QK operator on the Wan2.2
+workload and on every other workload (one thread and all cores), the
+KvRmsNormRopeCache workloads (MLA V1 prefill, also with PA_BLK_BNSD indexing,
+V1 decode quantised, also as a HIP-graph replay, V2 split) timed the same way,
+hot (back to back) and cold (each launch alone after a 1 GiB pass that evicts
+L2 and the MALL: frac_cold after writing 1 GiB, the stated protocol, and
+frac_cold_read after reading it), and the other forms of the QK operator on the Wan2.2
 shape: per-head norm, and the two passes of the across-heads norm split over
 tp = 4 ranks at one rank's share (10 + 10 heads); and the QKV projection
 (75600 x 5120 -> 15360 on the matrix cores, bf16 operands and FP8 ROW_MX
@@ -159,11 +161,10 @@ def forms_measure(torch, W, Q, d, flush, cold_iters):
         for _ in range(5):
             step()
         hot = time_hot(torch, step, 50)
-        cold = time_cold(torch, step, cold_iters, flush)
-        res[name] = {"algorithmic_bytes": nbytes, "us_hot_mean": round(hot, 3), "us_cold_median": round(cold, 3),
-                     "gbs_hot": round(nbytes / hot / 1e3, 1), "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4),
-                     "frac_cold": round(nbytes / cold / 1e3 / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(kernel, "wan22_" + name)}
+        res[name] = {"algorithmic_bytes": nbytes, "us_hot_mean": round(hot, 3),
+                     "gbs_hot": round(nbytes / hot / 1e3, 1), "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4)}
+        res[name].update(cold_record(torch, step, cold_iters, flush, nbytes))
+        res[name]["traffic"] = measured_traffic(kernel, "wan22_" + name)
         del step
         torch.cuda.empty_cache()
     res["per_head"]["workload"] = "Wan2.2 S=75600, 40+40 heads x 128 bf16, per-head RMS, [128] gammas, out of place"
@@ -296,15 +297,20 @@ def time_hot(torch, step, iters):
     return e0.elapsed_time(e1) / iters * 1e3   # us per launch
 
 
-def time_cold(torch, step, iters, flush):
-    """Each launch timed alone after reading 1 GiB, which evicts L2 and the
-    256 MB MALL with clean lines (a write would leave dirty lines whose
-    write-back then overlaps the timed launch)."""
+def time_cold(torch, step, iters, flush, how="write"):
+    """Median time of launches each timed alone after a pass over a 1 GiB
+    scratch tensor that evicts L2 and the 256 MB MALL. how='write' fills the
+    tensor (the stated cold protocol: the dirty lines it leaves are written
+    back while the timed launch runs, as after any producer kernel);
+    how='read' sums it, which leaves clean lines (nothing to write back)."""
     s = torch.cuda.current_stream()
     sink = torch.zeros((), dtype=flush.dtype, device=flush.device)
     times = []
-    for _ in range(iters):
-        sink.copy_(flush.sum())
+    for i in range(iters):
+        if how == "write":
+            flush.fill_(float(i & 1))
+        else:
+            sink.copy_(flush.sum())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
         step()
@@ -313,6 +319,18 @@ def time_cold(torch, step, iters, flush):
         times.append(e0.elapsed_time(e1) * 1e3)
     times.sort()
     return times[len(times) // 2]
+
+
+def cold_record(torch, step, iters, flush, nbytes):
+    """Cold medians under both flushes: us_cold_median / frac_cold after a
+    1 GiB write (the stated protocol), us_cold_read_median / frac_cold_read
+    after a 1 GiB read."""
+    w = time_cold(torch, step, iters, flush, "write")
+    r = time_cold(torch, step, iters, flush, "read")
+    return {"us_cold_median": round(w, 3), "gbs_cold": round(nbytes / w / 1e3, 1),
+            "frac_cold": round(nbytes / w / 1e3 / PEAK_HBM_GBS, 4),
+            "us_cold_read_median": round(r, 3), "gbs_cold_read": round(nbytes / r / 1e3, 1),
+            "frac_cold_read": round(nbytes / r / 1e3 / PEAK_HBM_GBS, 4)}
 
 
 def cpu_baseline(torch, W, d, cfg):
@@ -360,13 +378,89 @@ def cpu_baseline(torch, W, d, cfg):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(n * per_token / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "tokens_per_s": round(n / t, 1), "seconds": round(t, 3), "cpu_model": model,
-            "one_thread": {"value": round(n1 * per_token / t1 / 1e9, 4), "unit": "GB/s", "tokens": n1,
-                           "seconds": round(t1, 3)},
-            "sample": f"first {n} of {cfg.seq} tokens of the same workload (median of 3 runs), fp64 C oracle, "
-                      f"OpenMP over tokens, {threads} threads, bf16 outputs encoded; one_thread: first {n1} "
-                      f"tokens on 1 thread"}
+    res = {"value": round(n * per_token / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "tokens_per_s": round(n / t, 1), "seconds": round(t, 3), "cpu_model": model,
+           "one_thread": {"value": round(n1 * per_token / t1 / 1e9, 4), "unit": "GB/s", "tokens": n1,
+                          "seconds": round(t1, 3)},
+           "sample": f"first {n} of {cfg.seq} tokens of the same workload (median of 3 runs), fp64 C oracle, "
+                     f"OpenMP over tokens, {threads} threads, bf16 outputs encoded; one_thread: first {n1} "
+                     f"tokens on 1 thread"}
+    per = {"wan22_self_attn": {
+        "tokens": cfg.seq, "sampled": True,
+        "all_cores": {"threads": threads, "tokens": n, "seconds": round(t, 4), "tokens_per_s": round(n / t, 1),
+                      "gbs": res["value"]},
+        "one_thread": {"threads": 1, "tokens": n1, "seconds": round(t1, 4), "tokens_per_s": round(n1 / t1, 1),
+                       "gbs": round(n1 * per_token / t1 / 1e9, 4)}}}
+    per.update(cpu_other_configs(torch, W, threads))
+    res["per_config"] = per
+    return res
+
+
+def cpu_other_configs(torch, W, threads):
+    """The oracle on the other four workloads, in full, on all cores (median
+    of 3 runs) and on one thread (one run): the tiny across-heads case and the
+    three MLA cache workloads (inputs drawn on the host with the same recipe,
+    caches zero-filled host arrays updated in place)."""
+    import numpy as np
+    import oracle
+
+    def host(t):
+        t = t.contiguous()
+        if t.dtype in (torch.bfloat16, torch.float16):
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2]
+
+    def record(fn, tokens, nbytes, loops=1):
+        out = {"tokens": tokens}
+        for key, th, reps in (("all_cores", threads, 3), ("one_thread", 1, 1)):
+            sec = timed(lambda: [fn(th) for _ in range(loops)], reps) / loops
+            out[key] = {"threads": th, "seconds": round(sec, 6), "tokens_per_s": round(tokens / sec, 1),
+                        "gbs": round(nbytes / sec / 1e9, 4)}
+        return out
+
+    per = {}
+    c1 = W.TINY_ACROSS_HEADS
+    d1 = W.make_across_heads(c1, device="cpu")
+    hd, nq, nk = c1.head_dim, c1.n_q_heads, c1.n_k_heads
+    flat = d1["qkv"].reshape(-1, d1["qkv"].shape[-1])
+    args1 = (np.ascontiguousarray(host(flat[:, : nq * hd])), np.ascontiguousarray(host(flat[:, nq * hd:])),
+             host(d1["q_gamma"]), host(d1["k_gamma"]), host(d1["cos"].reshape(-1, hd)),
+             host(d1["sin"].reshape(-1, hd)))
+    dt1 = {torch.float32: oracle.F32, torch.bfloat16: oracle.BF16}[c1.dtype]
+    per[c1.name] = record(lambda th: oracle.qk_norm_rope_across_heads(*args1, c1.eps, nq, nk, hd, dt1, nthreads=th,
+                                                                      values=False),
+                          c1.batch * c1.seq, W.algorithmic_bytes_across_heads(c1), loops=200)
+    codes = {torch.bfloat16: oracle.BF16, torch.float16: oracle.F16, torch.int8: oracle.INT8,
+             torch.float8_e4m3fn: oracle.E4M3FN, torch.float8_e5m2: oracle.E5M2}
+    modes = {W.NORM: oracle.NORM, W.PA_BNSD: oracle.PA_BNSD, W.PA_BLK_BNSD: oracle.PA_BLK_BNSD}
+    for cfg in (W.MLA_V1_PREFILL, W.MLA_V1_DECODE_QUANT, W.MLA_V2_SPLIT):
+        d = W.make_kv_cache(cfg, device="cpu", prefill=False)
+        kc = np.zeros(tuple(d["k_cache"].shape), oracle.STORAGE[codes[cfg.k_cache_dtype]])
+        cc = np.zeros(tuple(d["ckv_cache"].shape), oracle.STORAGE[codes[cfg.ckv_cache_dtype]])
+        q = lambda t: None if t is None else t.numpy()
+        ins = dict(kv=host(d["kv"]), v=None if d["v"] is None else host(d["v"]), gamma=host(d["gamma"]),
+                   cos=host(d["cos"]), sin=host(d["sin"]), index=d["index"].numpy())
+
+        def run(th, cfg=cfg, ins=ins, kc=kc, cc=cc, d=d):
+            oracle.kv_rmsnorm_rope_cache(
+                ins["kv"], ins["v"], ins["gamma"], ins["cos"], ins["sin"], ins["index"], kc, cc,
+                rms_size=cfg.rms_size, rope_size=cfg.rope_size, eps=cfg.eps, cache_mode=modes[cfg.cache_mode],
+                in_dtype=codes[cfg.dtype], k_dtype=codes[cfg.k_cache_dtype], ckv_dtype=codes[cfg.ckv_cache_dtype],
+                block_size=cfg.block_size, k_scale=q(d["k_scale"]), k_offset=q(d["k_offset"]),
+                v_scale=q(d["v_scale"]), v_offset=q(d["v_offset"]), is_output_kv=cfg.is_output_kv,
+                nthreads=th, copy_caches=False)
+        per[cfg.name] = record(run, cfg.batch * cfg.seq, W.algorithmic_bytes_kv_cache(cfg),
+                               loops=20 if cfg.batch * cfg.heads * cfg.seq < 4096 else 1)
+        del d, ins, kc, cc
+    return per
 
 
 def graph_replay_us(torch, step, calls=100, replays=20):
@@ -411,16 +505,14 @@ def kv_measure(torch, W, Q, flush, cold_iters):
         # settle), then the median of three runs of 200
         time_hot(torch, step, 200)
         hot = sorted(time_hot(torch, step, 200) for _ in range(3))[1]
-        cold = time_cold(torch, step, cold_iters, flush)
         nbytes = W.algorithmic_bytes_kv_cache(cfg)
         tokens = cfg.batch * cfg.seq
         rec = {"algorithmic_bytes": nbytes, "tokens": tokens, "rows": cfg.batch * cfg.heads * cfg.seq,
-               "us_cold_median": round(cold, 3), "us_hot_mean": round(hot, 3),
-               "gbs_cold": round(nbytes / cold / 1e3, 1), "gbs_hot": round(nbytes / hot / 1e3, 1),
-               "frac_cold": round(nbytes / cold / 1e3 / PEAK_HBM_GBS, 4),
-               "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4),
-               "tokens_per_s_cold": round(tokens / cold * 1e6, 1),
-               "traffic": measured_traffic("kv_rmsnorm_rope_cache", name)}
+               "us_hot_mean": round(hot, 3), "gbs_hot": round(nbytes / hot / 1e3, 1),
+               "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4)}
+        rec.update(cold_record(torch, step, cold_iters, flush, nbytes))
+        rec["tokens_per_s_cold"] = round(tokens / rec["us_cold_median"] * 1e6, 1)
+        rec["traffic"] = measured_traffic("kv_rmsnorm_rope_cache", name)
         if name == "mla_v1_decode_quant":
             rec["us_graph_replay_per_call"] = round(graph_replay_us(torch, step), 3)
         out[name] = rec
@@ -620,7 +712,7 @@ def main():
     value = nbytes * args.steps / wall / 1e9
 
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
-    cold_us = time_cold(torch, step, args.cold_iters, flush)
+    cold = cold_record(torch, step, args.cold_iters, flush, nbytes)
     copy_src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
     copy_dst = torch.empty_like(copy_src)
     copy_us = time_hot(torch, lambda: copy_dst.copy_(copy_src), 20)
@@ -638,8 +730,9 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("qk_across_heads", cfg.name),
                      "kernel": "qk_across_heads_kernel", "algorithmic_bytes_per_launch": nbytes,
-                     "avg_launch_us": round(launch_us, 3), "cold_launch_us_median": round(cold_us, 3),
-                     "frac_cold": round(nbytes / cold_us / 1e3 / PEAK_HBM_GBS, 4)},
+                     "avg_launch_us": round(launch_us, 3), "cold_launch_us_median": cold["us_cold_median"],
+                     "frac_cold": cold["frac_cold"], "cold_read_launch_us_median": cold["us_cold_read_median"],
+                     "frac_cold_read": cold["frac_cold_read"]},
         "copy_reference": {"what": "1 GiB device-to-device copy (hipMemcpy), read + write bytes / time",
                            "gbs": round(2 * (1 << 30) / copy_us / 1e3, 1),
                            "frac": round(2 * (1 << 30) / copy_us / 1e3 / PEAK_HBM_GBS, 4)},
