@@ -48,16 +48,16 @@ PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 matrix-core peak
 METRIC = "achieved HBM GB/s (% of MI355X peak) + tokens/s for fused norm+RoPE(+cache)"
 KERNEL_SOURCES = {
     "qk_across_heads": ["qk_rmsnorm_rope_amd/csrc/qk_across_heads.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
-                        "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+                        "qk_rmsnorm_rope_amd/csrc/device_common.h", "qk_rmsnorm_rope_amd/csrc/plan.cpp"],
     "qk_per_head": ["qk_rmsnorm_rope_amd/csrc/qk_per_head.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
-                    "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+                    "qk_rmsnorm_rope_amd/csrc/device_common.h", "qk_rmsnorm_rope_amd/csrc/plan.cpp"],
     "qk_split": ["qk_rmsnorm_rope_amd/csrc/qk_split.hip", "qk_rmsnorm_rope_amd/csrc/qk_kernel.h",
-                 "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+                 "qk_rmsnorm_rope_amd/csrc/device_common.h", "qk_rmsnorm_rope_amd/csrc/plan.cpp"],
     "qkv_proj": ["qk_rmsnorm_rope_amd/csrc/qkv_proj.hip", "qk_rmsnorm_rope_amd/csrc/device_common.h"],
     "kv_rmsnorm_rope_cache": ["qk_rmsnorm_rope_amd/csrc/kv_rmsnorm_rope_cache.hip",
                               "qk_rmsnorm_rope_amd/csrc/kv_rmsnorm_rope_cache_f16.hip",
                               "qk_rmsnorm_rope_amd/csrc/kv_kernel.h",
-                              "qk_rmsnorm_rope_amd/csrc/device_common.h"],
+                              "qk_rmsnorm_rope_amd/csrc/device_common.h", "qk_rmsnorm_rope_amd/csrc/plan.cpp"],
 }
 
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqknr.so")
-SOURCES = ["api.cpp", "qk_across_heads.hip", "qk_per_head.hip", "qk_split.hip", "permute.hip",
+SOURCES = ["api.cpp", "plan.cpp", "qk_across_heads.hip", "qk_per_head.hip", "qk_split.hip", "permute.hip",
            "qkv_proj.hip", "kv_rmsnorm_rope_cache.hip",
            "kv_rmsnorm_rope_cache_f16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

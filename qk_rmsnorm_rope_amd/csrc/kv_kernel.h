@@ -275,10 +275,7 @@ __device__ __forceinline__ RowPos row_pos(const KvParams &p, uint32_t blk, int s
 // lds_param_bytes (<= 2 KB), and every row of the wave has the same head
 // (checked from its first and last row). Only the
 // wave writes and reads its region, and LDS accesses of one wave complete in
-// order, so no barrier is needed.
-
-constexpr int kWaveParamFloats = 512;   // at most 2 KB per wave: two 16-byte pieces per lane
-
+// order, so no barrier is needed. (At most kWaveParamFloats per wave.)
 struct WaveParams {
     float4 v[2];      // staged 16-byte pieces of this lane (lane, lane + 64)
     uint32_t wp;      // byte offset of the wave's region in kv_lds

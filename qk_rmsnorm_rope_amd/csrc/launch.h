@@ -165,10 +165,17 @@ struct KvParams {
     float eps;
 };
 
+// Staged quantisation parameters of one wave: at most 512 floats (2 KB, two
+// 16-byte pieces per lane), [scale[width] | offset[width]].
+constexpr int kWaveParamFloats = 512;
+
 // Lane geometry of the two row parts and their register slots; returns 0 and
 // sets ca/cb, or -1 if a row is too wide.
 int kv_plan(KvParams &p, int vec, bool v2, int &ca, int &cb);
 // elem_type: 1 bf16, 2 f16. vec: 8 or 4.
 hipError_t kv_launch(KvParams &p, int elem_type, int vec, bool v2, hipStream_t stream);
+// The kernel instantiations of one element type (one translation unit each).
+hipError_t kv_launch_bf16(const KvParams &p, int vec, bool v2, int ca, int cb, hipStream_t stream);
+hipError_t kv_launch_f16(const KvParams &p, int vec, bool v2, int ca, int cb, hipStream_t stream);
 
 }  // namespace qknr

@@ -110,19 +110,38 @@ def _inputs(c, device):
     return d
 
 
+def _host_args(Q, i):
+    """Case i's argument struct on CPU tensors (a split case: its first shard),
+    with the tensors it points into."""
+    c = _draw(i)
+    d = _inputs(c, "cpu")
+    q, k = _views(d, c)
+    if c["form"] == "split":
+        lq, lk = c["n_q"] // c["tp"], c["n_k"] // c["tp"]
+        q, k = q[:, :, :lq], k[:, :, :lk]
+        d["q_gamma"], d["k_gamma"] = d["q_gamma"][: lq * c["head_dim"]], d["k_gamma"][: lk * c["head_dim"]]
+    a = Q.qk_args(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"], eps=c["eps"],
+                  apply_norm=c["norm"], apply_rope=c["rope"], per_head=c["form"] == "per_head")
+    return c, a, (d, q, k)
+
+
+def host_call_status(Q, i):
+    """Status of case i's entry point called on CPU tensors (no GPU: past
+    validation and planning the launch itself fails)."""
+    import ctypes
+    c, a, keep = _host_args(Q, i)
+    if c["form"] == "split":
+        sums = torch.empty(2, c["batch"] * c["seq"], dtype=torch.float32)
+        return Q._lib.qknr_qk_sumsq_across_heads(ctypes.byref(a), ctypes.c_void_p(sums.data_ptr()), None)
+    fn = Q._lib.qknr_qk_norm_rope_per_head if c["form"] == "per_head" else Q._lib.qknr_qk_norm_rope_across_heads
+    return fn(ctypes.byref(a), None)
+
+
 def test_random_qk_cases_are_legal_calls():
     """Host validation accepts every drawn case (CPU tensors; nothing runs on a GPU)."""
     import qk_rmsnorm_rope_amd as Q
     for i in range(N_CASES):
-        c = _draw(i)
-        d = _inputs(c, "cpu")
-        q, k = _views(d, c)
-        if c["form"] == "split":
-            lq, lk = c["n_q"] // c["tp"], c["n_k"] // c["tp"]
-            q, k = q[:, :, :lq], k[:, :, :lk]
-            d["q_gamma"], d["k_gamma"] = d["q_gamma"][: lq * c["head_dim"]], d["k_gamma"][: lk * c["head_dim"]]
-        a = Q.qk_args(q, k, d["q_gamma"], d["k_gamma"], d["cos"], d["sin"], eps=c["eps"],
-                      apply_norm=c["norm"], apply_rope=c["rope"], per_head=c["form"] == "per_head")
+        c, a, keep = _host_args(Q, i)
         assert Q.qk_validate(a) == 0, f"case {i} ({c}): {Q.last_error()}"
 
 
