@@ -26,6 +26,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv] 
        python bench.py --profile {across,per_head,split_sumsq,split_apply,proj,proj_fp8,
                                   kv_v1_prefill,kv_v1_decode,kv_v2,copy}
        (a short fixed run of one kernel, for rocprofv3 counter collection)
+       python bench.py --ceiling
+       (plain stream kernels with the operators' read/write mixes at 32 MB - 3.1 GB,
+       the bandwidth ceiling the operators are compared with)
        python bench.py --summarize DIR
        (turn the rocprofv3 CSVs under DIR into the text summaries and the
        traffic record under profiles/; CPU only)
@@ -97,6 +100,8 @@ def parse():
                     choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "proj_fp8", "kv_v1_prefill",
                              "kv_v1_decode", "kv_v2", "copy"])
     ap.add_argument("--summarize", default=None, metavar="DIR")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="sweep plain stream kernels with the operators' read/write mixes (bench_stream.hip)")
     return ap.parse_args()
 
 
@@ -671,6 +676,114 @@ def summarize(prof_dir):
     print(json.dumps(record, indent=1))
 
 
+STREAM_LIB = os.path.join(ROOT, "libbench_stream.so")
+
+
+def ceiling(torch, W, Q, cold_iters):
+    """Same-process sweep of plain stream kernels (bench_stream.hip) that read
+    and write the operators' byte mixes at 32 MB - 3.1 GB, hot (back to back)
+    and cold after a 1 GiB write and after a 1 GiB read, next to the three
+    bandwidth-bound operators at their own sizes; the persistent-grid form of
+    the stream at the operators' sizes as well."""
+    import ctypes
+    lib = ctypes.CDLL(STREAM_LIB)
+    lib.bench_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_void_p]
+    lib.bench_stream.restype = ctypes.c_int
+    mb = 1 << 20
+    mixes = {"mla_v1_prefill": W.algorithmic_read_write_kv_cache(W.MLA_V1_PREFILL),
+             "mla_v2_split": W.algorithmic_read_write_kv_cache(W.MLA_V2_SPLIT),
+             "wan22_self_attn": W.algorithmic_read_write_across_heads(W.WAN22_SELF_ATTN),
+             "write_only": (0, 1), "read_only": (1, 0)}
+    own = {k: sum(v) for k, v in mixes.items() if k in ("mla_v1_prefill", "mla_v2_split", "wan22_self_attn")}
+    sizes = sorted({32 * mb, 64 * mb, 256 * mb, 512 * mb, 1024 * mb, 3135 * mb} | set(own.values()))
+    top = max(sizes)
+    src = torch.empty(top, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(top, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+
+    def measure(name, total, rfrac_pair, nt_store, grid):
+        r, w = rfrac_pair
+        rb = (total * r // (r + w)) // 16 * 16
+        wb = (total - rb) // 16 * 16
+        step = lambda: lib.bench_stream(src.data_ptr(), rb, dst.data_ptr(), wb, nt_store, grid, stream)
+        if step() != 0:
+            raise RuntimeError("stream launch failed")
+        for _ in range(3):
+            step()
+        hot = sorted(time_hot(torch, step, 20) for _ in range(3))[1]
+        rec = {"mix": name, "bytes": rb + wb, "read_bytes": rb, "write_bytes": wb, "nt_store": nt_store,
+               "grid": grid or "one piece per thread", "us_hot": round(hot, 3),
+               "frac_hot": round((rb + wb) / hot / 1e3 / PEAK_HBM_GBS, 4)}
+        rec.update(cold_record(torch, step, cold_iters, flush, rb + wb))
+        rows.append(rec)
+        print(json.dumps(rec), flush=True)
+
+    for name, pair in mixes.items():
+        for total in sizes:
+            for nt in (1, 0):
+                measure(name, total, pair, nt, 0)
+    for name in own:
+        for grid in (1024, 2048, 4096, 8192):
+            measure(name, own[name], mixes[name], 1, grid)
+    del src, dst
+    torch.cuda.empty_cache()
+    ops = {}
+    for name, cfg in (("mla_v1_prefill", W.MLA_V1_PREFILL), ("mla_v2_split", W.MLA_V2_SPLIT)):
+        d, step = kv_setup(torch, W, Q, cfg)
+        for _ in range(5):
+            step()
+        time_hot(torch, step, 200)
+        hot = sorted(time_hot(torch, step, 200) for _ in range(3))[1]
+        nbytes = W.algorithmic_bytes_kv_cache(cfg)
+        ops[name] = {"bytes": nbytes, "us_hot": round(hot, 3), "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4)}
+        ops[name].update(cold_record(torch, step, cold_iters, flush, nbytes))
+        del d, step
+        torch.cuda.empty_cache()
+    cfg, d, step = across_setup(torch, W, Q)
+    for _ in range(5):
+        step()
+    nbytes = W.algorithmic_bytes_across_heads(cfg)
+    hot = time_hot(torch, step, 20)
+    ops["wan22_self_attn"] = {"bytes": nbytes, "us_hot": round(hot, 3),
+                              "frac_hot": round(nbytes / hot / 1e3 / PEAK_HBM_GBS, 4)}
+    ops["wan22_self_attn"].update(cold_record(torch, step, cold_iters, flush, nbytes))
+    for name, rec in ops.items():
+        print(json.dumps(dict(rec, operator=name)), flush=True)
+    print(ceiling_table(rows, ops))
+
+
+def ceiling_table(rows, ops):
+    """The sweep as a text table: fraction of 8 TB/s hot / cold (write flush) /
+    cold (read flush) per mix and size, best of the store kinds, and the
+    operators at their sizes."""
+    out = ["fraction of 8 TB/s: hot | cold after 1 GiB write | cold after 1 GiB read "
+           "(plain stream, best of nt / ordinary stores, one piece per thread)"]
+    mixes = []
+    for r in rows:
+        if r["mix"] not in mixes:
+            mixes.append(r["mix"])
+    for mix in mixes:
+        out.append(f"{mix}:")
+        sizes = sorted({r["bytes"] for r in rows if r["mix"] == mix and r["grid"] == "one piece per thread"})
+        for b in sizes:
+            rs = [r for r in rows if r["mix"] == mix and r["bytes"] == b and r["grid"] == "one piece per thread"]
+            best = lambda k: max(r[k] for r in rs)
+            out.append(f"  {b / 1e6:9.1f} MB  {best('frac_hot'):.3f} | {best('frac_cold'):.3f} | "
+                       f"{best('frac_cold_read'):.3f}   ({min(r['us_cold_median'] for r in rs):.2f} us cold)")
+        ps = [r for r in rows if r["mix"] == mix and r["grid"] != "one piece per thread"]
+        for r in ps:
+            out.append(f"  persistent grid {r['grid']:>5} blocks, {r['bytes'] / 1e6:.1f} MB: {r['frac_hot']:.3f} | "
+                       f"{r['frac_cold']:.3f} | {r['frac_cold_read']:.3f}")
+    out.append("operators (same process):")
+    for name, r in ops.items():
+        out.append(f"  {name:16s} {r['bytes'] / 1e6:9.1f} MB  {r['frac_hot']:.3f} | {r['frac_cold']:.3f} | "
+                   f"{r['frac_cold_read']:.3f}   ({r['us_hot']:.2f} us hot, {r['us_cold_median']:.2f} us cold)")
+    return "\n".join(out)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -689,6 +802,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile:
         profile_run(torch, W, Q, args.profile)
+        return
+    if args.ceiling:
+        ceiling(torch, W, Q, args.cold_iters)
         return
 
     cfg, d, step = across_setup(torch, W, Q)

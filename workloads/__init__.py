@@ -418,10 +418,16 @@ def algorithmic_bytes_per_head(cfg: AcrossHeadsConfig) -> int:
 def algorithmic_bytes_across_heads(cfg: AcrossHeadsConfig) -> int:
     """Bytes the across-heads pass must move: Q and K read and written once,
     cos and sin read once per token, both gammas read once."""
+    rd, wr = algorithmic_read_write_across_heads(cfg)
+    return rd + wr
+
+
+def algorithmic_read_write_across_heads(cfg: AcrossHeadsConfig):
+    """The across-heads pass's algorithmic bytes split into (read, written)."""
     e = torch.tensor([], dtype=cfg.dtype).element_size()
     T = cfg.batch * cfg.seq
     cq, ck = cfg.n_q_heads * cfg.head_dim, cfg.n_k_heads * cfg.head_dim
-    return e * (T * (2 * (cq + ck) + 2 * cfg.head_dim) + cq + ck)
+    return e * (T * ((cq + ck) + 2 * cfg.head_dim) + cq + ck), e * T * (cq + ck)
 
 
 def algorithmic_bytes_kv_cache(cfg: KvCacheConfig) -> int:
@@ -429,6 +435,12 @@ def algorithmic_bytes_kv_cache(cfg: KvCacheConfig) -> int:
     once; one k row and one ckv row written per (b, n, s) token with a valid
     index; k_rope / c_kv written when requested; gamma and quant params read
     once."""
+    rd, wr = algorithmic_read_write_kv_cache(cfg)
+    return rd + wr
+
+
+def algorithmic_read_write_kv_cache(cfg: KvCacheConfig):
+    """The KV operator's algorithmic bytes split into (read, written)."""
     e = torch.tensor([], dtype=cfg.dtype).element_size()
     rows = cfg.batch * cfg.heads * cfg.seq
     tokens = cfg.batch * cfg.seq
@@ -445,7 +457,7 @@ def algorithmic_bytes_kv_cache(cfg: KvCacheConfig) -> int:
         if spec is not None:
             n = {"1": 1, "D": width, "1D": width, "ND": cfg.heads * width}[spec[2]]
             small += 4 * n
-    return rd + wr + small
+    return rd + small, wr
 
 
 def math_check():  # pragma: no cover - documentation helper
