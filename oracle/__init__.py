@@ -71,6 +71,8 @@ def _load():
         lib.oracle_qk_sumsq.restype = i32
         lib.oracle_linear.argtypes = [i64, i64, i64, i32, p, i32, p, p, i32, p, p, i32, p, p, i32]
         lib.oracle_linear.restype = i32
+        lib.oracle_linear_mx.argtypes = [i64, i64, i64, p, p, p, i64, p, i64, p, i32, p, p, i32, p, p, i32]
+        lib.oracle_linear_mx.restype = i32
         lib.oracle_kv_rmsnorm_rope_cache.argtypes = (
             [i64] * 7 + [i32] + [p] * 5 + [i64, p, i32, i64, i64, i32, i32, p, p]
             + [p] * 4 + [f64, i32] + [p] * 6 + [i32])
@@ -223,6 +225,36 @@ def linear(a, w, a_dtype, w_dtype=None, bias=None, bias_dtype=None, a_scale=None
     rc = _load().oracle_linear(S, H, I, a_dtype, _ptr(a), w_dtype, _ptr(w), _ptr(b), bias_dtype, _ptr(asc),
                                _ptr(wsc), out_dtype if out_dtype is not None else F64, _ptr(out), _ptr(val),
                                nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    return out, val
+
+
+def linear_mx(a, w, a_block_scale, w_block_scale, bias=None, bias_dtype=BF16, a_scale=None, w_scale=None,
+              out_dtype=None, nthreads=None):
+    """The projection with MXFP8 operands (OCP MX: E4M3 codes, one E8M0 scale
+    per 32 values along H): O = (A*Xa) @ (W*Xw)^T * a_scale * w_scale + bias.
+
+    a: [S, H] E4M3 codes (uint8); w: [I, H] E4M3 codes; a_block_scale [S, H/32],
+    w_block_scale [I, H/32] E8M0 bytes (uint8); bias [I] storage of bias_dtype;
+    ROW_MX scales fp64 or None. Returns (encoded output or None, exact fp64 [S, I]).
+    """
+    a = _c(a, np.uint8)
+    w = _c(w, np.uint8)
+    S, H = a.shape
+    I = w.shape[0]
+    assert w.shape == (I, H) and H % 32 == 0
+    abs_ = _c(a_block_scale, np.uint8)
+    wbs = _c(w_block_scale, np.uint8)
+    assert abs_.shape == (S, H // 32) and wbs.shape == (I, H // 32)
+    b = _c(bias, STORAGE[bias_dtype]) if bias is not None else None
+    asc = np.ascontiguousarray(a_scale, dtype=np.float64) if a_scale is not None else None
+    wsc = np.ascontiguousarray(w_scale, dtype=np.float64) if w_scale is not None else None
+    out = np.empty((S, I), STORAGE[out_dtype]) if out_dtype is not None else None
+    val = np.empty((S, I), np.float64)
+    rc = _load().oracle_linear_mx(S, H, I, _ptr(a), _ptr(w), _ptr(abs_), H // 32, _ptr(wbs), H // 32, _ptr(b),
+                                  bias_dtype, _ptr(asc), _ptr(wsc), out_dtype if out_dtype is not None else F64,
+                                  _ptr(out), _ptr(val), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle rejected the sizes")
     return out, val

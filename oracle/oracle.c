@@ -378,6 +378,50 @@ int oracle_linear(int64_t S, int64_t H, int64_t I, int a_dtype, const void *A, i
     return 0;
 }
 
+/* E8M0 (OCP Microscaling shared scale): an unsigned biased exponent, value
+ * 2^(e - 127); 255 is NaN. */
+static double dec_e8m0(uint8_t e) {
+    return e == 255 ? NAN : ldexp(1.0, (int)e - 127);
+}
+
+/*
+ * [qkv_cte] "Upstream behavior" names MXFP8 among the projection's
+ * quantisation modes without defining it; read as the OCP Microscaling (MX)
+ * format: FP8 E4M3 elements in blocks of 32 consecutive values along the
+ * contraction axis, each block with one E8M0 scale, element value = code *
+ * 2^(e - 127). For the projection both operands are MX along H:
+ *   O[s, i] = (sum_h A[s, h] * X(a_bs[s, h / 32]) * W[i, h] * X(w_bs[i, h / 32]))
+ *             * a_scale[s] * w_scale[i] + bias[i],
+ * a_bs [S, H/32] and w_bs [I, H/32] E8M0 bytes (row strides a_bs_stride,
+ * w_bs_stride), the ROW_MX scales optional (NULL = 1) as in oracle_linear.
+ * H must be a multiple of 32. Evaluated in fp64 over h in order; O rounded
+ * once to out_dtype; o_val (if given) the exact value. Returns 0 or -1.
+ */
+int oracle_linear_mx(int64_t S, int64_t H, int64_t I, const void *A, const void *W, const uint8_t *a_bs,
+                     int64_t a_bs_stride, const uint8_t *w_bs, int64_t w_bs_stride, const void *bias,
+                     int bias_dtype, const double *a_scale, const double *w_scale, int out_dtype, void *O,
+                     double *o_val, int nthreads) {
+    if (S < 0 || H < 32 || H % 32 || I < 1 || a_bs_stride < H / 32 || w_bs_stride < H / 32) return -1;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t s = 0; s < S; s++) {
+        for (int64_t i = 0; i < I; i++) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; h++) {
+                double a = load(ORC_E4M3FN, A, s * H + h) * dec_e8m0(a_bs[s * a_bs_stride + h / 32]);
+                double w = load(ORC_E4M3FN, W, i * H + h) * dec_e8m0(w_bs[i * w_bs_stride + h / 32]);
+                acc += a * w;
+            }
+            if (a_scale) acc *= a_scale[s];
+            if (w_scale) acc *= w_scale[i];
+            if (bias) acc += load(bias_dtype, bias, i);
+            if (O) store(out_dtype, O, s * I + i, acc);
+            if (o_val) o_val[s * I + i] = acc;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* (b) KvRmsNormRopeCache                                                     */
 /* ------------------------------------------------------------------------ */

@@ -54,6 +54,10 @@ MUTANTS = {
                                  "acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, (h * I + i) % (I * H));"),
     "linear_bias_dropped": ("            if (bias) acc += load(bias_dtype, bias, i);\n", ""),
     "linear_weight_scale_dropped": ("            if (w_scale) acc *= w_scale[i];\n", ""),
+    "mx_weight_block_scale_ignored": ("* dec_e8m0(w_bs[i * w_bs_stride + h / 32]);", "* 1.0;"),
+    "mx_e8m0_bias_128": ("return e == 255 ? NAN : ldexp(1.0, (int)e - 127);",
+                         "return e == 255 ? NAN : ldexp(1.0, (int)e - 128);"),
+    "mx_first_block_scale_for_every_block": ("a_bs[s * a_bs_stride + h / 32]", "a_bs[s * a_bs_stride]"),
     "c_kv_from_raw_in_v1": ("c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : y[i];",
                             "c_src[i] = v2 ? load(in_dtype, v, row * Dv + i) : load(in_dtype, kv, kv0 + i);"),
 }

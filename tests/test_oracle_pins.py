@@ -300,6 +300,89 @@ def test_linear_fp8_row_scaled_and_identity_weight():
     np.testing.assert_array_equal(v, x + bias)
 
 
+def test_linear_mx_golden_hand_cases():
+    g = _golden("linear_mx_hand.json")
+    for c in g["cases"]:
+        bias = None if c["bias"] is None else np.array(c["bias"], np.float64)
+        _, v = oracle.linear_mx(np.array(g["A"], np.uint8), np.array(g["W"], np.uint8),
+                                np.array(g["a_block_scale"], np.uint8), np.array(g["w_block_scale"], np.uint8),
+                                bias=bias, bias_dtype=oracle.F64, a_scale=c["a_scale"], w_scale=c["w_scale"],
+                                nthreads=1)
+        np.testing.assert_array_equal(v, c["out"])
+
+
+def _mx_operands(rng, S, H, I):
+    ac = rng.integers(0, 256, (S, H)).astype(np.uint8)
+    wc = rng.integers(0, 256, (I, H)).astype(np.uint8)
+    ac[(ac & 0x7F) == 0x7F] = 0                       # no NaN codes
+    wc[(wc & 0x7F) == 0x7F] = 0
+    abs_ = rng.integers(110, 140, (S, H // 32)).astype(np.uint8)
+    wbs = rng.integers(110, 140, (I, H // 32)).astype(np.uint8)
+    return ac, wc, abs_, wbs
+
+
+def test_linear_mx_matches_dequantised_matmul():
+    """Library special case: decode the codes with torch's E4M3 cast, expand
+    each block scale over its 32 values with numpy (2.0 ** (e - 127)), then a
+    plain fp64 matmul."""
+    rng = np.random.default_rng(32)
+    S, H, I = 7, 160, 11
+    ac, wc, abs_, wbs = _mx_operands(rng, S, H, I)
+    asc, wsc = rng.uniform(0.5, 2, S), rng.uniform(0.5, 2, I)
+    bias = rng.standard_normal(I)
+    _, v = oracle.linear_mx(ac, wc, abs_, wbs, bias=bias, bias_dtype=oracle.F64, a_scale=asc, w_scale=wsc,
+                            nthreads=2)
+    dec = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()
+    ad = dec(ac) * np.repeat(2.0 ** (abs_.astype(np.float64) - 127), 32, axis=1)
+    wd = dec(wc) * np.repeat(2.0 ** (wbs.astype(np.float64) - 127), 32, axis=1)
+    ref = (ad @ wd.T) * asc[:, None] * wsc[None, :] + bias
+    np.testing.assert_allclose(v, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_linear_mx_block_exponent_closed_form():
+    """Raising one block's E8M0 exponent by one doubles exactly that block's
+    share of the sum: the output moves by the block's own partial dot product
+    (computed from the oracle with every other block's codes zeroed)."""
+    rng = np.random.default_rng(33)
+    S, H, I = 3, 128, 4
+    ac, wc, abs_, wbs = _mx_operands(rng, S, H, I)
+    _, v0 = oracle.linear_mx(ac, wc, abs_, wbs, nthreads=1)
+    for blk in range(H // 32):
+        only = np.zeros_like(ac)
+        only[:, blk * 32:(blk + 1) * 32] = ac[:, blk * 32:(blk + 1) * 32]
+        _, part = oracle.linear_mx(only, wc, abs_, wbs, nthreads=1)
+        bumped = abs_.copy()
+        bumped[:, blk] += 1
+        _, v1 = oracle.linear_mx(ac, wc, bumped, wbs, nthreads=1)
+        # (fp64 rounding of the two sums: a few ulps of their magnitudes)
+        tol = 1e-13 * (np.abs(v0).max() + np.abs(v1).max())
+        np.testing.assert_allclose(v1 - v0, part, rtol=0, atol=tol)
+        wb = wbs.copy()
+        wb[:, blk] += 1
+        _, v2 = oracle.linear_mx(ac, wc, abs_, wb, nthreads=1)
+        np.testing.assert_allclose(v2 - v0, part, rtol=0, atol=1e-13 * (np.abs(v0).max() + np.abs(v2).max()))
+        assert np.abs(part).max() > 1e3 * tol        # the moved share is far above the rounding
+
+
+def test_linear_mx_brute_force_tiny():
+    rng = np.random.default_rng(34)
+    S, H, I = 2, 64, 3
+    ac, wc, abs_, wbs = _mx_operands(rng, S, H, I)
+    bias = torch.from_numpy(rng.standard_normal(I)).to(torch.bfloat16)
+    bbits = bias.view(torch.int16).numpy().view(np.uint16)
+    out, v = oracle.linear_mx(ac, wc, abs_, wbs, bias=bbits, bias_dtype=oracle.BF16, out_dtype=oracle.BF16,
+                              nthreads=1)
+    for s_ in range(S):
+        for i in range(I):
+            acc = 0.0
+            for h in range(H):
+                acc += (brute.e4m3fn_value(int(ac[s_, h])) * 2.0 ** (int(abs_[s_, h // 32]) - 127) *
+                        brute.e4m3fn_value(int(wc[i, h])) * 2.0 ** (int(wbs[i, h // 32]) - 127))
+            acc += brute.bf16_value(int(bbits[i]))
+            assert abs(v[s_, i] - acc) <= 1e-12 * (1 + abs(acc))
+            assert out[s_, i] == brute.encode_nearest("bf16", acc)
+
+
 def test_across_heads_brute_force_tiny():
     rng = np.random.default_rng(5)
     for (T, nq, nk, d, norm, rope) in [(3, 2, 2, 4, 1, 1), (2, 3, 1, 6, 1, 1), (2, 1, 0, 2, 1, 1),
