@@ -97,8 +97,8 @@ def parse():
     ap.add_argument("--no-proj", action="store_true", help="skip the QKV projection")
     ap.add_argument("--cold-iters", type=int, default=50)
     ap.add_argument("--profile", default=None,
-                    choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "proj_fp8", "kv_v1_prefill",
-                             "kv_v1_decode", "kv_v2", "copy"])
+                    choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "proj_fp8", "proj_mxfp8",
+                             "kv_v1_prefill", "kv_v1_decode", "kv_v2", "copy"])
     ap.add_argument("--summarize", default=None, metavar="DIR")
     ap.add_argument("--ceiling", action="store_true",
                     help="sweep plain stream kernels with the operators' read/write mixes (bench_stream.hip)")
@@ -270,6 +270,47 @@ def proj_measure(torch, W, Q):
         f8["unfused_library_pipeline_us"] = round(f8["library_gemm_torch_scaled_mm_us"] +
                                                   res["single_pass_epilogue_us"], 1)
     res["fp8_row_mx"] = f8
+    torch.cuda.empty_cache()
+    mx = proj_mx_measure(torch, W, Q)
+    mx["fused_pipeline_us"] = round(mx["projection_with_sums_us"] + res["apply_pass_us"], 1)
+    if "library_gemm_torch_scaled_mm_us" in mx:
+        mx["unfused_library_pipeline_us"] = round(mx["library_gemm_torch_scaled_mm_us"] +
+                                                  res["single_pass_epilogue_us"], 1)
+    res["mxfp8"] = mx
+    return res
+
+
+def proj_mx_measure(torch, W, Q):
+    """The same projection with MXFP8 operands (E4M3 codes, one E8M0 scale per
+    32 values of hidden on both operands), next to torch._scaled_mm with the
+    same block scales where the library supports them."""
+    cfg = W.WAN22_QKV_PROJ_MXFP8
+    d = W.make_qkv_projection(cfg, device="cuda")
+    S, I = cfg.seq, d["out_features"]
+    flops = W.flops_qkv_projection(cfg)
+    out = torch.empty(S, I, dtype=torch.bfloat16, device="cuda")
+    sums = torch.empty(2, S, 40, dtype=torch.float32, device="cuda")
+    proj = Q.prepare_qkv_projection(d["a8"], d["w8"], d["bias"], out=out, q_cols=5120, k_cols=5120, sumsq=sums,
+                                    a_block_scale=d["a_bs"], w_block_scale=d["w_bs"])
+    res = {"workload": "the same projection with MXFP8 operands: E4M3 codes, one E8M0 scale per 32 values of "
+                       "hidden on A and on W (OCP MX)"}
+    for _ in range(3):
+        proj()
+    us = time_hot(torch, proj, 10)
+    res["projection_with_sums_us"] = round(us, 1)
+    res["projection_tflops"] = round(flops / us / 1e6, 1)
+    res["projection_frac_fp8_peak"] = round(flops / us / 1e6 / PEAK_FP8_TFLOPS, 4)
+    try:
+        sa, sb = d["a_bs"].view(torch.float8_e8m0fnu), d["w_bs"].view(torch.float8_e8m0fnu)
+        wt = d["w8"].t()
+        lib = lambda: torch._scaled_mm(d["a8"], wt, scale_a=sa, scale_b=sb, bias=None, out_dtype=torch.bfloat16)
+        for _ in range(3):
+            lib()
+        lus = time_hot(torch, lib, 10)
+        res["library_gemm_torch_scaled_mm_us"] = round(lus, 1)
+        res["library_gemm_tflops"] = round(flops / lus / 1e6, 1)
+    except Exception as e:                      # the library path is a reference only
+        res["library_gemm_error"] = str(e)[:200]
     return res
 
 
@@ -543,12 +584,15 @@ def profile_run(torch, W, Q, which):
         step = forms_setup(torch, W, Q, which)
     elif which == "proj":
         step = proj_setup(torch, W, Q)[2]
-    elif which == "proj_fp8":
-        d = W.make_qkv_projection(W.WAN22_QKV_PROJ_FP8, device="cuda")
+    elif which in ("proj_fp8", "proj_mxfp8"):
+        mx = which == "proj_mxfp8"
+        d = W.make_qkv_projection(W.WAN22_QKV_PROJ_MXFP8 if mx else W.WAN22_QKV_PROJ_FP8, device="cuda")
         out = torch.empty(d["cfg"].seq, d["out_features"], dtype=torch.bfloat16, device="cuda")
         sums = torch.empty(2, d["cfg"].seq, 40, dtype=torch.float32, device="cuda")
+        sc = (dict(a_block_scale=d["a_bs"], w_block_scale=d["w_bs"]) if mx else
+              dict(a_scale=d["a_scale"], w_scale=d["w_scale"]))
         step = Q.prepare_qkv_projection(d["a8"], d["w8"], d["bias"], out=out, q_cols=5120, k_cols=5120,
-                                        sumsq=sums, a_scale=d["a_scale"], w_scale=d["w_scale"])
+                                        sumsq=sums, **sc)
     else:
         cfg = {"kv_v1_prefill": W.MLA_V1_PREFILL, "kv_v1_decode": W.MLA_V1_DECODE_QUANT,
                "kv_v2": W.MLA_V2_SPLIT}[which]
@@ -567,8 +611,9 @@ PROFILE_WORKLOADS = {
     "per_head": ("qk_per_head", "wan22_per_head", ", 1>(qknr::QkParams)"),
     "split_sumsq": ("qk_split", "wan22_split_sumsq", ", 2>(qknr::QkParams)"),
     "split_apply": ("qk_split", "wan22_split_apply", ", 3>(qknr::QkParams)"),
-    "proj": ("qkv_proj", "wan22_qkv_projection", "qkv_proj_kernel<false>"),
-    "proj_fp8": ("qkv_proj", "wan22_qkv_projection_fp8", "qkv_proj_kernel<true>"),
+    "proj": ("qkv_proj", "wan22_qkv_projection", "qkv_proj_kernel<false, false>"),
+    "proj_fp8": ("qkv_proj", "wan22_qkv_projection_fp8", "qkv_proj_kernel<true, false>"),
+    "proj_mxfp8": ("qkv_proj", "wan22_qkv_projection_mxfp8", "qkv_proj_kernel<true, true>"),
     "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v1_decode": ("kv_rmsnorm_rope_cache", "mla_v1_decode_quant", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v2": ("kv_rmsnorm_rope_cache", "mla_v2_split", "kv_rmsnorm_rope_cache_kernel"),
@@ -622,7 +667,9 @@ def summarize(prof_dir):
             c = W.WAN22_QKV_PROJ      # compulsory bytes: A, W (and scales), bias read once; out, sums written once
             eb = 1 if wname.endswith("fp8") else 2
             alg = eb * (c.seq * c.hidden + 15360 * c.hidden) + 2 * (15360 + c.seq * 15360) + 4 * 2 * 40 * c.seq
-            if eb == 1:
+            if wname.endswith("mxfp8"):
+                alg += (c.seq + 15360) * c.hidden // 32      # the E8M0 block scales
+            elif eb == 1:
                 alg += 4 * (c.seq + 15360)
         elif wname == "wan22_per_head":
             alg = W.algorithmic_bytes_per_head(W.WAN22_SELF_ATTN)
@@ -659,7 +706,8 @@ def summarize(prof_dir):
             "python -u bench.py --profile <w>\n"
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write_<w> -o p -- "
             "python -u bench.py --profile <w>\n"
-            "  for <w> in across per_head split_sumsq split_apply proj proj_fp8 kv_v1_prefill kv_v1_decode kv_v2 copy;\n"
+            "  for <w> in across per_head split_sumsq split_apply proj proj_fp8 proj_mxfp8 kv_v1_prefill kv_v1_decode "
+            "kv_v2 copy;\n"
             "  then "
             "python bench.py --summarize <dir>\n")
     calib = (f"calibration (copy of 1 GiB, __amd_rocclr_copyBuffer): FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE "

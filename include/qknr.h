@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define QKNR_ABI_VERSION 2
+#define QKNR_ABI_VERSION 3
 
 /* status codes */
 #define QKNR_OK 0
@@ -231,16 +231,24 @@ typedef struct qknr_permute_args {
 
 int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream_t stream);
 
+/* qknr_proj_args.scale_mode */
+#define QKNR_PROJ_SCALE_ROW 0   /* a_scale / w_scale per row / per output channel (ROW_MX), or none */
+#define QKNR_PROJ_SCALE_MX32 1  /* OCP MX block scales: one E8M0 byte per 32 values of K, on a and w */
+
 /*
  * The QKV projection with step a of the across-heads norm fused into its
  * epilogue ("Kernel reference: qkv_cte": "Upstream behavior" for
- * O[S, I] = A[S, H] @ W + bias with I = (n_q + 2*n_kv)*d_head, Design
- * section 1 step a for sum(x^2) accumulated as the output tiles are copied
- * out). On matrix cores (bf16 or FP8 E4M3 operands, fp32 accumulation):
- *   out[m, n] = RNE_bf16( sum_k a[m, k] * w[n, k] * a_scale[m] * w_scale[n] + bias[n] )
- * (a NULL scale is 1: bf16 operands normally have none; FP8 operands with a
- * per-row activation scale and a per-output-channel weight scale are the
- * page's ROW_MX mode).
+ * O[S, I] = A[S, H] @ W + bias with I = (n_q + 2*n_kv)*d_head and the
+ * MXFP8 / ROW_MX quantisation modes, Design section 1 step a for sum(x^2)
+ * accumulated as the output tiles are copied out). On matrix cores (bf16 or
+ * FP8 E4M3 operands, fp32 accumulation):
+ *   out[m, n] = RNE_bf16( sum_k A[m, k] * W[n, k] * a_scale[m] * w_scale[n] + bias[n] )
+ * where, with scale_mode QKNR_PROJ_SCALE_MX32 (MXFP8, the OCP Microscaling
+ * format), A[m, k] = a[m, k] * 2^(a_block_scale[m, k/32] - 127) and
+ * W[n, k] = w[n, k] * 2^(w_block_scale[n, k/32] - 127); otherwise A = a and
+ * W = w. A NULL a_scale / w_scale is 1 (bf16 operands normally have none;
+ * FP8 operands with a per-row activation scale and a per-output-channel
+ * weight scale are the page's ROW_MX mode; MXFP8 usually has none).
  * for m < rows, n < out_features, and, when q_cols > 0, for every 128-column
  * tile of the Q columns [0, q_cols) and of the K columns [q_cols, q_cols +
  * k_cols), the per-row sum of the squares of the stored (rounded) values:
@@ -252,6 +260,7 @@ int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream
  * Arguments:
  *   dtype            QKNR_BF16 or QKNR_FP8_E4M3FN: the type of a and w; bias
  *       and out are bf16 in both cases.
+ *   scale_mode       QKNR_PROJ_SCALE_ROW, or QKNR_PROJ_SCALE_MX32 (FP8 only).
  *   rows, in_features, out_features   M = B*S >= 0, K = H (a multiple of 128
  *       bytes: 64 bf16 or 128 FP8 values), N = I (multiple of 128).
  *   a [rows, in_features] with row stride a_row_stride; w [out_features,
@@ -263,10 +272,17 @@ int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream
  *   q_cols, k_cols   multiples of 128 with q_cols + k_cols <= out_features;
  *       k_cols is 0 or q_cols. q_cols = 0: no sums (sumsq ignored).
  *   sumsq            fp32 [(k_cols ? 2 : 1) * P * rows], 4-byte aligned.
+ *   a_block_scale [rows, in_features/32], w_block_scale [out_features,
+ *       in_features/32]   E8M0 bytes (MX32 only; NULL otherwise), row strides
+ *       a_block_scale_stride / w_block_scale_stride in bytes, multiples of 4
+ *       and >= in_features/32; pointers 4-byte aligned. The code 255 (NaN)
+ *       is not supported (the result is unspecified).
+ * Errors: INVALID_ARGUMENT for a violated rule above (nothing launched),
+ * UNSUPPORTED for an operand type or scale mode that is not built.
  */
 typedef struct qknr_proj_args {
     int32_t dtype;
-    int32_t reserved;
+    int32_t scale_mode;
     int64_t rows;
     int64_t in_features;
     int64_t out_features;
@@ -282,6 +298,10 @@ typedef struct qknr_proj_args {
     float *sumsq;
     const float *a_scale;
     const float *w_scale;
+    const uint8_t *a_block_scale;
+    int64_t a_block_scale_stride;
+    const uint8_t *w_block_scale;
+    int64_t w_block_scale_stride;
 } qknr_proj_args;
 
 int32_t qknr_qkv_projection(const qknr_proj_args *args, hipStream_t stream);

@@ -42,6 +42,7 @@ OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR = 0, 1, 2, 3
 F32, BF16, F16, INT8, FP8_E4M3FN, FP8_E5M2 = 0, 1, 2, 3, 4, 5
 CACHE_NORM, CACHE_PA_BNSD, CACHE_PA_BLK_BNSD = 0, 1, 2
 QSHAPE_SCALAR, QSHAPE_CHANNEL, QSHAPE_HEAD_CHANNEL = 0, 1, 2
+PROJ_SCALE_ROW, PROJ_SCALE_MX32 = 0, 1
 
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16,
           torch.int8: INT8, torch.float8_e4m3fn: FP8_E4M3FN, torch.float8_e5m2: FP8_E5M2}
@@ -71,10 +72,11 @@ class QkArgs(ctypes.Structure):
 class ProjArgs(ctypes.Structure):
     """Mirror of ``qknr_proj_args``."""
     _fields_ = [
-        ("dtype", _i32), ("reserved", _i32), ("rows", _i64), ("in_features", _i64), ("out_features", _i64),
+        ("dtype", _i32), ("scale_mode", _i32), ("rows", _i64), ("in_features", _i64), ("out_features", _i64),
         ("a", _p), ("a_row_stride", _i64), ("w", _p), ("w_row_stride", _i64), ("bias", _p),
         ("out", _p), ("out_row_stride", _i64), ("q_cols", _i64), ("k_cols", _i64), ("sumsq", _p),
-        ("a_scale", _p), ("w_scale", _p),
+        ("a_scale", _p), ("w_scale", _p), ("a_block_scale", _p), ("a_block_scale_stride", _i64),
+        ("w_block_scale", _p), ("w_block_scale_stride", _i64),
     ]
 
 
@@ -392,10 +394,13 @@ def prepare_qk_apply_across_heads(q, k, q_gamma, k_gamma, cos, sin, sumsq, *, ep
                      (q, k, q_out, k_out, q_gamma, k_gamma, cos, sin, sumsq))
 
 
-def proj_args(a, w, bias, out, *, q_cols=0, k_cols=0, sumsq=None, a_scale=None, w_scale=None) -> ProjArgs:
+def proj_args(a, w, bias, out, *, q_cols=0, k_cols=0, sumsq=None, a_scale=None, w_scale=None,
+              a_block_scale=None, w_block_scale=None) -> ProjArgs:
     """Fill ``qknr_proj_args``: a [M, K], w [N, K] (a linear layer's weight),
     both bf16 or both float8_e4m3fn; bias [N] and out [M, N] bf16; a_scale [M]
-    and w_scale [N] float32 or None; last dimensions contiguous."""
+    and w_scale [N] float32 or None; last dimensions contiguous. MXFP8:
+    a_block_scale [M, K/32] and w_block_scale [N, K/32], E8M0 scale bytes
+    (uint8 or float8_e8m0fnu), both given (scale_mode MX32) or both None."""
     if a.dim() != 2 or w.dim() != 2 or out.dim() != 2:
         raise ValueError("a, w and out must be 2-D ([M, K], [N, K], [M, N])")
     M, K = a.shape
@@ -428,14 +433,27 @@ def proj_args(a, w, bias, out, *, q_cols=0, k_cols=0, sumsq=None, a_scale=None, 
             raise ValueError(f"sumsq must be a contiguous float32 tensor of {need} elements")
     r.sumsq = _ptr(sumsq) if q_cols else None
     r.a_scale, r.w_scale = _ptr(a_scale), _ptr(w_scale)
+    if (a_block_scale is None) != (w_block_scale is None):
+        raise ValueError("a_block_scale and w_block_scale come together")
+    if a_block_scale is not None:
+        for name, t, n in (("a_block_scale", a_block_scale, M), ("w_block_scale", w_block_scale, N)):
+            if t.dim() != 2 or t.shape[0] != n or t.shape[1] != K // 32 or t.element_size() != 1:
+                raise ValueError(f"{name} must be a [{n}, {K // 32}] tensor of E8M0 bytes")
+            _last_dim_contiguous(name, t)
+        r.scale_mode = PROJ_SCALE_MX32
+        r.a_block_scale, r.a_block_scale_stride = _ptr(a_block_scale), a_block_scale.stride(0)
+        r.w_block_scale, r.w_block_scale_stride = _ptr(w_block_scale), w_block_scale.stride(0)
+    else:
+        r.scale_mode = PROJ_SCALE_ROW
     r._keep = (bias,)
     return r
 
 
 def qkv_projection(a, w, bias=None, *, out=None, q_cols=0, k_cols=0, sumsq=None, a_scale=None, w_scale=None,
-                   stream=None):
+                   a_block_scale=None, w_block_scale=None, stream=None):
     """out = (a @ w.T) * a_scale[:, None] * w_scale[None, :] + bias on matrix
-    cores (bf16 operands, or float8_e4m3fn operands with ROW_MX scales; the
+    cores (bf16 operands, or float8_e4m3fn operands with ROW_MX scales and/or
+    MXFP8 block scales -- one E8M0 byte per 32 values of K on a and on w; the
     output is bf16), plus, for q_cols > 0, the
     per-row sums of squares of each 128-column tile of the Q columns
     [0, q_cols) and K columns [q_cols, q_cols + k_cols): fp32
@@ -446,17 +464,20 @@ def qkv_projection(a, w, bias=None, *, out=None, q_cols=0, k_cols=0, sumsq=None,
         out = torch.empty(M, N, dtype=torch.bfloat16, device=a.device)
     if q_cols and sumsq is None:
         sumsq = torch.empty(2 if k_cols else 1, M, q_cols // 128, dtype=torch.float32, device=a.device)
-    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq, a_scale=a_scale, w_scale=w_scale)
+    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq, a_scale=a_scale, w_scale=w_scale,
+                  a_block_scale=a_block_scale, w_block_scale=w_block_scale)
     with torch.cuda.device(a.device):
         _check(_lib.qknr_qkv_projection(ctypes.byref(r), _stream(a.device, stream)))
     return out, sumsq
 
 
 def prepare_qkv_projection(a, w, bias=None, *, out, q_cols=0, k_cols=0, sumsq=None, a_scale=None,
-                           w_scale=None, stream=None):
+                           w_scale=None, a_block_scale=None, w_block_scale=None, stream=None):
     """Prepared form of :func:`qkv_projection` (arguments marshalled once)."""
-    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq, a_scale=a_scale, w_scale=w_scale)
-    return _prepared(_lib.qknr_qkv_projection, r, (), a.device, stream, (a, w, bias, out, sumsq, a_scale, w_scale))
+    r = proj_args(a, w, bias, out, q_cols=q_cols, k_cols=k_cols, sumsq=sumsq, a_scale=a_scale, w_scale=w_scale,
+                  a_block_scale=a_block_scale, w_block_scale=w_block_scale)
+    return _prepared(_lib.qknr_qkv_projection, r, (), a.device, stream,
+                     (a, w, bias, out, sumsq, a_scale, w_scale, a_block_scale, w_block_scale))
 
 
 def permute_args(src, dst, head_dim, *, dim=-1, first=0, n_heads=None, inverse=False) -> PermuteArgs:

@@ -418,6 +418,13 @@ int32_t qknr_qkv_projection(const qknr_proj_args *a, hipStream_t stream) {
         return fail(QKNR_UNSUPPORTED, "the projection is built for QKNR_BF16 and QKNR_FP8_E4M3FN operands");
     const bool fp8 = a->dtype == QKNR_FP8_E4M3FN;
     const int eb = fp8 ? 1 : 2;
+    if (a->scale_mode != QKNR_PROJ_SCALE_ROW && a->scale_mode != QKNR_PROJ_SCALE_MX32)
+        return fail(QKNR_UNSUPPORTED, "scale_mode %d is not built (QKNR_PROJ_SCALE_ROW, QKNR_PROJ_SCALE_MX32 are)",
+                    a->scale_mode);
+    const bool mx = a->scale_mode == QKNR_PROJ_SCALE_MX32;
+    if (mx && !fp8) return fail(QKNR_INVALID_ARGUMENT, "MX block scales need FP8 operands (QKNR_FP8_E4M3FN)");
+    if (!mx && (a->a_block_scale || a->w_block_scale))
+        return fail(QKNR_INVALID_ARGUMENT, "block scales are given only with scale_mode QKNR_PROJ_SCALE_MX32");
     if (a->rows < 0 || a->in_features < 1 || a->out_features < 1)
         return fail(QKNR_INVALID_ARGUMENT, "rows >= 0, in_features >= 1, out_features >= 1");
     if ((a->in_features * eb) % 128 || a->out_features % 128)
@@ -432,7 +439,15 @@ int32_t qknr_qkv_projection(const qknr_proj_args *a, hipStream_t stream) {
         return fail(QKNR_INVALID_ARGUMENT, "row strides must cover a row");
     if ((a->a_row_stride * eb) % 16 || (a->w_row_stride * eb) % 16 || a->out_row_stride % 8)
         return fail(QKNR_UNSUPPORTED, "row strides must be multiples of 16 bytes");
+    const int64_t blocks = a->in_features / 32;        // MX blocks per row (in_features is a multiple of 128)
+    if (mx && (a->a_block_scale_stride < blocks || a->w_block_scale_stride < blocks ||
+               a->a_block_scale_stride % 4 || a->w_block_scale_stride % 4))
+        return fail(QKNR_INVALID_ARGUMENT,
+                    "block-scale row strides must be >= in_features/32 bytes and multiples of 4");
     if (a->rows == 0) return ok();
+    if (mx && (!a->a_block_scale || !a->w_block_scale || !aligned(a->a_block_scale, 4) ||
+               !aligned(a->w_block_scale, 4)))
+        return fail(QKNR_INVALID_ARGUMENT, "MX mode needs a_block_scale and w_block_scale, 4-byte aligned");
     if (!a->a || !a->w || !a->out) return fail(QKNR_INVALID_ARGUMENT, "a, w and out are required");
     if (!aligned(a->a, 16) || !aligned(a->w, 16) || !aligned(a->out, 16) || !aligned(a->bias, 2) ||
         !aligned(a->a_scale, 4) || !aligned(a->w_scale, 4))
@@ -454,7 +469,9 @@ int32_t qknr_qkv_projection(const qknr_proj_args *a, hipStream_t stream) {
         span(a->w, a->out_features, a->w_row_stride, a->in_features, eb),
         a->bias ? span(a->bias, 1, 0, a->out_features, 2) : none,
         a->a_scale ? span(a->a_scale, 1, 0, a->rows, 4) : none,
-        a->w_scale ? span(a->w_scale, 1, 0, a->out_features, 4) : none};
+        a->w_scale ? span(a->w_scale, 1, 0, a->out_features, 4) : none,
+        mx ? span(a->a_block_scale, a->rows, a->a_block_scale_stride, blocks, 1) : none,
+        mx ? span(a->w_block_scale, a->out_features, a->w_block_scale_stride, blocks, 1) : none};
     for (const auto &r : ins)
         if (r.first < o.second && o.first < r.second) return fail(QKNR_INVALID_ARGUMENT, "out overlaps an input");
     qknr::ProjParams p{};
@@ -463,6 +480,10 @@ int32_t qknr_qkv_projection(const qknr_proj_args *a, hipStream_t stream) {
     p.m = a->rows; p.n = a->out_features; p.k = a->in_features;
     p.lda = a->a_row_stride; p.ldw = a->w_row_stride; p.ldo = a->out_row_stride;
     p.q_cols = a->q_cols; p.k_cols = a->k_cols; p.parts = a->q_cols / 128;
+    if (mx) {
+        p.a_bs = a->a_block_scale; p.w_bs = a->w_block_scale;
+        p.lda_bs = a->a_block_scale_stride; p.ldw_bs = a->w_block_scale_stride;
+    }
     hipError_t e = qknr::proj_launch(p, fp8, stream);
     if (e != hipSuccess) return fail(QKNR_DEVICE_ERROR, "launch failed: %s", hipGetErrorString(e));
     return ok();

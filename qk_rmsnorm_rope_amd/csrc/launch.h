@@ -96,7 +96,8 @@ struct PermuteParams {
 hipError_t permute_launch(const PermuteParams &p, int unit, hipStream_t stream);
 
 // QKV projection O[m, n] = sum_k A[m, k] W[n, k] (* a_scale[m] * w_scale[n])
-// + bias[n] (bf16 or FP8 E4M3 operands, fp32 accumulation, bf16 bias and
+// + bias[n] (bf16 or FP8 E4M3 operands, the FP8 ones optionally with MX block
+// scales along k, fp32 accumulation, bf16 bias and
 // output) with per-row partial sums of squares of the Q columns
 // [0, q_cols) and the K columns [q_cols, q_cols + k_cols) of each 128-column
 // tile: sumsq[(seg*m + row)*parts + part], parts = q_cols / 128.
@@ -111,6 +112,10 @@ struct ProjParams {
     int64_t m, n, k, lda, ldw, ldo;
     int64_t q_cols, k_cols, parts;
     uint32_t tiles_m, tiles_n; // set by the launcher
+    // MXFP8: E8M0 scale bytes, one per 32 values of k ([m, k/32] and [n, k/32],
+    // row strides in bytes, multiples of 4); nullptr: no block scales
+    const uint8_t *a_bs, *w_bs;
+    int64_t lda_bs, ldw_bs;
 };
 // n a multiple of 128, k of 128 bytes; leading dimensions multiples of 16 bytes.
 hipError_t proj_launch(ProjParams &p, bool fp8, hipStream_t stream);

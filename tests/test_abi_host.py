@@ -47,6 +47,7 @@ def test_header_constants_match_binding():
     assert consts["QKNR_CACHE_NORM"] == Q.CACHE_NORM and consts["QKNR_CACHE_PA_BNSD"] == Q.CACHE_PA_BNSD
     assert consts["QKNR_CACHE_PA_BLK_BNSD"] == Q.CACHE_PA_BLK_BNSD
     assert consts["QKNR_QSHAPE_HEAD_CHANNEL"] == Q.QSHAPE_HEAD_CHANNEL
+    assert consts["QKNR_PROJ_SCALE_ROW"] == Q.PROJ_SCALE_ROW and consts["QKNR_PROJ_SCALE_MX32"] == Q.PROJ_SCALE_MX32
 
 
 def test_struct_layouts_match_c(tmp_path):
@@ -184,6 +185,12 @@ def test_permute_empty_tensor_is_a_noop():
                                                        None)) == Q.OK
 
 
+# a legal MXFP8 call: FP8 operands, K = 256 (8 blocks of 32), block scales 4-byte aligned
+_MX = dict(dtype=Q.FP8_E4M3FN, scale_mode=Q.PROJ_SCALE_MX32, in_features=256, a_row_stride=256,
+           w_row_stride=256, a_block_scale=0xA00000, a_block_scale_stride=8, w_block_scale=0xB00000,
+           w_block_scale_stride=8)
+
+
 def _proj(**kw):
     a = Q.ProjArgs()
     a.dtype, a.rows, a.in_features, a.out_features = Q.BF16, 300, 128, 384
@@ -212,10 +219,28 @@ def _proj(**kw):
     (dict(out=0x100000 + 64), Q.INVALID_ARGUMENT),                                   # out overlaps a
     (dict(a=0x100008), Q.UNSUPPORTED),                                               # not 16-byte aligned
     (dict(rows=-1), Q.INVALID_ARGUMENT),
-])
+    (dict(scale_mode=7), Q.UNSUPPORTED),
+    (dict(scale_mode=Q.PROJ_SCALE_MX32), Q.INVALID_ARGUMENT),                       # MX needs FP8 operands
+    (dict(a_block_scale=0xA00000), Q.INVALID_ARGUMENT),                              # block scales without MX
+] + [(dict(_MX, **kw), code) for kw, code in [
+    (dict(a_block_scale=None), Q.INVALID_ARGUMENT),
+    (dict(w_block_scale=0xB00002), Q.INVALID_ARGUMENT),                              # not 4-byte aligned
+    (dict(a_block_scale_stride=4), Q.INVALID_ARGUMENT),                              # shorter than K/32 = 8
+    (dict(w_block_scale_stride=10), Q.INVALID_ARGUMENT),                             # not a multiple of 4
+    (dict(a_block_scale=0x400000 + 64), Q.INVALID_ARGUMENT),                         # overlaps out
+]])
 def test_projection_rejects_invalid_arguments(kw, code):
     assert int(Q._lib.qknr_qkv_projection(ctypes.byref(_proj(**kw)), None)) == code
     assert Q.last_error() != ""
+
+
+def test_projection_mx_arguments_pass_validation():
+    """A legal MXFP8 call gets past validation (then fails to launch on this
+    GPU-less host, or would launch)."""
+    rc = int(Q._lib.qknr_qkv_projection(ctypes.byref(_proj(**_MX)), None))
+    assert rc in (Q.OK, Q.DEVICE_ERROR), Q.last_error()
+    if rc == Q.DEVICE_ERROR:
+        assert "launch failed" in Q.last_error()
 
 
 def test_projection_zero_rows_is_a_noop():

@@ -3,15 +3,17 @@ across-heads norm in its epilogue) and of the projection -> apply path.
 
 Cases: a small ragged case (300 rows: two row-tiles, the second partial;
 3 column tiles: Q, K and V) with bias; no bias and no sums; FP8 E4M3 operands
-with ROW_MX scales (and without scales); the Wan2.2 width
+with ROW_MX scales (and without scales); MXFP8 operands (one E8M0 scale per
+32 values of hidden on both operands; alone and with ROW_MX scales as well,
+blocks whose scales span 2^-20..2^20, an all-zero block); the Wan2.2 width
 (hidden 5120 -> 15360 columns, 40 + 40 + 40 heads) at 1000 rows with sampled
 rows against the oracle, the per-tile sums against fp64 sums of the stored
 outputs, and the projection -> apply path against the oracle's across-heads
 operator on the stored Q|K; the full S = 75600 case on sampled rows; two runs
-bit-identical -- the last two with bf16 and with FP8 ROW_MX operands; and 16
+bit-identical -- the last two with bf16, FP8 ROW_MX and MXFP8 operands; 16
 seeded random shapes (1-1500 rows, hidden up to 1024 bf16 / 2048 FP8 values,
 1-4 Q heads with as many or fewer K heads, with or without bias, sums over
-Q and K, Q only, or none).
+Q and K, Q only, or none) and 8 more with MXFP8 operands.
 
 The projection's outputs are checked against the oracle's exact fp64 values
 at the bf16 bar; the sums against fp64 sums of the kernel's own stored bf16
@@ -36,8 +38,17 @@ def Q():
     return lib
 
 
-def _oracle_rows(d, rows, with_bias=True):
+def _codes(t):
+    return t.view(torch.uint8).cpu().numpy()
+
+
+def _oracle_rows(d, rows, with_bias=True, row_scales=False):
     bias = host(d["bias"]) if with_bias else None
+    if d["cfg"].operands == "mxfp8":
+        sc = dict(a_scale=d["a_scale"].cpu().numpy()[rows], w_scale=d["w_scale"].cpu().numpy()) if row_scales else {}
+        _, v = oracle.linear_mx(_codes(d["a8"])[rows], _codes(d["w8"]), d["a_bs"].cpu().numpy()[rows],
+                                d["w_bs"].cpu().numpy(), bias=bias, bias_dtype=oracle.BF16, **sc)
+        return v
     if d["cfg"].operands == "fp8":
         a8 = d["a8"][torch.as_tensor(rows, device=d["a8"].device)].view(torch.uint8).cpu().numpy()
         _, v = oracle.linear(a8, d["w8"].view(torch.uint8).cpu().numpy(), oracle.E4M3FN, bias=bias,
@@ -52,6 +63,10 @@ def _fp8_magnitude(d, rows, scaled=True):
     """sum_k |a_k w_k| of the FP8 operands (times the scales), per output."""
     a = np.abs(oracle.decode(oracle.E4M3FN, d["a8"].view(torch.uint8).cpu().numpy()[rows]))
     w = np.abs(oracle.decode(oracle.E4M3FN, d["w8"].view(torch.uint8).cpu().numpy()))
+    if d["cfg"].operands == "mxfp8":      # each value times its block's scale
+        a = a * np.repeat(2.0 ** (d["a_bs"].cpu().numpy()[rows].astype(np.float64) - 127), 32, axis=1)
+        w = w * np.repeat(2.0 ** (d["w_bs"].cpu().numpy().astype(np.float64) - 127), 32, axis=1)
+        scaled = scaled and "a_scale" in d
     mag = a @ w.T
     if scaled:
         mag *= d["a_scale"].cpu().double().numpy()[rows][:, None] * d["w_scale"].cpu().double().numpy()[None, :]
@@ -60,13 +75,15 @@ def _fp8_magnitude(d, rows, scaled=True):
 
 def _check_out(d, got, rows, what):
     ref = _oracle_rows(d, rows)
-    if d["cfg"].operands == "fp8":
+    if d["cfg"].operands in ("fp8", "mxfp8"):
         check_dot(got, ref, _fp8_magnitude(d, rows), d["cfg"].hidden, what)
     else:
         check_float(got, ref, what)
 
 
 def _project(Q, d, **kw):
+    if d["cfg"].operands == "mxfp8":
+        return Q.qkv_projection(d["a8"], d["w8"], d["bias"], a_block_scale=d["a_bs"], w_block_scale=d["w_bs"], **kw)
     if d["cfg"].operands == "fp8":
         return Q.qkv_projection(d["a8"], d["w8"], d["bias"], a_scale=d["a_scale"], w_scale=d["w_scale"], **kw)
     return Q.qkv_projection(d["a"], d["w"], d["bias"], **kw)
@@ -127,6 +144,29 @@ def test_fp8_small_ragged_with_scales(Q):
     check_dot(o2, v, _fp8_magnitude(d, np.arange(300), scaled=False), 256, "fp8-small/unscaled")
 
 
+def test_mxfp8_small_ragged_alone_and_with_row_scales(Q):
+    """MXFP8 operands (K = 384 values = 3 k steps, 12 blocks), 300 rows, bias,
+    sums; block scales pushed to span 2^-20..2^20 and one all-zero block;
+    then the same codes with ROW_MX scales on top of the block scales."""
+    d = W.make_qkv_projection(W.WAN22_QKV_PROJ_MXFP8, device="cuda", seq=300, hidden=384, n_q_heads=1,
+                              n_k_heads=1, seed=12)
+    g = torch.Generator(device="cuda").manual_seed(12)
+    d["a_bs"] = (d["a_bs"].int() + torch.randint(-10, 11, d["a_bs"].shape, generator=g, device="cuda")).to(torch.uint8)
+    d["w_bs"] = (d["w_bs"].int() + torch.randint(-10, 11, d["w_bs"].shape, generator=g, device="cuda")).to(torch.uint8)
+    d["a8"].view(torch.uint8)[7, 64:96] = 0                      # an all-zero block
+    out, s = _project(Q, d, q_cols=128, k_cols=128)
+    torch.cuda.synchronize()
+    rows = np.arange(300)
+    _check_out(d, out, rows, "mx-small/out")
+    _check_sums(out, s, 128, 128, "mx-small")
+    d["a_scale"] = torch.rand(300, generator=g, device="cuda") + 0.5
+    d["w_scale"] = torch.rand(384, generator=g, device="cuda") + 0.5
+    o2, _ = Q.qkv_projection(d["a8"], d["w8"], d["bias"], a_block_scale=d["a_bs"], w_block_scale=d["w_bs"],
+                             a_scale=d["a_scale"], w_scale=d["w_scale"])
+    torch.cuda.synchronize()
+    check_dot(o2, _oracle_rows(d, rows, row_scales=True), _fp8_magnitude(d, rows), 384, "mx-small/row-scaled")
+
+
 def test_strided_operands_and_output(Q):
     """Row strides larger than the rows: a slice of a wider activation buffer
     and an output written into a wider buffer."""
@@ -142,8 +182,11 @@ def test_strided_operands_and_output(Q):
     assert bool((big[:, :64] == 7.0).all()) and bool((big[:, 448:] == 7.0).all())
 
 
-def _wan(seq, fp8=False):
-    return W.make_qkv_projection(W.WAN22_QKV_PROJ_FP8 if fp8 else W.WAN22_QKV_PROJ, device="cuda", seq=seq)
+_WAN_CFG = {"bf16": W.WAN22_QKV_PROJ, "fp8_row_mx": W.WAN22_QKV_PROJ_FP8, "mxfp8": W.WAN22_QKV_PROJ_MXFP8}
+
+
+def _wan(seq, mode="bf16"):
+    return W.make_qkv_projection(_WAN_CFG[mode], device="cuda", seq=seq)
 
 
 def _apply(Q, d, out, s):
@@ -157,10 +200,10 @@ def _apply(Q, d, out, s):
     return qi, ki, q, k
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8_row_mx"])
-def test_wan_width_projection_sums_and_apply(Q, fp8):
+@pytest.mark.parametrize("mode", sorted(_WAN_CFG))
+def test_wan_width_projection_sums_and_apply(Q, mode):
     S = 1000
-    d = _wan(S, fp8)
+    d = _wan(S, mode)
     out, s = _project(Q, d, q_cols=5120, k_cols=5120)
     torch.cuda.synchronize()
     assert tuple(s.shape) == (2, S, 40)
@@ -178,16 +221,16 @@ def test_wan_width_projection_sums_and_apply(Q, fp8):
     # V columns are the projection's, untouched by the apply pass
     ref = _oracle_rows(d, rows)[:, 10240:]
     got = out[torch.as_tensor(rows, device="cuda"), 10240:]
-    if fp8:
+    if mode != "bf16":
         check_dot(got, ref, _fp8_magnitude(d, rows)[:, 10240:], 5120, "wan1000/v")
     else:
         check_float(got, ref, "wan1000/v")
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8_row_mx"])
-def test_wan_full_size_sampled_and_deterministic(Q, fp8):
+@pytest.mark.parametrize("mode", sorted(_WAN_CFG))
+def test_wan_full_size_sampled_and_deterministic(Q, mode):
     S = 75600
-    d = _wan(S, fp8)
+    d = _wan(S, mode)
     out, s = _project(Q, d, q_cols=5120, k_cols=5120)
     out2 = torch.empty_like(out)
     s2 = torch.empty_like(s)
@@ -243,3 +286,31 @@ def test_random_projection_shapes(Q, i):
         _check_sums(out, s, q_cols, k_cols, f"random-{i}")
     else:
         assert s is None
+
+
+def _draw_mx(i):
+    """Seeded random MXFP8 shapes: rows 1-1500, hidden 128-2048 FP8 values,
+    1-4 Q heads and as many or fewer K heads, bias or not, sums or not."""
+    rng = np.random.default_rng(9300 + i)
+    nq = int(rng.integers(1, 5))
+    nk = int(rng.choice([nq, max(1, nq - 1), 1]))
+    return dict(seq=int(rng.integers(1, 1501)), hidden=128 * int(rng.integers(1, 17)), n_q=nq, n_k=nk,
+                bias=bool(rng.random() < 0.7), sums=nk == nq and bool(rng.random() < 0.7), seed=9300 + i)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_mxfp8_shapes(Q, i):
+    c = _draw_mx(i)
+    print(f"mx case {i}: {c}", flush=True)
+    d = W.make_qkv_projection(W.WAN22_QKV_PROJ_MXFP8, device="cuda", seq=c["seq"], hidden=c["hidden"],
+                              n_q_heads=c["n_q"], n_k_heads=c["n_k"], seed=c["seed"])
+    if not c["bias"]:
+        d["bias"] = None
+    q_cols, k_cols = (128 * c["n_q"], 128 * c["n_k"]) if c["sums"] else (0, 0)
+    out, s = _project(Q, d, q_cols=q_cols, k_cols=k_cols)
+    torch.cuda.synchronize()
+    rows = np.arange(c["seq"])
+    check_dot(out, _oracle_rows(d, rows, with_bias=c["bias"]), _fp8_magnitude(d, rows), c["hidden"],
+              f"mx-random-{i}/out")
+    if q_cols:
+        _check_sums(out, s, q_cols, k_cols, f"mx-random-{i}")

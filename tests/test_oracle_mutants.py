@@ -52,8 +52,18 @@ MUTANTS = {
                           "            double v = load(dtype, x, t * n * d + c);\n            ss += fabs(v);"),
     "linear_weight_transposed": ("acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, i * H + h);",
                                  "acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, (h * I + i) % (I * H));"),
-    "linear_bias_dropped": ("            if (bias) acc += load(bias_dtype, bias, i);\n", ""),
-    "linear_weight_scale_dropped": ("            if (w_scale) acc *= w_scale[i];\n", ""),
+    "linear_bias_dropped": ("acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, i * H + h);\n"
+                            "            if (a_scale) acc *= a_scale[s];\n"
+                            "            if (w_scale) acc *= w_scale[i];\n"
+                            "            if (bias) acc += load(bias_dtype, bias, i);\n",
+                            "acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, i * H + h);\n"
+                            "            if (a_scale) acc *= a_scale[s];\n"
+                            "            if (w_scale) acc *= w_scale[i];\n"),
+    "linear_weight_scale_dropped": ("acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, i * H + h);\n"
+                                    "            if (a_scale) acc *= a_scale[s];\n"
+                                    "            if (w_scale) acc *= w_scale[i];\n",
+                                    "acc += load(a_dtype, A, s * H + h) * load(w_dtype, W, i * H + h);\n"
+                                    "            if (a_scale) acc *= a_scale[s];\n"),
     "mx_weight_block_scale_ignored": ("* dec_e8m0(w_bs[i * w_bs_stride + h / 32]);", "* 1.0;"),
     "mx_e8m0_bias_128": ("return e == 255 ? NAN : ldexp(1.0, (int)e - 127);",
                          "return e == 255 ? NAN : ldexp(1.0, (int)e - 128);"),

@@ -172,7 +172,8 @@ class QkvProjectionConfig:
     dtype: torch.dtype
     eps: float
     seed: int
-    operands: str = "bf16"   # "bf16", or "fp8": E4M3 codes with per-row / per-channel scales (ROW_MX)
+    operands: str = "bf16"   # "bf16"; "fp8": E4M3 codes with per-row / per-channel scales (ROW_MX);
+    #                           "mxfp8": E4M3 codes with one E8M0 scale per 32 values of hidden (OCP MX)
 
 
 # Wan2.2-A14B self-attention: hidden 5120, 40 heads of 128 for Q, K and V.
@@ -181,6 +182,8 @@ WAN22_QKV_PROJ = QkvProjectionConfig(
     head_dim=128, dtype=torch.bfloat16, eps=1e-6, seed=1006)
 WAN22_QKV_PROJ_FP8 = dataclasses.replace(WAN22_QKV_PROJ, name="wan22_qkv_projection_fp8", seed=1007,
                                          operands="fp8")
+WAN22_QKV_PROJ_MXFP8 = dataclasses.replace(WAN22_QKV_PROJ, name="wan22_qkv_projection_mxfp8", seed=1008,
+                                           operands="mxfp8")
 
 
 def quantize_rows_e4m3(x: torch.Tensor):
@@ -191,6 +194,23 @@ def quantize_rows_e4m3(x: torch.Tensor):
     scale = amax / 448.0
     codes = (x.float() / scale[:, None]).to(torch.float8_e4m3fn)
     return codes, scale.contiguous()
+
+
+def quantize_mx_e4m3(x: torch.Tensor):
+    """MXFP8 conversion of the operands along their last axis (what the
+    producer of an MX operand hands over, following the OCP Microscaling
+    format's conversion): per block of 32 values, the shared scale is the
+    power of two X = 2^(floor(log2(max|block|)) - 8) (8 = the exponent of
+    E4M3's largest normal, 448), stored as the E8M0 byte log2(X) + 127; the
+    elements are RNE(x / X) in E4M3, clamped to +-448 first (x / X can reach
+    just under 512). An all-zero block gets the scale 2^-127. Returns (codes
+    as float8_e4m3fn, E8M0 scale bytes as uint8 [..., K/32])."""
+    xb = x.float().unflatten(-1, (-1, 32))
+    amax = xb.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-38))) - 8.0, torch.full_like(amax, -127.0))
+    e = e.clamp(-127.0, 127.0)
+    codes = (xb / torch.exp2(e)[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).flatten(-2)
+    return codes.contiguous(), (e + 127.0).to(torch.uint8).contiguous()
 
 
 def make_qkv_projection(cfg: QkvProjectionConfig, device="cpu", **override):
@@ -220,6 +240,10 @@ def make_qkv_projection(cfg: QkvProjectionConfig, device="cpu", **override):
         # FP8 operands from the same draws, quantised per activation row and per output channel
         d["a8"], d["a_scale"] = quantize_rows_e4m3(a)
         d["w8"], d["w_scale"] = quantize_rows_e4m3(w)
+    elif cfg.operands == "mxfp8":
+        # MXFP8 operands from the same draws: one E8M0 scale per 32 values along hidden
+        d["a8"], d["a_bs"] = quantize_mx_e4m3(a)
+        d["w8"], d["w_bs"] = quantize_mx_e4m3(w)
     return d
 
 
