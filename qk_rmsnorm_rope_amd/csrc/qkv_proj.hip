@@ -13,8 +13,11 @@
 // to a [segment][part][row] array, and the apply kernel adds the parts.
 //
 // MI355X design:
-//   * 256 x 256 output tile per workgroup of 8 waves (2 x 4), each wave
-//     128 x 64 = 4 x 2 tiles of 32 x 32 MFMAs with fp32 accumulators:
+//   * 256 x 384 (bf16) or 256 x 256 (FP8) output tile per workgroup of 8 waves
+//     (2 x 4), each wave 128 x 96 = 4 x 3 or 128 x 64 = 4 x 2 tiles of 32 x 32
+//     MFMAs with fp32 accumulators (the wider tile moves a fifth fewer LDS and
+//     copy bytes per flop; its 192 accumulators fill the registers two waves
+//     per SIMD leave, so only bf16's narrower fragments fit beside them):
 //     v_mfma_f32_32x32x16_bf16, or for FP8 v_mfma_scale_f32_32x32x64_f8f6f4,
 //     whose per-lane scale operands carry the MX block scales (a substep's
 //     64 k values are two MX blocks; lane l passes the scale of row l % 32's
@@ -32,7 +35,8 @@
 //   * tiles move global -> LDS with global_load_lds_dwordx4 (no registers):
 //     each wave instruction fills 8 rows of 128 bytes, and a 16-byte chunk c
 //     of row r sits in slot c ^ ((r >> 1) & 7), so the fragment reads of 16
-//     consecutive rows hit 16 disjoint bank groups; two k-step buffers (128 KB)
+//     consecutive rows hit 16 disjoint bank groups; two k-step buffers (128 KB,
+//     160 KB for the 384-wide tile)
 //     let the next step's loads run under the current step's MFMAs, with one
 //     barrier per k step;
 //   * workgroups go round-robin over the 8 XCDs; each XCD takes a contiguous
@@ -41,10 +45,11 @@
 //     column-tiles and read each k step of 12 tiles through its L2 instead
 //     of 32 (measured: L2 misses 6.5x the compulsory bytes, against 16x when
 //     the XCDs share one row-tile each); the weight (157 MB) fits the MALL;
-//   * epilogue: bias, RNE to bf16, the tile staged through LDS and written
-//     with 16-byte stores, the sums of squares taken from the rounded values
-//     (the values the apply pass reads back) with 16-lane DPP reductions, one
-//     per 128-column half of the tile.
+//   * epilogue: scales, bias, RNE to bf16 into packed registers (the
+//     accumulators die there), the tile staged through LDS (in two row halves
+//     for the 384-wide tile) and written with 16-byte stores, the sums of
+//     squares taken from the rounded values (the values the apply pass reads
+//     back) with 16-lane DPP reductions, one per 128-column part of a row.
 #include "device_common.h"
 #include "launch.h"
 
@@ -56,28 +61,42 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256;
+constexpr int BM = 256;
 constexpr int ROW_BYTES = 128;                      // one k step of one tile row, in bytes
 constexpr int WAVES_M = 2, WAVES_N = 4;             // wave grid of a workgroup (two per SIMD)
 constexpr int THREADS = 64 * WAVES_M * WAVES_N;
 constexpr int NWAVES = WAVES_M * WAVES_N;
-constexpr int MT = BM / WAVES_M / 32, NT = BN / WAVES_N / 32;   // 32x32 MFMA tiles per wave
-constexpr int LOADS = (BM / 8) / NWAVES;            // LDS-DMA instructions per wave per operand and k step
-constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;  // one k step of A and W tiles (64 KB)
-constexpr int LDC_S = BN + 8;                       // LDS row stride of the staged output tile (elements)
+constexpr int MT = BM / WAVES_M / 32;               // 32x32 MFMA tiles per wave along M
+constexpr int LOADS = (BM / 8) / NWAVES;            // LDS-DMA instructions per wave and k step for A
 constexpr int GROUP_M = 8;
-constexpr int LDS_BYTES_AB = 2 * STAGE_BYTES;       // two k-step buffers: 128 KB
-constexpr int LDS_BYTES_C = BM * LDC_S * 2 + BM * 4;   // 132 KB output tile + the row scales
+// The block tile is BM x BN, BN = 256 (wave tiles 128 x 64) or 384 (128 x 96: a
+// fifth fewer LDS and copy bytes per flop; the accumulators then fill the
+// registers two waves per SIMD leave, so only bf16 fragments fit beside them).
+template <int BN>
+struct Tile {
+    static constexpr int NT = BN / WAVES_N / 32;            // 32x32 MFMA tiles per wave along N
+    static constexpr int LOADS_W = (BN / 8) / NWAVES;       // LDS-DMA instructions per wave and k step for W
+    static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;   // one k step of A and W: 64 or 80 KB
+    static constexpr int LDS_BYTES_AB = 2 * STAGE_BYTES;    // two k-step buffers: 128 or 160 KB
+    static constexpr int LDC_S = BN + 8;                    // LDS row stride of the staged output (elements)
+    static constexpr int PASSES = BN == 256 ? 1 : 2;        // output staged in row halves when it would not fit
+    static constexpr int ROWS_PER_PASS = BM / PASSES;
+    static constexpr int LDS_BYTES_C = ROWS_PER_PASS * LDC_S * 2 + BM * 4;   // staged rows + the row scales
+};
+constexpr int LDS_BYTES_AB = Tile<256>::LDS_BYTES_AB;     // the MX path's tile buffers (BN = 256)
+constexpr int STAGE_BYTES = Tile<256>::STAGE_BYTES;
+constexpr int LDS_BYTES_C = Tile<256>::LDS_BYTES_C;
 // MX block scales: groups of 4 k steps (16 scale bytes per tile row and
 // operand), two group buffers after the tile buffers
 constexpr int MX_GROUP = 4;                          // k steps per scale group
 constexpr int MX_OPERAND_BYTES = BM * MX_GROUP * 4;  // one group of one operand's 256 rows: 4 KB
 constexpr int MX_BYTES = 2 * 2 * MX_OPERAND_BYTES;   // two groups x (A, W): 16 KB
+template <int BN>
 constexpr int lds_bytes(bool mx) {
-    const int ab = LDS_BYTES_AB + (mx ? MX_BYTES : 0);
-    return ab > LDS_BYTES_C ? ab : LDS_BYTES_C;
+    const int ab = Tile<BN>::LDS_BYTES_AB + (mx ? MX_BYTES : 0);
+    return ab > Tile<BN>::LDS_BYTES_C ? ab : Tile<BN>::LDS_BYTES_C;
 }
-static_assert(BM == BN, "one scale-group layout for both operands");
+static_assert(lds_bytes<384>(false) <= 160 * 1024 && lds_bytes<256>(true) <= 160 * 1024, "LDS of one CU");
 
 // Word index of (tile row r, k step j of the group) in a group buffer: rows of
 // four words, rotated by r / 8, so that the 32 rows of one MFMA tile read at
@@ -93,7 +112,17 @@ __device__ __forceinline__ U4 ld_lds16(const void *p) { return *reinterpret_cast
 
 // LDS slot of logical 16-byte chunk c (0..7) of tile row r (rows of 128 bytes):
 // 16 consecutive rows of one chunk land in 16 distinct 4-bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+__host__ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Global source of one 16-byte piece of a tile copy: tile row `row` (rows at
+// or past `lim` read the last valid row: any valid data, never stored), row
+// pitch `ld_bytes`, the logical chunk that lands in LDS slot `slot`.
+__host__ __device__ __forceinline__ const uint8_t *tile_src(const void *base, int64_t r0, int64_t lim,
+                                                            int64_t ld_bytes, int row, int slot) {
+    int64_t r = r0 + row;
+    if (r >= lim) r = lim - 1;
+    return reinterpret_cast<const uint8_t *>(base) + r * ld_bytes + swz(row, slot) * 16;
+}
 
 // Sum of squares of the 8 bf16 values of a 16-byte chunk (fp32).
 __device__ __forceinline__ float sumsq8(const U4 &v) {
@@ -154,12 +183,16 @@ __device__ __forceinline__ f32x16_t mfma_mx(const Frag<true> &a, const Frag<true
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a.v, b.v, c, 0, 0, 0, sa, 0, sb);
 }
 
-template <bool FP8, bool MX>
+template <bool FP8, bool MX, int BN>
 __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
     static_assert(FP8 || !MX, "MX block scales come with FP8 operands");
+    static_assert(!MX || BN == 256, "the MX scale groups are laid out for 256-wide tiles");
+    using TL = Tile<BN>;
+    constexpr int NT = TL::NT, LOADS_W = TL::LOADS_W, STAGE_BYTES = TL::STAGE_BYTES, LDC_S = TL::LDC_S;
+    constexpr int LDS_BYTES_AB = TL::LDS_BYTES_AB;
     constexpr int EB = FP8 ? 1 : 2;                 // operand bytes per element
     constexpr int KSUB = FP8 ? 2 : 4;               // MFMA substeps per 128-byte k step
-    __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes(MX)];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[lds_bytes<BN>(MX)];
 
     // tile order: a contiguous range of logical tiles per XCD (workgroup i runs on
     // XCD i % 8), grouped by GROUP_M row-tiles
@@ -178,34 +211,25 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    // LDS-DMA sources: wave `wave`, instruction j fills tile rows 8*(LOADS*wave + j) .. +7
-    // of A, then the same rows of W; lane l -> row + l/8, slot l%8, holding logical
-    // chunk swz(row, l%8).
-    const uint8_t *a_src[LOADS], *w_src[LOADS];
-    {
-        const int slot = lane & 7;
-#pragma unroll
-        for (int j = 0; j < LOADS; j++) {
-            const int row = 8 * (LOADS * wave + j) + (lane >> 3);
-            const int c = swz(row, slot);
-            int64_t ra = m0 + row;
-            if (ra >= p.m) ra = p.m - 1;             // rows past M: any valid data, never stored
-            int64_t rw = n0 + row;
-            if (rw >= p.n) rw = p.n - 1;             // columns past N (a final half tile)
-            a_src[j] = reinterpret_cast<const uint8_t *>(p.a) + (ra * p.lda) * EB + c * 16;
-            w_src[j] = reinterpret_cast<const uint8_t *>(p.w) + (rw * p.ldw) * EB + c * 16;
-        }
-    }
+    // LDS-DMA: copy j of wave `wave` fills tile rows 8*(L*wave + j) .. +7 of an
+    // operand (L = LOADS for A, LOADS_W for W); lane l -> row + l/8, LDS slot l%8,
+    // holding logical chunk swz(row, l%8). Sources are computed at each copy
+    // from the operand base (fewer live registers than one pointer per copy).
+    const int slot = lane & 7;
     auto issue_loads = [&](int ks, int buf) {
         uint8_t *as = lds + buf * STAGE_BYTES;
         uint8_t *bs = as + BM * ROW_BYTES;
         const int64_t k0 = (int64_t)ks * ROW_BYTES;
 #pragma unroll
         for (int j = 0; j < LOADS; j++)
-            __builtin_amdgcn_global_load_lds(a_src[j] + k0, as + (LOADS * wave + j) * 8 * ROW_BYTES, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                tile_src(p.a, m0, p.m, p.lda * EB, 8 * (LOADS * wave + j) + (lane >> 3), slot) + k0,
+                as + (LOADS * wave + j) * 8 * ROW_BYTES, 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < LOADS; j++)
-            __builtin_amdgcn_global_load_lds(w_src[j] + k0, bs + (LOADS * wave + j) * 8 * ROW_BYTES, 16, 0, 0);
+        for (int j = 0; j < LOADS_W; j++)
+            __builtin_amdgcn_global_load_lds(
+                tile_src(p.w, n0, p.n, p.ldw * EB, 8 * (LOADS_W * wave + j) + (lane >> 3), slot) + k0,
+                bs + (LOADS_W * wave + j) * 8 * ROW_BYTES, 16, 0, 0);
     };
 
     f32x16_t acc[MT][NT];
@@ -306,9 +330,14 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
         __syncthreads();                          // ... everyone's, and no wave still reads `buf`
     }
 
-    // epilogue 1: scales, bias, round to bf16, stage the 256 x 256 tile in LDS
-    uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);           // [BM][LDC_S]
-    float *row_scale = reinterpret_cast<float *>(lds + BM * LDC_S * 2);
+    // epilogue: scales, bias, RNE to bf16, the tile staged in LDS (in two row
+    // halves when the whole tile would not fit: pass q stages the rows of the
+    // waves with wm == q), then 16-byte coalesced stores, 16 lanes per
+    // 128-column part of a row, and that part's sum of the squares of the
+    // stored values when it lies in Q or K
+    constexpr int PASSES = TL::PASSES, RPP = TL::ROWS_PER_PASS, PARTS = BN / 128;
+    uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);           // [RPP][LDC_S]
+    float *row_scale = reinterpret_cast<float *>(lds + RPP * LDC_S * 2);
     if (p.a_scale && t < BM) {
         int64_t r = m0 + t;
         if (r >= p.m) r = p.m - 1;
@@ -316,6 +345,11 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
     }
     __syncthreads();
     const uint16_t *bias = reinterpret_cast<const uint16_t *>(p.bias);
+    uint16_t *o_base = reinterpret_cast<uint16_t *>(p.o);
+    const int g16 = t >> 4, l16 = t & 15;
+    // finished values, two rows of one column per register (bf16 pairs): the
+    // accumulators are dead from here on
+    uint32_t pk[MT][NT][8];
 #pragma unroll
     for (int ni = 0; ni < NT; ni++) {
         const int col = wn * (NT * 32) + ni * 32 + fr;
@@ -326,60 +360,79 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
 #pragma unroll
         for (int mi = 0; mi < MT; mi++) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
+            for (int r = 0; r < 16; r += 2) {
                 const int row = wm * (MT * 32) + mi * 32 + fc * 4 + (r >> 2) * 8 + (r & 3);
-                float v = acc[mi][ni][r];
-                if (p.a_scale) v *= row_scale[row];
-                if (p.w_scale) v *= cs;
-                const uint32_t packed = pack_bf16(v + bv, 0.0f);
-                Cs[row * LDC_S + col] = (uint16_t)(packed & 0xFFFFu);
+                float v0 = acc[mi][ni][r], v1 = acc[mi][ni][r + 1];
+                if (p.a_scale) {
+                    v0 *= row_scale[row];
+                    v1 *= row_scale[row + 1];
+                }
+                if (p.w_scale) {
+                    v0 *= cs;
+                    v1 *= cs;
+                }
+                pk[mi][ni][r >> 1] = pack_bf16(v0 + bv, v1 + bv);
             }
         }
     }
-    __syncthreads();
-
-    // epilogue 2: 16-byte coalesced stores (32 lanes per 512-byte row) and the
-    // per-row sums of squares of each 128-column half that lies in Q or K
-    const int half = (lane >> 4) & 1;             // lanes 0-15: columns 0..127, 16-31: 128..255
-    const int64_t hc0 = n0 + half * 128;
-    int seg = -1;
-    int64_t part = 0;
-    if (hc0 < p.q_cols) {
-        seg = 0;
-        part = hc0 / 128;
-    } else if (hc0 >= p.q_cols && hc0 < p.q_cols + p.k_cols) {
-        seg = 1;
-        part = (hc0 - p.q_cols) / 128;
-    }
-    const bool col_ok = hc0 < p.n;
-    uint16_t *o_base = reinterpret_cast<uint16_t *>(p.o);
-    const int cr = t >> 5, cc = t & 31;
-    constexpr int ROWS_PER_PASS = THREADS / 32;
+#pragma unroll
+    for (int pass = 0; pass < PASSES; pass++) {
+        if (PASSES == 1 || wm == pass) {
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) {
+                const int col = wn * (NT * 32) + ni * 32 + fr;
+#pragma unroll
+                for (int mi = 0; mi < MT; mi++) {
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const int row = wm * (MT * 32) + mi * 32 + fc * 4 + (r >> 2) * 8 + (r & 3) - pass * RPP;
+                        Cs[row * LDC_S + col] = (uint16_t)(pk[mi][ni][r >> 1] & 0xFFFFu);
+                        Cs[(row + 1) * LDC_S + col] = (uint16_t)(pk[mi][ni][r >> 1] >> 16);
+                    }
+                }
+            }
+        }
+        __syncthreads();
 #pragma unroll 4
-    for (int j = 0; j < BM / ROWS_PER_PASS; j++) {
-        const int row = cr + ROWS_PER_PASS * j;
-        const U4 v = ld_lds16(Cs + row * LDC_S + cc * 8);
-        const bool ok = m0 + row < p.m;
-        if (ok && col_ok) st_global16(o_base + (m0 + row) * p.ldo + n0 + cc * 8, v);
-        const float ss = group_sum<16>(sumsq8(v));
-        if (seg >= 0 && ok && (cc & 15) == 0) p.sumsq[((int64_t)seg * p.m + m0 + row) * p.parts + part] = ss;
+        for (int rp = g16; rp < RPP * PARTS; rp += THREADS / 16) {
+            const int rs = rp / PARTS, part_t = rp % PARTS;   // staged row, 128-column part of the tile
+            const int row = pass * RPP + rs;
+            const int64_t c0 = n0 + part_t * 128;
+            const U4 v = ld_lds16(Cs + rs * LDC_S + part_t * 128 + l16 * 8);
+            const bool ok = m0 + row < p.m;
+            if (ok && c0 < p.n) st_global16(o_base + (m0 + row) * p.ldo + c0 + l16 * 8, v);
+            const float ss = group_sum<16>(sumsq8(v));
+            int seg = -1;
+            int64_t part = 0;
+            if (c0 < p.q_cols) {
+                seg = 0;
+                part = c0 / 128;
+            } else if (c0 < p.q_cols + p.k_cols) {
+                seg = 1;
+                part = (c0 - p.q_cols) / 128;
+            }
+            if (seg >= 0 && ok && l16 == 0) p.sumsq[((int64_t)seg * p.m + m0 + row) * p.parts + part] = ss;
+        }
+        if (pass + 1 < PASSES) __syncthreads();
     }
 }
 
 }  // namespace
 
 hipError_t proj_launch(ProjParams &p, bool fp8, hipStream_t stream) {
+    // bf16 operands: 256 x 384 tiles; FP8 (with or without MX scales): 256 x 256
+    const int bn = fp8 ? 256 : 384;
     p.tiles_m = (uint32_t)((p.m + BM - 1) / BM);
-    p.tiles_n = (uint32_t)((p.n + BN - 1) / BN);
+    p.tiles_n = (uint32_t)((p.n + bn - 1) / bn);
     const uint64_t tiles = (uint64_t)p.tiles_m * p.tiles_n;
     if (tiles == 0) return hipSuccess;
     const uint64_t grid = (tiles + 7) / 8 * 8;          // a whole number of tiles per XCD
     if (fp8 && p.a_bs)
-        hipLaunchKernelGGL((qkv_proj_kernel<true, true>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
+        hipLaunchKernelGGL((qkv_proj_kernel<true, true, 256>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
     else if (fp8)
-        hipLaunchKernelGGL((qkv_proj_kernel<true, false>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
+        hipLaunchKernelGGL((qkv_proj_kernel<true, false, 256>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL((qkv_proj_kernel<false, false>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
+        hipLaunchKernelGGL((qkv_proj_kernel<false, false, 384>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
