@@ -412,8 +412,8 @@ def cpu_baseline(torch, W, d, cfg):
 
     probe = 2048
     t_probe = run(probe)
-    # about 10 s of oracle CPU time (threads x wall), at most the whole workload
-    n = int(min(cfg.seq, max(probe, probe * 10.0 / max(t_probe * threads, 1e-6))))
+    # about 20 s of oracle CPU time (threads x wall), at most the whole workload
+    n = int(min(cfg.seq, max(probe, probe * 20.0 / max(t_probe * threads, 1e-6))))
     t = sorted(run(n) for _ in range(3))[1]
     n1 = 4096
     t1 = run1(n1)
@@ -611,9 +611,9 @@ PROFILE_WORKLOADS = {
     "per_head": ("qk_per_head", "wan22_per_head", ", 1>(qknr::QkParams)"),
     "split_sumsq": ("qk_split", "wan22_split_sumsq", ", 2>(qknr::QkParams)"),
     "split_apply": ("qk_split", "wan22_split_apply", ", 3>(qknr::QkParams)"),
-    "proj": ("qkv_proj", "wan22_qkv_projection", "qkv_proj_kernel<false, false>"),
-    "proj_fp8": ("qkv_proj", "wan22_qkv_projection_fp8", "qkv_proj_kernel<true, false>"),
-    "proj_mxfp8": ("qkv_proj", "wan22_qkv_projection_mxfp8", "qkv_proj_kernel<true, true>"),
+    "proj": ("qkv_proj", "wan22_qkv_projection", "qkv_proj_kernel<false, false, 384>"),
+    "proj_fp8": ("qkv_proj", "wan22_qkv_projection_fp8", "qkv_proj_kernel<true, false, 256>"),
+    "proj_mxfp8": ("qkv_proj", "wan22_qkv_projection_mxfp8", "qkv_proj_kernel<true, true, 256>"),
     "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v1_decode": ("kv_rmsnorm_rope_cache", "mla_v1_decode_quant", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v2": ("kv_rmsnorm_rope_cache", "mla_v2_split", "kv_rmsnorm_rope_cache_kernel"),
