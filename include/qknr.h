@@ -266,8 +266,9 @@ int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream
  *   a [rows, in_features] with row stride a_row_stride; w [out_features,
  *       in_features] (a linear layer's weight) with row stride w_row_stride;
  *       bias [out_features] or NULL; out [rows, out_features] with row stride
- *       out_row_stride. Strides are elements and multiples of 16 bytes;
- *       pointers 16-byte aligned. out must not overlap a, w or bias.
+ *       out_row_stride. Strides are elements and multiples of 16 bytes
+ *       (a_row_stride and w_row_stride at most 4 MiB in bytes); pointers
+ *       16-byte aligned. out must not overlap a, w or bias.
  *   a_scale [rows], w_scale [out_features]   fp32 or NULL.
  *   q_cols, k_cols   multiples of 128 with q_cols + k_cols <= out_features;
  *       k_cols is 0 or q_cols. q_cols = 0: no sums (sumsq ignored).
@@ -278,7 +279,8 @@ int32_t qknr_interleaved_to_rotate_half(const qknr_permute_args *args, hipStream
  *       and >= in_features/32; pointers 4-byte aligned. The code 255 (NaN)
  *       is not supported (the result is unspecified).
  * Errors: INVALID_ARGUMENT for a violated rule above (nothing launched),
- * UNSUPPORTED for an operand type or scale mode that is not built.
+ * UNSUPPORTED for an operand type or scale mode that is not built, or a row
+ * stride beyond the limits above.
  */
 typedef struct qknr_proj_args {
     int32_t dtype;

@@ -34,6 +34,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_launch_stubs(lib: str) -> None:
+    """Refuse a library that references a kernel's host launch stub without
+    defining it. The host pass of a kernel template can fail to instantiate
+    (for instance when a lambda in it calls a device-only function) without an
+    error; the shared library then links with the stub undefined and fails
+    only when it is loaded."""
+    r = subprocess.run(["nm", "-u", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        return                                   # no nm: nothing to check with
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(lib)
+        raise RuntimeError("kernel launch stubs left undefined (host pass of the kernel failed): "
+                           + ", ".join(missing))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libqknr.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
@@ -44,6 +60,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    _check_launch_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

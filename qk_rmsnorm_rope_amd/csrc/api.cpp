@@ -439,6 +439,8 @@ int32_t qknr_qkv_projection(const qknr_proj_args *a, hipStream_t stream) {
         return fail(QKNR_INVALID_ARGUMENT, "row strides must cover a row");
     if ((a->a_row_stride * eb) % 16 || (a->w_row_stride * eb) % 16 || a->out_row_stride % 8)
         return fail(QKNR_UNSUPPORTED, "row strides must be multiples of 16 bytes");
+    if (a->a_row_stride * eb > (4LL << 20) || a->w_row_stride * eb > (4LL << 20))
+        return fail(QKNR_UNSUPPORTED, "a and w row strides above 4 MiB (tile copies use 32-bit offsets)");
     const int64_t blocks = a->in_features / 32;        // MX blocks per row (in_features is a multiple of 128)
     if (mx && (a->a_block_scale_stride < blocks || a->w_block_scale_stride < blocks ||
                a->a_block_scale_stride % 4 || a->w_block_scale_stride % 4))

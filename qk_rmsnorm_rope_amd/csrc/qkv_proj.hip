@@ -32,7 +32,10 @@
 //     values), so both types share the LDS tiling below;
 //   * both operands are K-contiguous (W is [I, H], a linear layer's weight), so
 //     every MFMA operand is one 16-byte LDS read;
-//   * tiles move global -> LDS with global_load_lds_dwordx4 (no registers):
+//   * tiles move global -> LDS with buffer_load_dwordx4 ... lds (no
+//     registers; a buffer resource per tile, so each copy's address is a
+//     32-bit lane offset fixed for the tile plus the k step in a scalar
+//     register: 8 % faster than 64-bit per-lane addresses on the bf16 tile):
 //     each wave instruction fills 8 rows of 128 bytes, and a 16-byte chunk c
 //     of row r sits in slot c ^ ((r >> 1) & 7), so the fragment reads of 16
 //     consecutive rows hit 16 disjoint bank groups; two k-step buffers (128 KB,
@@ -114,14 +117,25 @@ __device__ __forceinline__ U4 ld_lds16(const void *p) { return *reinterpret_cast
 // 16 consecutive rows of one chunk land in 16 distinct 4-bank groups.
 __host__ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// Global source of one 16-byte piece of a tile copy: tile row `row` (rows at
-// or past `lim` read the last valid row: any valid data, never stored), row
-// pitch `ld_bytes`, the logical chunk that lands in LDS slot `slot`.
-__host__ __device__ __forceinline__ const uint8_t *tile_src(const void *base, int64_t r0, int64_t lim,
-                                                            int64_t ld_bytes, int row, int slot) {
-    int64_t r = r0 + row;
-    if (r >= lim) r = lim - 1;
-    return reinterpret_cast<const uint8_t *>(base) + r * ld_bytes + swz(row, slot) * 16;
+// Tile copies read through a buffer resource based at the tile's first row:
+// the lane's 32-bit offset (row * pitch + the place of its 16-byte chunk) and
+// the k step's byte offset in a scalar register; the LDS destination of a
+// wave's copy is 64 consecutive 16-byte pieces.
+struct TileRsrc {
+    __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ TileRsrc tile_rsrc(const void *base, int64_t bytes) {
+    return TileRsrc{__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000)};
+}
+__device__ __forceinline__ void copy16_to_lds(const TileRsrc &t, uint8_t *lds_dst, uint32_t lane_offset,
+                                              int k_offset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.r, (lds_u8 *)lds_dst, 16, lane_offset, k_offset, 0, 0);
+}
+// Lane offset of one 16-byte piece of a tile copy: tile row `row` (rows at or
+// past `rows` read the last valid row: any valid data, never stored), row
+// pitch `pitch` bytes, the logical chunk that lands in LDS slot `slot`.
+__device__ __forceinline__ uint32_t tile_offset(int row, int rows, int64_t pitch, int slot) {
+    return (uint32_t)((int64_t)min(row, rows - 1) * pitch + swz(row, slot) * 16);
 }
 
 // Sum of squares of the 8 bf16 values of a 16-byte chunk (fp32).
@@ -213,23 +227,29 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
 
     // LDS-DMA: copy j of wave `wave` fills tile rows 8*(L*wave + j) .. +7 of an
     // operand (L = LOADS for A, LOADS_W for W); lane l -> row + l/8, LDS slot l%8,
-    // holding logical chunk swz(row, l%8). Sources are computed at each copy
-    // from the operand base (fewer live registers than one pointer per copy).
+    // holding logical chunk swz(row, l%8). The offsets are set once per tile; a
+    // k step only moves the scalar offset.
     const int slot = lane & 7;
+    const int64_t a_pitch = p.lda * EB, w_pitch = p.ldw * EB;
+    const int a_rows = (int)min((int64_t)BM, p.m - m0), w_rows = (int)min((int64_t)BN, p.n - n0);
+    const TileRsrc ra = tile_rsrc(reinterpret_cast<const uint8_t *>(p.a) + m0 * a_pitch,
+                                  (int64_t)(a_rows - 1) * a_pitch + p.k * EB);
+    const TileRsrc rw = tile_rsrc(reinterpret_cast<const uint8_t *>(p.w) + n0 * w_pitch,
+                                  (int64_t)(w_rows - 1) * w_pitch + p.k * EB);
+    uint32_t a_off[LOADS], w_off[LOADS_W];
+#pragma unroll
+    for (int j = 0; j < LOADS; j++) a_off[j] = tile_offset(8 * (LOADS * wave + j) + (lane >> 3), a_rows, a_pitch, slot);
+#pragma unroll
+    for (int j = 0; j < LOADS_W; j++)
+        w_off[j] = tile_offset(8 * (LOADS_W * wave + j) + (lane >> 3), w_rows, w_pitch, slot);
     auto issue_loads = [&](int ks, int buf) {
         uint8_t *as = lds + buf * STAGE_BYTES;
         uint8_t *bs = as + BM * ROW_BYTES;
-        const int64_t k0 = (int64_t)ks * ROW_BYTES;
+        const int k0 = ks * ROW_BYTES;
 #pragma unroll
-        for (int j = 0; j < LOADS; j++)
-            __builtin_amdgcn_global_load_lds(
-                tile_src(p.a, m0, p.m, p.lda * EB, 8 * (LOADS * wave + j) + (lane >> 3), slot) + k0,
-                as + (LOADS * wave + j) * 8 * ROW_BYTES, 16, 0, 0);
+        for (int j = 0; j < LOADS; j++) copy16_to_lds(ra, as + (LOADS * wave + j) * 8 * ROW_BYTES, a_off[j], k0);
 #pragma unroll
-        for (int j = 0; j < LOADS_W; j++)
-            __builtin_amdgcn_global_load_lds(
-                tile_src(p.w, n0, p.n, p.ldw * EB, 8 * (LOADS_W * wave + j) + (lane >> 3), slot) + k0,
-                bs + (LOADS_W * wave + j) * 8 * ROW_BYTES, 16, 0, 0);
+        for (int j = 0; j < LOADS_W; j++) copy16_to_lds(rw, bs + (LOADS_W * wave + j) * 8 * ROW_BYTES, w_off[j], k0);
     };
 
     f32x16_t acc[MT][NT];

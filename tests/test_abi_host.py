@@ -216,6 +216,8 @@ def _proj(**kw):
     (dict(sumsq=None), Q.INVALID_ARGUMENT),
     (dict(sumsq=0x800002), Q.INVALID_ARGUMENT),
     (dict(a_row_stride=120), Q.INVALID_ARGUMENT),                                    # shorter than a row
+    (dict(a_row_stride=(4 << 20) // 2 + 8), Q.UNSUPPORTED),                          # pitch above 4 MiB
+    (dict(w_row_stride=(4 << 20) // 2 + 8), Q.UNSUPPORTED),
     (dict(out=0x100000 + 64), Q.INVALID_ARGUMENT),                                   # out overlaps a
     (dict(a=0x100008), Q.UNSUPPORTED),                                               # not 16-byte aligned
     (dict(rows=-1), Q.INVALID_ARGUMENT),
