@@ -43,11 +43,14 @@
 //     let the next step's loads run under the current step's MFMAs, with one
 //     barrier per k step;
 //   * workgroups go round-robin over the 8 XCDs; each XCD takes a contiguous
-//     range of tiles ordered in groups of 8 row-tiles, row-tile fastest, so
-//     the ~32 workgroups running together on one XCD cover 8 row-tiles x 4
-//     column-tiles and read each k step of 12 tiles through its L2 instead
-//     of 32 (measured: L2 misses 6.5x the compulsory bytes, against 16x when
-//     the XCDs share one row-tile each); the weight (157 MB) fits the MALL;
+//     range of tiles ordered in groups of 3 row-tiles, row-tile fastest, so
+//     the ~32 workgroups running together on one XCD cover 3 row-tiles x ~11
+//     column-tiles and share each k step of them through its L2. The weight
+//     (157 MB bf16) stays in the MALL while A streams from HBM, so narrow
+//     groups (each A row-tile re-read by few waves of column-tiles, the
+//     weight re-read from the MALL more often) are fastest: measured on
+//     Wan2.2, groups of 2 / 3 / 4 / 6 / 8 row-tiles take 9.85 / 9.77 / 9.80 /
+//     9.90 / 9.95 ms (bf16) and 5.04 / 5.03 / 5.10 / 5.31 / 5.48 ms (FP8);
 //   * epilogue: scales, bias, RNE to bf16 into packed registers (the
 //     accumulators die there), the tile staged through LDS (in two row halves
 //     for the 384-wide tile) and written with 16-byte stores, the sums of
@@ -71,7 +74,7 @@ constexpr int THREADS = 64 * WAVES_M * WAVES_N;
 constexpr int NWAVES = WAVES_M * WAVES_N;
 constexpr int MT = BM / WAVES_M / 32;               // 32x32 MFMA tiles per wave along M
 constexpr int LOADS = (BM / 8) / NWAVES;            // LDS-DMA instructions per wave and k step for A
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 3;
 // The block tile is BM x BN, BN = 256 (wave tiles 128 x 64) or 384 (128 x 96: a
 // fifth fewer LDS and copy bytes per flop; the accumulators then fill the
 // registers two waves per SIMD leave, so only bf16 fragments fit beside them).
