@@ -23,8 +23,8 @@ next to the unfused pipeline of a library GEMM (torch.addmm /
 torch._scaled_mm, hipBLASLt) and the single-pass epilogue kernel.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv] [--no-forms] [--no-proj]
-       python bench.py --profile {across,per_head,split_sumsq,split_apply,proj,proj_fp8,
-                                  kv_v1_prefill,kv_v1_decode,kv_v2,copy}
+       python bench.py --profile {across,per_head,split_sumsq,split_apply,proj,proj_fp8,proj_mxfp8,
+                                  proj_lib,proj_fp8_lib,kv_v1_prefill,kv_v1_decode,kv_v2,copy}
        (a short fixed run of one kernel, for rocprofv3 counter collection)
        python bench.py --ceiling
        (plain stream kernels with the operators' read/write mixes at 32 MB - 3.1 GB,
@@ -98,7 +98,7 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=50)
     ap.add_argument("--profile", default=None,
                     choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "proj_fp8", "proj_mxfp8",
-                             "kv_v1_prefill", "kv_v1_decode", "kv_v2", "copy"])
+                             "proj_lib", "proj_fp8_lib", "kv_v1_prefill", "kv_v1_decode", "kv_v2", "copy"])
     ap.add_argument("--summarize", default=None, metavar="DIR")
     ap.add_argument("--ceiling", action="store_true",
                     help="sweep plain stream kernels with the operators' read/write mixes (bench_stream.hip)")
@@ -584,6 +584,13 @@ def profile_run(torch, W, Q, which):
         step = forms_setup(torch, W, Q, which)
     elif which == "proj":
         step = proj_setup(torch, W, Q)[2]
+    elif which == "proj_lib":                  # the library GEMM of the same projection (hipBLASLt)
+        step = proj_setup(torch, W, Q)[5]
+    elif which == "proj_fp8_lib":
+        d = W.make_qkv_projection(W.WAN22_QKV_PROJ_FP8, device="cuda")
+        wt, sa, sb = d["w8"].t(), d["a_scale"][:, None].contiguous(), d["w_scale"][None, :].contiguous()
+        step = lambda: torch._scaled_mm(d["a8"], wt, scale_a=sa, scale_b=sb, bias=d["bias"],
+                                        out_dtype=torch.bfloat16)
     elif which in ("proj_fp8", "proj_mxfp8"):
         mx = which == "proj_mxfp8"
         d = W.make_qkv_projection(W.WAN22_QKV_PROJ_MXFP8 if mx else W.WAN22_QKV_PROJ_FP8, device="cuda")
