@@ -31,6 +31,18 @@ def test_library_exports_every_declared_function():
         assert hasattr(Q._lib, n)
 
 
+def test_every_kernel_launch_stub_is_defined():
+    """Each kernel the library launches has its host stub defined in the library
+    (a kernel template whose host pass failed would leave it undefined, and the
+    library would fail only when loaded on the GPU host)."""
+    out = subprocess.run(["nm", Q.LIB_PATH], capture_output=True, text=True).stdout
+    undefined = [ln for ln in out.splitlines() if "__device_stub__" in ln and " U " in ln]
+    assert not undefined, undefined
+    defined = [ln for ln in out.splitlines() if "__device_stub__" in ln]
+    for kernel in ("qkv_proj_kernel", "qk_kernel", "kv_rmsnorm_rope_cache_kernel", "permute_kernel"):
+        assert any(kernel in ln for ln in defined), kernel
+
+
 def test_version_matches_header():
     m = re.search(r"#define QKNR_ABI_VERSION (\d+)", open(HEADER).read())
     assert Q.version() == int(m.group(1))
