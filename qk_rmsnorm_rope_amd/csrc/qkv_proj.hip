@@ -134,6 +134,10 @@ __device__ __forceinline__ void copy16_to_lds(const TileRsrc &t, uint8_t *lds_ds
                                               int k_offset) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(t.r, (lds_u8 *)lds_dst, 16, lane_offset, k_offset, 0, 0);
 }
+__device__ __forceinline__ void copy4_to_lds(const TileRsrc &t, uint8_t *lds_dst, uint32_t lane_offset,
+                                             int k_offset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.r, (lds_u8 *)lds_dst, 4, lane_offset, k_offset, 0, 0);
+}
 // Lane offset of one 16-byte piece of a tile copy: tile row `row` (rows at or
 // past `rows` read the last valid row: any valid data, never stored), row
 // pitch `pitch` bytes, the logical chunk that lands in LDS slot `slot`.
@@ -276,19 +280,25 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
     // lands on word 64i + L, k step j = (L % 4 - r / 8) % 4. k steps past the
     // last (a partial last group) copy nothing. In substep kk lane half fc
     // passes the scale of block 2*kk + fc (see Frag<true>).
-    const uint8_t *mx_src[MX ? 4 : 1];
+    uint32_t mx_off[MX ? 4 : 1];
     int mx_j[MX ? 4 : 1];
+    TileRsrc mx_ra{}, mx_rw{};
     if constexpr (MX) {
+        // one buffer resource per operand's scale rows of the tile, like the
+        // tile copies; lane offset row * stride + the word's place, the group's
+        // 16 bytes as the scalar offset
+        const int64_t blocks = p.k / 32;                      // scale bytes per row in use
+        mx_ra = tile_rsrc(p.a_bs + m0 * p.lda_bs, (int64_t)(a_rows - 1) * p.lda_bs + blocks);
+        mx_rw = tile_rsrc(p.w_bs + n0 * p.ldw_bs, (int64_t)(w_rows - 1) * p.ldw_bs + blocks);
         const int lane_r = lane >> 2;
 #pragma unroll
         for (int c = 0; c < 4; c++) {              // copies 0,1: A rows of copy 2*wave + c; 2,3: W rows
             const bool is_w = c >= 2;
             const int r = 16 * (2 * wave + (c & 1)) + lane_r;
             mx_j[c] = ((lane & 3) - (r >> 3)) & (MX_GROUP - 1);
-            int64_t gr = (is_w ? n0 : m0) + r;
-            const int64_t lim = is_w ? p.n : p.m;
-            if (gr >= lim) gr = lim - 1;           // rows past M or N: any valid row, never stored
-            mx_src[c] = (is_w ? p.w_bs + gr * p.ldw_bs : p.a_bs + gr * p.lda_bs) + 4 * mx_j[c];
+            // rows past M or N read the last valid row: any valid data, never stored
+            const int rc = min(r, (is_w ? w_rows : a_rows) - 1);
+            mx_off[c] = (uint32_t)(rc * (is_w ? p.ldw_bs : p.lda_bs) + 4 * mx_j[c]);
         }
     }
     auto issue_scales = [&](int g) {
@@ -298,8 +308,8 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
             for (int c = 0; c < 4; c++) {
                 const int copy = 2 * wave + (c & 1);
                 if (g * MX_GROUP + mx_j[c] < ksteps)
-                    __builtin_amdgcn_global_load_lds(mx_src[c] + 4 * MX_GROUP * g,
-                                                     dst + (c >= 2 ? MX_OPERAND_BYTES : 0) + copy * 256, 4, 0, 0);
+                    copy4_to_lds(c >= 2 ? mx_rw : mx_ra, dst + (c >= 2 ? MX_OPERAND_BYTES : 0) + copy * 256,
+                                 mx_off[c], 4 * MX_GROUP * g);
             }
         }
     };
