@@ -36,6 +36,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-kv] 
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -98,7 +99,8 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=50)
     ap.add_argument("--profile", default=None,
                     choices=["across", "per_head", "split_sumsq", "split_apply", "proj", "proj_fp8", "proj_mxfp8",
-                             "proj_lib", "proj_fp8_lib", "kv_v1_prefill", "kv_v1_decode", "kv_v2", "copy"])
+                             "proj_lib", "proj_fp8_lib", "kv_v1_prefill", "kv_v1_prefill_pa_blk", "kv_v1_decode",
+                             "kv_v2", "copy"])
     ap.add_argument("--summarize", default=None, metavar="DIR")
     ap.add_argument("--ceiling", action="store_true",
                     help="sweep plain stream kernels with the operators' read/write mixes (bench_stream.hip)")
@@ -600,6 +602,8 @@ def profile_run(torch, W, Q, which):
               dict(a_scale=d["a_scale"], w_scale=d["w_scale"]))
         step = Q.prepare_qkv_projection(d["a8"], d["w8"], d["bias"], out=out, q_cols=5120, k_cols=5120,
                                         sumsq=sums, **sc)
+    elif which == "kv_v1_prefill_pa_blk":
+        d, step = kv_setup(torch, W, Q, W.MLA_V1_PREFILL, cache_mode=W.PA_BLK_BNSD)
     else:
         cfg = {"kv_v1_prefill": W.MLA_V1_PREFILL, "kv_v1_decode": W.MLA_V1_DECODE_QUANT,
                "kv_v2": W.MLA_V2_SPLIT}[which]
@@ -622,6 +626,7 @@ PROFILE_WORKLOADS = {
     "proj_fp8": ("qkv_proj", "wan22_qkv_projection_fp8", "qkv_proj_kernel<true, false, 256>"),
     "proj_mxfp8": ("qkv_proj", "wan22_qkv_projection_mxfp8", "qkv_proj_kernel<true, true, 256>"),
     "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill", "kv_rmsnorm_rope_cache_kernel"),
+    "kv_v1_prefill_pa_blk": ("kv_rmsnorm_rope_cache", "mla_v1_prefill_pa_blk_bnsd", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v1_decode": ("kv_rmsnorm_rope_cache", "mla_v1_decode_quant", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v2": ("kv_rmsnorm_rope_cache", "mla_v2_split", "kv_rmsnorm_rope_cache_kernel"),
 }
@@ -660,7 +665,17 @@ def summarize(prof_dir):
                 key = (r["Kernel_Name"], r["Grid_Size_X"])
                 durs.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     cfgs = {"wan22_self_attn": W.WAN22_SELF_ATTN, "mla_v1_prefill": W.MLA_V1_PREFILL,
+            "mla_v1_prefill_pa_blk_bnsd": dataclasses.replace(W.MLA_V1_PREFILL, cache_mode=W.PA_BLK_BNSD),
             "mla_v1_decode_quant": W.MLA_V1_DECODE_QUANT, "mla_v2_split": W.MLA_V2_SPLIT}
+    # trace lines are keyed by kernel and grid; workloads that share both share the line
+    shared = {}
+    for prof, (kernel, wname, needle) in PROFILE_WORKLOADS.items():
+        kn = [k for k in counters("fetch", prof) if needle in k]
+        if not kn:
+            continue
+        for fpath in glob.glob(os.path.join(prof_dir, f"pmc_fetch_{prof}", "*counter_collection.csv")):
+            for g in {r["Grid_Size"] for r in csv.DictReader(open(fpath)) if r["Kernel_Name"] == kn[0]}:
+                shared.setdefault((kn[0], g), []).append(wname)
     record = {"calibration": {"copy_bytes": 1 << 30, "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw,
                               "fetch_scale": f_scale, "write_scale": w_scale},
               "kernels": {}}
@@ -699,7 +714,9 @@ def summarize(prof_dir):
         lines.append(f"workload {wname}: kernel {kname}")
         for (k, g), v in sorted(durs.items()):
             if k == kname and g in grids:
-                lines.append(f"  trace grid {g}: {len(v)} dispatches, median {statistics.median(v):.2f} us, "
+                both = shared.get((k, g), [wname])
+                note = f" (the dispatches of {' and '.join(both)})" if len(both) > 1 else ""
+                lines.append(f"  trace grid {g}{note}: {len(v)} dispatches, median {statistics.median(v):.2f} us, "
                              f"mean {statistics.mean(v):.2f} us, min {min(v):.2f} us, max {max(v):.2f} us")
         lines.append(f"  FETCH_SIZE {f:.1f} KiB x {f_scale:.4f} + WRITE_SIZE {w:.1f} KiB x {w_scale:.4f} "
                      f"= {hbm / 1e6:.3f} MB per launch; algorithmic {alg / 1e6:.3f} MB "
@@ -713,8 +730,8 @@ def summarize(prof_dir):
             "python -u bench.py --profile <w>\n"
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write_<w> -o p -- "
             "python -u bench.py --profile <w>\n"
-            "  for <w> in across per_head split_sumsq split_apply proj proj_fp8 proj_mxfp8 kv_v1_prefill kv_v1_decode "
-            "kv_v2 copy;\n"
+            "  for <w> in across per_head split_sumsq split_apply proj proj_fp8 proj_mxfp8 kv_v1_prefill "
+            "kv_v1_prefill_pa_blk kv_v1_decode kv_v2 copy;\n"
             "  then "
             "python bench.py --summarize <dir>\n")
     calib = (f"calibration (copy of 1 GiB, __amd_rocclr_copyBuffer): FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE "

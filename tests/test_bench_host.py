@@ -17,7 +17,8 @@ import bench  # noqa: E402  (module import runs nothing: main() is behind __name
 WORKLOAD_KERNEL = {
     "wan22_self_attn": "qk_across_heads", "wan22_per_head": "qk_per_head", "wan22_split_sumsq": "qk_split",
     "wan22_split_apply": "qk_split", "wan22_qkv_projection": "qkv_proj", "wan22_qkv_projection_fp8": "qkv_proj", "wan22_qkv_projection_mxfp8": "qkv_proj",
-    "mla_v1_prefill": "kv_rmsnorm_rope_cache", "mla_v1_decode_quant": "kv_rmsnorm_rope_cache",
+    "mla_v1_prefill": "kv_rmsnorm_rope_cache", "mla_v1_prefill_pa_blk_bnsd": "kv_rmsnorm_rope_cache",
+    "mla_v1_decode_quant": "kv_rmsnorm_rope_cache",
     "mla_v2_split": "kv_rmsnorm_rope_cache",
 }
 
