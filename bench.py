@@ -623,7 +623,7 @@ PROFILE_WORKLOADS = {
     "split_sumsq": ("qk_split", "wan22_split_sumsq", ", 2>(qknr::QkParams)"),
     "split_apply": ("qk_split", "wan22_split_apply", ", 3>(qknr::QkParams)"),
     "proj": ("qkv_proj", "wan22_qkv_projection", "qkv_proj_kernel<false, false, 384>"),
-    "proj_fp8": ("qkv_proj", "wan22_qkv_projection_fp8", "qkv_proj_kernel<true, false, 256>"),
+    "proj_fp8": ("qkv_proj", "wan22_qkv_projection_fp8", "qkv_proj_kernel<true, false, 384>"),
     "proj_mxfp8": ("qkv_proj", "wan22_qkv_projection_mxfp8", "qkv_proj_kernel<true, true, 256>"),
     "kv_v1_prefill": ("kv_rmsnorm_rope_cache", "mla_v1_prefill", "kv_rmsnorm_rope_cache_kernel"),
     "kv_v1_prefill_pa_blk": ("kv_rmsnorm_rope_cache", "mla_v1_prefill_pa_blk_bnsd", "kv_rmsnorm_rope_cache_kernel"),

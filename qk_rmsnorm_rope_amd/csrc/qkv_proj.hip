@@ -13,11 +13,13 @@
 // to a [segment][part][row] array, and the apply kernel adds the parts.
 //
 // MI355X design:
-//   * 256 x 384 (bf16) or 256 x 256 (FP8) output tile per workgroup of 8 waves
-//     (2 x 4), each wave 128 x 96 = 4 x 3 or 128 x 64 = 4 x 2 tiles of 32 x 32
-//     MFMAs with fp32 accumulators (the wider tile moves a fifth fewer LDS and
-//     copy bytes per flop; its 192 accumulators fill the registers two waves
-//     per SIMD leave, so only bf16's narrower fragments fit beside them):
+//   * 256 x 384 (bf16, FP8 ROW_MX) or 256 x 256 (MXFP8) output tile per
+//     workgroup of 8 waves (2 x 4), each wave 128 x 96 = 4 x 3 or 128 x 64 =
+//     4 x 2 tiles of 32 x 32 MFMAs with fp32 accumulators (the wider tile moves
+//     a fifth fewer LDS and copy bytes per flop; its 192 accumulators fill most
+//     of the registers two waves per SIMD leave, so FP8's wider fragments are
+//     read one A fragment at a time; MXFP8's block scales need LDS the wider
+//     tile's two 80 KB k-step buffers leave no room for):
 //     v_mfma_f32_32x32x16_bf16, or for FP8 v_mfma_scale_f32_32x32x64_f8f6f4,
 //     whose per-lane scale operands carry the MX block scales (a substep's
 //     64 k values are two MX blocks; lane l passes the scale of row l % 32's
@@ -51,11 +53,18 @@
 //     weight re-read from the MALL more often) are fastest: measured on
 //     Wan2.2, groups of 2 / 3 / 4 / 6 / 8 row-tiles take 9.85 / 9.77 / 9.80 /
 //     9.90 / 9.95 ms (bf16) and 5.04 / 5.03 / 5.10 / 5.31 / 5.48 ms (FP8);
-//   * epilogue: scales, bias, RNE to bf16 into packed registers (the
-//     accumulators die there), the tile staged through LDS (in two row halves
-//     for the 384-wide tile) and written with 16-byte stores, the sums of
-//     squares taken from the rounded values (the values the apply pass reads
-//     back) with 16-lane DPP reductions, one per 128-column part of a row.
+//   * the MFMAs take W as the first operand (they compute the transposed
+//     tile), so each lane's accumulators hold four consecutive output columns
+//     of one row per 8-column group: the epilogue applies scales and bias
+//     from LDS copies (loaded before the k loop), rounds to bf16 and stages
+//     the tile through LDS with 8-byte writes (in two passes of half of every
+//     wave's rows for the 384-wide tile), then writes it with 16-byte stores
+//     and takes the sums of squares from the rounded values (the values the
+//     apply pass reads back) with 16-lane DPP reductions, one per 128-column
+//     part of a row. With the accumulators in the other layout (one column,
+//     four rows per lane) the staging took 2-byte writes and the packing
+//     per-element scale selects: measured on Wan2.2, this layout makes the
+//     projection 2-3 % faster with bit-identical outputs.
 #include "device_common.h"
 #include "launch.h"
 
@@ -87,7 +96,8 @@ struct Tile {
     static constexpr int LDC_S = BN + 8;                    // LDS row stride of the staged output (elements)
     static constexpr int PASSES = BN == 256 ? 1 : 2;        // output staged in row halves when it would not fit
     static constexpr int ROWS_PER_PASS = BM / PASSES;
-    static constexpr int LDS_BYTES_C = ROWS_PER_PASS * LDC_S * 2 + BM * 4;   // staged rows + the row scales
+    // staged rows + per-column bias and scale + per-row scale (fp32)
+    static constexpr int LDS_BYTES_C = ROWS_PER_PASS * LDC_S * 2 + (2 * BN + BM) * 4;
 };
 constexpr int LDS_BYTES_AB = Tile<256>::LDS_BYTES_AB;     // the MX path's tile buffers (BN = 256)
 constexpr int STAGE_BYTES = Tile<256>::STAGE_BYTES;
@@ -314,6 +324,15 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
         }
     };
 
+    // the epilogue's per-column bias and channel scale (thread t: column t) and
+    // per-row scale (thread t: row t), loaded now so that their latency is not
+    // paid after the k loop
+    float pre_b = 0.0f, pre_w = 1.0f, pre_a = 1.0f;
+    if (t < BN && n0 + t < p.n) {
+        if (p.bias) pre_b = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p.bias)[n0 + t] << 16);
+        if (p.w_scale) pre_w = p.w_scale[n0 + t];
+    }
+    if (t < BM && p.a_scale) pre_a = p.a_scale[min(m0 + t, p.m - 1)];
     issue_loads(0, 0);
     issue_scales(0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -333,6 +352,24 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
         }
         const uint8_t *as = lds + buf * STAGE_BYTES;
         const uint8_t *bs = as + BM * ROW_BYTES;
+      if constexpr (FP8 && !MX && BN == 384) {
+        // FP8 fragments are twice as wide: with the W fragments of a substep held,
+        // each A fragment is read just before its row of MFMAs, so that only one
+        // A fragment is live beside the 192 accumulators
+#pragma unroll
+        for (int kk = 0; kk < KSUB; kk++) {
+            Frag<FP8> bfr[NT];
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) bfr[ni].read(bs, wn * (NT * 32) + ni * 32 + fr, kk, fc);
+#pragma unroll
+            for (int mi = 0; mi < MT; mi++) {
+                Frag<FP8> a1;
+                a1.read(as, wm * (MT * 32) + mi * 32 + fr, kk, fc);
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++) acc[mi][ni] = mfma(bfr[ni], a1, acc[mi][ni]);
+            }
+        }
+      } else
 #pragma unroll
         for (int kk = 0; kk < KSUB; kk++) {
             Frag<FP8> af[MT], bfr[NT];
@@ -351,110 +388,131 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
                 for (int mi = 0; mi < MT; mi++)
 #pragma unroll
                     for (int ni = 0; ni < NT; ni++)
-                        acc[mi][ni] = mfma_mx(af[mi], bfr[ni], acc[mi][ni], sa[mi], sb[ni]);
+                        acc[mi][ni] = mfma_mx(bfr[ni], af[mi], acc[mi][ni], sb[ni], sa[mi]);
             } else {
 #pragma unroll
                 for (int mi = 0; mi < MT; mi++)
 #pragma unroll
-                    for (int ni = 0; ni < NT; ni++) acc[mi][ni] = mfma(af[mi], bfr[ni], acc[mi][ni]);
+                    for (int ni = 0; ni < NT; ni++) acc[mi][ni] = mfma(bfr[ni], af[mi], acc[mi][ni]);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);            // this wave's loads of the next step have landed
         __syncthreads();                          // ... everyone's, and no wave still reads `buf`
     }
 
-    // epilogue: scales, bias, RNE to bf16, the tile staged in LDS (in two row
-    // halves when the whole tile would not fit: pass q stages the rows of the
-    // waves with wm == q), then 16-byte coalesced stores, 16 lanes per
-    // 128-column part of a row, and that part's sum of the squares of the
-    // stored values when it lies in Q or K
+    // epilogue. The MFMAs above take W as the first operand, so each lane's
+    // accumulators hold, for one row (token) m, four consecutive output columns
+    // 8i + 4(lane / 32) + 0..3 of each 32-column tile (i = 0..3). Scales, bias,
+    // RNE to bf16 in registers; the tile is staged in LDS with 8-byte writes
+    // (in two passes of half the rows of every wave when it would not fit),
+    // then written with 16-byte coalesced stores, 16 lanes per 128-column part
+    // of a row, with that part's sum of the squares of the stored values when
+    // it lies in Q or K.
     constexpr int PASSES = TL::PASSES, RPP = TL::ROWS_PER_PASS, PARTS = BN / 128;
-    uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);           // [RPP][LDC_S]
-    float *row_scale = reinterpret_cast<float *>(lds + RPP * LDC_S * 2);
-    if (p.a_scale && t < BM) {
-        int64_t r = m0 + t;
-        if (r >= p.m) r = p.m - 1;
-        row_scale[t] = p.a_scale[r];
+    constexpr int MT_PASS = MT / PASSES, WROWS = MT_PASS * 32;   // a wave's rows per pass
+    uint8_t *Cs = lds;                                            // [RPP][LDC_S] bf16
+    float *col_bias = reinterpret_cast<float *>(lds + RPP * LDC_S * 2);
+    float *col_scale = col_bias + BN;
+    float *row_scale = col_scale + BN;
+    if (t < BN) {
+        col_bias[t] = pre_b;
+        col_scale[t] = pre_w;
     }
+    if (t < BM) row_scale[t] = pre_a;
     __syncthreads();
-    const uint16_t *bias = reinterpret_cast<const uint16_t *>(p.bias);
-    uint16_t *o_base = reinterpret_cast<uint16_t *>(p.o);
+    const bool scaled = p.a_scale || p.w_scale;
     const int g16 = t >> 4, l16 = t & 15;
-    // finished values, two rows of one column per register (bf16 pairs): the
-    // accumulators are dead from here on
-    uint32_t pk[MT][NT][8];
+    // read-out: per 128-column part of the tile, its place in the output, and
+    // the segment (Q: 0, K: 1, none: -1) and part index of its sums
+    const int rows_in = (int)min((int64_t)BM, p.m - m0);
+    uint16_t *o_tile = reinterpret_cast<uint16_t *>(p.o) + m0 * p.ldo + n0 + l16 * 8;
+    float *const sq_q = p.sumsq + m0 * p.parts, *const sq_k = p.sumsq + (p.m + m0) * p.parts;
+    int part_seg[PARTS], part_idx[PARTS];
+    bool part_in[PARTS];
 #pragma unroll
-    for (int ni = 0; ni < NT; ni++) {
-        const int col = wn * (NT * 32) + ni * 32 + fr;
-        const bool col_in = n0 + col < p.n;
-        float bv = 0.0f, cs = 1.0f;
-        if (bias && col_in) bv = __uint_as_float((uint32_t)bias[n0 + col] << 16);
-        if (p.w_scale && col_in) cs = p.w_scale[n0 + col];
-#pragma unroll
-        for (int mi = 0; mi < MT; mi++) {
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const int row = wm * (MT * 32) + mi * 32 + fc * 4 + (r >> 2) * 8 + (r & 3);
-                float v0 = acc[mi][ni][r], v1 = acc[mi][ni][r + 1];
-                if (p.a_scale) {
-                    v0 *= row_scale[row];
-                    v1 *= row_scale[row + 1];
-                }
-                if (p.w_scale) {
-                    v0 *= cs;
-                    v1 *= cs;
-                }
-                pk[mi][ni][r >> 1] = pack_bf16(v0 + bv, v1 + bv);
-            }
-        }
+    for (int q = 0; q < PARTS; q++) {
+        const int64_t c0 = n0 + q * 128;
+        part_in[q] = c0 < p.n;
+        part_seg[q] = c0 < p.q_cols ? 0 : (c0 < p.q_cols + p.k_cols ? 1 : -1);
+        part_idx[q] = (int)(part_seg[q] == 0 ? c0 / 128 : (c0 - p.q_cols) / 128);
     }
 #pragma unroll
     for (int pass = 0; pass < PASSES; pass++) {
-        if (PASSES == 1 || wm == pass) {
+        if (pass > 0) __syncthreads();              // the previous pass's rows are read out
 #pragma unroll
-            for (int ni = 0; ni < NT; ni++) {
-                const int col = wn * (NT * 32) + ni * 32 + fr;
+        for (int ni = 0; ni < NT; ni++) {
+            const int cb = wn * (NT * 32) + ni * 32 + 4 * fc;       // + 8i: the lane's 4 columns
+            float bv[16], ws[16];
 #pragma unroll
-                for (int mi = 0; mi < MT; mi++) {
+            for (int i = 0; i < 4; i++) {
+                const U4 b4 = ld_lds16(col_bias + cb + 8 * i);
+                bv[4 * i] = __uint_as_float(b4.x);
+                bv[4 * i + 1] = __uint_as_float(b4.y);
+                bv[4 * i + 2] = __uint_as_float(b4.z);
+                bv[4 * i + 3] = __uint_as_float(b4.w);
+            }
+            if (scaled) {
 #pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const int row = wm * (MT * 32) + mi * 32 + fc * 4 + (r >> 2) * 8 + (r & 3) - pass * RPP;
-                        Cs[row * LDC_S + col] = (uint16_t)(pk[mi][ni][r >> 1] & 0xFFFFu);
-                        Cs[(row + 1) * LDC_S + col] = (uint16_t)(pk[mi][ni][r >> 1] >> 16);
-                    }
+                for (int i = 0; i < 4; i++) {
+                    const U4 w4 = ld_lds16(col_scale + cb + 8 * i);
+                    ws[4 * i] = __uint_as_float(w4.x);
+                    ws[4 * i + 1] = __uint_as_float(w4.y);
+                    ws[4 * i + 2] = __uint_as_float(w4.z);
+                    ws[4 * i + 3] = __uint_as_float(w4.w);
+                }
+            }
+#pragma unroll
+            for (int mh = 0; mh < MT_PASS; mh++) {
+                const int mi = pass * MT_PASS + mh;
+                const int srow = wm * WROWS + mh * 32 + fr;            // staged row
+                float v[16];
+#pragma unroll
+                for (int r = 0; r < 16; r++) v[r] = acc[mi][ni][r];
+                if (scaled) {
+                    const float as = row_scale[wm * (MT * 32) + mi * 32 + fr];
+#pragma unroll
+                    for (int r = 0; r < 16; r++) v[r] = v[r] * as * ws[r];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const uint32_t lo = pack_bf16(v[4 * i] + bv[4 * i], v[4 * i + 1] + bv[4 * i + 1]);
+                    const uint32_t hi = pack_bf16(v[4 * i + 2] + bv[4 * i + 2], v[4 * i + 3] + bv[4 * i + 3]);
+                    *reinterpret_cast<uint2 *>(Cs + srow * (LDC_S * 2) + (cb + 8 * i) * 2) = make_uint2(lo, hi);
                 }
             }
         }
         __syncthreads();
+        constexpr int ITERS = RPP * PARTS / (THREADS / 16);
+        static_assert(RPP * PARTS % (THREADS / 16) == 0, "whole read-out iterations");
 #pragma unroll 4
-        for (int rp = g16; rp < RPP * PARTS; rp += THREADS / 16) {
+        for (int it = 0; it < ITERS; it++) {
+            const int rp = g16 + it * (THREADS / 16);
             const int rs = rp / PARTS, part_t = rp % PARTS;   // staged row, 128-column part of the tile
-            const int row = pass * RPP + rs;
-            const int64_t c0 = n0 + part_t * 128;
-            const U4 v = ld_lds16(Cs + rs * LDC_S + part_t * 128 + l16 * 8);
-            const bool ok = m0 + row < p.m;
-            if (ok && c0 < p.n) st_global16(o_base + (m0 + row) * p.ldo + c0 + l16 * 8, v);
-            const float ss = group_sum<16>(sumsq8(v));
-            int seg = -1;
-            int64_t part = 0;
-            if (c0 < p.q_cols) {
-                seg = 0;
-                part = c0 / 128;
-            } else if (c0 < p.q_cols + p.k_cols) {
-                seg = 1;
-                part = (c0 - p.q_cols) / 128;
-            }
-            if (seg >= 0 && ok && l16 == 0) p.sumsq[((int64_t)seg * p.m + m0 + row) * p.parts + part] = ss;
+            const U4 vv = ld_lds16(Cs + rs * (LDC_S * 2) + (part_t * 128 + l16 * 8) * 2);
+            const int row = (rs / WROWS) * (MT * 32) + pass * WROWS + rs % WROWS;   // its row in the tile
+            int seg = part_seg[0], pidx = part_idx[0];
+            bool pin = part_in[0];
+#pragma unroll
+            for (int q = 1; q < PARTS; q++)
+                if (part_t == q) {
+                    seg = part_seg[q];
+                    pidx = part_idx[q];
+                    pin = part_in[q];
+                }
+            const bool ok = row < rows_in;
+            if (ok && pin) st_global16(o_tile + (int64_t)row * p.ldo + part_t * 128, vv);
+            const float ss = group_sum<16>(sumsq8(vv));
+            if (seg >= 0 && ok && l16 == 0) (seg ? sq_k : sq_q)[(int64_t)row * p.parts + pidx] = ss;
         }
-        if (pass + 1 < PASSES) __syncthreads();
     }
 }
 
 }  // namespace
 
 hipError_t proj_launch(ProjParams &p, bool fp8, hipStream_t stream) {
-    // bf16 operands: 256 x 384 tiles; FP8 (with or without MX scales): 256 x 256
-    const int bn = fp8 ? 256 : 384;
+    // bf16 and FP8 ROW_MX operands: 256 x 384 tiles; MXFP8 (whose block scales
+    // also take LDS): 256 x 256
+    const int bn = (fp8 && p.a_bs) ? 256 : 384;
     p.tiles_m = (uint32_t)((p.m + BM - 1) / BM);
     p.tiles_n = (uint32_t)((p.n + bn - 1) / bn);
     const uint64_t tiles = (uint64_t)p.tiles_m * p.tiles_n;
@@ -463,7 +521,7 @@ hipError_t proj_launch(ProjParams &p, bool fp8, hipStream_t stream) {
     if (fp8 && p.a_bs)
         hipLaunchKernelGGL((qkv_proj_kernel<true, true, 256>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
     else if (fp8)
-        hipLaunchKernelGGL((qkv_proj_kernel<true, false, 256>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
+        hipLaunchKernelGGL((qkv_proj_kernel<true, false, 384>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
     else
         hipLaunchKernelGGL((qkv_proj_kernel<false, false, 384>), dim3((uint32_t)grid), dim3(THREADS), 0, stream, p);
     return hipGetLastError();
