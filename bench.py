@@ -65,11 +65,37 @@ KERNEL_SOURCES = {
 }
 
 
+def strip_comments(src):
+    """C/C++ source without its comments and trailing blanks (string and
+    character literals kept), so that an edit of comments alone does not mark
+    the counters taken on the code as stale."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = [ln.rstrip() for ln in "".join(out).split("\n")]
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

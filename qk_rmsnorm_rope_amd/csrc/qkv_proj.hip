@@ -85,8 +85,8 @@ constexpr int MT = BM / WAVES_M / 32;               // 32x32 MFMA tiles per wave
 constexpr int LOADS = (BM / 8) / NWAVES;            // LDS-DMA instructions per wave and k step for A
 constexpr int GROUP_M = 3;
 // The block tile is BM x BN, BN = 256 (wave tiles 128 x 64) or 384 (128 x 96: a
-// fifth fewer LDS and copy bytes per flop; the accumulators then fill the
-// registers two waves per SIMD leave, so only bf16 fragments fit beside them).
+// fifth fewer LDS and copy bytes per flop; the accumulators then fill most of
+// the registers two waves per SIMD leave).
 template <int BN>
 struct Tile {
     static constexpr int NT = BN / WAVES_N / 32;            // 32x32 MFMA tiles per wave along N

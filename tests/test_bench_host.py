@@ -54,3 +54,10 @@ def test_traffic_is_within_a_few_percent_of_the_algorithmic_bytes():
         kernel = WORKLOAD_KERNEL[workload]
         ratio = bench.measured_traffic(kernel, workload) / nbytes
         assert 0.99 < ratio < 1.02, (workload, ratio)
+
+
+def test_source_hash_ignores_comments_but_not_code():
+    src = 'int f(int a) {  // doubles a\n    /* the "result" */\n    return a * 2;   \n}\nconst char *s = "x // y";\n'
+    assert bench.strip_comments(src) == bench.strip_comments(src.replace("doubles a", "twice a"))
+    assert bench.strip_comments(src) != bench.strip_comments(src.replace("a * 2", "a * 3"))
+    assert '"x // y"' in bench.strip_comments(src)
