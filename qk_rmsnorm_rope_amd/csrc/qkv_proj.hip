@@ -155,19 +155,6 @@ __device__ __forceinline__ uint32_t tile_offset(int row, int rows, int64_t pitch
     return (uint32_t)((int64_t)min(row, rows - 1) * pitch + swz(row, slot) * 16);
 }
 
-// Sum of squares of the 8 bf16 values of a 16-byte chunk (fp32).
-__device__ __forceinline__ float sumsq8(const U4 &v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float a = lo_bf16(w[i]), b = hi_bf16(w[i]);
-        s = fmaf(a, a, s);
-        s = fmaf(b, b, s);
-    }
-    return s;
-}
-
 // One MFMA operand of substep kk of a k step: the lane's 16 (bf16) or 32
 // (FP8) bytes of tile row `row`; lanes l and l + 32 hold the two halves of the
 // substep's k range (any split works as long as A and W use the same one,
@@ -425,7 +412,7 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
     // read-out: per 128-column part of the tile, its place in the output, and
     // the segment (Q: 0, K: 1, none: -1) and part index of its sums
     const int rows_in = (int)min((int64_t)BM, p.m - m0);
-    uint16_t *o_tile = reinterpret_cast<uint16_t *>(p.o) + m0 * p.ldo + n0 + l16 * 8;
+    uint16_t *o_lane = reinterpret_cast<uint16_t *>(p.o) + (m0 + g16) * p.ldo + n0 + l16 * 8;
     float *const sq_q = p.sumsq + m0 * p.parts, *const sq_k = p.sumsq + (p.m + m0) * p.parts;
     int part_seg[PARTS], part_idx[PARTS];
     bool part_in[PARTS];
@@ -482,27 +469,27 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
             }
         }
         __syncthreads();
-        constexpr int ITERS = RPP * PARTS / (THREADS / 16);
-        static_assert(RPP * PARTS % (THREADS / 16) == 0, "whole read-out iterations");
-#pragma unroll 4
-        for (int it = 0; it < ITERS; it++) {
-            const int rp = g16 + it * (THREADS / 16);
-            const int rs = rp / PARTS, part_t = rp % PARTS;   // staged row, 128-column part of the tile
-            const U4 vv = ld_lds16(Cs + rs * (LDC_S * 2) + (part_t * 128 + l16 * 8) * 2);
-            const int row = (rs / WROWS) * (MT * 32) + pass * WROWS + rs % WROWS;   // its row in the tile
-            int seg = part_seg[0], pidx = part_idx[0];
-            bool pin = part_in[0];
+        // read-out, part by part: the 32 groups of 16 lanes take staged rows
+        // g16, g16 + 32, ..., so that each lane's row offset is fixed and the
+        // part, the rest of the row and the LDS offset are known at compile time
+        constexpr int RGROUPS = THREADS / 16, RITERS = RPP / RGROUPS;
+        static_assert(RPP % RGROUPS == 0 && WROWS % RGROUPS == 0, "whole read-out iterations");
+        const uint8_t *cs_lane = Cs + g16 * (LDC_S * 2) + l16 * 16;
 #pragma unroll
-            for (int q = 1; q < PARTS; q++)
-                if (part_t == q) {
-                    seg = part_seg[q];
-                    pidx = part_idx[q];
-                    pin = part_in[q];
-                }
-            const bool ok = row < rows_in;
-            if (ok && pin) st_global16(o_tile + (int64_t)row * p.ldo + part_t * 128, vv);
-            const float ss = group_sum<16>(sumsq8(vv));
-            if (seg >= 0 && ok && l16 == 0) (seg ? sq_k : sq_q)[(int64_t)row * p.parts + pidx] = ss;
+        for (int q = 0; q < PARTS; q++) {
+#pragma unroll
+            for (int it = 0; it < RITERS; it++) {
+                // staged row g16 + 32 it is tile row r0 + g16
+                const int r0 = (it * RGROUPS / WROWS) * (MT * 32) + pass * WROWS + (it * RGROUPS) % WROWS;
+                const U4 v = ld_lds16(cs_lane + it * RGROUPS * (LDC_S * 2) + q * 256);
+                const int row = r0 + g16;
+                const bool ok = row < rows_in;
+                if (ok && part_in[q]) st_global16(o_lane + (int64_t)r0 * p.ldo + q * 128, v);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                const float ss = group_sum<16>(sumsq_bf16_words<8>(w, 0.0f));
+                if (part_seg[q] >= 0 && ok && l16 == 0)
+                    (part_seg[q] ? sq_k : sq_q)[(int64_t)row * p.parts + part_idx[q]] = ss;
+            }
         }
     }
 }
