@@ -167,6 +167,30 @@ def test_mxfp8_small_ragged_alone_and_with_row_scales(Q):
     check_dot(o2, _oracle_rows(d, rows, row_scales=True), _fp8_magnitude(d, rows), 384, "mx-small/row-scaled")
 
 
+def test_bf16_with_row_and_channel_scales(Q):
+    """bf16 operands with ROW_MX scales (both, either alone), 300 rows (a ragged
+    row tile): the epilogue's scaled path. Unit scales must give the unscaled
+    output bit for bit (x * 1 * 1 = x in fp32)."""
+    d = _small(seq=300, hidden=256, heads=1, seed=15)
+    g = torch.Generator(device="cuda").manual_seed(15)
+    asc = torch.rand(300, generator=g, device="cuda") + 0.5
+    wsc = torch.rand(384, generator=g, device="cuda") + 0.5
+    rows = np.arange(300)
+    a_h, w_h, b_h = host(d["a"]), host(d["w"]), host(d["bias"])
+    for name, sa, sw in (("both", asc, wsc), ("row", asc, None), ("channel", None, wsc)):
+        out, s = Q.qkv_projection(d["a"], d["w"], d["bias"], a_scale=sa, w_scale=sw, q_cols=128, k_cols=128)
+        torch.cuda.synchronize()
+        _, ref = oracle.linear(a_h, w_h, oracle.BF16, bias=b_h, bias_dtype=oracle.BF16,
+                               a_scale=None if sa is None else sa.cpu().numpy(),
+                               w_scale=None if sw is None else sw.cpu().numpy())
+        check_float(out, ref, f"bf16-scaled-{name}/out")
+        _check_sums(out, s, 128, 128, f"bf16-scaled-{name}")
+    plain, _ = Q.qkv_projection(d["a"], d["w"], d["bias"])
+    ones, _ = Q.qkv_projection(d["a"], d["w"], d["bias"], a_scale=torch.ones_like(asc), w_scale=torch.ones_like(wsc))
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), ones.view(torch.int16))
+
+
 def test_strided_operands_and_output(Q):
     """Row strides larger than the rows: a slice of a wider activation buffer
     and an output written into a wider buffer."""
