@@ -9,8 +9,9 @@
 // norm, accumulates each token's sum(x^2) over the Q and the K segment while
 // the finished output tile is copied out (Design section 1, step a), so that
 // only the apply pass (step c) re-reads Q and K. Here the copy-out is the
-// GEMM epilogue: each output tile's Q or K columns add one partial sum per row
-// to a [segment][part][row] array, and the apply kernel adds the parts.
+// GEMM epilogue: each 128-column part of an output tile that lies in Q or K
+// writes one partial sum per row to a [segment][row][part] array (token-major,
+// so the apply kernel loads a row's parts together and adds them).
 //
 // MI355X design:
 //   * 256 x 384 (bf16, FP8 ROW_MX) or 256 x 256 (MXFP8) output tile per
@@ -40,10 +41,10 @@
 //     register: 8 % faster than 64-bit per-lane addresses on the bf16 tile):
 //     each wave instruction fills 8 rows of 128 bytes, and a 16-byte chunk c
 //     of row r sits in slot c ^ ((r >> 1) & 7), so the fragment reads of 16
-//     consecutive rows hit 16 disjoint bank groups; two k-step buffers (128 KB,
-//     160 KB for the 384-wide tile)
-//     let the next step's loads run under the current step's MFMAs, with one
-//     barrier per k step;
+//     consecutive rows hit 16 disjoint bank groups; two k-step buffers (160 KB
+//     for the 384-wide tile, 128 KB plus the block scales for MXFP8) let the
+//     next step's loads run under the current step's MFMAs, with one barrier
+//     per k step;
 //   * workgroups go round-robin over the 8 XCDs; each XCD takes a contiguous
 //     range of tiles ordered in groups of 3 row-tiles, row-tile fastest, so
 //     the ~32 workgroups running together on one XCD cover 3 row-tiles x ~11
@@ -52,16 +53,19 @@
 //     groups (each A row-tile re-read by few waves of column-tiles, the
 //     weight re-read from the MALL more often) are fastest: measured on
 //     Wan2.2, groups of 2 / 3 / 4 / 6 / 8 row-tiles take 9.85 / 9.77 / 9.80 /
-//     9.90 / 9.95 ms (bf16) and 5.04 / 5.03 / 5.10 / 5.31 / 5.48 ms (FP8);
+//     9.90 / 9.95 ms (bf16) and 5.04 / 5.03 / 5.10 / 5.31 / 5.48 ms (FP8, then
+//     on 256-wide tiles);
 //   * the MFMAs take W as the first operand (they compute the transposed
 //     tile), so each lane's accumulators hold four consecutive output columns
 //     of one row per 8-column group: the epilogue applies scales and bias
 //     from LDS copies (loaded before the k loop), rounds to bf16 and stages
 //     the tile through LDS with 8-byte writes (in two passes of half of every
-//     wave's rows for the 384-wide tile), then writes it with 16-byte stores
-//     and takes the sums of squares from the rounded values (the values the
-//     apply pass reads back) with 16-lane DPP reductions, one per 128-column
-//     part of a row. With the accumulators in the other layout (one column,
+//     wave's rows for the 384-wide tile), then reads it out part by part
+//     (each 16-lane group a fixed row offset, so the addresses are constants)
+//     with 16-byte stores, and takes the sums of squares from the rounded
+//     values (the values the apply pass reads back) with v_dot2 on bf16 pairs
+//     and 16-lane DPP reductions, one per 128-column part of a row. With the
+//     accumulators in the other layout (one column,
 //     four rows per lane) the staging took 2-byte writes and the packing
 //     per-element scale selects: measured on Wan2.2, this layout makes the
 //     projection 2-3 % faster with bit-identical outputs.
