@@ -46,15 +46,16 @@
 //     next step's loads run under the current step's MFMAs, with one barrier
 //     per k step;
 //   * workgroups go round-robin over the 8 XCDs; each XCD takes a contiguous
-//     range of tiles ordered in groups of 3 row-tiles, row-tile fastest, so
-//     the ~32 workgroups running together on one XCD cover 3 row-tiles x ~11
+//     range of tiles ordered in groups of 4 row-tiles, row-tile fastest, so
+//     the ~32 workgroups running together on one XCD cover 4 row-tiles x 8
 //     column-tiles and share each k step of them through its L2. The weight
 //     (157 MB bf16) stays in the MALL while A streams from HBM, so narrow
 //     groups (each A row-tile re-read by few waves of column-tiles, the
 //     weight re-read from the MALL more often) are fastest: measured on
-//     Wan2.2, groups of 2 / 3 / 4 / 6 / 8 row-tiles take 9.85 / 9.77 / 9.80 /
-//     9.90 / 9.95 ms (bf16) and 5.04 / 5.03 / 5.10 / 5.31 / 5.48 ms (FP8, then
-//     on 256-wide tiles);
+//     Wan2.2 with this kernel, groups of 2 / 3 / 4 / 5 / 6 row-tiles take
+//     9.03 / 9.10-9.18 / 8.97-9.02 / 9.16-9.29 / 9.27-9.30 ms (bf16),
+//     4.61-4.62 / 4.61-4.62 / 4.53-4.58 / 4.57-4.58 / 4.61 ms (FP8) and
+//     5.11 / 5.05-5.09 / 5.01-5.05 / 5.46-5.48 / 5.36-5.41 ms (MXFP8);
 //   * the MFMAs take W as the first operand (they compute the transposed
 //     tile), so each lane's accumulators hold four consecutive output columns
 //     of one row per 8-column group: the epilogue applies scales and bias
@@ -87,7 +88,7 @@ constexpr int THREADS = 64 * WAVES_M * WAVES_N;
 constexpr int NWAVES = WAVES_M * WAVES_N;
 constexpr int MT = BM / WAVES_M / 32;               // 32x32 MFMA tiles per wave along M
 constexpr int LOADS = (BM / 8) / NWAVES;            // LDS-DMA instructions per wave and k step for A
-constexpr int GROUP_M = 3;
+constexpr int GROUP_M = 4;
 // The block tile is BM x BN, BN = 256 (wave tiles 128 x 64) or 384 (128 x 96: a
 // fifth fewer LDS and copy bytes per flop; the accumulators then fill most of
 // the registers two waves per SIMD leave).
