@@ -23,8 +23,8 @@
 //     block scales need LDS the wider tile's two 80 KB k-step buffers leave no
 //     room for):
 //     v_mfma_f32_32x32x16_bf16 (on the 384-wide bf16 tile v_mfma_f32_16x16x32_bf16,
-//     8 x 6 per wave, the W fragments of a substep held and two A fragments in
-//     flight: 2 % faster, bit-identical), or for FP8 v_mfma_scale_f32_32x32x64_f8f6f4,
+//     8 x 6 per wave, the W fragments of a substep held and four A fragments in
+//     flight: 3 % faster, bit-identical), or for FP8 v_mfma_scale_f32_32x32x64_f8f6f4,
 //     whose per-lane scale operands carry the MX block scales (a substep's
 //     64 k values are two MX blocks; lane l passes the scale of row l % 32's
 //     block l / 32, and each lane holds 16 values of each block, the layout
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
     };
 
     // bf16 on the 384-wide tile: 16 x 16 x 32 MFMAs, 8 x 6 of them per wave (the
-    // same 128 x 96 wave tile; 2 % faster than 32 x 32 x 16 on Wan2.2, bit-identical)
+    // same 128 x 96 wave tile; 3 % faster than 32 x 32 x 16 on Wan2.2, bit-identical)
     constexpr bool M16 = !FP8 && BN == 384;
     f32x16_t acc[M16 ? 1 : MT][M16 ? 1 : NT];
     f32x4_t acc16[M16 ? 8 : 1][M16 ? 6 : 1];
@@ -374,21 +374,21 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
                 const int row = wn * 96 + ni * 16 + r16;
                 b16[ni] = __builtin_bit_cast(bf16x8_t, ld_lds16(bs + row * ROW_BYTES + swz(row, kk * 4 + c16) * 16));
             }
-            bf16x8_t a_cur, a_next;
-            {
-                const int row = wm * 128 + r16;
-                a_cur = __builtin_bit_cast(bf16x8_t, ld_lds16(as + row * ROW_BYTES + swz(row, kk * 4 + c16) * 16));
-            }
+            // A fragments read three row blocks ahead of their MFMAs (four in flight)
+            auto rda = [&](int mi) {
+                const int row = wm * 128 + mi * 16 + r16;
+                return __builtin_bit_cast(bf16x8_t, ld_lds16(as + row * ROW_BYTES + swz(row, kk * 4 + c16) * 16));
+            };
+            bf16x8_t a0 = rda(0), a1 = rda(1), a2 = rda(2), a3;
 #pragma unroll
             for (int mi = 0; mi < 8; mi++) {
-                if (mi + 1 < 8) {
-                    const int row = wm * 128 + (mi + 1) * 16 + r16;
-                    a_next = __builtin_bit_cast(bf16x8_t, ld_lds16(as + row * ROW_BYTES + swz(row, kk * 4 + c16) * 16));
-                }
+                if (mi + 3 < 8) a3 = rda(mi + 3);
 #pragma unroll
                 for (int ni = 0; ni < 6; ni++)
-                    acc16[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b16[ni], a_cur, acc16[mi][ni], 0, 0, 0);
-                a_cur = a_next;
+                    acc16[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b16[ni], a0, acc16[mi][ni], 0, 0, 0);
+                a0 = a1;
+                a1 = a2;
+                a2 = a3;
             }
         }
       } else if constexpr (FP8 && !MX && BN == 384) {
