@@ -47,7 +47,9 @@
 //     consecutive rows hit 16 disjoint bank groups; two k-step buffers (160 KB
 //     for the 384-wide tile, 128 KB plus the block scales for MXFP8) let the
 //     next step's loads run under the current step's MFMAs, with one barrier
-//     per k step;
+//     per k step; with FP8 operands the four waves of one half issue the
+//     copies of both waves on their SIMD, so that the other keeps the matrix
+//     core busy meanwhile;
 //   * workgroups go round-robin over the 8 XCDs; each XCD takes a contiguous
 //     range of tiles ordered in groups of 4 row-tiles, row-tile fastest, so
 //     the ~32 workgroups running together on one XCD cover 4 row-tiles x 8
@@ -264,6 +266,36 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
 #pragma unroll
         for (int j = 0; j < LOADS_W; j++) copy16_to_lds(rw, bs + (LOADS_W * wave + j) * 8 * ROW_BYTES, w_off[j], k0);
     };
+    // FP8 operands: in the k loop, wave w < 4 also issues the copies of wave
+    // w + 4, which shares its SIMD, so that one of the two keeps the matrix core
+    // busy while the other's copies queue (Wan2.2: MXFP8 -4 %, FP8 ROW_MX -1 %;
+    // bf16 +1 %, so it keeps one share per wave). The partner's rows lie 32 L
+    // rows further; rows past the tile's valid ones read the last valid row's
+    // last chunk (in bounds for every k step, never stored).
+    constexpr bool PAIR_COPY = FP8;
+    [[maybe_unused]] const bool copier = !PAIR_COPY || wave < NWAVES / 2;
+    const uint32_t pair_a = (uint32_t)(8 * LOADS * (NWAVES / 2) * a_pitch);
+    const uint32_t pair_w = (uint32_t)(8 * LOADS_W * (NWAVES / 2) * w_pitch);
+    const uint32_t last_a = (uint32_t)((int64_t)(a_rows - 1) * a_pitch + ROW_BYTES - 16);
+    const uint32_t last_w = (uint32_t)((int64_t)(w_rows - 1) * w_pitch + ROW_BYTES - 16);
+    auto issue_pair_loads = [&](int ks, int buf) {
+        uint8_t *as = lds + buf * STAGE_BYTES;
+        uint8_t *bs = as + BM * ROW_BYTES;
+        const int k0 = ks * ROW_BYTES;
+        const int pw = wave + NWAVES / 2;
+        uint32_t da = pair_a, dw = pair_w, ma = last_a, mw = last_w;
+        asm volatile("" : "+s"(da), "+s"(dw), "+s"(ma), "+s"(mw));   // partner offsets formed here, not held
+#pragma unroll
+        for (int j = 0; j < LOADS; j++) copy16_to_lds(ra, as + (LOADS * wave + j) * 8 * ROW_BYTES, a_off[j], k0);
+#pragma unroll
+        for (int j = 0; j < LOADS; j++)
+            copy16_to_lds(ra, as + (LOADS * pw + j) * 8 * ROW_BYTES, min(a_off[j] + da, ma), k0);
+#pragma unroll
+        for (int j = 0; j < LOADS_W; j++) copy16_to_lds(rw, bs + (LOADS_W * wave + j) * 8 * ROW_BYTES, w_off[j], k0);
+#pragma unroll
+        for (int j = 0; j < LOADS_W; j++)
+            copy16_to_lds(rw, bs + (LOADS_W * pw + j) * 8 * ROW_BYTES, min(w_off[j] + dw, mw), k0);
+    };
 
     // bf16 on the 384-wide tile: 16 x 16 x 32 MFMAs, 8 x 6 of them per wave (the
     // same 128 x 96 wave tile; 3 % faster than 32 x 32 x 16 on Wan2.2, bit-identical)
@@ -346,7 +378,11 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
     __syncthreads();
     for (int ks = 0; ks < ksteps; ks++) {
         const int buf = ks & 1;
-        if (ks + 1 < ksteps) issue_loads(ks + 1, buf ^ 1);
+        if constexpr (PAIR_COPY) {
+            if (ks + 1 < ksteps && copier) issue_pair_loads(ks + 1, buf ^ 1);
+        } else if (ks + 1 < ksteps) {
+            issue_loads(ks + 1, buf ^ 1);
+        }
         uint32_t asw[MX ? MT : 1], wsw[MX ? NT : 1];   // this k step's scale words of the lane's rows
         if constexpr (MX) {
             const int g = ks / MX_GROUP, j = ks % MX_GROUP;
