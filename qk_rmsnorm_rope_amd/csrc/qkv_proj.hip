@@ -271,7 +271,8 @@ __global__ __launch_bounds__(THREADS) void qkv_proj_kernel(ProjParams p) {
     // busy while the other's copies queue (Wan2.2: MXFP8 -4 %, FP8 ROW_MX -1 %;
     // bf16 +1 %, so it keeps one share per wave). The partner's rows lie 32 L
     // rows further; rows past the tile's valid ones read the last valid row's
-    // last chunk (in bounds for every k step, never stored).
+    // last chunk (in bounds for every k step, never stored). With row pitches
+    // of at most 4 MiB the sums stay below 2^32 (at most 575 rows of pitch).
     constexpr bool PAIR_COPY = FP8;
     [[maybe_unused]] const bool copier = !PAIR_COPY || wave < NWAVES / 2;
     const uint32_t pair_a = (uint32_t)(8 * LOADS * (NWAVES / 2) * a_pitch);
