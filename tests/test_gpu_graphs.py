@@ -144,14 +144,14 @@ def test_across_heads_graph_replays(Q):
         _same(outs["graph"], outs["eager"], f"replay {r}")
 
 
-@pytest.mark.parametrize("operands", ["bf16", "fp8"])
+@pytest.mark.parametrize("operands", ["bf16", "fp8", "mxfp8"])
 def test_projection_then_apply_graph_replays(Q, operands):
     """QKV projection with sums, then the apply pass, captured as one graph
-    (Wan2.2 width, 300 tokens); bf16 operands, and FP8 with row / channel
-    scales (a kernel that spills two registers per lane to the private
-    segment, which every replay needs too)."""
-    fp8 = operands == "fp8"
-    d = W.make_qkv_projection(W.WAN22_QKV_PROJ_FP8 if fp8 else W.WAN22_QKV_PROJ, device="cuda", seq=300)
+    (Wan2.2 width, 300 tokens); bf16 operands, FP8 with row / channel scales
+    (a kernel that spills two registers per lane to the private segment,
+    which every replay needs too) and MXFP8 with block scales."""
+    cfg = {"bf16": W.WAN22_QKV_PROJ, "fp8": W.WAN22_QKV_PROJ_FP8, "mxfp8": W.WAN22_QKV_PROJ_MXFP8}[operands]
+    d = W.make_qkv_projection(cfg, device="cuda", seq=300)
     S, nq, nk, hd = 300, 40, 40, 128
     bufs = {w: (torch.zeros(S, d["out_features"], dtype=torch.bfloat16, device="cuda"),
                 torch.zeros(2, S, 40, dtype=torch.float32, device="cuda")) for w in ("graph", "eager")}
@@ -162,9 +162,13 @@ def test_projection_then_apply_graph_replays(Q, operands):
         k = out[:, nq * hd: (nq + nk) * hd].unflatten(-1, (nk, hd)).unsqueeze(0)
 
         def make(stream=None):
-            if fp8:
+            if operands == "fp8":
                 proj = Q.prepare_qkv_projection(d["a8"], d["w8"], d["bias"], out=out, q_cols=5120, k_cols=5120,
                                                 sumsq=sums, a_scale=d["a_scale"], w_scale=d["w_scale"],
+                                                stream=stream)
+            elif operands == "mxfp8":
+                proj = Q.prepare_qkv_projection(d["a8"], d["w8"], d["bias"], out=out, q_cols=5120, k_cols=5120,
+                                                sumsq=sums, a_block_scale=d["a_bs"], w_block_scale=d["w_bs"],
                                                 stream=stream)
             else:
                 proj = Q.prepare_qkv_projection(d["a"], d["w"], d["bias"], out=out, q_cols=5120, k_cols=5120,
@@ -181,10 +185,11 @@ def test_projection_then_apply_graph_replays(Q, operands):
     eager = make_for("eager")()
     gen = torch.Generator(device="cuda").manual_seed(9)
     for r in range(REPLAYS):
-        if fp8:        # new codes and row scales, written eagerly (rows rotated)
+        if operands != "bf16":    # new codes and row scales, written eagerly (rows rotated)
             codes = d["a8"].view(torch.uint8)
             codes.copy_(codes.roll(r + 1, 0))
-            d["a_scale"].copy_(d["a_scale"].roll(r + 1, 0))
+            row_scales = d["a_scale"] if operands == "fp8" else d["a_bs"]
+            row_scales.copy_(row_scales.roll(r + 1, 0))
         else:
             d["a"].copy_(torch.randn(d["a"].shape, generator=gen, device="cuda").to(d["a"].dtype))
         torch.cuda.synchronize()
