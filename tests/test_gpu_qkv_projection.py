@@ -206,12 +206,16 @@ def test_strided_operands_and_output(Q):
     assert bool((big[:, :64] == 7.0).all()) and bool((big[:, 448:] == 7.0).all())
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-def test_row_pitch_at_the_limit(Q, fp8):
+@pytest.mark.parametrize("mode", ["bf16", "fp8", "mxfp8"])
+def test_row_pitch_at_the_limit(Q, mode):
     """A and W with row pitches of exactly 4 MiB (the largest the entry point
     accepts): the tile copies' 32-bit lane offsets then reach ~1.5 GiB within a
-    tile. 300 rows (a partial second row-tile), 384 output columns."""
-    cfg = W.WAN22_QKV_PROJ_FP8 if fp8 else W.WAN22_QKV_PROJ
+    tile, and with FP8 operands the copies a wave issues for its SIMD partner
+    (rows 128 or 192 further) ~2.3 GiB before their clamp. 300 rows (a partial
+    second row-tile), 384 output columns (a partial tile of the 256-wide MXFP8
+    kernel)."""
+    cfg = {"bf16": W.WAN22_QKV_PROJ, "fp8": W.WAN22_QKV_PROJ_FP8, "mxfp8": W.WAN22_QKV_PROJ_MXFP8}[mode]
+    fp8 = mode != "bf16"
     d = W.make_qkv_projection(cfg, device="cuda", seq=300, hidden=256, n_q_heads=1, n_k_heads=1, seed=19)
     a_src, w_src = (d["a8"], d["w8"]) if fp8 else (d["a"], d["w"])
     pitch = (4 << 20) // a_src.element_size()
@@ -219,10 +223,15 @@ def test_row_pitch_at_the_limit(Q, fp8):
     w = torch.empty_strided(tuple(w_src.shape), (pitch, 1), dtype=w_src.dtype, device="cuda")
     a.copy_(a_src)
     w.copy_(w_src)
-    sc = dict(a_scale=d["a_scale"], w_scale=d["w_scale"]) if fp8 else {}
+    if mode == "fp8":
+        sc = dict(a_scale=d["a_scale"], w_scale=d["w_scale"])
+    elif mode == "mxfp8":
+        sc = dict(a_block_scale=d["a_bs"], w_block_scale=d["w_bs"])
+    else:
+        sc = {}
     out, s = Q.qkv_projection(a, w, d["bias"], q_cols=128, k_cols=128, **sc)
     torch.cuda.synchronize()
-    _check_out(d, out, np.arange(300), f"pitch-limit/{'fp8' if fp8 else 'bf16'}")
+    _check_out(d, out, np.arange(300), f"pitch-limit/{mode}")
     _check_sums(out, s, 128, 128, "pitch-limit")
     del a, w
     torch.cuda.empty_cache()
